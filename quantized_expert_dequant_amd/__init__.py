@@ -1,0 +1,177 @@
+"""Python binding of libmoe.so: quantized MoE decode on AMD Instinct MI355X (gfx950).
+
+Argument marshalling only.  Every step of the decode path runs in the HIP
+kernels behind the C ABI declared in ``include/moe.h``; this module turns torch
+tensors (device memory allocated by PyTorch) into pointers and passes the
+current HIP stream.  There is no CPU fallback: if ``libmoe.so`` is missing the
+import of any entry point raises.
+"""
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe.h")
+
+MOE_OK = 0
+MOE_EINVAL = -1
+MOE_EUNSUPPORTED = -2
+MOE_EHIP = -3
+
+KERNEL_ROUTER = 1
+KERNEL_GATEUP = 2
+KERNEL_DOWN = 3
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (code %d)" % (msg, code))
+        self.code = code
+
+
+class LayerDesc(ctypes.Structure):
+    """moe_layer_desc (include/moe.h)."""
+    _fields_ = [("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("experts", ctypes.c_void_p), ("w_router", ctypes.c_void_p),
+                ("logit_bias", ctypes.c_void_p), ("shared_weight", ctypes.c_float),
+                ("renormalize", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmoe.so is not built (%s); run `python -m quantized_expert_dequant_amd.build`"
+                               % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        i32, sz, vp, f32 = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+        dp = ctypes.POINTER(LayerDesc)
+        sig = {
+            "moe_expert_record_bytes": (sz, [i32, i32, i32, i32]),
+            "moe_workspace_bytes": (sz, [dp, i32]),
+            "moe_route_workspace_bytes": (sz, [i32, i32, i32]),
+            "moe_stack_extra_bytes": (sz, [i32, i32]),
+            "moe_pack_experts": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]),
+            "moe_dequant_expert": (i32, [i32, i32, i32, i32, vp, vp, vp]),
+            "moe_route_topk": (i32, [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]),
+            "moe_expert_ffn_q4": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_expert_ffn_q2": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_layer_decode": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_rmsnorm": (i32, [vp, i32, i32, f32, vp, vp]),
+            "moe_stack_decode": (i32, [dp, i32, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
+            "moe_set_timing_events": (i32, [i32, vp, vp]),
+            "moe_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_functions():
+    """Names of the functions include/moe.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def last_error():
+    return lib().moe_last_error().decode()
+
+
+def _check(rc):
+    if rc != MOE_OK:
+        raise MoeError(rc, last_error())
+    return rc
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_desc(H, I, E, K, bits, experts, w_router, logit_bias=None, shared_weight=1.0, renormalize=True, group=64):
+    return LayerDesc(H, I, E, K, bits, group, _p(experts), _p(w_router), _p(logit_bias), float(shared_weight),
+                     int(bool(renormalize)))
+
+
+def record_bytes(bits, H, I, group=64):
+    return lib().moe_expert_record_bytes(bits, H, I, group)
+
+
+def workspace_bytes(desc, B):
+    return lib().moe_workspace_bytes(ctypes.byref(desc), B)
+
+
+def route_workspace_bytes(B, E, K):
+    return lib().moe_route_workspace_bytes(B, E, K)
+
+
+def stack_extra_bytes(B, H):
+    return lib().moe_stack_extra_bytes(B, H)
+
+
+def pack_experts(bits, H, I, n, gate, up, down, scales, biases, slab, first, stream=None, group=64):
+    return _check(lib().moe_pack_experts(bits, H, I, group, n, _p(gate), _p(up), _p(down), _p(scales), _p(biases),
+                                         _p(slab), first, _stream(stream)))
+
+
+def dequant_expert(bits, H, I, record, W_out, stream=None, group=64):
+    return _check(lib().moe_dequant_expert(bits, H, I, group, _p(record), _p(W_out), _stream(stream)))
+
+
+def route_topk(x, B, w_router, logit_bias, H, E, K, idx_out, w_out, ws, ws_bytes, renormalize=True, stream=None):
+    return _check(lib().moe_route_topk(_p(x), B, _p(w_router), _p(logit_bias), H, E, K, int(bool(renormalize)),
+                                       _p(idx_out), _p(w_out), _p(ws), ws_bytes, _stream(stream)))
+
+
+def expert_ffn(desc, x, B, idx, w, y_out, ws, ws_bytes, stream=None):
+    fn = lib().moe_expert_ffn_q4 if desc.bits == 4 else lib().moe_expert_ffn_q2
+    return _check(fn(ctypes.byref(desc), _p(x), B, _p(idx), _p(w), _p(y_out), _p(ws), ws_bytes, _stream(stream)))
+
+
+def expert_ffn_q4(desc, x, B, idx, w, y_out, ws, ws_bytes, stream=None):
+    return _check(lib().moe_expert_ffn_q4(ctypes.byref(desc), _p(x), B, _p(idx), _p(w), _p(y_out), _p(ws),
+                                          ws_bytes, _stream(stream)))
+
+
+def expert_ffn_q2(desc, x, B, idx, w, y_out, ws, ws_bytes, stream=None):
+    return _check(lib().moe_expert_ffn_q2(ctypes.byref(desc), _p(x), B, _p(idx), _p(w), _p(y_out), _p(ws),
+                                          ws_bytes, _stream(stream)))
+
+
+def layer_decode(desc, x, B, y_out, idx_out, w_out, ws, ws_bytes, stream=None):
+    return _check(lib().moe_layer_decode(ctypes.byref(desc), _p(x), B, _p(y_out), _p(idx_out), _p(w_out), _p(ws),
+                                         ws_bytes, _stream(stream)))
+
+
+def rmsnorm(y, B, H, eps, x_out, stream=None):
+    return _check(lib().moe_rmsnorm(_p(y), B, H, eps, _p(x_out), _stream(stream)))
+
+
+def stack_decode(descs, x, B, eps, y_out, idx_out, w_out, ws, ws_bytes, stream=None):
+    arr = (LayerDesc * len(descs))(*descs)
+    return _check(lib().moe_stack_decode(arr, len(descs), _p(x), B, eps, _p(y_out), _p(idx_out), _p(w_out), _p(ws),
+                                         ws_bytes, _stream(stream)))
+
+
+def set_timing_events(kernel, start_event, stop_event):
+    """Record raw hipEvent_t handles (ints) around every launch of `kernel`; None, None clears."""
+    return _check(lib().moe_set_timing_events(kernel, start_event, stop_event))

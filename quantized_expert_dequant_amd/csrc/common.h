@@ -1,0 +1,175 @@
+// common.h - packed expert layout and device helpers shared by the gfx950 kernels.
+//
+// Packed record of one expert (bits = 4 or 2, G_h = H/64, G_i = I/64 groups per row),
+// byte-for-byte the same size as the canonical expert:
+//   [gu_codes]  I row pairs, each [gate row codes (H*bits/8 B) | up row codes (H*bits/8 B)]
+//   [gu_sb]     I x G_h entries of 8 B: bf16 (gate scale, gate bias, up scale, up bias)
+//   [d_codes]   H rows of I*bits/8 B
+//   [d_sb]      H x G_i entries of 4 B: bf16 (scale, bias)
+// Inside a row the codes of group g are split into 16-byte chunks; chunk j of
+// group g sits at chunk position j*G + g (4-bit: 2 chunks per group, 2-bit: 1),
+// so that 64 lanes working on 64 consecutive groups issue fully contiguous
+// 16-byte loads.  Within a chunk the codes keep the canonical order (low bits =
+// lower column), which puts columns (c, c+4) (4-bit) or (c, c+8) (2-bit) in the
+// two 16-bit halves of a dword: masking one field of each half and OR-ing in the
+// fp16 pattern of 1024 turns two codes into the fp16 pair (1024 + t*q_a, 1024 + t*q_b)
+// with t a power of two, ready for v_dot2 against an fp16 pair of activations.
+//
+// Activation operand ("prep") of a vector v split in groups of 64:
+//   q  [8][G] uint4: 32 fp16 pairs per group; pair p of group g is element p%4
+//                    of uint4 (p/4)*G + g.  Pair p holds v_h at columns
+//                    4-bit: (8*(p/4) + p%4, +4);  2-bit: (16*(p/8) + p%8, +8),
+//                    where v_h = fp16(v * 2^-e_g) with a power-of-two per-group scale.
+//   st [G]    float4: (C_g, S_g, 2^e_g, 0) with S_g = sum of v over the group and
+//                    C_g = 1024 * sum_p (v_h pair sum) / t(p) + mid * sum_c (v_h - v 2^-e_g):
+//                    the offset the fp16 code patterns add to the dot products, plus
+//                    the code midpoint (7.5 or 1.5) times the group's rounding error.
+// Per group and row:  sum_c (s*q_c + b) v_c ~= s * 2^e_g * (sum_t acc_t / t - C_g) + b * S_g,
+// where sum_t acc_t / t - C_g = sum_c (q_c - mid) v_h,c + mid * sum_c v_c 2^-e_g: the
+// fp16 rounding of v only meets the zero-mean part of the codes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+struct Layout {
+    int bits, H, I, Gh, Gi;
+    long long hb, ib;  // code bytes per gate/up row and per down row
+    long long off_gu_sb, off_d_codes, off_d_sb, record;
+};
+
+__host__ __device__ inline Layout make_layout(int bits, int H, int I)
+{
+    Layout L;
+    L.bits = bits;
+    L.H = H;
+    L.I = I;
+    L.Gh = H / 64;
+    L.Gi = I / 64;
+    L.hb = (long long)H * bits / 8;
+    L.ib = (long long)I * bits / 8;
+    L.off_gu_sb = 2LL * I * L.hb;
+    L.off_d_codes = L.off_gu_sb + 8LL * I * L.Gh;
+    L.off_d_sb = L.off_d_codes + (long long)H * L.ib;
+    L.record = L.off_d_sb + 4LL * H * L.Gi;
+    return L;
+}
+
+// lanes cooperating on one row: G rounded up to a power of two, at most 64
+__host__ __device__ inline int lanes_per_row(int G)
+{
+    int l = 1;
+    while (l < G && l < 64) l <<= 1;
+    return l;
+}
+
+__device__ inline float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Opaque register constants: keeps the masks in SGPRs and the fp16 pattern in a
+// VGPR so each code pair costs a single v_and_or_b32 (gfx9 VOP3 takes no literals).
+struct Masks {
+    uint32_t magic, m4a, m4b, m2[5];
+};
+
+__device__ inline Masks load_masks()
+{
+    Masks m;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m.magic));
+    asm volatile("s_mov_b32 %0, 0xf000f" : "=s"(m.m4a));
+    asm volatile("s_mov_b32 %0, 0xf000f0" : "=s"(m.m4b));
+    asm volatile("s_mov_b32 %0, 0x30003" : "=s"(m.m2[0]));
+    asm volatile("s_mov_b32 %0, 0xc000c" : "=s"(m.m2[1]));
+    asm volatile("s_mov_b32 %0, 0x300030" : "=s"(m.m2[2]));
+    asm volatile("s_mov_b32 %0, 0xc000c0" : "=s"(m.m2[3]));
+    asm volatile("s_mov_b32 %0, 0x3000300" : "=s"(m.m2[4]));
+    return m;
+}
+
+__device__ inline float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
+}
+
+// 4-bit: one group = two 16-byte chunks c0 (columns 0..31) and c1 (32..63);
+// xp = the group's 8 uint4 of activation pairs.  Returns sum_t acc_t / t.
+__device__ inline float group_dot_q4(const Masks& M, uint4 c0, uint4 c1, const uint4* xp)
+{
+    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    float a1 = 0.f, a16 = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+        const uint32_t v = w[d], v8 = v >> 8;
+        const uint4 x = xp[d];
+        a1 = dot2((v & M.m4a) | M.magic, x.x, a1);
+        a16 = dot2((v & M.m4b) | M.magic, x.y, a16);
+        a1 = dot2((v8 & M.m4a) | M.magic, x.z, a1);
+        a16 = dot2((v8 & M.m4b) | M.magic, x.w, a16);
+    }
+    return fmaf(a16, 0.0625f, a1);
+}
+
+// 2-bit: one group = one 16-byte chunk (4 dwords of 16 codes).
+__device__ inline float group_dot_q2(const Masks& M, uint4 c0, const uint4* xp)
+{
+    const uint32_t w[4] = {c0.x, c0.y, c0.z, c0.w};
+    float a1 = 0.f, a4 = 0.f, a16 = 0.f, a64 = 0.f, a256 = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t v = w[d], v10 = v >> 10;
+        const uint4 x0 = xp[2 * d], x1 = xp[2 * d + 1];
+        a1 = dot2((v & M.m2[0]) | M.magic, x0.x, a1);
+        a4 = dot2((v & M.m2[1]) | M.magic, x0.y, a4);
+        a16 = dot2((v & M.m2[2]) | M.magic, x0.z, a16);
+        a64 = dot2((v & M.m2[3]) | M.magic, x0.w, a64);
+        a256 = dot2((v & M.m2[4]) | M.magic, x1.x, a256);
+        a1 = dot2((v10 & M.m2[0]) | M.magic, x1.y, a1);
+        a4 = dot2((v10 & M.m2[1]) | M.magic, x1.z, a4);
+        a16 = dot2((v10 & M.m2[2]) | M.magic, x1.w, a16);
+    }
+    float r = fmaf(a256, 1.f / 256.f, a64 * (1.f / 64.f));
+    r = fmaf(a16, 1.f / 16.f, r);
+    r = fmaf(a4, 0.25f, r);
+    return r + a1;
+}
+
+// divisor t of pair p (see the prep layout above)
+__device__ inline float pair_class_inv(int bits, int p)
+{
+    if (bits == 4) return (p & 1) ? 0.0625f : 1.f;
+    switch (p & 7) {
+    case 0: case 5: return 1.f;
+    case 1: case 6: return 0.25f;
+    case 2: case 7: return 0.0625f;
+    case 3: return 1.f / 64.f;
+    default: return 1.f / 256.f;
+    }
+}
+
+template <typename T>
+__device__ inline T wave_sum(T v, int width = 64)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        if (off < width) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ inline float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// sum across groups of `width` consecutive lanes (width a power of two <= 64)
+__device__ inline float lane_group_sum(float v, int width)
+{
+    for (int off = width >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace moe

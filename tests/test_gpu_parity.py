@@ -1,0 +1,228 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bars: expert indices and grouping bit-exact; routing weights within 1e-6
+relative; layer outputs within max|dy| / max|y_ref| <= 2e-3 per token; the
+packed layout's dequantized weights bit-exact against the oracle's exact
+dequantization rounded once to fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import quantized_expert_dequant_amd as moe
+from quantized_expert_dequant_amd.slab import DeviceLayer, upload_experts, workspace
+
+from helpers import TOL, W_RTOL, WORKLOADS, build_layer, oracle_layer, oracle_route, rel_err, seed_of
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    moe.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ pack ----
+
+@pytest.mark.parametrize("bits,H,I", [(4, 512, 128), (2, 512, 128), (4, 4096, 1024), (2, 4096, 1024),
+                                      (4, 704, 192), (2, 704, 192), (4, 64, 64)])
+def test_pack_dequant_bit_exact(bits, H, I):
+    n = 3
+    c = synth.experts(77, 5, 0, n, bits, H, I)
+    slab = upload_experts(lambda f, k: synth.experts(77, 5, f, k, bits, H, I), n, bits, H, I, chunk=2)
+    rb = moe.record_bytes(bits, H, I)
+    W = torch.empty(3 * I * H, dtype=torch.float32, device=DEV)
+    for e in range(n):
+        moe.dequant_expert(bits, H, I, slab[e * rb:(e + 1) * rb], W)
+        Wg, Wu, Wd = oracle.dequant_expert(bits, H, I, c.gate[e], c.up[e], c.down[e], c.scales[e], c.biases[e])
+        ref = np.concatenate([Wg.ravel(), Wu.ravel(), Wd.ravel()]).astype(np.float32)
+        np.testing.assert_array_equal(W.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------- router ----
+
+def _gpu_route(x, Wr, prior, K, renorm=True):
+    B, H = x.shape
+    E = Wr.shape[0]
+    ws_n = moe.route_workspace_bytes(B, E, K)
+    ws = torch.zeros(ws_n, dtype=torch.uint8, device=DEV)
+    idx = torch.empty((B, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((B, K), dtype=torch.float32, device=DEV)
+    moe.route_topk(_t(x), B, _t(Wr), None if prior is None else _t(prior), H, E, K, idx, w, ws, ws_n,
+                   renormalize=renorm)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,B", [(0, 16), (1, 8), (4, 64)])
+def test_router_matches_oracle(n, B):
+    cfg, seed = WORKLOADS[n], seed_of(n)
+    x = synth.tokens(seed, 100, B, cfg["H"])
+    Wr, prior, lg, sel = oracle_route(cfg, seed, 0, x)
+    idx, w = _gpu_route(x, Wr, prior, cfg["K"])
+    for b in range(B):
+        ref_idx, ref_w, margin = sel[b]
+        assert margin > 1e-9, "near-tie: routing comparison would be meaningless (token %d)" % b
+        np.testing.assert_array_equal(idx[b], ref_idx)
+        np.testing.assert_allclose(w[b], ref_w, rtol=W_RTOL)
+
+
+def test_router_raw_softmax_and_ties():
+    rng = np.random.default_rng(4)
+    E, H, K = 40, 256, 6
+    Wr = rng.normal(0, 1 / 16, (E, H)).astype(np.float32)
+    x = rng.normal(0, 1, (4, H)).astype(np.float32)
+    lg = oracle.router_logits(x, Wr)
+    for b in range(4):               # make expert 33 an exact twin of each token's best expert
+        pass
+    top = int(np.argmax(lg[0]))
+    Wr[33] = Wr[top]
+    Wr[35] = Wr[top]
+    lg = oracle.router_logits(x, Wr)
+    idx, w = _gpu_route(x, Wr, None, K, renorm=False)
+    for b in range(4):
+        ref_idx, ref_w, _ = oracle.topk(lg[b], K, renormalize=False)
+        np.testing.assert_array_equal(idx[b], ref_idx)
+        np.testing.assert_allclose(w[b], ref_w, rtol=W_RTOL)
+    i0 = list(idx[0])
+    assert i0[:3] == sorted([top, 33, 35])
+
+
+# ------------------------------------------------------------------ layer ----
+
+@pytest.fixture(scope="module")
+def layers():
+    cache = {}
+
+    def get(n):
+        if n not in cache:
+            cache[n] = build_layer(WORKLOADS[n], seed_of(n))
+        return cache[n]
+
+    yield get
+    cache.clear()
+
+
+def _decode(layer, x):
+    B = x.shape[0]
+    ws, n = workspace(layer.desc, B)
+    y = torch.empty((B, layer.H), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, layer.K), dtype=torch.int32, device=DEV)
+    w = torch.empty((B, layer.K), dtype=torch.float32, device=DEV)
+    moe.layer_decode(layer.desc, _t(x), B, y, idx, w, ws, n)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def _check_layer(n, y, idx, w, x, layer_id=0):
+    cfg, seed = WORKLOADS[n], seed_of(n)
+    y_ref, idx_ref, w_ref, margin = oracle_layer(cfg, seed, layer_id, x)
+    assert np.all(margin > 1e-9)
+    np.testing.assert_array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
+    for b in range(x.shape[0]):
+        err = rel_err(y[b], y_ref[b])
+        assert err <= TOL, "token %d: rel err %.3e" % (b, err)
+    return max(rel_err(y[b], y_ref[b]) for b in range(x.shape[0]))
+
+
+@pytest.mark.parametrize("step", range(4))
+def test_layer_decode_tiny(layers, step):
+    L = layers(0)
+    x = synth.tokens(seed_of(0), step, 1, L.H)
+    y, idx, w = _decode(L, x)
+    _check_layer(0, y, idx, w, x)
+
+
+def test_layer_decode_tiny_several_tokens(layers):
+    L = layers(0)
+    x = synth.tokens(seed_of(0), 50, 7, L.H)
+    y, idx, w = _decode(L, x)
+    _check_layer(0, y, idx, w, x)
+
+
+@pytest.mark.parametrize("n", [1, 2])
+@pytest.mark.parametrize("step", range(3))
+def test_layer_decode_full_size(layers, n, step):
+    L = layers(n)
+    x = synth.tokens(seed_of(n), step, 1, L.H)
+    y, idx, w = _decode(L, x)
+    err = _check_layer(n, y, idx, w, x)
+    print("workload %d step %d: max rel err %.2e" % (n, step, err))
+
+
+def test_layer_decode_is_deterministic(layers):
+    L = layers(1)
+    x = synth.tokens(seed_of(1), 9, 1, L.H)
+    a = _decode(L, x)
+    b = _decode(L, x)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+@pytest.mark.parametrize("n", [0, 1, 2])
+def test_expert_ffn_given_routing(layers, n):
+    L = layers(n)
+    cfg, seed = WORKLOADS[n], seed_of(n)
+    x = synth.tokens(seed, 20, 2, L.H)
+    y_ref, idx_ref, w_ref, _ = oracle_layer(cfg, seed, 0, x)
+    ws, nb = workspace(L.desc, 2)
+    y = torch.empty((2, L.H), dtype=torch.float32, device=DEV)
+    fn = moe.expert_ffn_q4 if L.bits == 4 else moe.expert_ffn_q2
+    fn(L.desc, _t(x), 2, _t(idx_ref.astype(np.int32)), _t(w_ref.astype(np.float32)), y, ws, nb)
+    torch.cuda.synchronize()
+    for b in range(2):
+        assert rel_err(y.cpu().numpy()[b], y_ref[b]) <= TOL
+
+
+def test_invalid_expert_ids_give_nan_not_fault(layers):
+    L = layers(0)
+    x = synth.tokens(seed_of(0), 3, 3, L.H)
+    _, idx_ref, w_ref, _ = oracle_layer(WORKLOADS[0], seed_of(0), 0, x)
+    idx = idx_ref.astype(np.int32).copy()
+    idx[1, 2] = -1
+    idx[2, 0] = L.E           # the shared slot id is not a routed expert
+    ws, nb = workspace(L.desc, 3)
+    y = torch.empty((3, L.H), dtype=torch.float32, device=DEV)
+    moe.expert_ffn_q4(L.desc, _t(x), 3, _t(idx), _t(w_ref.astype(np.float32)), y, ws, nb)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    assert np.all(np.isfinite(yh[0]))
+    assert np.all(np.isnan(yh[1])) and np.all(np.isnan(yh[2]))
+
+
+def test_ragged_shapes_and_batch():
+    """Group counts that are not powers of two, E not a multiple of 4, B = 3."""
+    cfg = dict(H=704, I=192, E=37, K=5, bits=4, zipf=None)
+    for bits in (4, 2):
+        cfg["bits"] = bits
+        L = build_layer(cfg, 4242)
+        x = synth.tokens(4242, 0, 3, cfg["H"])
+        y, idx, w = _decode(L, x)
+        y_ref, idx_ref, w_ref, _ = oracle_layer(cfg, 4242, 0, x)
+        np.testing.assert_array_equal(idx, idx_ref)
+        np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
+        for b in range(3):
+            assert rel_err(y[b], y_ref[b]) <= TOL
+
+
+def test_rmsnorm_matches_oracle():
+    y = synth.tokens(5, 0, 3, 4096) * 7.0
+    x = torch.empty((3, 4096), dtype=torch.float32, device=DEV)
+    moe.rmsnorm(_t(y), 3, 4096, 1e-6, x)
+    torch.cuda.synchronize()
+    for b in range(3):
+        ref = oracle.rms_renorm(y[b].astype(np.float64), 1e-6)
+        np.testing.assert_allclose(x.cpu().numpy()[b], ref, rtol=1e-6, atol=1e-7)
