@@ -31,10 +31,9 @@
  *     Work is enqueued asynchronously; no call synchronizes the host and none
  *     allocates device or pinned memory.
  *   - Scratch memory is a caller-provided workspace `ws` of at least the
- *     size the matching *_workspace_bytes query returns.  It must be
- *     zero-filled once before its first use; the library leaves it in that
- *     state after every call.  Calls that share a workspace must be ordered
- *     on one stream.
+ *     size the matching *_workspace_bytes query returns; its contents need no
+ *     initialization.  Calls that share a workspace must be ordered on one
+ *     stream.
  *   - Return value: MOE_OK, or a negative MOE_E* code.  On an error return
  *     nothing has been enqueued and no output has been written;
  *     moe_last_error() describes the failure (thread-local).  Faults inside
@@ -180,9 +179,10 @@ int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* x,
  * the launch stream (hipEvent_t handles created by the caller, passed as
  * void*), so the caller can read the kernel's own duration with
  * hipEventElapsedTime.  NULL, NULL clears the hook.  Kernels:
- *   MOE_KERNEL_ROUTER  router logits + top-K
- *   MOE_KERNEL_GATEUP  fused gate/up dequant-GEMV + SwiGLU (the dominant kernel)
- *   MOE_KERNEL_DOWN    down dequant-GEMV + weighted combine
+ *   MOE_KERNEL_ROUTER  router logits (+ the token's dequant operand)
+ *   MOE_KERNEL_GATEUP  top-K + fused gate/up dequant-GEMV + SwiGLU over the active
+ *                      experts (the dominant kernel: 2/3 of the expert bytes)
+ *   MOE_KERNEL_DOWN    down dequant-GEMV + router-weighted combine
  */
 #define MOE_KERNEL_ROUTER 1
 #define MOE_KERNEL_GATEUP 2

@@ -149,27 +149,160 @@ __device__ inline float pair_class_inv(int bits, int p)
     }
 }
 
+// ---- cross-lane exchange without LDS: DPP for partners inside a row of 16
+// lanes, gfx950 permlane16/32 swaps across rows.  Every step combines a lane
+// with its partner as op(own, partner), so for commutative ops all lanes of a
+// group end with bit-identical results.
+template <int CTRL>
+__device__ inline uint32_t dpp32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+struct ArgMax {  // (value, id): larger value first, equal values -> lower id first
+    double v;
+    int id;
+};
+
+template <int CTRL>
+__device__ inline float xchg(float v) { return __uint_as_float(dpp32<CTRL>(__float_as_uint(v))); }
+template <int CTRL>
+__device__ inline double xchg(double v)
+{
+    uint2 u = __builtin_bit_cast(uint2, v);
+    u.x = dpp32<CTRL>(u.x);
+    u.y = dpp32<CTRL>(u.y);
+    return __builtin_bit_cast(double, u);
+}
+template <int CTRL>
+__device__ inline ArgMax xchg(ArgMax a) { return ArgMax{xchg<CTRL>(a.v), (int)dpp32<CTRL>((uint32_t)a.id)}; }
+
+template <int CTRL>
+__device__ inline uint64_t xchg(uint64_t v)
+{
+    uint2 u = __builtin_bit_cast(uint2, v);
+    u.x = dpp32<CTRL>(u.x);
+    u.y = dpp32<CTRL>(u.y);
+    return __builtin_bit_cast(uint64_t, u);
+}
+
+struct KeyId {  // (key, id): larger key first, equal keys -> lower id first
+    uint64_t key;
+    int id;
+};
+template <int CTRL>
+__device__ inline KeyId xchg(KeyId a)
+{
+    uint2 u = __builtin_bit_cast(uint2, a.key);
+    u.x = dpp32<CTRL>(u.x);
+    u.y = dpp32<CTRL>(u.y);
+    return KeyId{__builtin_bit_cast(uint64_t, u), (int)dpp32<CTRL>((uint32_t)a.id)};
+}
+
+template <bool ROW32>
+__device__ inline void swap_u32(uint32_t v, uint32_t& a, uint32_t& b)
+{
+    if (ROW32) {
+        auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        a = p[0];
+        b = p[1];
+    } else {
+        auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        a = p[0];
+        b = p[1];
+    }
+}
+template <bool ROW32>
+__device__ inline void swap(float v, float& a, float& b)
+{
+    uint32_t x, y;
+    swap_u32<ROW32>(__float_as_uint(v), x, y);
+    a = __uint_as_float(x);
+    b = __uint_as_float(y);
+}
+template <bool ROW32>
+__device__ inline void swap(double v, double& a, double& b)
+{
+    uint2 u = __builtin_bit_cast(uint2, v), p, q;
+    swap_u32<ROW32>(u.x, p.x, q.x);
+    swap_u32<ROW32>(u.y, p.y, q.y);
+    a = __builtin_bit_cast(double, p);
+    b = __builtin_bit_cast(double, q);
+}
+template <bool ROW32>
+__device__ inline void swap(uint64_t v, uint64_t& a, uint64_t& b)
+{
+    uint2 u = __builtin_bit_cast(uint2, v), p, q;
+    swap_u32<ROW32>(u.x, p.x, q.x);
+    swap_u32<ROW32>(u.y, p.y, q.y);
+    a = __builtin_bit_cast(uint64_t, p);
+    b = __builtin_bit_cast(uint64_t, q);
+}
+template <bool ROW32>
+__device__ inline void swap(KeyId v, KeyId& a, KeyId& b)
+{
+    uint2 u = __builtin_bit_cast(uint2, v.key), p, q;
+    swap_u32<ROW32>(u.x, p.x, q.x);
+    swap_u32<ROW32>(u.y, p.y, q.y);
+    uint32_t x, y;
+    swap_u32<ROW32>((uint32_t)v.id, x, y);
+    a = KeyId{__builtin_bit_cast(uint64_t, p), (int)x};
+    b = KeyId{__builtin_bit_cast(uint64_t, q), (int)y};
+}
+template <bool ROW32>
+__device__ inline void swap(ArgMax v, ArgMax& a, ArgMax& b)
+{
+    swap<ROW32>(v.v, a.v, b.v);
+    uint32_t x, y;
+    swap_u32<ROW32>((uint32_t)v.id, x, y);
+    a.id = (int)x;
+    b.id = (int)y;
+}
+
+// all-reduce over aligned groups of `width` lanes (a power of two <= 64)
+template <typename T, typename Op>
+__device__ inline T group_reduce(T v, Op op, int width)
+{
+    if (width > 1) v = op(v, xchg<0xB1>(v));   // quad_perm [1,0,3,2]
+    if (width > 2) v = op(v, xchg<0x4E>(v));   // quad_perm [2,3,0,1]
+    if (width > 4) v = op(v, xchg<0x141>(v));  // row_half_mirror
+    if (width > 8) v = op(v, xchg<0x140>(v));  // row_mirror
+    if (width > 16) {
+        T a, b;
+        swap<false>(v, a, b);
+        v = op(a, b);
+    }
+    if (width > 32) {
+        T a, b;
+        swap<true>(v, a, b);
+        v = op(a, b);
+    }
+    return v;
+}
+
+struct OpAdd {
+    template <typename T>
+    __device__ T operator()(T a, T b) const { return a + b; }
+};
+struct OpMax {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpKeyMax {
+    __device__ KeyId operator()(KeyId a, KeyId b) const
+    {
+        return (b.key > a.key || (b.key == a.key && b.id < a.id)) ? b : a;
+    }
+};
+struct OpArgMax {
+    __device__ ArgMax operator()(ArgMax a, ArgMax b) const
+    {
+        return (b.v > a.v || (b.v == a.v && b.id < a.id)) ? b : a;
+    }
+};
+
 template <typename T>
-__device__ inline T wave_sum(T v, int width = 64)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        if (off < width) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
-__device__ inline float wave_max(float v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-// sum across groups of `width` consecutive lanes (width a power of two <= 64)
-__device__ inline float lane_group_sum(float v, int width)
-{
-    for (int off = width >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
+__device__ inline T wave_sum(T v) { return group_reduce(v, OpAdd(), 64); }
+__device__ inline float wave_max(float v) { return group_reduce(v, OpMax(), 64); }
+__device__ inline float lane_group_sum(float v, int width) { return group_reduce(v, OpAdd(), width); }
 
 }  // namespace moe

@@ -8,18 +8,23 @@
 //
 // Per-token path ([LLMAPIS] section 深度分析: route, read, dequantize, compute,
 // combine):
-//   k_prep    activation -> fp16 pairs + per-group stats (the operand of the
-//             folded dequant: scale*x and bias*x per group, the FMA rearrangement
-//             described in [LLMAPIS] section 深度分析, applied per group of 64)
-//   k_router  logits (fp32 products accumulated in fp64), softmax, top-K
-//   k_gateup  fused gate/up dequant-GEMV + SiLU*mul over the K routed + shared experts
+//   k_router  logits (fp32 products accumulated in fp64); also preps the token:
+//             fp16 pairs + per-group stats, the operand of the folded dequant
+//             (scale*x and bias*x per group, the FMA rearrangement described in
+//             [LLMAPIS] section 深度分析, applied per group of 64)
+//   k_gateup  softmax / top-K per wave, then the fused gate/up dequant-GEMV +
+//             SiLU*mul over the K routed + shared experts
 //   k_down    down dequant-GEMV + router-weighted combine in one pass (no atomics)
+//   k_prep    the token prep alone, for callers that bring their own routing
+//   k_topk    softmax / top-K alone, for the router entry point
 #include <hip/hip_ext.h>
 
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
+
+__device__ inline uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // ----------------------------------------------------------------------------
 // pack: canonical -> packed record
@@ -141,18 +146,17 @@ void launch_dequant(const Layout& L, const void* rec, float* W, hipStream_t s)
 }
 
 // ----------------------------------------------------------------------------
-// prep: fp32 vectors [n_vec][len] -> fp16 pairs + stats, one wave per group
+// prep of the token activations: fp32 [B][H] -> fp16 pairs + per-group stats.
+// One wave per (token, group); shared by the standalone prep kernel and the
+// router kernel, which preps the token while it computes the logits.
 // ----------------------------------------------------------------------------
 __device__ inline float exp2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
 template <int BITS>
-__global__ __launch_bounds__(256) void k_prep(const float* __restrict__ v, int len, int G,
-                                              uint4* __restrict__ q, float4* __restrict__ st)
+__device__ void prep_group(const float* __restrict__ v, int G, int vec, int g, int lane, uint4* __restrict__ q,
+                           float4* __restrict__ st)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int g = blockIdx.x * 4 + wave, vec = blockIdx.y;
-    if (g >= G) return;
-    const float val = v[(long long)vec * len + g * 64 + lane];
+    const float val = v[(long long)vec * G * 64 + g * 64 + lane];
     const float amax = wave_max(fabsf(val));
     int e = 0;
     if (amax > 0.f && amax <= 3.4e38f) {
@@ -185,288 +189,405 @@ __global__ __launch_bounds__(256) void k_prep(const float* __restrict__ v, int l
     if (lane == 0) st[(long long)vec * G + g] = make_float4(C, S, exp2i(e), 0.f);
 }
 
+template <int BITS>
+__global__ __launch_bounds__(256) void k_prep(const float* __restrict__ v, int n_vec, int G, uint4* __restrict__ q,
+                                              float4* __restrict__ st)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int i = blockIdx.x * 4 + wave; i < n_vec * G; i += gridDim.x * 4) {
+        const int vec = i / G, g = i - vec * G;
+        prep_group<BITS>(v, G, vec, g, lane, q, st);
+    }
+}
+
 void launch_prep(int bits, const float* v, int n_vec, int len, uint4* q, float4* st, hipStream_t s)
 {
     const int G = len / 64;
-    dim3 grid((G + 3) / 4, n_vec);
+    int blocks = (n_vec * G + 3) / 4;
+    if (blocks > 1024) blocks = 1024;
     if (bits == 4)
-        hipLaunchKernelGGL(k_prep<4>, grid, dim3(256), 0, s, v, len, G, q, st);
+        hipLaunchKernelGGL(k_prep<4>, dim3(blocks), dim3(256), 0, s, v, n_vec, G, q, st);
     else
-        hipLaunchKernelGGL(k_prep<2>, grid, dim3(256), 0, s, v, len, G, q, st);
+        hipLaunchKernelGGL(k_prep<2>, dim3(blocks), dim3(256), 0, s, v, n_vec, G, q, st);
 }
 
 // ----------------------------------------------------------------------------
-// router: logits + (last block) softmax / top-K
+// routing: logits (fp32 products accumulated in fp64), then softmax / top-K
 // ----------------------------------------------------------------------------
-__device__ inline bool ranks_before(double va, int ia, double vb, int ib)
+
+// Selection key of a logit: an order-preserving map of the double onto a
+// 64-bit integer (larger logit, larger key) whose lowest 10 bits are replaced
+// by 1023 - id.  One unsigned compare then ranks (logit desc, id asc); logits
+// that agree to 2^-43 relative (below what fp64 summation order fixes) count
+// as equal and go to the lower id.  Needs E <= 1024.
+__device__ inline uint64_t select_key(double d, int id)
 {
-    return va > vb || (va == vb && ia < ib);
+    const uint64_t u = (uint64_t)__double_as_longlong(d);
+    const uint64_t k = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+    return (k & ~1023ull) | (uint64_t)(1023 - id);
+}
+__device__ inline int key_id(uint64_t k) { return 1023 - (int)(k & 1023ull); }
+__device__ inline double key_value(uint64_t k)  // the logit to within 2^-42 relative
+{
+    const uint64_t u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+    return __longlong_as_double((long long)u);
 }
 
-// one wave selects the top K of token b's E logits
-__device__ void topk_wave(const double* __restrict__ lg, int E, int K, int renorm, int lane,
-                          int32_t* __restrict__ idx_out, float* __restrict__ w_out)
+// Load the logits a wave selects from: lane l holds ids l + 64 j, j < 16
+// (clamped indices: every lane loads, the selection masks ids >= E).
+__device__ inline void topk_load(const double* __restrict__ lg, int E, int lane, double (&lv)[16])
+{
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lv[j] = lg[min(lane + 64 * j, E - 1)];
+}
+
+struct OpU64Max {
+    __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return b > a ? b : a; }
+};
+
+// Top-K of one token's E logits by one wave.  Lane k < K returns the k-th
+// expert (rank order) and its routing weight; every lane sees the same selection.
+template <int KMAX>
+__device__ void topk_select(const double (&lv)[16], int E, int K, int renorm, int lane, int& my_id, float& my_w)
 {
     const int NL = (E + 63) / 64;  // <= 16
-    double lv[16];
-    uint32_t taken = 0;
+    uint64_t key[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int id = lane + 64 * j;
-        if (j < NL && id < E)
-            lv[j] = __builtin_nontemporal_load(lg + id);
-        else {
-            lv[j] = -INFINITY;
-            taken |= 1u << j;
-        }
+        key[j] = (j < NL && id < E) ? select_key(lv[j], id) : 0ull;
     }
-    double my_v = -INFINITY;
-    int my_id = 0x7FFFFFFF;
-    double lmax = -INFINITY;
-    for (int k = 0; k < K; ++k) {
-        double bv = -INFINITY;
-        int bid = 0x7FFFFFFF;
+    uint64_t mine = 0ull, top = 0ull;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int id = lane + 64 * j;
-            if (!(taken & (1u << j)) && ranks_before(lv[j], id, bv, bid)) {
-                bv = lv[j];
-                bid = id;
-            }
-        }
+    for (int k = 0; k < KMAX; ++k) {
+        if (k >= K) break;
+        uint64_t best = 0ull;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const double ov = __shfl_xor(bv, off, 64);
-            const int oid = __shfl_xor(bid, off, 64);
-            if (ranks_before(ov, oid, bv, bid)) {
-                bv = ov;
-                bid = oid;
-            }
-        }
-        if (bid != 0x7FFFFFFF && (bid & 63) == lane) taken |= 1u << (bid >> 6);
-        if (k == 0) lmax = bv;
-        if (lane == k) {
-            my_v = bv;
-            my_id = bid;
-        }
-    }
-    const double ew = (lane < K) ? exp(my_v - lmax) : 0.0;
-    double denom;
-    if (renorm) {
-        denom = wave_sum(ew);
-    } else {
-        double part = 0.0;
+        for (int j = 0; j < 16; ++j) best = key[j] > best ? key[j] : best;
+        best = group_reduce(best, OpU64Max(), 64);
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            if (j < NL && lane + 64 * j < E) part += exp(lv[j] - lmax);
-        denom = wave_sum(part);
+        for (int j = 0; j < 16; ++j) key[j] = (key[j] == best) ? 0ull : key[j];  // keys are unique
+        if (k == 0) top = best;
+        if (lane == k) mine = best;
     }
-    if (lane < K) {
-        idx_out[lane] = my_id;
-        w_out[lane] = (float)(ew / denom);
-    }
+    my_id = (lane < K) ? key_id(mine) : 0x7FFFFFFF;
+    const double lmax = key_value(top);
+    // softmax weights in fp32: exp of logit differences, renormalized over the K
+    const float ew = (lane < K) ? __expf((float)(key_value(mine) - lmax)) : 0.f;
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if (j < NL && lane + 64 * j < E) part += __expf((float)(lv[j] - lmax));
+    const float denom = renorm ? wave_sum(ew) : wave_sum(part);
+    my_w = ew / denom;
 }
 
-__global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int B, const float* __restrict__ W,
-                                                const float* __restrict__ bias, int H, int E, int K, int renorm,
-                                                double* __restrict__ logits, unsigned* __restrict__ counter,
-                                                int32_t* __restrict__ idx_out, float* __restrict__ w_out)
+// logits[b][e] = W_r[e] . x[b] (+ bias[e]); one wave per expert.  The token's
+// dequant operand (fp16 pairs + stats) is prepared by the same launch.
+__device__ inline double dot4d(float4 w, float4 x, double acc)
+{
+    acc = fma((double)w.x, (double)x.x, acc);
+    acc = fma((double)w.y, (double)x.y, acc);
+    acc = fma((double)w.z, (double)x.z, acc);
+    return fma((double)w.w, (double)x.w, acc);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int B, int prepB,
+                                                const float* __restrict__ W, const float* __restrict__ bias, int H,
+                                                int E, double* __restrict__ logits, uint4* __restrict__ xq,
+                                                float4* __restrict__ xst)
 {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int e = blockIdx.x * 4 + wave;
     const int n4 = H >> 2;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
     if (e < E) {
         const float4* W4 = reinterpret_cast<const float4*>(W) + (long long)e * n4;
         const double bb = bias ? (double)bias[e] : 0.0;
         if (n4 <= 1024) {
-            float4 wv[16];
+            // token 0's activations (cache-resident) first, then the router row (HBM)
+            // clamped indices: every load is unconditional (no branch, no serialising wait);
+            // columns past H are zeroed after the loads
+            float4 xv[16], wv[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int c = lane + 64 * i;
-                wv[i] = c < n4 ? W4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            for (int i = 0; i < 16; ++i) xv[i] = x4[min(lane + 64 * i, n4 - 1)];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) wv[i] = W4[min(lane + 64 * i, n4 - 1)];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (lane + 64 * i >= n4) wv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
             for (int b = 0; b < B; ++b) {
-                const float4* x4 = reinterpret_cast<const float4*>(x) + (long long)b * n4;
+                if (b > 0) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) xv[i] = x4[(long long)b * n4 + min(lane + 64 * i, n4 - 1)];
+                }
                 double acc = 0.0;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int c = lane + 64 * i;
-                    if (c < n4) {
-                        const float4 xv = x4[c];
-                        acc = fma((double)wv[i].x, (double)xv.x, acc);
-                        acc = fma((double)wv[i].y, (double)xv.y, acc);
-                        acc = fma((double)wv[i].z, (double)xv.z, acc);
-                        acc = fma((double)wv[i].w, (double)xv.w, acc);
-                    }
-                }
+                for (int i = 0; i < 16; ++i) acc = dot4d(wv[i], xv[i], acc);
                 acc = wave_sum(acc);
                 if (lane == 0) logits[(long long)b * E + e] = acc + bb;
             }
         } else {
             for (int b = 0; b < B; ++b) {
-                const float4* x4 = reinterpret_cast<const float4*>(x) + (long long)b * n4;
                 double acc = 0.0;
-                for (int c = lane; c < n4; c += 64) {
-                    const float4 wv = W4[c], xv = x4[c];
-                    acc = fma((double)wv.x, (double)xv.x, acc);
-                    acc = fma((double)wv.y, (double)xv.y, acc);
-                    acc = fma((double)wv.z, (double)xv.z, acc);
-                    acc = fma((double)wv.w, (double)xv.w, acc);
-                }
+                for (int c = lane; c < n4; c += 64) acc = dot4d(W4[c], x4[(long long)b * n4 + c], acc);
                 acc = wave_sum(acc);
                 if (lane == 0) logits[(long long)b * E + e] = acc + bb;
             }
         }
     }
-    // the last block to arrive selects the experts of every token
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1u) == gridDim.x - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int b = wave; b < B; b += 4)
-        topk_wave(logits + (long long)b * E, E, K, renorm, lane, idx_out + (long long)b * K, w_out + (long long)b * K);
-    __syncthreads();
-    if (threadIdx.x == 0) *counter = 0u;
+    const int Gh = H / 64;
+    for (int i = blockIdx.x * 4 + wave; i < prepB * Gh; i += gridDim.x * 4) {
+        const int vec = i / Gh, g = i - vec * Gh;
+        prep_group<BITS>(x, Gh, vec, g, lane, xq, xst);
+    }
 }
 
-void launch_router(const float* x, int B, const float* W, const float* bias, int H, int E, int K, int renorm,
-                   double* logits, unsigned* counter, int32_t* idx, float* w, hipStream_t s, Timing t)
+void launch_router(int bits, const float* x, int B, const float* W, const float* bias, int H, int E, double* logits,
+                   uint4* xq, float4* xst, hipStream_t s, Timing t)
 {
-    hipExtLaunchKernelGGL(k_router, dim3((E + 3) / 4), dim3(256), 0, s, t.start, t.stop, 0, x, B, W, bias, H, E, K,
-                          renorm, logits, counter, idx, w);
+    int blocks = (E + 3) / 4;
+    const int prepB = xq ? B : 0;
+    const int prep_blocks = (prepB * (H / 64) + 3) / 4;
+    if (blocks < prep_blocks) blocks = prep_blocks < 1024 ? prep_blocks : 1024;
+    if (bits == 2)
+        hipExtLaunchKernelGGL(k_router<2>, dim3(blocks), dim3(256), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
+                              H, E, logits, xq, xst);
+    else
+        hipExtLaunchKernelGGL(k_router<4>, dim3(blocks), dim3(256), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
+                              H, E, logits, xq, xst);
+}
+
+// one wave per token: logits -> idx, w
+__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits, int B, int E, int K, int renorm,
+                                              int32_t* __restrict__ idx, float* __restrict__ w)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int b = blockIdx.x * 4 + wave;
+    if (b >= B) return;
+    int id;
+    float wt;
+    double lv[16];
+    topk_load(logits + (long long)b * E, E, lane, lv);
+    topk_select<32>(lv, E, K, renorm, lane, id, wt);
+    if (lane < K) {
+        idx[(long long)b * K + lane] = id;
+        w[(long long)b * K + lane] = wt;
+    }
+}
+
+void launch_topk(const double* logits, int B, int E, int K, int renorm, int32_t* idx, float* w, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_topk, dim3((B + 3) / 4), dim3(256), 0, s, logits, B, E, K, renorm, idx, w);
 }
 
 // ----------------------------------------------------------------------------
-// fused gate/up dequant-GEMV + SwiGLU, per (token, expert slot)
+// gate/up: fused dequant-GEMV of the gate and up rows + SwiGLU, for every
+// active expert of one token.  A wave owns RPW rows (RPP rows per pass when a
+// row has fewer than 64 groups) of all K+1 experts.  It first issues the
+// shared expert's loads (no routing needed), then selects the token's experts
+// from the logits while those loads are in flight (or takes the caller's
+// routing), then issues the routed experts' loads.  h = silu(g) * u is written
+// as fp16(h / 256) straight into the pair layout the down GEMV reads.
 // ----------------------------------------------------------------------------
-__device__ inline uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+constexpr int GU_RPW = 1;   // row passes per wave
+constexpr int GU_SC = 5;    // expert slots held in registers per round
+constexpr int DN_RPW = 1;   // row passes per wave, down
+constexpr int DN_SC = 5;    // expert slots staged per LDS round, down
+constexpr float H_SCALE = 256.f;  // h is carried as fp16(h / 256)
 
-template <int BITS, int RPW>
-__global__ __launch_bounds__(256) void k_gateup(const uint8_t* __restrict__ slab, Layout L,
-                                                const uint4* __restrict__ xq, const float4* __restrict__ xst,
-                                                const int32_t* __restrict__ idx, int K, int E,
-                                                float* __restrict__ h)
+struct FfnArgs {
+    const uint8_t* slab;
+    Layout L;
+    const uint4* xq;
+    const float4* xst;
+    const double* logits;  // route from logits (nullptr: use idx / w)
+    int renorm;
+    int32_t* idx;          // [B][K]: read, or written by block 0 when routing from logits
+    float* w;
+    int K, E;
+    float shared_w;
+    uint16_t* hq;          // [B*(K+1)][8][Gi] uint4 viewed as fp16 halves
+    float* y;
+    int sc;                // down: slots per LDS round
+};
+
+template <int BITS>
+struct SlotRegs {
+    uint4 g0, g1, u0, u1;
+    uint2 sb;
+};
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
 {
-    const int slot = blockIdx.y, KS = K + 1;
-    const int b = slot / KS, k = slot - b * KS;
-    const int e = (k < K) ? idx[b * K + k] : E;
-    const bool bad = (k < K) && (e < 0 || e >= E);
+    const Layout& L = A.L;
+    const int b = blockIdx.y, K = A.K, KS = K + 1;
     const int G = L.Gh, LPR = lanes_per_row(G), RPP = 64 / LPR;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sub = lane / LPR, gl = lane & (LPR - 1);
-    const int row0 = (blockIdx.x * 4 + wave) * RPW * RPP + sub;
-    float* hrow = h + (long long)slot * L.I;
-    if (bad) {
-#pragma unroll
-        for (int p = 0; p < RPW; ++p) {
-            const int r = row0 + p * RPP;
-            if (gl == 0 && r < L.I) hrow[r] = __builtin_nanf("");
-        }
-        return;
-    }
-    const uint8_t* rec = slab + (long long)e * L.record;
+    const int row0 = (blockIdx.x * 4 + wave) * GU_RPW * RPP + sub;
     const Masks M = load_masks();
-    float gacc[RPW], uacc[RPW];
-#pragma unroll
-    for (int p = 0; p < RPW; ++p) gacc[p] = uacc[p] = 0.f;
+    uint16_t* hq_tok = A.hq + (long long)b * KS * L.Gi * 64;
 
-    for (int g0 = 0; g0 < G; g0 += LPR) {
-        const int g = g0 + gl;
-        const bool gv = g < G;
-        uint4 xp[8];
-        float4 st = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (gv) {
+    // routing inputs first: they are cache-resident and gate every routed load
+    double lv[16];
+    int my_id = 0;
+    float my_w = 0.f;
+    if (A.logits)
+        topk_load(A.logits + (long long)b * A.E, A.E, lane, lv);
+    else if (lane < K)
+        my_id = A.idx[(long long)b * K + lane];
+    bool routed = false;
+
+    auto issue = [&](SlotRegs<BITS> (&R)[GU_RPW], int e, int g, bool gv) {
+        const uint8_t* rec = A.slab + (long long)e * L.record;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) xp[j] = xq[((long long)b * 8 + j) * G + g];
-            st = xst[(long long)b * G + g];
-        }
-        uint4 gc0[RPW], gc1[RPW], uc0[RPW], uc1[RPW];
-        uint2 sb[RPW];
-#pragma unroll
-        for (int p = 0; p < RPW; ++p) {
+        for (int p = 0; p < GU_RPW; ++p) {
             const int r = row0 + p * RPP;
             if (gv && r < L.I) {
                 const uint8_t* base = rec + (long long)r * 2 * L.hb;
-                gc0[p] = ld16(base + g * 16);
-                uc0[p] = ld16(base + L.hb + g * 16);
+                R[p].g0 = ld16(base + g * 16);
+                R[p].u0 = ld16(base + L.hb + g * 16);
                 if (BITS == 4) {
-                    gc1[p] = ld16(base + (G + g) * 16);
-                    uc1[p] = ld16(base + L.hb + (G + g) * 16);
+                    R[p].g1 = ld16(base + (G + g) * 16);
+                    R[p].u1 = ld16(base + L.hb + (G + g) * 16);
                 }
-                sb[p] = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)r * G + g) * 8);
+                R[p].sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)r * G + g) * 8);
             }
         }
+    };
+
+    // slot order: the shared expert first (pos 0), then routed expert k at pos k + 1
+    for (int r0 = 0; r0 < KS; r0 += GU_SC) {
+        const int nr = min(GU_SC, KS - r0);
+        float gacc[GU_SC][GU_RPW], uacc[GU_SC][GU_RPW];
+        int eid[GU_SC];
 #pragma unroll
-        for (int p = 0; p < RPW; ++p) {
-            const int r = row0 + p * RPP;
-            if (gv && r < L.I) {
-                float dg, du;
-                if (BITS == 4) {
-                    dg = group_dot_q4(M, gc0[p], gc1[p], xp);
-                    du = group_dot_q4(M, uc0[p], uc1[p], xp);
-                } else {
-                    dg = group_dot_q2(M, gc0[p], xp);
-                    du = group_dot_q2(M, uc0[p], xp);
+        for (int i = 0; i < GU_SC; ++i)
+#pragma unroll
+            for (int p = 0; p < GU_RPW; ++p) gacc[i][p] = uacc[i][p] = 0.f;
+        for (int g0 = 0; g0 < G; g0 += LPR) {
+            const int g = g0 + gl;
+            const bool gv = g < G;
+            uint4 xp[8];
+            float4 st = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (gv) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) xp[j] = A.xq[((long long)b * 8 + j) * G + g];
+                st = A.xst[(long long)b * G + g];
+            }
+            SlotRegs<BITS> R[GU_SC][GU_RPW];
+            int i0 = 0;
+            if (r0 == 0) {
+                eid[0] = A.E;  // the shared expert needs no routing: its loads go out first
+                issue(R[0], A.E, g, gv);
+                i0 = 1;
+                if (!routed) {
+                    if (A.logits) {
+                        topk_select<32>(lv, A.E, K, A.renorm, lane, my_id, my_w);
+                        if (blockIdx.x == 0 && wave == 0 && lane < K) {
+                            A.idx[(long long)b * K + lane] = my_id;
+                            A.w[(long long)b * K + lane] = my_w;
+                        }
+                    }
+                    routed = true;
                 }
-                gacc[p] = fmaf(bf16_lo(sb[p].x) * st.z, dg - st.x, fmaf(bf16_hi(sb[p].x), st.y, gacc[p]));
-                uacc[p] = fmaf(bf16_lo(sb[p].y) * st.z, du - st.x, fmaf(bf16_hi(sb[p].y), st.y, uacc[p]));
+            }
+#pragma unroll
+            for (int i = 0; i < GU_SC; ++i) {
+                if (i < i0 || i >= nr) continue;
+                int e = __builtin_amdgcn_readlane(my_id, r0 + i - 1);
+                if (e < 0 || e >= A.E) e = -2;  // invalid id: its h becomes NaN
+                eid[i] = e;
+                if (e >= 0) issue(R[i], e, g, gv);
+            }
+#pragma unroll
+            for (int i = 0; i < GU_SC; ++i)
+#pragma unroll
+                for (int p = 0; p < GU_RPW; ++p) {
+                    const int r = row0 + p * RPP;
+                    if (i < nr && eid[i] >= 0 && gv && r < L.I) {
+                        float dg, du;
+                        if (BITS == 4) {
+                            dg = group_dot_q4(M, R[i][p].g0, R[i][p].g1, xp);
+                            du = group_dot_q4(M, R[i][p].u0, R[i][p].u1, xp);
+                        } else {
+                            dg = group_dot_q2(M, R[i][p].g0, xp);
+                            du = group_dot_q2(M, R[i][p].u0, xp);
+                        }
+                        const uint2 sb = R[i][p].sb;
+                        gacc[i][p] = fmaf(bf16_lo(sb.x) * st.z, dg - st.x, fmaf(bf16_hi(sb.x), st.y, gacc[i][p]));
+                        uacc[i][p] = fmaf(bf16_lo(sb.y) * st.z, du - st.x, fmaf(bf16_hi(sb.y), st.y, uacc[i][p]));
+                    }
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < GU_SC; ++i) {
+            if (i >= nr) continue;
+            const int pos = r0 + i;
+            const int k = pos == 0 ? K : pos - 1;
+            uint16_t* hq = hq_tok + (long long)k * L.Gi * 64;
+#pragma unroll
+            for (int p = 0; p < GU_RPW; ++p) {
+                const float gg = lane_group_sum(gacc[i][p], LPR);
+                const float uu = lane_group_sum(uacc[i][p], LPR);
+                const int r = row0 + p * RPP;
+                if (gl == 0 && r < L.I) {
+                    const float h = eid[i] < 0 ? __builtin_nanf("") : gg / (1.f + __expf(-gg)) * uu;
+                    // input column r of the down GEMV, in the pair layout
+                    const int grp = r >> 6, cc = r & 63;
+                    int pp, hi;
+                    if (BITS == 4) {
+                        pp = 4 * (cc >> 3) + (cc & 3);
+                        hi = (cc >> 2) & 1;
+                    } else {
+                        pp = 8 * (cc >> 4) + (cc & 7);
+                        hi = (cc >> 3) & 1;
+                    }
+                    hq[((long long)(pp >> 2) * L.Gi + grp) * 8 + (pp & 3) * 2 + hi] =
+                        __builtin_bit_cast(uint16_t, (_Float16)(h * (1.f / H_SCALE)));
+                }
             }
         }
     }
-#pragma unroll
-    for (int p = 0; p < RPW; ++p) {
-        const float g = lane_group_sum(gacc[p], LPR);
-        const float u = lane_group_sum(uacc[p], LPR);
-        const int r = row0 + p * RPP;
-        if (gl == 0 && r < L.I) hrow[r] = g / (1.f + __expf(-g)) * u;
-    }
-}
-
-constexpr int GU_RPW = 2;
-
-int gateup_rows_per_block(const Layout& L) { return 4 * GU_RPW * (64 / lanes_per_row(L.Gh)); }
-
-void launch_gateup(const Layout& L, const void* slab, const uint4* xq, const float4* xst, const int32_t* idx,
-                   int B, int K, int E, float* h, hipStream_t s, Timing t)
-{
-    const int rpb = gateup_rows_per_block(L);
-    dim3 grid((L.I + rpb - 1) / rpb, B * (K + 1));
-    if (L.bits == 4)
-        hipExtLaunchKernelGGL((k_gateup<4, GU_RPW>), grid, dim3(256), 0, s, t.start, t.stop, 0, (const uint8_t*)slab,
-                              L, xq, xst, idx, K, E, h);
-    else
-        hipExtLaunchKernelGGL((k_gateup<2, GU_RPW>), grid, dim3(256), 0, s, t.start, t.stop, 0, (const uint8_t*)slab,
-                              L, xq, xst, idx, K, E, h);
 }
 
 // ----------------------------------------------------------------------------
-// down dequant-GEMV + weighted combine, per token; output rows owned by one wave
+// down: dequant-GEMV of the down rows + router-weighted combine, one pass.  A
+// block owns output rows of one token for every active expert.  It fetches
+// the token's h pairs (cache-resident) first, then issues its weight loads,
+// stages h in LDS and derives each group's stats there while the weights
+// stream in, and writes y = sum_k w_k Wd_k h_k + shared_weight * Wd_s h_s.
 // ----------------------------------------------------------------------------
-constexpr int DN_SC = 8;  // expert slots staged per LDS round
-constexpr int DN_RPW = 1;
+constexpr int DN_HREG = 4;  // uint4 of h staged per thread per round
 
-template <int BITS, int RPW>
-__global__ __launch_bounds__(256) void k_down(const uint8_t* __restrict__ slab, Layout L,
-                                              const uint4* __restrict__ hq, const float4* __restrict__ hst,
-                                              const int32_t* __restrict__ idx, const float* __restrict__ w, int K,
-                                              int E, float shared_w, int sc, float* __restrict__ y)
+template <int BITS>
+__global__ __launch_bounds__(256) void k_down(FfnArgs A)
 {
-    extern __shared__ uint4 lds[];  // [sc][9][G]: 8 uint4 of pairs, then the stats float4
-    const int b = blockIdx.y, KS = K + 1;
+    extern __shared__ uint4 lds[];  // [sc][9][Gi]: 8 uint4 of h pairs, then the group stats
+    const Layout& L = A.L;
+    const int b = blockIdx.y, K = A.K, KS = K + 1;
     const int G = L.Gi, LPR = lanes_per_row(G), RPP = 64 / LPR;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int sub = lane / LPR, gl = lane & (LPR - 1);
-    const int row0 = (blockIdx.x * 4 + wave) * RPW * RPP + sub;
+    const int row0 = (blockIdx.x * 4 + wave) * DN_RPW * RPP + sub;
     const Masks M = load_masks();
-    float acc[RPW];
+    const uint4* hq4 = reinterpret_cast<const uint4*>(A.hq) + (long long)b * KS * 8 * G;
+    float acc[DN_RPW];
 #pragma unroll
-    for (int p = 0; p < RPW; ++p) acc[p] = 0.f;
+    for (int p = 0; p < DN_RPW; ++p) acc[p] = 0.f;
 
-    for (int s0 = 0; s0 < KS; s0 += sc) {
-        const int ns = min(sc, KS - s0);
+    for (int s0 = 0; s0 < KS; s0 += A.sc) {
+        const int ns = min(A.sc, KS - s0);
+        const int n = ns * 8 * G;  // <= 256 * DN_HREG
+        // the round's h pairs (cache-resident) first; clamped indices keep every load in bounds
+        static_assert(DN_HREG == 4, "h staging is written out for four loads per thread");
+        const uint4* hsrc = hq4 + (long long)s0 * 8 * G;
+        const int t0 = threadIdx.x, t1 = t0 + 256, t2 = t0 + 512, t3 = t0 + 768;
+        const uint4 hv0 = hsrc[t0 < n ? t0 : 0], hv1 = hsrc[t1 < n ? t1 : 0];
+        const uint4 hv2 = hsrc[t2 < n ? t2 : 0], hv3 = hsrc[t3 < n ? t3 : 0];
         const uint8_t* rec[DN_SC];
         float wt[DN_SC];
 #pragma unroll
@@ -475,22 +596,19 @@ __global__ __launch_bounds__(256) void k_down(const uint8_t* __restrict__ slab, 
             wt[s] = 0.f;
             if (s < ns) {
                 const int k = s0 + s;
-                const int e = (k < K) ? idx[b * K + k] : E;
-                const bool bad = (k < K) && (e < 0 || e >= E);
-                wt[s] = bad ? __builtin_nanf("") : ((k < K) ? w[b * K + k] : shared_w);
-                rec[s] = bad ? nullptr : slab + (long long)e * L.record;
+                const int e = (k < K) ? A.idx[b * K + k] : A.E;
+                const bool bad = (k < K) && (e < 0 || e >= A.E);
+                wt[s] = bad ? __builtin_nanf("") : ((k < K) ? A.w[b * K + k] : A.shared_w);
+                rec[s] = bad ? nullptr : A.slab + (long long)e * L.record;
             }
         }
-        if (s0 > 0) __syncthreads();  // previous round's LDS reads are done
-        for (int g0 = 0; g0 < G; g0 += LPR) {
-            const int g = g0 + gl;
-            const bool gv = g < G;
-            uint4 c0[DN_SC][RPW], c1[DN_SC][RPW];
-            uint32_t sbv[DN_SC][RPW];
+        uint4 c0[DN_SC][DN_RPW], c1[DN_SC][DN_RPW];
+        uint32_t sbv[DN_SC][DN_RPW];
+        auto issue = [&](int g, bool gv) {
 #pragma unroll
             for (int s = 0; s < DN_SC; ++s)
 #pragma unroll
-                for (int p = 0; p < RPW; ++p) {
+                for (int p = 0; p < DN_RPW; ++p) {
                     const int r = row0 + p * RPP;
                     if (rec[s] && gv && r < L.H) {
                         const uint8_t* base = rec[s] + L.off_d_codes + (long long)r * L.ib;
@@ -499,28 +617,18 @@ __global__ __launch_bounds__(256) void k_down(const uint8_t* __restrict__ slab, 
                         sbv[s][p] = *reinterpret_cast<const uint32_t*>(rec[s] + L.off_d_sb + ((long long)r * G + g) * 4);
                     }
                 }
-            if (g0 == 0) {
-                // stage this round's activation operands
-                const int n = ns * 9 * G;
-                for (int t = threadIdx.x; t < n; t += 256) {
-                    const int s = t / (9 * G), rem = t - s * 9 * G, j = rem / G, gg = rem - j * G;
-                    const long long slot = (long long)b * KS + s0 + s;
-                    lds[t] = (j < 8) ? hq[(slot * 8 + j) * G + gg]
-                                     : __builtin_bit_cast(uint4, hst[slot * G + gg]);
-                }
-                __syncthreads();
-            }
+        };
+        auto compute = [&](int g, bool gv) {
 #pragma unroll
             for (int s = 0; s < DN_SC; ++s) {
-                if (s >= ns) break;
-                if (!gv) continue;
+                if (s >= ns || !gv) continue;
                 uint4 xp[8];
-                const uint4* src = lds + (long long)s * 9 * G + g;
+                const uint4* src = lds + s * 9 * G + g;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) xp[j] = src[j * G];
                 const float4 st = __builtin_bit_cast(float4, src[8 * G]);
 #pragma unroll
-                for (int p = 0; p < RPW; ++p) {
+                for (int p = 0; p < DN_RPW; ++p) {
                     const int r = row0 + p * RPP;
                     if (r < L.H) {
                         if (!rec[s]) {
@@ -534,37 +642,335 @@ __global__ __launch_bounds__(256) void k_down(const uint8_t* __restrict__ slab, 
                     }
                 }
             }
+        };
+        if (s0 > 0) __syncthreads();  // the previous round's LDS reads are done
+        issue(gl, gl < G);
+        auto stage = [&](int t, uint4 v) {
+            if (t < n) {
+                const int s = t / (8 * G), rem = t - s * 8 * G;
+                lds[s * 9 * G + rem] = v;
+            }
+        };
+        stage(t0, hv0);
+        stage(t1, hv1);
+        stage(t2, hv2);
+        stage(t3, hv3);
+        __syncthreads();
+        // group stats of the staged h: C = 1024 sum_p (pair sum) / t(p), S = sum h
+        for (int t = threadIdx.x; t < ns * G * 4; t += 256) {
+            const int item = t >> 2, part = t & 3;
+            const int s = item / G, gg = item - s * G;
+            float off = 0.f, sum = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 2 * part + jj;
+                const uint4 u = lds[s * 9 * G + j * G + gg];
+                const uint32_t pr[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int el = 0; el < 4; ++el) {
+                    const h2 hh = __builtin_bit_cast(h2, pr[el]);
+                    const float ps = (float)hh.x + (float)hh.y;
+                    off = fmaf(pair_class_inv(BITS, 4 * j + el), ps, off);
+                    sum += ps;
+                }
+            }
+            off = group_reduce(off, OpAdd(), 4);
+            sum = group_reduce(sum, OpAdd(), 4);
+            if (part == 0)
+                lds[s * 9 * G + 8 * G + gg] =
+                    __builtin_bit_cast(uint4, make_float4(1024.f * off, H_SCALE * sum, H_SCALE, 0.f));
+        }
+        __syncthreads();
+        compute(gl, gl < G);
+        for (int g0 = LPR; g0 < G; g0 += LPR) {
+            issue(g0 + gl, g0 + gl < G);
+            compute(g0 + gl, g0 + gl < G);
         }
     }
 #pragma unroll
-    for (int p = 0; p < RPW; ++p) {
+    for (int p = 0; p < DN_RPW; ++p) {
         const float v = lane_group_sum(acc[p], LPR);
         const int r = row0 + p * RPP;
-        if (gl == 0 && r < L.H) y[(long long)b * L.H + r] = v;
+        if (gl == 0 && r < L.H) A.y[(long long)b * L.H + r] = v;
     }
+}
+
+// ----------------------------------------------------------------------------
+// Straight-line fast path for the common shapes (K+1 <= 9 experts per token,
+// H <= 4096, I <= 4096): one group pass, one round of slots, every load at a
+// clamped in-bounds address and every boundary handled by selects, so the
+// compiler can keep the loads of all phases in flight and wait only for what
+// each phase needs.
+// ----------------------------------------------------------------------------
+template <int BITS, int KS, bool ROUTE>
+__global__ __launch_bounds__(256) void k_gateup_fast(FfnArgs A)
+{
+    constexpr int K = KS - 1;
+    const Layout& L = A.L;
+    const int b = blockIdx.y;
+    const int G = L.Gh, LPR = lanes_per_row(G), RPP = 64 / LPR;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sub = lane / LPR, gl = lane & (LPR - 1);
+    const bool gv = gl < G;
+    const int g = gv ? gl : G - 1;
+    const int r = (blockIdx.x * 4 + wave) * RPP + sub;
+    const bool rv = r < L.I;
+    const int rc = rv ? r : L.I - 1;
+    const Masks M = load_masks();
+
+    // 1. routing inputs (cache-resident, they gate the routed loads)
+    double lv[16];
+    int my_id = 0;
+    float my_w = 0.f;
+    if (ROUTE) {
+        const double* lg = A.logits + (long long)b * A.E;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) lv[j] = lg[min(lane + 64 * j, A.E - 1)];
+    } else {
+        my_id = A.idx[(long long)b * K + min(lane, K - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. the token's dequant operand
+    uint4 xp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xp[j] = A.xq[((long long)b * 8 + j) * G + g];
+    const float4 st = A.xst[(long long)b * G + g];
+
+    SlotRegs<BITS> R[KS];
+    auto issue = [&](SlotRegs<BITS>& S, int e) {
+        const uint8_t* rec = A.slab + (long long)e * L.record;
+        const uint8_t* base = rec + (long long)rc * 2 * L.hb;
+        S.g0 = ld16(base + g * 16);
+        S.u0 = ld16(base + L.hb + g * 16);
+        if (BITS == 4) {
+            S.g1 = ld16(base + (G + g) * 16);
+            S.u1 = ld16(base + L.hb + (G + g) * 16);
+        }
+        S.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)rc * G + g) * 8);
+    };
+    // 3. the shared expert needs no routing: its loads go out first
+    issue(R[K], A.E);
+    __builtin_amdgcn_sched_barrier(0);
+    // 4. select the routed experts while those loads are in flight
+    if (ROUTE) {
+        topk_select<K>(lv, A.E, K, A.renorm, lane, my_id, my_w);
+        if (blockIdx.x == 0 && wave == 0 && lane < K) {
+            A.idx[(long long)b * K + lane] = my_id;
+            A.w[(long long)b * K + lane] = my_w;
+        }
+    }
+    // 5. the routed experts' loads (an invalid id reads expert 0 and yields NaN)
+    bool bad[KS];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int e = __builtin_amdgcn_readlane(my_id, k);
+        bad[k] = (e < 0 || e >= A.E);
+        issue(R[k], bad[k] ? 0 : e);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bad[K] = false;
+    // 6. dequant-GEMV of every slot, shared first (its data arrives first)
+    uint16_t* hq_tok = A.hq + (long long)b * KS * L.Gi * 64;
+    const int grp = rc >> 6, cc = rc & 63;
+    int pp, hi;
+    if (BITS == 4) {
+        pp = 4 * (cc >> 3) + (cc & 3);
+        hi = (cc >> 2) & 1;
+    } else {
+        pp = 8 * (cc >> 4) + (cc & 7);
+        hi = (cc >> 3) & 1;
+    }
+    const long long hoff = ((long long)(pp >> 2) * L.Gi + grp) * 8 + (pp & 3) * 2 + hi;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+        const int k = (i == 0) ? K : i - 1;
+        float dg, du;
+        if (BITS == 4) {
+            dg = group_dot_q4(M, R[k].g0, R[k].g1, xp);
+            du = group_dot_q4(M, R[k].u0, R[k].u1, xp);
+        } else {
+            dg = group_dot_q2(M, R[k].g0, xp);
+            du = group_dot_q2(M, R[k].u0, xp);
+        }
+        const uint2 sb = R[k].sb;
+        float ga = fmaf(bf16_lo(sb.x) * st.z, dg - st.x, bf16_hi(sb.x) * st.y);
+        float ua = fmaf(bf16_lo(sb.y) * st.z, du - st.x, bf16_hi(sb.y) * st.y);
+        ga = lane_group_sum(gv ? ga : 0.f, LPR);
+        ua = lane_group_sum(gv ? ua : 0.f, LPR);
+        const float h = bad[k] ? __builtin_nanf("") : ga / (1.f + __expf(-ga)) * ua;
+        if (gl == 0 && rv)
+            hq_tok[(long long)k * L.Gi * 64 + hoff] = __builtin_bit_cast(uint16_t, (_Float16)(h * (1.f / H_SCALE)));
+    }
+}
+
+template <int BITS, int KS>
+__global__ __launch_bounds__(256) void k_down_fast(FfnArgs A)
+{
+    constexpr int K = KS - 1;
+    extern __shared__ uint4 lds[];  // h pairs [KS][8][Gi], then stats [KS][Gi]
+    const Layout& L = A.L;
+    const int b = blockIdx.y;
+    const int G = L.Gi, LPR = lanes_per_row(G), RPP = 64 / LPR;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sub = lane / LPR, gl = lane & (LPR - 1);
+    const bool gv = gl < G;
+    const int g = gv ? gl : G - 1;
+    const int r = (blockIdx.x * 4 + wave) * RPP + sub;
+    const bool rv = r < L.H;
+    const int rc = rv ? r : L.H - 1;
+    const Masks M = load_masks();
+    const int n = KS * 8 * G;  // <= 1024
+    // 1. the token's h pairs (cache-resident)
+    const uint4* hsrc = reinterpret_cast<const uint4*>(A.hq) + (long long)b * n;
+    const int t0 = threadIdx.x, t1 = t0 + 256, t2 = t0 + 512, t3 = t0 + 768;
+    const uint4 hv0 = hsrc[t0 < n ? t0 : 0], hv1 = hsrc[t1 < n ? t1 : 0];
+    const uint4 hv2 = hsrc[t2 < n ? t2 : 0], hv3 = hsrc[t3 < n ? t3 : 0];
+    __builtin_amdgcn_sched_barrier(0);  // keep the h loads ahead of the weight loads
+    // 2. the routing and every slot's down rows
+    int eid[KS];
+    float wt[KS];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {  // all routing loads first, then one wait
+        eid[k] = A.idx[b * K + k];
+        wt[k] = A.w[b * K + k];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const bool bad = (eid[k] < 0 || eid[k] >= A.E);
+        eid[k] = bad ? 0 : eid[k];
+        wt[k] = bad ? __builtin_nanf("") : wt[k];
+    }
+    eid[K] = A.E;
+    wt[K] = A.shared_w;
+    uint4 c0[KS], c1[KS];
+    uint32_t sbv[KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const uint8_t* rec = A.slab + (long long)eid[k] * L.record;
+        const uint8_t* base = rec + L.off_d_codes + (long long)rc * L.ib;
+        c0[k] = ld16(base + g * 16);
+        if (BITS == 4) c1[k] = ld16(base + (G + g) * 16);
+        sbv[k] = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)rc * G + g) * 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. stage h and derive each group's stats while the weights stream in
+    if (t0 < n) lds[t0] = hv0;
+    if (t1 < n) lds[t1] = hv1;
+    if (t2 < n) lds[t2] = hv2;
+    if (t3 < n) lds[t3] = hv3;
+    __syncthreads();
+    uint4* lst = lds + n;
+    for (int t = threadIdx.x; t < KS * G * 4; t += 256) {
+        const int item = t >> 2, part = t & 3;
+        const int s = item / G, gg = item - s * G;
+        float off = 0.f, sum = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * part + jj;
+            const uint4 u = lds[(s * 8 + j) * G + gg];
+            const uint32_t pr[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int el = 0; el < 4; ++el) {
+                const h2 hh = __builtin_bit_cast(h2, pr[el]);
+                const float ps = (float)hh.x + (float)hh.y;
+                off = fmaf(pair_class_inv(BITS, 4 * j + el), ps, off);
+                sum += ps;
+            }
+        }
+        off = group_reduce(off, OpAdd(), 4);
+        sum = group_reduce(sum, OpAdd(), 4);
+        if (part == 0) lst[item] = __builtin_bit_cast(uint4, make_float4(1024.f * off, H_SCALE * sum, H_SCALE, 0.f));
+    }
+    __syncthreads();
+    // 4. dequant-GEMV and combine
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        uint4 xp[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xp[j] = lds[(k * 8 + j) * G + g];
+        const float4 sv = __builtin_bit_cast(float4, lst[k * G + g]);
+        const float d = (BITS == 4) ? group_dot_q4(M, c0[k], c1[k], xp) : group_dot_q2(M, c0[k], xp);
+        const float part = fmaf(bf16_lo(sbv[k]) * sv.z, d - sv.x, bf16_hi(sbv[k]) * sv.y);
+        acc = fmaf(wt[k], part, acc);
+    }
+    acc = lane_group_sum(gv ? acc : 0.f, LPR);
+    if (gl == 0 && rv) A.y[(long long)b * L.H + r] = acc;
 }
 
 int down_slots_per_round(const Layout& L)
 {
-    const int per_slot = 9 * L.Gi * 16;
-    int sc = (64 * 1024) / per_slot;
+    int sc = (256 * DN_HREG) / (8 * L.Gi);  // h of a round fits the per-thread staging registers
     if (sc > DN_SC) sc = DN_SC;
     return sc;  // >= 1 for I <= 16384
 }
 
-void launch_down(const Layout& L, const void* slab, const uint4* hq, const float4* hst, const int32_t* idx,
-                 const float* w, int B, int K, int E, float shared_w, float* y, hipStream_t s, Timing t)
+template <int BITS, int KS>
+void launch_fast_ks(bool route, dim3 fg, dim3 fd, size_t flds, const FfnArgs& A, hipStream_t s, Timing tg, Timing td)
 {
-    const int rpb = 4 * DN_RPW * (64 / lanes_per_row(L.Gi));
-    const int sc = down_slots_per_round(L);
-    const size_t lds = (size_t)sc * 9 * L.Gi * 16;
-    dim3 grid((L.H + rpb - 1) / rpb, B);
-    if (L.bits == 4)
-        hipExtLaunchKernelGGL((k_down<4, DN_RPW>), grid, dim3(256), lds, s, t.start, t.stop, 0, (const uint8_t*)slab,
-                              L, hq, hst, idx, w, K, E, shared_w, sc, y);
+    if (route)
+        hipExtLaunchKernelGGL((k_gateup_fast<BITS, KS, true>), fg, dim3(256), 0, s, tg.start, tg.stop, 0, A);
     else
-        hipExtLaunchKernelGGL((k_down<2, DN_RPW>), grid, dim3(256), lds, s, t.start, t.stop, 0, (const uint8_t*)slab,
-                              L, hq, hst, idx, w, K, E, shared_w, sc, y);
+        hipExtLaunchKernelGGL((k_gateup_fast<BITS, KS, false>), fg, dim3(256), 0, s, tg.start, tg.stop, 0, A);
+    hipExtLaunchKernelGGL((k_down_fast<BITS, KS>), fd, dim3(256), flds, s, td.start, td.stop, 0, A);
+}
+
+template <int BITS>
+void launch_fast(int KS, bool route, dim3 fg, dim3 fd, size_t flds, const FfnArgs& A, hipStream_t s, Timing tg,
+                 Timing td)
+{
+    switch (KS) {
+    case 2: launch_fast_ks<BITS, 2>(route, fg, fd, flds, A, s, tg, td); break;
+    case 3: launch_fast_ks<BITS, 3>(route, fg, fd, flds, A, s, tg, td); break;
+    case 5: launch_fast_ks<BITS, 5>(route, fg, fd, flds, A, s, tg, td); break;
+    case 7: launch_fast_ks<BITS, 7>(route, fg, fd, flds, A, s, tg, td); break;
+    default: launch_fast_ks<BITS, 9>(route, fg, fd, flds, A, s, tg, td); break;
+    }
+}
+
+void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4* xst, const double* logits,
+                int renorm, int32_t* idx, float* w, int B, int K, int E, float shared_w, void* hq, float* y,
+                hipStream_t s, Timing t_gateup, Timing t_down)
+{
+    FfnArgs A;
+    A.slab = (const uint8_t*)slab;
+    A.L = L;
+    A.xq = xq;
+    A.xst = xst;
+    A.logits = logits;
+    A.renorm = renorm;
+    A.idx = idx;
+    A.w = w;
+    A.K = K;
+    A.E = E;
+    A.shared_w = shared_w;
+    A.hq = (uint16_t*)hq;
+    A.y = y;
+    A.sc = down_slots_per_round(L);
+    const int grows = 4 * GU_RPW * (64 / lanes_per_row(L.Gh));
+    const int drows = 4 * DN_RPW * (64 / lanes_per_row(L.Gi));
+    const dim3 ggrid((L.I + grows - 1) / grows, B), dgrid((L.H + drows - 1) / drows, B);
+    const int KS = K + 1;
+    const bool fast = L.Gh <= 64 && L.Gi <= 64 && KS * 8 * L.Gi <= 1024 &&
+                      (KS == 2 || KS == 3 || KS == 5 || KS == 7 || KS == 9);
+    if (fast) {
+        const dim3 fg((L.I + 4 * (64 / lanes_per_row(L.Gh)) - 1) / (4 * (64 / lanes_per_row(L.Gh))), B);
+        const dim3 fd((L.H + 4 * (64 / lanes_per_row(L.Gi)) - 1) / (4 * (64 / lanes_per_row(L.Gi))), B);
+        const size_t flds = (size_t)KS * 9 * L.Gi * 16;
+        if (L.bits == 4)
+            launch_fast<4>(KS, logits != nullptr, fg, fd, flds, A, s, t_gateup, t_down);
+        else
+            launch_fast<2>(KS, logits != nullptr, fg, fd, flds, A, s, t_gateup, t_down);
+        return;
+    }
+    const size_t lds = (size_t)A.sc * 9 * L.Gi * 16;
+    if (L.bits == 4) {
+        hipExtLaunchKernelGGL(k_gateup<4>, ggrid, dim3(256), 0, s, t_gateup.start, t_gateup.stop, 0, A);
+        hipExtLaunchKernelGGL(k_down<4>, dgrid, dim3(256), lds, s, t_down.start, t_down.stop, 0, A);
+    } else {
+        hipExtLaunchKernelGGL(k_gateup<2>, ggrid, dim3(256), 0, s, t_gateup.start, t_gateup.stop, 0, A);
+        hipExtLaunchKernelGGL(k_down<2>, dgrid, dim3(256), lds, s, t_down.start, t_down.stop, 0, A);
+    }
 }
 
 // ----------------------------------------------------------------------------

@@ -91,18 +91,15 @@ int check_desc(const char* fn, const moe_layer_desc* d, int B)
 
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace sections (each 256-byte aligned).  The counter word must be zero
-// between calls; the router's last block resets it.
+// Workspace sections (each 256-byte aligned): the logits, the routing (when
+// the caller does not want it back), the token's dequant operand and h.
 struct Work {
-    unsigned* counter;
     double* logits;
     int32_t* idx;
     float* w;
     uint4* xq;
     float4* xst;
-    float* h;
-    uint4* hq;
-    float4* hst;
+    void* hq;
     size_t bytes;
 };
 
@@ -117,15 +114,12 @@ Work carve(void* ws, int B, int H, int I, int E, int K)
         return q;
     };
     const size_t Gh = H / 64, Gi = I / 64, S = (size_t)B * (K + 1);
-    W.counter = (unsigned*)take(256);
     W.logits = (double*)take((size_t)B * E * 8);
     W.idx = (int32_t*)take((size_t)B * K * 4);
     W.w = (float*)take((size_t)B * K * 4);
     W.xq = (uint4*)take((size_t)B * Gh * 128);
     W.xst = (float4*)take((size_t)B * Gh * 16);
-    W.h = (float*)take(S * I * 4);
-    W.hq = (uint4*)take(S * Gi * 128);
-    W.hst = (float4*)take(S * Gi * 16);
+    W.hq = take(S * Gi * 128);
     W.bytes = off;
     return W;
 }
@@ -135,17 +129,6 @@ int hip_status(const char* fn)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", fn, hipGetErrorString(e));
     return ok();
-}
-
-int ffn_impl(const char* fn, const moe_layer_desc* d, const float* x, int B, const int32_t* idx, const float* w,
-             float* y, const Work& W, hipStream_t s)
-{
-    const Layout L = make_layout(d->bits, d->H, d->I);
-    launch_prep(d->bits, x, B, d->H, W.xq, W.xst, s);
-    launch_gateup(L, d->experts, W.xq, W.xst, idx, B, d->K, d->E, W.h, s, g_timing[KID_GATEUP]);
-    launch_prep(d->bits, W.h, B * (d->K + 1), d->I, W.hq, W.hst, s);
-    launch_down(L, d->experts, W.hq, W.hst, idx, w, B, d->K, d->E, d->shared_weight, y, s, g_timing[KID_DOWN]);
-    return hip_status(fn);
 }
 
 }  // namespace
@@ -182,7 +165,7 @@ size_t moe_workspace_bytes(const moe_layer_desc* desc, int B)
 size_t moe_route_workspace_bytes(int B, int E, int K)
 {
     if (check_routing("moe_route_workspace_bytes", B, E, K)) return 0;
-    return 256 + up256((size_t)B * E * 8);
+    return up256((size_t)B * E * 8);
 }
 
 size_t moe_stack_extra_bytes(int B, int H)
@@ -238,9 +221,9 @@ int moe_route_topk(const float* x, int B, const float* w_router, const float* lo
     CHECK_PTR(ws);
     const size_t need = moe_route_workspace_bytes(B, E, K);
     if (ws_bytes < need) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
-    char* p = (char*)ws;
-    launch_router(x, B, w_router, logit_bias, H, E, K, renormalize ? 1 : 0, (double*)(p + 256), (unsigned*)p,
-                  idx_out, w_out, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    launch_router(4, x, B, w_router, logit_bias, H, E, (double*)ws, nullptr, nullptr, s, g_timing[KID_ROUTER]);
+    launch_topk((const double*)ws, B, E, K, renormalize ? 1 : 0, idx_out, w_out, s);
     return hip_status(fn);
 }
 
@@ -257,7 +240,12 @@ static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, cons
     CHECK_PTR(ws);
     const Work W = carve(ws, B, desc->H, desc->I, desc->E, desc->K);
     if (ws_bytes < W.bytes) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, W.bytes);
-    return ffn_impl(fn, desc, x, B, idx, w, y_out, W, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    const Layout L = make_layout(desc->bits, desc->H, desc->I);
+    launch_prep(desc->bits, x, B, desc->H, W.xq, W.xst, s);
+    launch_ffn(L, desc->experts, W.xq, W.xst, nullptr, 0, const_cast<int32_t*>(idx), const_cast<float*>(w), B,
+               desc->K, desc->E, desc->shared_weight, W.hq, y_out, s, g_timing[KID_GATEUP], g_timing[KID_DOWN]);
+    return hip_status(fn);
 }
 
 int moe_expert_ffn_q4(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx, const float* w,
@@ -277,9 +265,12 @@ static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, i
 {
     int32_t* idx = idx_out ? idx_out : W.idx;
     float* w = w_out ? w_out : W.w;
-    launch_router(x, B, d->w_router, d->logit_bias, d->H, d->E, d->K, d->renormalize ? 1 : 0, W.logits, W.counter,
-                  idx, w, s, g_timing[KID_ROUTER]);
-    return ffn_impl(fn, d, x, B, idx, w, y_out, W, s);
+    const Layout L = make_layout(d->bits, d->H, d->I);
+    launch_router(d->bits, x, B, d->w_router, d->logit_bias, d->H, d->E, W.logits, W.xq, W.xst, s,
+                  g_timing[KID_ROUTER]);
+    launch_ffn(L, d->experts, W.xq, W.xst, W.logits, d->renormalize ? 1 : 0, idx, w, B, d->K, d->E,
+               d->shared_weight, W.hq, y_out, s, g_timing[KID_GATEUP], g_timing[KID_DOWN]);
+    return hip_status(fn);
 }
 
 int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y_out, int32_t* idx_out,

@@ -55,7 +55,7 @@ def test_workspace_sizes():
     assert 0 < w1 < w64
     assert moe.workspace_bytes(d, 0) == 0
     assert moe.workspace_bytes(d, 257) == 0
-    assert moe.route_workspace_bytes(1, 512, 4) >= 256 + 512 * 8
+    assert moe.route_workspace_bytes(1, 512, 4) >= 512 * 8
     assert moe.stack_extra_bytes(1, 4096) == 2 * 16384
 
 
