@@ -233,40 +233,46 @@ __device__ inline double key_value(uint64_t k)  // the logit to within 2^-42 rel
     return __longlong_as_double((long long)u);
 }
 
-// Load the logits a wave selects from: lane l holds ids l + 64 j, j < 16
+// Load the logits a wave selects from: lane l holds ids l + 64 j, j < NL
 // (clamped indices: every lane loads, the selection masks ids >= E).
-__device__ inline void topk_load(const double* __restrict__ lg, int E, int lane, double (&lv)[16])
+template <int NL>
+__device__ inline void topk_load(const double* __restrict__ lg, int E, int lane, double (&lv)[NL])
 {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) lv[j] = lg[min(lane + 64 * j, E - 1)];
+    for (int j = 0; j < NL; ++j) lv[j] = lg[min(lane + 64 * j, E - 1)];
 }
 
 struct OpU64Max {
     __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return b > a ? b : a; }
 };
 
-// Top-K of one token's E logits by one wave.  Lane k < K returns the k-th
-// expert (rank order) and its routing weight; every lane sees the same selection.
-template <int KMAX>
-__device__ void topk_select(const double (&lv)[16], int E, int K, int renorm, int lane, int& my_id, float& my_w)
+// Top-K of one token's E <= 64 * NL logits by one wave.  Lane k < K returns
+// the k-th expert (rank order) and its routing weight; every lane sees the
+// same selection.  All loops have compile-time trip counts, so the keys stay
+// in registers.
+template <int KMAX, int NL>
+__device__ void topk_select(const double (&lv)[NL], int E, int K, int renorm, int lane, int& my_id, float& my_w)
 {
-    const int NL = (E + 63) / 64;  // <= 16
-    uint64_t key[16];
+    uint64_t key[NL];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < NL; ++j) {
         const int id = lane + 64 * j;
-        key[j] = (j < NL && id < E) ? select_key(lv[j], id) : 0ull;
+        key[j] = (id < E) ? select_key(lv[j], id) : 0ull;
     }
     uint64_t mine = 0ull, top = 0ull;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         if (k >= K) break;
-        uint64_t best = 0ull;
+        uint64_t t[NL];  // this lane's best remaining key: a tree over its candidates
 #pragma unroll
-        for (int j = 0; j < 16; ++j) best = key[j] > best ? key[j] : best;
-        best = group_reduce(best, OpU64Max(), 64);
+        for (int j = 0; j < NL; ++j) t[j] = key[j];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) key[j] = (key[j] == best) ? 0ull : key[j];  // keys are unique
+        for (int w = 1; w < NL; w *= 2)
+#pragma unroll
+            for (int j = 0; j + w < NL; j += 2 * w) t[j] = t[j + w] > t[j] ? t[j + w] : t[j];
+        const uint64_t best = group_reduce(t[0], OpU64Max(), 64);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) key[j] = (key[j] == best) ? 0ull : key[j];  // keys are unique
         if (k == 0) top = best;
         if (lane == k) mine = best;
     }
@@ -274,11 +280,16 @@ __device__ void topk_select(const double (&lv)[16], int E, int K, int renorm, in
     const double lmax = key_value(top);
     // softmax weights in fp32: exp of logit differences, renormalized over the K
     const float ew = (lane < K) ? __expf((float)(key_value(mine) - lmax)) : 0.f;
-    float part = 0.f;
+    float denom;
+    if (renorm) {
+        denom = wave_sum(ew);
+    } else {
+        float part = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-        if (j < NL && lane + 64 * j < E) part += __expf((float)(lv[j] - lmax));
-    const float denom = renorm ? wave_sum(ew) : wave_sum(part);
+        for (int j = 0; j < NL; ++j)
+            if (lane + 64 * j < E) part += __expf((float)(lv[j] - lmax));
+        denom = wave_sum(part);
+    }
     my_w = ew / denom;
 }
 
@@ -369,8 +380,8 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
     int id;
     float wt;
     double lv[16];
-    topk_load(logits + (long long)b * E, E, lane, lv);
-    topk_select<32>(lv, E, K, renorm, lane, id, wt);
+    topk_load<16>(logits + (long long)b * E, E, lane, lv);
+    topk_select<32, 16>(lv, E, K, renorm, lane, id, wt);
     if (lane < K) {
         idx[(long long)b * K + lane] = id;
         w[(long long)b * K + lane] = wt;
@@ -436,7 +447,7 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
     int my_id = 0;
     float my_w = 0.f;
     if (A.logits)
-        topk_load(A.logits + (long long)b * A.E, A.E, lane, lv);
+        topk_load<16>(A.logits + (long long)b * A.E, A.E, lane, lv);
     else if (lane < K)
         my_id = A.idx[(long long)b * K + lane];
     bool routed = false;
@@ -486,7 +497,7 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
                 i0 = 1;
                 if (!routed) {
                     if (A.logits) {
-                        topk_select<32>(lv, A.E, K, A.renorm, lane, my_id, my_w);
+                        topk_select<32, 16>(lv, A.E, K, A.renorm, lane, my_id, my_w);
                         if (blockIdx.x == 0 && wave == 0 && lane < K) {
                             A.idx[(long long)b * K + lane] = my_id;
                             A.w[(long long)b * K + lane] = my_w;
@@ -702,30 +713,38 @@ __global__ __launch_bounds__(256) void k_down(FfnArgs A)
 // compiler can keep the loads of all phases in flight and wait only for what
 // each phase needs.
 // ----------------------------------------------------------------------------
+constexpr int FAST_NL = 8;  // fast path: E <= 512 logits per token, 8 per lane
+
 template <int BITS, int KS, bool ROUTE>
 __global__ __launch_bounds__(256) void k_gateup_fast(FfnArgs A)
 {
     constexpr int K = KS - 1;
+    // a row's K+1 expert slots are split over two waves (the shared expert plus
+    // the first routed ones in half 0), so two waves per SIMD overlap one
+    // another's loads and arithmetic
+    constexpr int S0 = (KS + 1) / 2;  // slots of half 0: positions [0, S0)
+    constexpr int SMAX = S0;
     const Layout& L = A.L;
     const int b = blockIdx.y;
     const int G = L.Gh, LPR = lanes_per_row(G), RPP = 64 / LPR;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int half = wave & 1;
     const int sub = lane / LPR, gl = lane & (LPR - 1);
     const bool gv = gl < G;
     const int g = gv ? gl : G - 1;
-    const int r = (blockIdx.x * 4 + wave) * RPP + sub;
+    const int r = (blockIdx.x * 2 + (wave >> 1)) * RPP + sub;
     const bool rv = r < L.I;
     const int rc = rv ? r : L.I - 1;
     const Masks M = load_masks();
+    const int p0 = half ? S0 : 0;               // first slot position of this wave
+    const int np = half ? KS - S0 : S0;         // slots of this wave
 
     // 1. routing inputs (cache-resident, they gate the routed loads)
-    double lv[16];
+    double lv[FAST_NL];
     int my_id = 0;
     float my_w = 0.f;
     if (ROUTE) {
-        const double* lg = A.logits + (long long)b * A.E;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) lv[j] = lg[min(lane + 64 * j, A.E - 1)];
+        topk_load<FAST_NL>(A.logits + (long long)b * A.E, A.E, lane, lv);
     } else {
         my_id = A.idx[(long long)b * K + min(lane, K - 1)];
     }
@@ -736,7 +755,7 @@ __global__ __launch_bounds__(256) void k_gateup_fast(FfnArgs A)
     for (int j = 0; j < 8; ++j) xp[j] = A.xq[((long long)b * 8 + j) * G + g];
     const float4 st = A.xst[(long long)b * G + g];
 
-    SlotRegs<BITS> R[KS];
+    SlotRegs<BITS> R[SMAX];
     auto issue = [&](SlotRegs<BITS>& S, int e) {
         const uint8_t* rec = A.slab + (long long)e * L.record;
         const uint8_t* base = rec + (long long)rc * 2 * L.hb;
@@ -749,27 +768,29 @@ __global__ __launch_bounds__(256) void k_gateup_fast(FfnArgs A)
         S.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)rc * G + g) * 8);
     };
     // 3. the shared expert needs no routing: its loads go out first
-    issue(R[K], A.E);
+    if (half == 0) issue(R[0], A.E);
     __builtin_amdgcn_sched_barrier(0);
     // 4. select the routed experts while those loads are in flight
     if (ROUTE) {
-        topk_select<K>(lv, A.E, K, A.renorm, lane, my_id, my_w);
+        topk_select<K, FAST_NL>(lv, A.E, K, A.renorm, lane, my_id, my_w);
         if (blockIdx.x == 0 && wave == 0 && lane < K) {
             A.idx[(long long)b * K + lane] = my_id;
             A.w[(long long)b * K + lane] = my_w;
         }
     }
-    // 5. the routed experts' loads (an invalid id reads expert 0 and yields NaN)
-    bool bad[KS];
+    // 5. this wave's routed loads (an invalid id reads expert 0 and yields NaN)
+    bool bad[SMAX];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int e = __builtin_amdgcn_readlane(my_id, k);
-        bad[k] = (e < 0 || e >= A.E);
-        issue(R[k], bad[k] ? 0 : e);
+    for (int i = 0; i < SMAX; ++i) {
+        bad[i] = false;
+        const int pos = p0 + i;
+        if (i >= np || pos == 0) continue;
+        const int e = __builtin_amdgcn_readlane(my_id, pos - 1);
+        bad[i] = (e < 0 || e >= A.E);
+        issue(R[i], bad[i] ? 0 : e);
     }
     __builtin_amdgcn_sched_barrier(0);
-    bad[K] = false;
-    // 6. dequant-GEMV of every slot, shared first (its data arrives first)
+    // 6. dequant-GEMV of this wave's slots, in arrival order
     uint16_t* hq_tok = A.hq + (long long)b * KS * L.Gi * 64;
     const int grp = rc >> 6, cc = rc & 63;
     int pp, hi;
@@ -782,22 +803,24 @@ __global__ __launch_bounds__(256) void k_gateup_fast(FfnArgs A)
     }
     const long long hoff = ((long long)(pp >> 2) * L.Gi + grp) * 8 + (pp & 3) * 2 + hi;
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-        const int k = (i == 0) ? K : i - 1;
+    for (int i = 0; i < SMAX; ++i) {
+        if (i >= np) break;
+        const int pos = p0 + i;
+        const int k = (pos == 0) ? K : pos - 1;
         float dg, du;
         if (BITS == 4) {
-            dg = group_dot_q4(M, R[k].g0, R[k].g1, xp);
-            du = group_dot_q4(M, R[k].u0, R[k].u1, xp);
+            dg = group_dot_q4(M, R[i].g0, R[i].g1, xp);
+            du = group_dot_q4(M, R[i].u0, R[i].u1, xp);
         } else {
-            dg = group_dot_q2(M, R[k].g0, xp);
-            du = group_dot_q2(M, R[k].u0, xp);
+            dg = group_dot_q2(M, R[i].g0, xp);
+            du = group_dot_q2(M, R[i].u0, xp);
         }
-        const uint2 sb = R[k].sb;
+        const uint2 sb = R[i].sb;
         float ga = fmaf(bf16_lo(sb.x) * st.z, dg - st.x, bf16_hi(sb.x) * st.y);
         float ua = fmaf(bf16_lo(sb.y) * st.z, du - st.x, bf16_hi(sb.y) * st.y);
         ga = lane_group_sum(gv ? ga : 0.f, LPR);
         ua = lane_group_sum(gv ? ua : 0.f, LPR);
-        const float h = bad[k] ? __builtin_nanf("") : ga / (1.f + __expf(-ga)) * ua;
+        const float h = bad[i] ? __builtin_nanf("") : ga / (1.f + __expf(-ga)) * ua;
         if (gl == 0 && rv)
             hq_tok[(long long)k * L.Gi * 64 + hoff] = __builtin_bit_cast(uint16_t, (_Float16)(h * (1.f / H_SCALE)));
     }
@@ -951,10 +974,10 @@ void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4
     const int drows = 4 * DN_RPW * (64 / lanes_per_row(L.Gi));
     const dim3 ggrid((L.I + grows - 1) / grows, B), dgrid((L.H + drows - 1) / drows, B);
     const int KS = K + 1;
-    const bool fast = L.Gh <= 64 && L.Gi <= 64 && KS * 8 * L.Gi <= 1024 &&
+    const bool fast = L.Gh <= 64 && L.Gi <= 64 && KS * 8 * L.Gi <= 1024 && E <= 64 * FAST_NL &&
                       (KS == 2 || KS == 3 || KS == 5 || KS == 7 || KS == 9);
     if (fast) {
-        const dim3 fg((L.I + 4 * (64 / lanes_per_row(L.Gh)) - 1) / (4 * (64 / lanes_per_row(L.Gh))), B);
+        const dim3 fg((L.I + 2 * (64 / lanes_per_row(L.Gh)) - 1) / (2 * (64 / lanes_per_row(L.Gh))), B);
         const dim3 fd((L.H + 4 * (64 / lanes_per_row(L.Gi)) - 1) / (4 * (64 / lanes_per_row(L.Gi))), B);
         const size_t flds = (size_t)KS * 9 * L.Gi * 16;
         if (L.bits == 4)
