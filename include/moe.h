@@ -139,8 +139,10 @@ int moe_route_topk(const float* x, int B, const float* w_router, const float* lo
  * FFN_{idx[b][k]}(x[b]) + shared_weight * FFN_shared(x[b]).
  *   x: fp32 [B][H]; idx: int32 [B][K]; w: fp32 [B][K]; y_out: fp32 [B][H].
  * _q4 requires desc->bits == 4, _q2 requires desc->bits == 2.
- * B > 1 groups the tokens by expert so each active expert's weights are read
- * once per call.
+ * With 4-bit codes and B > 1 the tokens are grouped by expert (as
+ * moe_group_tokens) so each active expert's weights are read once per call and
+ * multiplied against all of its tokens on the matrix cores; 2-bit batches run
+ * token by token.
  */
 int moe_expert_ffn_q4(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx,
                       const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
@@ -154,6 +156,21 @@ int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const i
  */
 int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y_out,
                      int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Token -> expert grouping of a batch's routing ([LLMAPIS] section 深度分析: only
+ * the selected experts are read; with B tokens each selected expert is read
+ * once for all the tokens that chose it).  A stable counting sort of the B*K
+ * slots (slot i = b*K + k names expert idx[i]) by expert id:
+ *   offsets_out: int32 [E + 1]; the slots of expert e are positions
+ *     offsets_out[e] .. offsets_out[e+1]-1 of
+ *   tokens_out: int32 [B*K] (token b of the slot) and
+ *   slots_out:  int32 [B*K] (the slot index b*K + k), in increasing slot order.
+ * Slots whose id is outside [0, E) are left out (offsets_out[E] is the number
+ * placed).  All arrays are device memory owned by the caller; no workspace.
+ */
+int moe_group_tokens(const int32_t* idx, int B, int K, int E, int32_t* offsets_out,
+                     int32_t* tokens_out, int32_t* slots_out, void* stream);
 
 /*
  * x_out[b] = y[b] / sqrt(mean(y[b]^2) + eps), no gain, no residual: the

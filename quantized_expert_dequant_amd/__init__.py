@@ -62,6 +62,7 @@ def lib():
             "moe_expert_ffn_q4": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_expert_ffn_q2": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_layer_decode": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_group_tokens": (i32, [vp, i32, i32, i32, vp, vp, vp, vp]),
             "moe_rmsnorm": (i32, [vp, i32, i32, f32, vp, vp]),
             "moe_stack_decode": (i32, [dp, i32, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
             "moe_set_timing_events": (i32, [i32, vp, vp]),
@@ -160,6 +161,11 @@ def expert_ffn_q2(desc, x, B, idx, w, y_out, ws, ws_bytes, stream=None):
 def layer_decode(desc, x, B, y_out, idx_out, w_out, ws, ws_bytes, stream=None):
     return _check(lib().moe_layer_decode(ctypes.byref(desc), _p(x), B, _p(y_out), _p(idx_out), _p(w_out), _p(ws),
                                          ws_bytes, _stream(stream)))
+
+
+def group_tokens(idx, B, K, E, offsets_out, tokens_out, slots_out, stream=None):
+    return _check(lib().moe_group_tokens(_p(idx), B, K, E, _p(offsets_out), _p(tokens_out), _p(slots_out),
+                                         _stream(stream)))
 
 
 def rmsnorm(y, B, H, eps, x_out, stream=None):

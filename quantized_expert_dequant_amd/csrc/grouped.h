@@ -1,0 +1,51 @@
+// grouped.h - host-side interface of the batched decode path (grouped.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// Output of the grouping kernel.  offsets / tokens / slots: the assignments of
+// expert e are positions [offsets[e], offsets[e+1]) of tokens (token id) and
+// slots (slot b*K + k), in slot order.  The rest is the MFMA work list and may
+// be null together: grp_u[0] = U distinct routed experts; act_expert[0] = E
+// (the shared expert, all B tokens), act_expert[1 + j] = j-th active routed
+// expert by id; entries act_off[u] .. act_off[u+1] of ent_token belong to
+// act_expert[u]; slot_pos[b*K + k] = entry of that slot (-1: invalid id).
+struct GroupOut {
+    int32_t* offsets;     // [E + 1]
+    int32_t* tokens;      // [B*K]
+    int32_t* slots;       // [B*K]
+    int32_t* grp_u;       // [1]
+    int32_t* act_expert;  // [E + 1]
+    int32_t* act_off;     // [E + 2]
+    int32_t* ent_token;   // [B + B*K]
+    int32_t* slot_pos;    // [B*K]
+};
+
+// Workspace of the batched path, carved from the caller's buffer.
+struct GroupedWork {
+    double* partial;  // router partial logits [splits][B][E]
+    GroupOut g;
+    uint4* xhl;       // token operands [B][G_h][16] uint4
+    float* xscale;    // [B]
+    uint4* hb;        // h operands [B + B*K][8][G_i] uint4
+    float* part;      // down outputs [B + B*K][H]
+};
+
+bool grouped_supported(const Layout& L, int B, int K);
+size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E);
+GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E);
+int router_splits(int H);
+void launch_route_batched(const float* x, int B, const float* W, const float* bias, int H, int E, int K, int renorm,
+                          double* partial, double* logits, int32_t* idx, float* w, hipStream_t s, Timing t);
+void launch_group(const int32_t* idx, int B, int K, int E, const GroupOut& O, hipStream_t s);
+void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W, const float* x, const float* w,
+                        float shared_w, int B, int K, int E, float* y, hipStream_t s, Timing tg, Timing td);
+
+}  // namespace moe

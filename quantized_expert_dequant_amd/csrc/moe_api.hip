@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "../../include/moe.h"
+#include "grouped.h"
 #include "launch.h"
 
 using namespace moe;
@@ -92,7 +93,8 @@ int check_desc(const char* fn, const moe_layer_desc* d, int B)
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Workspace sections (each 256-byte aligned): the logits, the routing (when
-// the caller does not want it back), the token's dequant operand and h.
+// the caller does not want it back), the token's dequant operand and h; for a
+// batch that takes the grouped path, its sections follow.
 struct Work {
     double* logits;
     int32_t* idx;
@@ -100,10 +102,12 @@ struct Work {
     uint4* xq;
     float4* xst;
     void* hq;
+    bool grouped;
+    GroupedWork gw;
     size_t bytes;
 };
 
-Work carve(void* ws, int B, int H, int I, int E, int K)
+Work carve(void* ws, int bits, int B, int H, int I, int E, int K)
 {
     Work W;
     char* p = (char*)ws;
@@ -120,6 +124,14 @@ Work carve(void* ws, int B, int H, int I, int E, int K)
     W.xq = (uint4*)take((size_t)B * Gh * 128);
     W.xst = (float4*)take((size_t)B * Gh * 16);
     W.hq = take(S * Gi * 128);
+    const Layout L = make_layout(bits, H, I);
+    W.grouped = grouped_supported(L, B, K);
+    W.gw = GroupedWork{};
+    if (W.grouped) {
+        const size_t n = grouped_workspace_bytes(L, B, K, E);
+        if (p) W.gw = carve_grouped(p + off, L, B, K, E);
+        off += up256(n);
+    }
     W.bytes = off;
     return W;
 }
@@ -159,7 +171,7 @@ size_t moe_workspace_bytes(const moe_layer_desc* desc, int B)
     if (!desc || check_shape("moe_workspace_bytes", desc->bits, desc->H, desc->I, desc->group) ||
         check_routing("moe_workspace_bytes", B, desc->E, desc->K))
         return 0;
-    return carve(nullptr, B, desc->H, desc->I, desc->E, desc->K).bytes;
+    return carve(nullptr, desc->bits, B, desc->H, desc->I, desc->E, desc->K).bytes;
 }
 
 size_t moe_route_workspace_bytes(int B, int E, int K)
@@ -238,10 +250,16 @@ static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, cons
     CHECK_PTR4(w);
     CHECK_PTR(y_out);
     CHECK_PTR(ws);
-    const Work W = carve(ws, B, desc->H, desc->I, desc->E, desc->K);
+    const Work W = carve(ws, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
     if (ws_bytes < W.bytes) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, W.bytes);
     hipStream_t s = (hipStream_t)stream;
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
+    if (W.grouped) {
+        launch_group(idx, B, desc->K, desc->E, W.gw.g, s);
+        launch_ffn_grouped(L, desc->experts, W.gw, x, w, desc->shared_weight, B, desc->K, desc->E, y_out, s,
+                           g_timing[KID_GATEUP], g_timing[KID_DOWN]);
+        return hip_status(fn);
+    }
     launch_prep(desc->bits, x, B, desc->H, W.xq, W.xst, s);
     launch_ffn(L, desc->experts, W.xq, W.xst, nullptr, 0, const_cast<int32_t*>(idx), const_cast<float*>(w), B,
                desc->K, desc->E, desc->shared_weight, W.hq, y_out, s, g_timing[KID_GATEUP], g_timing[KID_DOWN]);
@@ -266,6 +284,14 @@ static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, i
     int32_t* idx = idx_out ? idx_out : W.idx;
     float* w = w_out ? w_out : W.w;
     const Layout L = make_layout(d->bits, d->H, d->I);
+    if (W.grouped) {
+        launch_route_batched(x, B, d->w_router, d->logit_bias, d->H, d->E, d->K, d->renormalize ? 1 : 0,
+                             W.gw.partial, nullptr, idx, w, s, g_timing[KID_ROUTER]);
+        launch_group(idx, B, d->K, d->E, W.gw.g, s);
+        launch_ffn_grouped(L, d->experts, W.gw, x, w, d->shared_weight, B, d->K, d->E, y_out, s,
+                           g_timing[KID_GATEUP], g_timing[KID_DOWN]);
+        return hip_status(fn);
+    }
     launch_router(d->bits, x, B, d->w_router, d->logit_bias, d->H, d->E, W.logits, W.xq, W.xst, s,
                   g_timing[KID_ROUTER]);
     launch_ffn(L, d->experts, W.xq, W.xst, W.logits, d->renormalize ? 1 : 0, idx, w, B, d->K, d->E,
@@ -286,9 +312,27 @@ int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y
     CHECK_OPT_PTR4(idx_out);
     CHECK_OPT_PTR4(w_out);
     CHECK_PTR(ws);
-    const Work W = carve(ws, B, desc->H, desc->I, desc->E, desc->K);
+    const Work W = carve(ws, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
     if (ws_bytes < W.bytes) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, W.bytes);
     return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, (hipStream_t)stream);
+}
+
+int moe_group_tokens(const int32_t* idx, int B, int K, int E, int32_t* offsets_out, int32_t* tokens_out,
+                     int32_t* slots_out, void* stream)
+{
+    const char* fn = "moe_group_tokens";
+    int rc = check_routing(fn, B, E, K);
+    if (rc) return rc;
+    CHECK_PTR4(idx);
+    CHECK_PTR4(offsets_out);
+    CHECK_PTR4(tokens_out);
+    CHECK_PTR4(slots_out);
+    GroupOut O{};
+    O.offsets = offsets_out;
+    O.tokens = tokens_out;
+    O.slots = slots_out;
+    launch_group(idx, B, K, E, O, (hipStream_t)stream);
+    return hip_status(fn);
 }
 
 int moe_rmsnorm(const float* y, int B, int H, float eps, float* x_out, void* stream)
@@ -324,7 +368,7 @@ int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* x,
     CHECK_OPT_PTR4(w_out);
     CHECK_PTR(ws);
     const moe_layer_desc& d0 = layers[0];
-    const Work W = carve(ws, B, d0.H, d0.I, d0.E, d0.K);
+    const Work W = carve(ws, d0.bits, B, d0.H, d0.I, d0.E, d0.K);
     const size_t vec = up256((size_t)B * d0.H * 4);
     const size_t need = W.bytes + 2 * vec;
     if (ws_bytes < need) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);

@@ -1,0 +1,175 @@
+"""GPU parity of the batched decode path (B > 1 tokens, 4-bit codes).
+
+The batch's B*K assignments are grouped by expert and every active expert is
+multiplied against all of its tokens on the matrix cores.  Bars: the grouping
+and the expert indices bit-exact against the oracle, routing weights within
+1e-6 relative, each token's output within max|dy| / max|y_ref| <= 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import quantized_expert_dequant_amd as moe
+from quantized_expert_dequant_amd.slab import workspace
+
+from helpers import TOL, W_RTOL, WORKLOADS, build_layer, oracle_layer, oracle_route, rel_err, seed_of
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    moe.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def layers():
+    cache = {}
+
+    def get(n):
+        if n not in cache:
+            cache[n] = build_layer(WORKLOADS[n], seed_of(n))
+        return cache[n]
+
+    yield get
+    cache.clear()
+
+
+def _zipf_selection(rng, B, K, E, s=1.1):
+    p = (np.arange(E) + 1.0) ** -s
+    p /= p.sum()
+    return np.stack([rng.choice(E, K, replace=False, p=p) for _ in range(B)]).astype(np.int32)
+
+
+# -------------------------------------------------------------- grouping ----
+
+def _group_gpu(idx, E):
+    B, K = idx.shape
+    off = torch.full((E + 1,), -7, dtype=torch.int32, device=DEV)
+    tok = torch.full((B * K,), -7, dtype=torch.int32, device=DEV)
+    sl = torch.full((B * K,), -7, dtype=torch.int32, device=DEV)
+    moe.group_tokens(_t(idx), B, K, E, off, tok, sl)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), tok.cpu().numpy(), sl.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["zipf", "dup_invalid", "one_token", "max"])
+def test_group_tokens_bit_exact(case):
+    rng = np.random.default_rng(11)
+    if case == "zipf":
+        E, idx = 512, _zipf_selection(rng, 64, 10, 512)
+    elif case == "dup_invalid":
+        E = 37
+        idx = rng.integers(-3, E + 3, size=(23, 7)).astype(np.int32)
+    elif case == "one_token":
+        E, idx = 16, np.array([[3, 0, 15, 7]], np.int32)
+    else:
+        E, idx = 1024, rng.integers(0, 1024, size=(256, 32)).astype(np.int32)
+    off, tok, sl = _group_gpu(idx, E)
+    off_r, tok_r, sl_r, _ = oracle.group_by_expert(idx, E)
+    n = off_r[E]
+    np.testing.assert_array_equal(off, off_r)
+    np.testing.assert_array_equal(tok[:n], tok_r[:n])
+    np.testing.assert_array_equal(sl[:n], sl_r[:n])
+    assert np.all(tok[n:] == -7) and np.all(sl[n:] == -7)   # nothing written past the placed slots
+
+
+# ----------------------------------------------------------------- layer ----
+
+def _decode(layer, x):
+    B = x.shape[0]
+    ws, n = workspace(layer.desc, B)
+    y = torch.empty((B, layer.H), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, layer.K), dtype=torch.int32, device=DEV)
+    w = torch.empty((B, layer.K), dtype=torch.float32, device=DEV)
+    moe.layer_decode(layer.desc, _t(x), B, y, idx, w, ws, n)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("B", [2, 16, 37])
+def test_batched_tiny_layer(layers, B):
+    """Every token of a tiny batch against the oracle (several 16-token tiles, ragged tail)."""
+    L = layers(0)
+    cfg, seed = WORKLOADS[0], seed_of(0)
+    x = synth.tokens(seed, 100 + B, B, L.H)
+    y, idx, w = _decode(L, x)
+    y_ref, idx_ref, w_ref, margin = oracle_layer(cfg, seed, 0, x)
+    assert np.all(margin > 1e-9)
+    np.testing.assert_array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
+    for b in range(B):
+        assert rel_err(y[b], y_ref[b]) <= TOL, "token %d" % b
+
+
+@pytest.mark.parametrize("step", range(2))
+def test_batched_full_size(layers, step):
+    """B=64, K=10 with the Zipf(1.1) prior: routing of all 64 tokens, outputs of sampled tokens."""
+    n = 4
+    L = layers(n)
+    cfg, seed = WORKLOADS[n], seed_of(n)
+    x = synth.tokens(seed, step, cfg["B"], L.H)
+    y, idx, w = _decode(L, x)
+    _, _, _, sel = oracle_route(cfg, seed, 0, x)
+    idx_ref = np.stack([s[0] for s in sel])
+    w_ref = np.stack([s[1] for s in sel])
+    assert min(s[2] for s in sel) > 1e-9
+    np.testing.assert_array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
+    sample = [0, 13, 31, 42, 63]
+    y_ref, _, _, _ = oracle_layer(cfg, seed, 0, x[sample])
+    errs = [rel_err(y[b], y_ref[j]) for j, b in enumerate(sample)]
+    print("batched step %d: distinct experts %d, max rel err %.2e" % (step, len(np.unique(idx)), max(errs)))
+    assert max(errs) <= TOL
+
+
+def test_batched_is_deterministic(layers):
+    L = layers(4)
+    x = synth.tokens(seed_of(4), 7, 64, L.H)
+    a = _decode(L, x)
+    b = _decode(L, x)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_batched_given_routing_duplicates_and_invalid(layers):
+    """Caller routing may repeat an expert within a token; an invalid id makes that token's row NaN."""
+    L = layers(0)
+    cfg, seed = WORKLOADS[0], seed_of(0)
+    B, K, E, H, I = 9, L.K, L.E, L.H, L.I
+    rng = np.random.default_rng(5)
+    x = synth.tokens(seed, 77, B, H)
+    idx = rng.integers(0, E, size=(B, K)).astype(np.int32)
+    idx[0] = [5, 5, 5, 2]
+    idx[4, 1] = -1
+    idx[7, 3] = E
+    w = rng.random((B, K)).astype(np.float32)
+    ws, nb = workspace(L.desc, B)
+    y = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    moe.expert_ffn_q4(L.desc, _t(x), B, _t(idx), _t(w), y, ws, nb)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    ex = {e: synth.experts(seed, 0, e, 1, 4, H, I) for e in range(E + 1)}
+
+    def ffn(e, xb):
+        c = ex[e]
+        return oracle.expert_ffn(4, H, I, c.gate[0], c.up[0], c.down[0], c.scales[0], c.biases[0], xb)[1]
+
+    for b in range(B):
+        if b in (4, 7):
+            assert np.all(np.isnan(yh[b]))
+            continue
+        ref = ffn(E, x[b]) + sum(float(w[b, k]) * ffn(int(idx[b, k]), x[b]) for k in range(K))
+        assert rel_err(yh[b], ref) <= TOL, "token %d" % b
