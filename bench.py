@@ -154,7 +154,7 @@ def cpu_baseline(c, budget_s=15.0):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("kernels.hip", "common.h"):
+    for f in ("kernels.hip", "grouped.hip", "common.h", "topk.h"):
         h.update(open(os.path.join(ROOT, "quantized_expert_dequant_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -313,11 +313,12 @@ def main():
     value = tokens_per_step / (ms_per_step / 1e3)
     idx_h = idx[W:W + K].cpu().numpy()
     if B > 1:
-        uniq = [len(np.unique(idx_h[i, 0])) for i in range(K)]
-        n_experts = float(np.mean(uniq)) + 1           # distinct routed experts + shared, per step
+        # the grouped path reads each distinct routed expert once per step, plus the shared one
+        uniq = [len(np.unique(idx_h[i, 0][(idx_h[i, 0] >= 0) & (idx_h[i, 0] < c["E"])])) for i in range(K)]
+        n_experts = float(np.mean(uniq)) + 1
     else:
         n_experts = c["K"] + 1
-    n_act = (c["K"] + 1) * (B if B > 1 else 1)
+    n_act = n_experts
     gu_bytes = gateup_bytes_per_expert(c) * n_act
     dn_bytes = down_bytes_per_expert(c) * n_act
     if dur[moe.KERNEL_GATEUP] is None:
@@ -349,7 +350,8 @@ def main():
             "global_batch": B, "rotation_copies": n_copies, "timing": "graph" if graph_ms else "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "kernel": "k_gateup", "bytes_per_launch": gu_bytes, "avg_us": round(gu_us, 3)},
+                     "kernel": "k_grouped_mfma<gate/up>" if B > 1 else "k_gateup_fast",
+                     "bytes_per_launch": round(gu_bytes), "avg_us": round(gu_us, 3)},
         "expert_weight_gbps": round(expert_gbps, 1),
         "expert_weight_frac_of_peak": round(expert_gbps / PEAK_HBM_GBPS, 4),
         "kernel_us": {"router": round(rt_us, 3), "gateup": round(gu_us, 3), "down": round(dn_us, 3)},

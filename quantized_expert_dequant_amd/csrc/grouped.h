@@ -13,17 +13,19 @@ namespace moe {
 // Output of the grouping kernel.  offsets / tokens / slots: the assignments of
 // expert e are positions [offsets[e], offsets[e+1]) of tokens (token id) and
 // slots (slot b*K + k), in slot order.  The rest is the MFMA work list and may
-// be null together: grp_u[0] = U distinct routed experts; act_expert[0] = E
-// (the shared expert, all B tokens), act_expert[1 + j] = j-th active routed
-// expert by id; entries act_off[u] .. act_off[u+1] of ent_token belong to
-// act_expert[u]; slot_pos[b*K + k] = entry of that slot (-1: invalid id).
+// be null together: the entries (0 .. B-1: the shared expert's, one per token;
+// B + p: position p of the sort) are cut into V = grp_u[0] groups of at most 32
+// entries of one expert, the shared expert's first, then the routed experts by
+// id; group v is expert act_expert[v] with entries act_off[v] .. act_off[v+1]-1,
+// whose tokens are ent_token[]; slot_pos[b*K + k] = entry of that slot (-1:
+// invalid id).
 struct GroupOut {
     int32_t* offsets;     // [E + 1]
     int32_t* tokens;      // [B*K]
     int32_t* slots;       // [B*K]
     int32_t* grp_u;       // [1]
-    int32_t* act_expert;  // [E + 1]
-    int32_t* act_off;     // [E + 2]
+    int32_t* act_expert;  // [V]
+    int32_t* act_off;     // [V + 1]
     int32_t* ent_token;   // [B + B*K]
     int32_t* slot_pos;    // [B*K]
 };
@@ -36,6 +38,7 @@ struct GroupedWork {
     float* xscale;    // [B]
     uint4* hb;        // h operands [B + B*K][8][G_i] uint4
     float* part;      // down outputs [B + B*K][H]
+    float* split;     // partial gate/up sums of tiles split between blocks
 };
 
 bool grouped_supported(const Layout& L, int B, int K);

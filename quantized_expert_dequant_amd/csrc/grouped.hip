@@ -15,16 +15,16 @@
 //
 // Kernels:
 //   k_router_tiled   fp64-accumulated logits of many tokens, split over H
-//   k_topk_split     sums the split partials in a fixed order, then top-K
+//   k_sum_slices     sums the H-slice partials in a fixed order
 //   k_group          stable counting sort of the assignments + the MFMA work list
 //   k_prep_tokens    token activations -> fp16 hi + lo MFMA operands
-//   k_grouped_mfma   gate/up (+ SwiGLU) or down dequant-GEMM per (expert, 128 rows)
+//   k_grouped_mfma   gate/up (+ SwiGLU) or down dequant-GEMM over (group, 128 rows, K chunk)
+//   k_fixup          SwiGLU of gate/up tiles whose K chunks two blocks shared
 //   k_combine        per-token routing-weighted sum of the down outputs
 #include <hip/hip_ext.h>
 
 #include "common.h"
 #include "grouped.h"
-#include "topk.h"
 
 namespace moe {
 
@@ -32,80 +32,76 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));  // native vector: copies stay in registers
 
+constexpr int GM_GROUP = 32;         // most tokens of one work-list group
+constexpr int GM_MAX_BLOCKS = 1024;  // most blocks of a stream-split launch
+
 __device__ inline f4 mfma16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
 // ----------------------------------------------------------------------------
 // Logits of B tokens: a block computes a tile of 32 experts x 32 tokens over a
-// 512-column slice of H; each thread keeps 2 x 2 outputs, accumulating the exact
-// fp32 products in fp64.  partial[split][b][e]; k_topk_split adds the slices in
+// 256-column slice of H; each thread keeps 2 x 2 outputs, accumulating the exact
+// fp32 products in fp64.  partial[slice][b][e]; k_sum_slices adds the slices in
 // slice order, so the logits do not depend on the launch.
 // ----------------------------------------------------------------------------
-constexpr int RT_E = 32, RT_B = 32, RT_SLICE = 512, RT_CHUNK = 64;
+constexpr int RT_E = 32, RT_B = 32, RT_SLICE = 256, RT_CHUNK = 64, RT_PITCH = RT_E + 2;
 
 __global__ __launch_bounds__(256) void k_router_tiled(const float* __restrict__ x, int B, const float* __restrict__ W,
                                                       int H, int E, double* __restrict__ partial)
 {
-    __shared__ float ws[RT_CHUNK][RT_E + 1];
-    __shared__ float xs[RT_CHUNK][RT_B + 1];
+    __shared__ float ws[RT_CHUNK][RT_PITCH];
+    __shared__ float xs[RT_CHUNK][RT_PITCH];
     const int e0 = blockIdx.x * RT_E, b0 = blockIdx.y * RT_B, split = blockIdx.z;
     const int tid = threadIdx.x;
     const int te = (tid & 15) * 2, tb = (tid >> 4) * 2;  // this thread's 2 experts x 2 tokens
-    double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
-    const int c_begin = split * RT_SLICE, c_end = min(H, c_begin + RT_SLICE);
+    double a00 = 0.0, a01 = 0.0, a10 = 0.0, a11 = 0.0;
+    const int c_begin = split * RT_SLICE, c_end = min(H, c_begin + RT_SLICE);  // H % 64 == 0
     for (int c0 = c_begin; c0 < c_end; c0 += RT_CHUNK) {
         // stage W[e0 .. e0+32)[c0 .. c0+64) and x[b0 .. b0+32)[c0 .. c0+64) as [column][row]
-        for (int t = tid; t < RT_CHUNK * RT_E; t += 256) {
-            const int r = t / RT_CHUNK, c = t - r * RT_CHUNK;
-            const int e = min(e0 + r, E - 1), b = min(b0 + r, B - 1), cc = min(c0 + c, H - 1);
-            ws[c][r] = W[(long long)e * H + cc];
-            xs[c][r] = x[(long long)b * H + cc];
+        float wv[8], xv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int t = tid + 256 * q, r = t >> 6, c = t & 63;
+            wv[q] = W[(long long)min(e0 + r, E - 1) * H + c0 + c];
+            xv[q] = x[(long long)min(b0 + r, B - 1) * H + c0 + c];
+        }
+        __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int t = tid + 256 * q, r = t >> 6, c = t & 63;
+            ws[c][r] = wv[q];
+            xs[c][r] = xv[q];
         }
         __syncthreads();
-        const int nc = min(RT_CHUNK, c_end - c0);
-        for (int c = 0; c < nc; ++c) {
-            const double w0 = ws[c][te], w1 = ws[c][te + 1];
-            const double x0 = xs[c][tb], x1 = xs[c][tb + 1];
-            acc[0][0] = fma(w0, x0, acc[0][0]);
-            acc[0][1] = fma(w0, x1, acc[0][1]);
-            acc[1][0] = fma(w1, x0, acc[1][0]);
-            acc[1][1] = fma(w1, x1, acc[1][1]);
+#pragma unroll 16
+        for (int c = 0; c < RT_CHUNK; ++c) {
+            const float2 w2 = *reinterpret_cast<const float2*>(&ws[c][te]);
+            const float2 x2 = *reinterpret_cast<const float2*>(&xs[c][tb]);
+            const double w0 = w2.x, w1 = w2.y, x0 = x2.x, x1 = x2.y;
+            a00 = fma(w0, x0, a00);
+            a01 = fma(w0, x1, a01);
+            a10 = fma(w1, x0, a10);
+            a11 = fma(w1, x1, a11);
         }
-        __syncthreads();
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int e = e0 + te + i, b = b0 + tb + j;
-            if (e < E && b < B) partial[((long long)split * B + b) * E + e] = acc[i][j];
-        }
+    double* out = partial + (long long)split * B * E;
+    const int e = e0 + te, b = b0 + tb;
+    if (e < E && b < B) out[(long long)b * E + e] = a00;
+    if (e < E && b + 1 < B) out[(long long)(b + 1) * E + e] = a01;
+    if (e + 1 < E && b < B) out[(long long)b * E + e + 1] = a10;
+    if (e + 1 < E && b + 1 < B) out[(long long)(b + 1) * E + e + 1] = a11;
 }
 
-// one wave per token: logits = sum of the slice partials (slice order) + bias, then top-K
-__global__ __launch_bounds__(256) void k_topk_split(const double* __restrict__ partial, int nsplit,
-                                                    const float* __restrict__ bias, int B, int E, int K, int renorm,
-                                                    double* __restrict__ logits, int32_t* __restrict__ idx,
-                                                    float* __restrict__ w)
+// logits[b][e] = sum of the slice partials in slice order + bias[e]
+__global__ __launch_bounds__(256) void k_sum_slices(const double* __restrict__ partial, int nslice,
+                                                    const float* __restrict__ bias, int BE, int E,
+                                                    double* __restrict__ logits)
 {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int b = blockIdx.x * 4 + wave;
-    if (b >= B) return;
-    double lv[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int e = min(lane + 64 * j, E - 1);
-        double s = 0.0;
-        for (int sp = 0; sp < nsplit; ++sp) s += partial[((long long)sp * B + b) * E + e];
-        lv[j] = s + (bias ? (double)bias[e] : 0.0);
-        if (logits && lane + 64 * j < E) logits[(long long)b * E + lane + 64 * j] = lv[j];
-    }
-    int id;
-    float wt;
-    topk_select<32, 16>(lv, E, K, renorm, lane, id, wt);
-    if (lane < K) {
-        idx[(long long)b * K + lane] = id;
-        w[(long long)b * K + lane] = wt;
-    }
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= BE) return;
+    double s = 0.0;
+#pragma unroll 8
+    for (int sp = 0; sp < nslice; ++sp) s += partial[(long long)sp * BE + i];
+    logits[i] = s + (bias ? (double)bias[i % E] : 0.0);
 }
 
 int router_splits(int H) { return (H + RT_SLICE - 1) / RT_SLICE; }
@@ -115,39 +111,53 @@ void launch_route_batched(const float* x, int B, const float* W, const float* bi
 {
     const dim3 grid((E + RT_E - 1) / RT_E, (B + RT_B - 1) / RT_B, router_splits(H));
     hipExtLaunchKernelGGL(k_router_tiled, grid, dim3(256), 0, s, t.start, t.stop, 0, x, B, W, H, E, partial);
-    hipLaunchKernelGGL(k_topk_split, dim3((B + 3) / 4), dim3(256), 0, s, partial, router_splits(H), bias, B, E, K,
-                       renorm, logits, idx, w);
+    hipLaunchKernelGGL(k_sum_slices, dim3((B * E + 255) / 256), dim3(256), 0, s, partial, router_splits(H), bias,
+                       B * E, E, logits);
+    launch_topk(logits, B, E, K, renorm, idx, w, s);
 }
 
 // ----------------------------------------------------------------------------
 // Grouping: stable counting sort of the B*K assignments (slot i = b*K + k holds
-// expert idx[i]) by expert id, in one block.  Thread e owns expert e: it counts
-// the slots naming e, the block scans the counts, and thread e then walks the
-// slots in order and places its own, so every expert's list keeps slot order.
-// Slots whose id is outside [0, E) are left out.
+// expert idx[i]) by expert id, in one block.  The block counts the slots of
+// every expert (LDS atomics) and scans the counts; then wave 0 walks the slots
+// 64 at a time in slot order: lanes naming the same expert find each other with
+// ballots over the id bits, take consecutive places after the expert's running
+// position in lane order, and the last of them advances it.  Every expert's
+// list therefore keeps slot order.  Slots whose id is outside [0, E) are left out.
+//
+// The work list of the MFMA kernels cuts every expert's entries into groups of
+// at most GM_GROUP tokens (the shared expert's B entries first, then the routed
+// experts by id), so that every group is one pass of the dequant-GEMM.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx, int B, int K, int E, GroupOut O)
 {
     __shared__ int sidx[MOE_MAX_B * MOE_MAX_K];
+    __shared__ int cnt[MOE_MAX_E];
     __shared__ int wsum[2][16];
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int n = B * K;
-    for (int i = tid; i < n; i += 1024) sidx[i] = idx[i];
+    const bool work = O.grp_u != nullptr;
+    for (int e = tid; e < E; e += 1024) cnt[e] = 0;
     __syncthreads();
-    int c = 0;
-    if (tid < E)
-        for (int i = 0; i < n; ++i) c += (sidx[i] == tid) ? 1 : 0;
-    const int f = c > 0 ? 1 : 0;
-    // exclusive scans of the counts and of the active flags over the block
+    for (int i = tid; i < n; i += 1024) {
+        const int e = idx[i];
+        sidx[i] = e;
+        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+        else if (work) O.slot_pos[i] = -1;
+    }
+    __syncthreads();
+    const int c = tid < E ? cnt[tid] : 0;
+    const int f = (c + GM_GROUP - 1) / GM_GROUP;  // groups of this expert
+    // exclusive scans of the counts and of the group counts over the block
     int sc = c, sf = f;
     for (int off = 1; off < 64; off <<= 1) {
         const int oc = __shfl_up(sc, off, 64), of = __shfl_up(sf, off, 64);
-        if ((tid & 63) >= off) {
+        if (lane >= off) {
             sc += oc;
             sf += of;
         }
     }
-    if ((tid & 63) == 63) {
+    if (lane == 63) {
         wsum[0][tid >> 6] = sc;
         wsum[1][tid >> 6] = sf;
     }
@@ -158,41 +168,54 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
         pf += wsum[1][q];
     }
     const int excl_c = pc + sc - c, excl_f = pf + sf - f;
-    const bool work = O.grp_u != nullptr;
-    if (tid < E) O.offsets[tid] = excl_c;
+    const int vs = (B + GM_GROUP - 1) / GM_GROUP;  // groups of the shared expert
+    if (tid < E) {
+        O.offsets[tid] = excl_c;
+        cnt[tid] = excl_c;  // running position of expert tid
+        if (work)
+            for (int j = 0; j < f; ++j) {
+                O.act_expert[vs + excl_f + j] = tid;
+                O.act_off[vs + excl_f + j] = B + excl_c + j * GM_GROUP;
+            }
+    }
     if (tid == E - 1) {
-        const int total = excl_c + c, U = excl_f + f;
+        const int total = excl_c + c, V = vs + excl_f + f;
         O.offsets[E] = total;
         if (work) {
-            // work list: the shared expert (every token) first, then the routed experts by id
-            O.grp_u[0] = U;
-            O.act_expert[0] = E;
-            O.act_off[0] = 0;
-            O.act_off[U + 1] = B + total;
+            O.grp_u[0] = V;
+            O.act_off[V] = B + total;
         }
     }
-    if (tid < E && f) {
-        if (work) {
-            O.act_expert[1 + excl_f] = tid;
-            O.act_off[1 + excl_f] = B + excl_c;
+    if (work) {
+        for (int j = tid; j < vs; j += 1024) {
+            O.act_expert[j] = E;
+            O.act_off[j] = j * GM_GROUP;
         }
-        int pos = excl_c;
-        for (int i = 0; i < n; ++i) {
-            if (sidx[i] != tid) continue;
+        for (int b = tid; b < B; b += 1024) O.ent_token[b] = b;
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    for (int base = 0; base < n; base += 64) {
+        const int i = base + lane;
+        const int e = i < n ? sidx[i] : -1;
+        const bool ok = e >= 0 && e < E;
+        uint64_t peers = __ballot(ok);
+#pragma unroll
+        for (int bit = 0; bit < 10; ++bit) {  // E <= 1024
+            const uint64_t m = __ballot((e >> bit) & 1);
+            peers &= ((e >> bit) & 1) ? m : ~m;
+        }
+        if (ok) {
+            const int rank = __popcll(peers & lt);
+            const int pos = cnt[e] + rank;
             O.tokens[pos] = i / K;
             O.slots[pos] = i;
             if (work) {
                 O.ent_token[B + pos] = i / K;
                 O.slot_pos[i] = B + pos;
             }
-            ++pos;
-        }
-    }
-    if (work) {
-        for (int b = tid; b < B; b += 1024) O.ent_token[b] = b;
-        for (int i = tid; i < n; i += 1024) {
-            const int e = sidx[i];
-            if (e < 0 || e >= E) O.slot_pos[i] = -1;
+            if ((peers >> lane) == 1ull) cnt[e] = pos + 1;  // the last lane of the group
         }
     }
 }
@@ -250,7 +273,7 @@ __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x
 // masked code pair gives (1024 + q_a, 1024 + q_b); subtracting 1024 is exact and
 // one fused multiply-add gives s*q + b, rounded once to fp16.
 // ----------------------------------------------------------------------------
-__device__ inline void dequant_chunk_q4(uint4 c, uint32_t sb, h8 (&out)[4])
+__device__ inline void dequant_chunk_q4(u4 c, uint32_t sb, uint32_t mask, uint32_t magic, h8 (&out)[4])
 {
     const _Float16 s = (_Float16)bf16_lo(sb), b = (_Float16)bf16_hi(sb);
     const h2 s2 = {s, s}, b2 = {b, b};
@@ -261,7 +284,7 @@ __device__ inline void dequant_chunk_q4(uint4 c, uint32_t sb, h8 (&out)[4])
         h2 p[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const uint32_t bits = ((wd[d] >> (4 * t)) & 0x000F000Fu) | 0x64006400u;
+            const uint32_t bits = ((wd[d] >> (4 * t)) & mask) | magic;  // (1024 + q_a, 1024 + q_b)
             const h2 q = __builtin_bit_cast(h2, bits) - k1024;
             p[t] = __builtin_elementwise_fma(q, s2, b2);
         }
@@ -270,27 +293,35 @@ __device__ inline void dequant_chunk_q4(uint4 c, uint32_t sb, h8 (&out)[4])
 }
 
 // ----------------------------------------------------------------------------
-// Grouped dequant-GEMM.  A work item is (active expert u, tile of 128 rows): a
-// block of 4 waves, 32 rows per wave as two 16-row MFMA tiles, multiplies the
-// item's rows by the expert's tokens, up to 64 at a time (four 16-token tiles).
-// K advances 128 columns (4 chunks of 16 bytes) per step: lane (i, kk) of a wave
-// holds chunk 4*step + kk of row i of each tile, and MFMA d (16 x 16 x 32)
-// takes dword d of the four lanes' chunks against the token operands of the
-// same 32 columns, staged in LDS as [tt][kk][d][hl][token].
+// Grouped dequant-GEMM.  A block of 8 waves owns a tile of 128 rows of one
+// group's expert (16 rows per wave) and multiplies it by the group's tokens
+// (at most 32: two 16-token MFMA tiles).  K advances 128 columns (4 chunks of
+// 16 bytes) per step: lane (i, kk) of a wave holds chunk 4*step + kk of its
+// row i, dequantizes it to fp16 (s*q + b), and MFMA d (16 x 16 x 32) takes
+// dword d of the four lanes' chunks against the token operands of the same 32
+// columns, staged in LDS as [tt][kk][d][hl][token].
 //
-// gfx9 counts outstanding vector loads in issue order, so each step issues the
-// next step's token operands (cache-resident) before the next step's weight
-// chunks (HBM); the LDS hand-over waits only for the former, and the barrier
-// leaves the weight loads in flight: the weights stream one step ahead.
+// Work split: the units (group, tile, K chunk) in that order are cut into
+// gridDim.x equal contiguous ranges, one per block, so every block streams the
+// same number of weight bytes (groups of <= 32 tokens keep the matrix work
+// below the memory time).  A tile whose K chunks fall into two blocks is
+// finished by k_fixup from the blocks' partial sums.
+//
+// Pipelining: each step first loads the next step's token operands (cache-
+// resident) into registers, then the weights of step + 3 (HBM) into a 4-slot
+// register ring; gfx9 counts outstanding vector loads in issue order, so the
+// LDS hand-over waits only for the token operands and the weight loads stay in
+// flight across the barrier.
 //
 // MODE_GATEUP: rows are gate/up row pairs; token operand x as fp16 hi + lo;
 //   writes h = silu(g) * u of each entry as fp16(h / 256) in the pair layout
 //   hb[entry][dword d < 8][G_i] (uint4 of 4 pairs).
-// MODE_DOWN: rows are down rows; token operand h (fp16); writes the entry's
-//   output row part[entry][H] in fp32.
+// MODE_DOWN: rows are down rows (one K chunk per tile); token operand h;
+//   writes the entry's output row part[entry][H] in fp32.
 // ----------------------------------------------------------------------------
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
-constexpr int GM_WAVES = 4, GM_TT = 4, GM_ROWS = GM_WAVES * 32;
+constexpr int GM_WAVES = 8, GM_ROWS = GM_WAVES * 16, GM_TT = 2, GM_THREADS = GM_WAVES * 64;
+constexpr int GM_KC_GATEUP = 4;  // K chunks per gate/up tile
 
 struct GroupedArgs {
     const uint8_t* slab;
@@ -302,193 +333,289 @@ struct GroupedArgs {
     const uint4* xhl;
     const float* xscale;
     uint4* hb;
-    float* part;
+    float* part;     // MODE_DOWN output
+    float* split;    // MODE_GATEUP partial sums [2 * gridDim.x][2][GM_GROUP][GM_ROWS]
 };
 
 template <int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_grouped_mfma(GroupedArgs A)
+struct GmShape {
+    static constexpr int NM = (MODE == MODE_GATEUP) ? 2 : 1;  // matrices per row: gate + up | down
+    static constexpr int HL = (MODE == MODE_GATEUP) ? 2 : 1;  // token operand parts: hi + lo | h
+    static constexpr int KC = (MODE == MODE_GATEUP) ? GM_KC_GATEUP : 1;
+    static constexpr int RING = (MODE == MODE_GATEUP) ? 3 : 4;  // weight ring slots (loads run RING-1 steps ahead)
+    static constexpr int NSTG = GM_TT * 4 * 4 * HL * 16;     // 16-byte elements staged per step
+    static constexpr int PER_T = NSTG / GM_THREADS;
+};
+
+__host__ __device__ inline int gm_tiles(const Layout& L, int mode) { return ((mode == MODE_GATEUP ? L.I : L.H) + GM_ROWS - 1) / GM_ROWS; }
+__host__ __device__ inline int gm_steps(const Layout& L, int mode) { return (2 * (mode == MODE_GATEUP ? L.Gh : L.Gi) + 3) / 4; }
+// first unit of block b when T units are cut into nb ranges (T * nb < 2^32)
+__device__ inline int gm_lo(int b, int T, int nb) { return (int)(((uint32_t)b * (uint32_t)T) / (uint32_t)nb); }
+// the block whose range holds unit x
+__device__ inline int gm_blk(int x, int T, int nb)
 {
-    constexpr int NM = (MODE == MODE_GATEUP) ? 2 : 1;  // matrices per row: gate + up | down
-    constexpr int HL = (MODE == MODE_GATEUP) ? 2 : 1;  // token operand parts: hi + lo | h
-    constexpr int NSTG = GM_TT * 4 * 4 * HL * 16;      // uint4 staged per step
-    constexpr int PER_T = NSTG / 256;
+    return (int)((((uint32_t)x + 1u) * (uint32_t)nb - 1u) / (uint32_t)T);
+}
+
+// h = silu(g * xs) * (u * xs) of entry ent, stored as fp16(h / 256) in the pair layout
+__device__ inline void store_h(const GroupedArgs& A, int ent, int row, float g, float u, float xs)
+{
+    g *= xs;
+    u *= xs;
+    const float h = g / (1.f + __expf(-g)) * u;
+    uint16_t* hrow = reinterpret_cast<uint16_t*>(A.hb + (long long)ent * 8 * A.L.Gi);
+    const int grp = row >> 6, cc = row & 63, dd = cc >> 3, r = cc & 7;
+    hrow[((long long)dd * A.L.Gi + grp) * 8 + (r & 3) * 2 + (r >> 2)] =
+        __builtin_bit_cast(uint16_t, (_Float16)(h * (1.f / 256.f)));
+}
+
+template <int MODE>
+__global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void k_grouped_mfma(GroupedArgs A)
+{
+    using S = GmShape<MODE>;
+    constexpr int NM = S::NM, HL = S::HL, KC = S::KC, NSTG = S::NSTG, PER_T = S::PER_T, RING = S::RING;
     __shared__ u4 bs[2][NSTG];
 
     const Layout& L = A.L;
     const int G = (MODE == MODE_GATEUP) ? L.Gh : L.Gi;
     const int NR = (MODE == MODE_GATEUP) ? L.I : L.H;
-    const int tiles = (NR + GM_ROWS - 1) / GM_ROWS;
-    const int n_items = (A.grp_u[0] + 1) * tiles;
+    const int tiles = gm_tiles(L, MODE);
+    const int nsteps = gm_steps(L, MODE);
+    const int T = A.grp_u[0] * tiles * KC;
+    const int nb = gridDim.x, blk = blockIdx.x;
+    const int lo = gm_lo(blk, T, nb), hi = gm_lo(blk + 1, T, nb);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = lane & 15, kk = lane >> 4;
-    const int nsteps = (2 * G + 3) / 4;  // 2 chunks per group, 4 chunks per step
+    const Masks M = load_masks();
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int u = item / tiles, tile = item - u * tiles;
+    struct WRegs {
+        u4 c[NM];
+        uint32_t sb[NM];
+    };
+
+    for (int x = lo; x < hi;) {
+        const int tau = x / KC, kc0 = x - tau * KC, kc1 = min(KC, kc0 + (hi - x));
+        const int u = tau / tiles, tile = tau - u * tiles;
+        const int k_begin = kc0 * nsteps / KC, k_end = kc1 * nsteps / KC;
         const int e = A.act_expert[u];
-        const int ent0 = A.act_off[u], n = A.act_off[u + 1] - ent0;
-        const int rbase = tile * GM_ROWS + wave * 32;
+        const int ent0 = A.act_off[u], n = A.act_off[u + 1] - ent0;  // 1 <= n <= GM_GROUP
+        const int ntt = (n + 15) / 16;
+        // addresses: uniform base + 32-bit byte offset (a record, the token and h
+        // operands are each far below 4 GiB)
         const uint8_t* rec = A.slab + (long long)e * L.record;
+        const int row = min(tile * GM_ROWS + wave * 16 + i, NR - 1);
+        const uint32_t row_off = (MODE == MODE_GATEUP) ? (uint32_t)(row * 2 * L.hb) : (uint32_t)(L.off_d_codes + row * L.ib);
+        const uint32_t sb_off = (MODE == MODE_GATEUP) ? (uint32_t)(L.off_gu_sb + (long long)row * G * 8)
+                                                      : (uint32_t)(L.off_d_sb + (long long)row * G * 4);
+        const uint32_t up_off = (uint32_t)L.hb;
+        const char* tok_base = (MODE == MODE_GATEUP) ? (const char*)A.xhl : (const char*)A.hb;
 
-        const uint8_t* rowp[2];
-        const uint8_t* sbp[2];
+        // element t = threadIdx.x + GM_THREADS q of a stage holds
+        // ((tt*4 + k2)*4 + d)*HL*16 + hl*16 + j; src[q] is its fixed part (token or
+        // entry row, hl, d), the step adds the chunk's group and half.  Chunks past the
+        // row end (2G not a multiple of 4) read a valid chunk and get zero weights.
+        int src[PER_T], k2q[PER_T];
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int row = min(rbase + 16 * rt + i, NR - 1);
+        for (int q = 0; q < PER_T; ++q) {
+            const int t = threadIdx.x + GM_THREADS * q;
+            const int j = t & 15, r1 = t >> 4;
+            const int hl = (HL == 2) ? (r1 & 1) : 0, r2 = r1 / HL;
+            const int d = r2 & 3, tt = r2 >> 4;
+            k2q[q] = (r2 >> 2) & 3;
+            const int m = min(tt * 16 + j, n - 1);
+            src[q] = (MODE == MODE_GATEUP) ? A.ent_token[ent0 + m] * G * 16 + hl * 8 + d : (ent0 + m) * 8 * G + d * G;
+        }
+        auto stage_load = [&](int ks, u4 (&st)[PER_T]) {
+#pragma unroll
+            for (int q = 0; q < PER_T; ++q) {
+                const int P = min(4 * ks + k2q[q], 2 * G - 1);
+                const int jh = P >= G ? 1 : 0, g = P - jh * G;
+                const uint32_t el = (MODE == MODE_GATEUP) ? (uint32_t)(src[q] + g * 16 + jh * 4)
+                                                          : (uint32_t)(src[q] + jh * 4 * G + g);
+                st[q] = *reinterpret_cast<const u4*>(tok_base + el * 16u);
+            }
+        };
+        auto weight_load = [&](int ks, WRegs& W) {
+            const int P = min(4 * ks + kk, 2 * G - 1), g = P >= G ? P - G : P;
+            const uint32_t co = row_off + (uint32_t)P * 16u;
+            W.c[0] = *reinterpret_cast<const u4*>(rec + co);
             if (MODE == MODE_GATEUP) {
-                rowp[rt] = rec + (long long)row * 2 * L.hb;
-                sbp[rt] = rec + L.off_gu_sb + (long long)row * G * 8;
+                W.c[NM - 1] = *reinterpret_cast<const u4*>(rec + (co + up_off));
+                const uint2 v = *reinterpret_cast<const uint2*>(rec + (sb_off + (uint32_t)g * 8u));
+                W.sb[0] = v.x;
+                W.sb[NM - 1] = v.y;
             } else {
-                rowp[rt] = rec + L.off_d_codes + (long long)row * L.ib;
-                sbp[rt] = rec + L.off_d_sb + (long long)row * G * 4;
+                W.sb[0] = *reinterpret_cast<const uint32_t*>(rec + (sb_off + (uint32_t)g * 4u));
+            }
+        };
+
+        float xs_lane[GM_TT];  // token scale of this lane's output column in each token tile
+#pragma unroll
+        for (int tt = 0; tt < GM_TT; ++tt)
+            xs_lane[tt] = (MODE == MODE_GATEUP) ? A.xscale[A.ent_token[ent0 + min(tt * 16 + i, n - 1)]] : 0.f;
+
+        f4 acc[NM][GM_TT];
+#pragma unroll
+        for (int mm = 0; mm < NM; ++mm)
+#pragma unroll
+            for (int tt = 0; tt < GM_TT; ++tt) acc[mm][tt] = f4{0.f, 0.f, 0.f, 0.f};
+
+        // Step ks: token operands of step ks + 2 -> registers (Sp), weights of step
+        // ks + RING - 1 -> the ring slot step ks - 1 used (Wp), multiply step ks
+        // (weights Wc, token operands in LDS stage ks & 1), then store the token
+        // operands of step ks + 1 (Sc, loaded one step earlier) into the other stage.
+        auto step = [&](int ks, const WRegs& Wc, WRegs& Wp, const u4 (&Sc)[PER_T], u4 (&Sp)[PER_T]) {
+            if (ks + 2 < k_end) stage_load(ks + 2, Sp);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + RING - 1 < k_end) weight_load(ks + RING - 1, Wp);
+            __builtin_amdgcn_sched_barrier(0);
+            const u4* buf = bs[(ks - k_begin) & 1];
+            const bool pad = 4 * ks + kk >= 2 * G;  // chunk past the row end: zero weights
+            h8 a[NM][4];
+#pragma unroll
+            for (int mm = 0; mm < NM; ++mm) dequant_chunk_q4(Wc.c[mm], pad ? 0u : Wc.sb[mm], M.m4a, M.magic, a[mm]);
+#pragma unroll
+            for (int tt = 0; tt < GM_TT; ++tt) {
+                if (tt < ntt) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+#pragma unroll
+                        for (int hl = 0; hl < HL; ++hl) {
+                            const h8 bv = __builtin_bit_cast(h8, buf[(((tt * 4 + kk) * 4 + d) * HL + hl) * 16 + i]);
+#pragma unroll
+                            for (int mm = 0; mm < NM; ++mm) acc[mm][tt] = mfma16(a[mm][d], bv, acc[mm][tt]);
+                        }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < k_end) {
+#pragma unroll
+                for (int q = 0; q < PER_T; ++q) bs[(ks + 1 - k_begin) & 1][threadIdx.x + GM_THREADS * q] = Sc[q];
+                __syncthreads();
+            }
+        };
+
+        WRegs R0, R1, R2, R3;
+        u4 S0[PER_T], S1[PER_T];
+        {
+            __syncthreads();  // LDS reads of the previous segment are done
+            if (k_begin < k_end) stage_load(k_begin, S0);
+            if (k_begin + 1 < k_end) stage_load(k_begin + 1, S1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (k_begin < k_end) weight_load(k_begin, R0);
+            if (k_begin + 1 < k_end) weight_load(k_begin + 1, R1);
+            if (RING == 4 && k_begin + 2 < k_end) weight_load(k_begin + 2, R2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (k_begin < k_end)
+#pragma unroll
+                for (int q = 0; q < PER_T; ++q) bs[0][threadIdx.x + GM_THREADS * q] = S0[q];
+            __syncthreads();
+        }
+        // token operands alternate between S1 (steps ks + 1 with ks even) and S0
+        if (RING == 4) {
+            for (int ks = k_begin; ks < k_end; ks += 4) {
+                step(ks, R0, R3, S1, S0);
+                if (ks + 1 >= k_end) break;
+                step(ks + 1, R1, R0, S0, S1);
+                if (ks + 2 >= k_end) break;
+                step(ks + 2, R2, R1, S1, S0);
+                if (ks + 3 >= k_end) break;
+                step(ks + 3, R3, R2, S0, S1);
+            }
+        } else {
+            for (int ks = k_begin; ks < k_end; ks += 6) {
+                step(ks, R0, R2, S1, S0);
+                if (ks + 1 >= k_end) break;
+                step(ks + 1, R1, R0, S0, S1);
+                if (ks + 2 >= k_end) break;
+                step(ks + 2, R2, R1, S1, S0);
+                if (ks + 3 >= k_end) break;
+                step(ks + 3, R0, R2, S0, S1);
+                if (ks + 4 >= k_end) break;
+                step(ks + 4, R1, R0, S1, S0);
+                if (ks + 5 >= k_end) break;
+                step(ks + 5, R2, R1, S0, S1);
             }
         }
 
-        for (int p0 = 0; p0 < n; p0 += 16 * GM_TT) {
-            const int ntt = min(GM_TT, (n - p0 + 15) / 16);
-
-            // token operands of step ks: element t = ((tt*4 + k2)*4 + d)*HL*16 + hl*16 + j.
-            // src[q]: the element's fixed part (token or entry row, hl, d); the step adds
-            // the chunk's group and half.  Chunks past the row end (2G not a multiple
-            // of 4) read a valid chunk; their weights are zeroed below.
-            int src[PER_T];
-            int k2q[PER_T];
+        // lane (i, kk) holds D[row 4*kk + v][token i] of each token tile
+        const int rbase = tile * GM_ROWS + wave * 16 + 4 * kk;
+        const bool whole = (kc0 == 0 && kc1 == KC);
+        float* sp = nullptr;
+        if (MODE == MODE_GATEUP && !whole)  // slot 2b: the block's first segment, 2b + 1: its last
+            sp = A.split + (long long)(2 * blk + (x == lo ? 0 : 1)) * 2 * GM_GROUP * GM_ROWS;
 #pragma unroll
-            for (int q = 0; q < PER_T; ++q) {
-                const int t = threadIdx.x + 256 * q;
-                const int j = t & 15, r1 = t >> 4;
-                const int hl = (HL == 2) ? (r1 & 1) : 0, r2 = r1 / HL;
-                const int d = r2 & 3, tt = r2 >> 4;
-                k2q[q] = (r2 >> 2) & 3;
-                const int m = min(p0 + tt * 16 + j, n - 1);
-                if (MODE == MODE_GATEUP)
-                    src[q] = A.ent_token[ent0 + m] * G * 16 + hl * 8 + d;
-                else
-                    src[q] = (ent0 + m) * 8 * G + d * G;
-            }
-            const u4* xhl = reinterpret_cast<const u4*>(A.xhl);
-            const u4* hbv = reinterpret_cast<const u4*>(A.hb);
-            auto stage_load = [&](int ks, u4 (&st)[PER_T]) {
+        for (int tt = 0; tt < GM_TT; ++tt) {
+            const int m = tt * 16 + i;
+            if (tt >= ntt || m >= n) continue;
+            const int ent = ent0 + m;
 #pragma unroll
-                for (int q = 0; q < PER_T; ++q) {
-                    const int P = min(4 * ks + k2q[q], 2 * G - 1);
-                    const int jh = P >= G ? 1 : 0, g = P - jh * G;
-                    if (MODE == MODE_GATEUP)
-                        st[q] = xhl[src[q] + g * 16 + jh * 4];
-                    else
-                        st[q] = hbv[src[q] + jh * 4 * G + g];
-                }
-            };
-            struct WRegs {
-                uint4 c[2][NM];
-                uint32_t sb[2][NM];
-            };
-            auto weight_load = [&](int ks, WRegs& W) {
-                const int P = min(4 * ks + kk, 2 * G - 1), g = P >= G ? P - G : P;
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    W.c[rt][0] = *reinterpret_cast<const uint4*>(rowp[rt] + (long long)P * 16);
-                    if (MODE == MODE_GATEUP) {
-                        W.c[rt][NM - 1] = *reinterpret_cast<const uint4*>(rowp[rt] + L.hb + (long long)P * 16);
-                        const uint2 v = *reinterpret_cast<const uint2*>(sbp[rt] + (long long)g * 8);
-                        W.sb[rt][0] = v.x;
-                        W.sb[rt][NM - 1] = v.y;
-                    } else {
-                        W.sb[rt][0] = *reinterpret_cast<const uint32_t*>(sbp[rt] + (long long)g * 4);
-                    }
-                }
-            };
-
-            f4 acc[2][NM][GM_TT];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int mm = 0; mm < NM; ++mm)
-#pragma unroll
-                    for (int tt = 0; tt < GM_TT; ++tt) acc[rt][mm][tt] = f4{0.f, 0.f, 0.f, 0.f};
-
-            u4 st[PER_T];
-            WRegs Wc, Wn;
-            __syncthreads();  // LDS reads of the previous item or pass are done
-            stage_load(0, st);
-            __builtin_amdgcn_sched_barrier(0);
-            weight_load(0, Wc);
-#pragma unroll
-            for (int q = 0; q < PER_T; ++q) bs[0][threadIdx.x + 256 * q] = st[q];
-            __syncthreads();
-
-            for (int ks = 0; ks < nsteps; ++ks) {
-                const bool more = ks + 1 < nsteps;
-                if (more) {
-                    stage_load(ks + 1, st);
-                    __builtin_amdgcn_sched_barrier(0);
-                    weight_load(ks + 1, Wn);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                const u4* buf = bs[ks & 1];
-                const bool pad = 4 * ks + kk >= 2 * G;  // chunk past the row end: zero weights
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
-                    h8 a[NM][4];
-#pragma unroll
-                    for (int mm = 0; mm < NM; ++mm) dequant_chunk_q4(Wc.c[rt][mm], pad ? 0u : Wc.sb[rt][mm], a[mm]);
-#pragma unroll
-                    for (int tt = 0; tt < GM_TT; ++tt) {
-                        if (tt < ntt) {
-#pragma unroll
-                            for (int d = 0; d < 4; ++d)
-#pragma unroll
-                                for (int hl = 0; hl < HL; ++hl) {
-                                    const h8 bv =
-                                        __builtin_bit_cast(h8, buf[(((tt * 4 + kk) * 4 + d) * HL + hl) * 16 + i]);
-#pragma unroll
-                                    for (int mm = 0; mm < NM; ++mm)
-                                        acc[rt][mm][tt] = mfma16(a[mm][d], bv, acc[rt][mm][tt]);
-                                }
-                        }
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                if (more) {
-#pragma unroll
-                    for (int q = 0; q < PER_T; ++q) bs[(ks + 1) & 1][threadIdx.x + 256 * q] = st[q];
-                    __syncthreads();
-                    Wc = Wn;
-                }
-            }
-
-            // lane (i, kk) holds D[row 4*kk + v][token i] of each tile
-#pragma unroll
-            for (int tt = 0; tt < GM_TT; ++tt) {
-                const int m = p0 + tt * 16 + i;
-                if (tt >= ntt || m >= n) continue;
-                const int ent = ent0 + m;
+            for (int v = 0; v < 4; ++v) {
+                const int r = rbase + v;
+                if (r >= NR) continue;
                 if (MODE == MODE_GATEUP) {
-                    const float xs = A.xscale[A.ent_token[ent]];
-                    uint16_t* hrow = reinterpret_cast<uint16_t*>(A.hb + (long long)ent * 8 * L.Gi);
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int row = rbase + 16 * rt + 4 * kk + v;
-                            if (row >= NR) continue;
-                            const float gg = acc[rt][0][tt][v] * xs, uu = acc[rt][NM - 1][tt][v] * xs;
-                            const float h = gg / (1.f + __expf(-gg)) * uu;
-                            const int grp = row >> 6, cc = row & 63, dd = cc >> 3, r = cc & 7;
-                            hrow[((long long)dd * L.Gi + grp) * 8 + (r & 3) * 2 + (r >> 2)] =
-                                __builtin_bit_cast(uint16_t, (_Float16)(h * (1.f / 256.f)));
-                        }
+                    if (whole) {
+                        store_h(A, ent, r, acc[0][tt][v], acc[NM - 1][tt][v], xs_lane[tt]);
+                    } else {
+                        const int rl = r - tile * GM_ROWS;
+                        sp[(0 * GM_GROUP + m) * GM_ROWS + rl] = acc[0][tt][v];
+                        sp[(1 * GM_GROUP + m) * GM_ROWS + rl] = acc[NM - 1][tt][v];
+                    }
                 } else {
-                    float* prow = A.part + (long long)ent * L.H;
-#pragma unroll
-                    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int row = rbase + 16 * rt + 4 * kk + v;
-                            if (row < NR) prow[row] = 256.f * acc[rt][0][tt][v];
-                        }
+                    A.part[(long long)ent * L.H + r] = 256.f * acc[0][tt][v];
                 }
             }
+        }
+        x += kc1 - kc0;
+    }
+}
+
+// Gate/up tiles whose K chunks were split between blocks: sum the blocks'
+// partial sums in K order, then SwiGLU.  Block b handles the tile in which its
+// range starts, when that start is inside a tile and no lower block starts
+// inside the same tile.
+__global__ __launch_bounds__(256) void k_fixup(GroupedArgs A, int nb)
+{
+    constexpr int KC = GM_KC_GATEUP;
+    const int tiles = gm_tiles(A.L, MODE_GATEUP);
+    const int T = A.grp_u[0] * tiles * KC;
+    const int b = blockIdx.x;
+    const int s0 = gm_lo(b, T, nb);
+    if (s0 >= T || s0 % KC == 0) return;
+    const int tau = s0 / KC;
+    if (gm_lo(b - 1, T, nb) > tau * KC) return;  // a lower block starts inside this tile
+    const int u = tau / tiles, tile = tau - u * tiles;
+    const int ent0 = A.act_off[u], n = A.act_off[u + 1] - ent0;
+    const int b_lo = gm_blk(tau * KC, T, nb), b_hi = gm_blk((tau + 1) * KC - 1, T, nb);
+    // the tile's partial slots in K order (at most KC blocks share a tile)
+    int slots[KC], ns = 0;
+    for (int bb = b_lo; bb <= b_hi && ns < KC; ++bb) {
+        const int l0 = gm_lo(bb, T, nb);
+        if (l0 == gm_lo(bb + 1, T, nb)) continue;  // empty range
+        slots[ns++] = (bb == b_lo && l0 < tau * KC) ? 2 * bb + 1 : 2 * bb;
+    }
+    __shared__ float xs_tok[GM_GROUP];
+    if (threadIdx.x < n) xs_tok[threadIdx.x] = A.xscale[A.ent_token[ent0 + threadIdx.x]];
+    __syncthreads();
+    // 4 elements per thread and pass, their loads issued together
+    for (int t0 = threadIdx.x; t0 < n * GM_ROWS; t0 += 4 * 256) {
+        float g[4] = {0.f, 0.f, 0.f, 0.f}, up[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < ns; ++j) {
+            const float* sp = A.split + (long long)slots[j] * 2 * GM_GROUP * GM_ROWS;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = min(t0 + q * 256, n * GM_ROWS - 1);
+                const int m = t / GM_ROWS, rl = t - m * GM_ROWS;
+                g[q] += sp[(0 * GM_GROUP + m) * GM_ROWS + rl];
+                up[q] += sp[(1 * GM_GROUP + m) * GM_ROWS + rl];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = t0 + q * 256;
+            const int m = t / GM_ROWS, rl = t - m * GM_ROWS;
+            const int r = tile * GM_ROWS + rl;
+            if (t < n * GM_ROWS && r < A.L.I) store_h(A, ent0 + m, r, g[q], up[q], xs_tok[m]);
         }
     }
 }
@@ -517,30 +644,34 @@ bool grouped_supported(const Layout& L, int B, int K)
     return L.bits == 4 && B >= 2 && B <= MOE_MAX_B && K <= MOE_MAX_K && L.H % 64 == 0 && L.I % 64 == 0;
 }
 
+// most work-list groups a call can produce: every expert's entries cut into groups of GM_GROUP
+static int max_groups(int B, int K, int E) { return (B + GM_GROUP - 1) / GM_GROUP + min(E, B * K) + (B * K) / GM_GROUP; }
+
 size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E)
 {
-    const size_t ents = (size_t)B * K + B;
+    const size_t ents = (size_t)B * K + B, V = max_groups(B, K, E);
     size_t n = 0;
     auto add = [&](size_t bytes) { n += (bytes + 255) & ~(size_t)255; };
     add(sizeof(double) * router_splits(L.H) * B * E);  // partial logits
     add(sizeof(int32_t) * (E + 1));                    // offsets
     add(sizeof(int32_t) * B * K);                      // tokens
     add(sizeof(int32_t) * B * K);                      // slots
-    add(sizeof(int32_t) * 4);                          // U
-    add(sizeof(int32_t) * (E + 1));                    // act_expert
-    add(sizeof(int32_t) * (E + 2));                    // act_off
+    add(sizeof(int32_t) * 4);                          // number of groups
+    add(sizeof(int32_t) * V);                          // act_expert
+    add(sizeof(int32_t) * (V + 1));                    // act_off
     add(sizeof(int32_t) * ents);                       // ent_token
     add(sizeof(int32_t) * B * K);                      // slot_pos
     add(16ull * B * L.Gh * 16);                        // xhl
     add(sizeof(float) * B);                            // xscale
     add(2ull * ents * L.I);                            // hb
     add(sizeof(float) * ents * L.H);                   // part
+    add(sizeof(float) * 2ull * GM_MAX_BLOCKS * 2 * GM_GROUP * GM_ROWS);  // split tiles
     return n;
 }
 
 GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E)
 {
-    const size_t ents = (size_t)B * K + B;
+    const size_t ents = (size_t)B * K + B, V = max_groups(B, K, E);
     char* p = (char*)base;
     auto take = [&](size_t bytes) {
         char* r = p;
@@ -553,27 +684,38 @@ GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E)
     W.g.tokens = (int32_t*)take(sizeof(int32_t) * B * K);
     W.g.slots = (int32_t*)take(sizeof(int32_t) * B * K);
     W.g.grp_u = (int32_t*)take(sizeof(int32_t) * 4);
-    W.g.act_expert = (int32_t*)take(sizeof(int32_t) * (E + 1));
-    W.g.act_off = (int32_t*)take(sizeof(int32_t) * (E + 2));
+    W.g.act_expert = (int32_t*)take(sizeof(int32_t) * V);
+    W.g.act_off = (int32_t*)take(sizeof(int32_t) * (V + 1));
     W.g.ent_token = (int32_t*)take(sizeof(int32_t) * ents);
     W.g.slot_pos = (int32_t*)take(sizeof(int32_t) * B * K);
     W.xhl = (uint4*)take(16ull * B * L.Gh * 16);
     W.xscale = (float*)take(sizeof(float) * B);
     W.hb = (uint4*)take(2ull * ents * L.I);
     W.part = (float*)take(sizeof(float) * ents * L.H);
+    W.split = (float*)take(sizeof(float) * 2ull * GM_MAX_BLOCKS * 2 * GM_GROUP * GM_ROWS);
     return W;
 }
 
-int grouped_grid(const Layout& L, int B, int K, int E, int mode)
+// blocks of the stream split: as many as stay resident together (the work is cut
+// into equal ranges, so all of them must run at once), at most GM_MAX_BLOCKS
+static int resident_blocks(const void* kernel, int threads)
 {
-    const int max_u = min(E, B * K) + 1;
-    const int NR = mode == MODE_GATEUP ? L.I : L.H;
-    return max_u * ((NR + GM_ROWS - 1) / GM_ROWS);
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GM_MAX_BLOCKS / 2;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    return max(1, min(GM_MAX_BLOCKS, cus * per_cu));
 }
 
 void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W, const float* x, const float* w,
                         float shared_w, int B, int K, int E, float* y, hipStream_t s, Timing tg, Timing td)
 {
+    static int nb_gu = 0, nb_dn = 0;  // per process: one device type
+    if (!nb_gu) {
+        nb_gu = resident_blocks((const void*)k_grouped_mfma<MODE_GATEUP>, GM_THREADS);
+        nb_dn = resident_blocks((const void*)k_grouped_mfma<MODE_DOWN>, GM_THREADS);
+    }
     hipLaunchKernelGGL(k_prep_tokens, dim3(B), dim3(256), 0, s, x, L.H, W.xhl, W.xscale);
     GroupedArgs A;
     A.slab = (const uint8_t*)slab;
@@ -586,10 +728,10 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     A.xscale = W.xscale;
     A.hb = W.hb;
     A.part = W.part;
-    hipExtLaunchKernelGGL(k_grouped_mfma<MODE_GATEUP>, dim3(grouped_grid(L, B, K, E, MODE_GATEUP)), dim3(256), 0, s,
-                          tg.start, tg.stop, 0, A);
-    hipExtLaunchKernelGGL(k_grouped_mfma<MODE_DOWN>, dim3(grouped_grid(L, B, K, E, MODE_DOWN)), dim3(256), 0, s,
-                          td.start, td.stop, 0, A);
+    A.split = W.split;
+    hipExtLaunchKernelGGL(k_grouped_mfma<MODE_GATEUP>, dim3(nb_gu), dim3(GM_THREADS), 0, s, tg.start, tg.stop, 0, A);
+    hipLaunchKernelGGL(k_fixup, dim3(nb_gu), dim3(256), 0, s, A, nb_gu);
+    hipExtLaunchKernelGGL(k_grouped_mfma<MODE_DOWN>, dim3(nb_dn), dim3(GM_THREADS), 0, s, td.start, td.stop, 0, A);
     hipLaunchKernelGGL(k_combine, dim3((L.H + 255) / 256, B), dim3(256), 0, s, W.part, W.g.slot_pos, w, K, L.H,
                        shared_w, y);
 }

@@ -173,3 +173,29 @@ def test_batched_given_routing_duplicates_and_invalid(layers):
             continue
         ref = ffn(E, x[b]) + sum(float(w[b, k]) * ffn(int(idx[b, k]), x[b]) for k in range(K))
         assert rel_err(yh[b], ref) <= TOL, "token %d" % b
+
+
+def test_batched_expert_with_more_than_32_tokens(layers):
+    """One expert chosen by 40 tokens is cut into two work-list groups; results stay per-token exact."""
+    L = layers(0)
+    cfg, seed = WORKLOADS[0], seed_of(0)
+    B, K, E, H, I = 40, L.K, L.E, L.H, L.I
+    rng = np.random.default_rng(9)
+    x = synth.tokens(seed, 88, B, H)
+    idx = np.stack([np.concatenate([[3], rng.choice([e for e in range(E) if e != 3], K - 1, replace=False)])
+                    for _ in range(B)]).astype(np.int32)
+    w = rng.random((B, K)).astype(np.float32)
+    ws, nb = workspace(L.desc, B)
+    y = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    moe.expert_ffn_q4(L.desc, _t(x), B, _t(idx), _t(w), y, ws, nb)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    ex = {e: synth.experts(seed, 0, e, 1, 4, H, I) for e in range(E + 1)}
+
+    def ffn(e, xb):
+        c = ex[e]
+        return oracle.expert_ffn(4, H, I, c.gate[0], c.up[0], c.down[0], c.scales[0], c.biases[0], xb)[1]
+
+    for b in range(B):
+        ref = ffn(E, x[b]) + sum(float(w[b, k]) * ffn(int(idx[b, k]), x[b]) for k in range(K))
+        assert rel_err(yh[b], ref) <= TOL, "token %d" % b
