@@ -53,7 +53,7 @@ extern "C" {
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)        /* null / misaligned pointer, bad shape, workspace too small */
-#define MOE_EUNSUPPORTED (-2)  /* bits not 2 or 4, group not 64, K > 32, E > 1024, B > 256 */
+#define MOE_EUNSUPPORTED (-2)  /* bits not 2 or 4, group not 64, K > 32, E > 1024, B > 256, H > 65536, I > 8192 */
 #define MOE_EHIP (-3)          /* the HIP runtime refused a launch */
 
 #define MOE_MAX_K 32

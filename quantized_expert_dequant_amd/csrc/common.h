@@ -149,6 +149,37 @@ __device__ inline float pair_class_inv(int bits, int p)
     }
 }
 
+// ---- h between the gate/up and down kernels.  h is written in fp32 in the
+// element order of the fp16 pair layout above (the 8 values of pair-layout
+// uint4 u sit at floats 8u .. 8u+7).  The down kernels scale each expert's h by
+// a power of two taken from its largest |h| and round it to fp16 pairs, so a
+// token whose h is tiny everywhere (saturated SiLU) keeps its relative precision.
+__device__ inline float exp2i_f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// exponent e with max|h| * 2^-e in [2^14, 2^15); 0 for zero or non-finite maxima
+__device__ inline int h_exponent(float amax)
+{
+    if (!(amax > 0.f) || !(amax <= 3.4e38f)) return 0;
+    const int e = ilogbf(amax) - 14;
+    return e < -110 ? -110 : (e > 113 ? 113 : e);
+}
+
+__device__ inline uint4 h_pairs(float4 a, float4 b, float inv)
+{
+    const h2 p0 = {(_Float16)(a.x * inv), (_Float16)(a.y * inv)};
+    const h2 p1 = {(_Float16)(a.z * inv), (_Float16)(a.w * inv)};
+    const h2 p2 = {(_Float16)(b.x * inv), (_Float16)(b.y * inv)};
+    const h2 p3 = {(_Float16)(b.z * inv), (_Float16)(b.w * inv)};
+    return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                      __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
+__device__ inline float absmax8(float4 a, float4 b)
+{
+    return fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                 fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+}
+
 // ---- cross-lane exchange without LDS: DPP for partners inside a row of 16
 // lanes, gfx950 permlane16/32 swaps across rows.  Every step combines a lane
 // with its partner as op(own, partner), so for commutative ops all lanes of a

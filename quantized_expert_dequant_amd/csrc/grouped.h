@@ -36,7 +36,9 @@ struct GroupedWork {
     GroupOut g;
     uint4* xhl;       // token operands [B][G_h][16] uint4
     float* xscale;    // [B]
-    uint4* hb;        // h operands [B + B*K][8][G_i] uint4
+    float* hb;        // h in fp32, pair-layout order [B + B*K][8][G_i][8]
+    uint4* hb16;      // h * 2^-e(entry) as fp16 pairs [B + B*K][8][G_i]
+    float* hscale;    // 2^e(entry) [B + B*K]
     float* part;      // down outputs [B + B*K][H]
     float* split;     // partial gate/up sums of tiles split between blocks
 };

@@ -20,6 +20,7 @@
 //   k_prep_tokens    token activations -> fp16 hi + lo MFMA operands
 //   k_grouped_mfma   gate/up (+ SwiGLU) or down dequant-GEMM over (group, 128 rows, K chunk)
 //   k_fixup          SwiGLU of gate/up tiles whose K chunks two blocks shared
+//   k_hconvert       h of every entry -> fp16 with the entry's power-of-two scale
 //   k_combine        per-token routing-weighted sum of the down outputs
 #include <hip/hip_ext.h>
 
@@ -314,10 +315,11 @@ __device__ inline void dequant_chunk_q4(u4 c, uint32_t sb, uint32_t mask, uint32
 // flight across the barrier.
 //
 // MODE_GATEUP: rows are gate/up row pairs; token operand x as fp16 hi + lo;
-//   writes h = silu(g) * u of each entry as fp16(h / 256) in the pair layout
-//   hb[entry][dword d < 8][G_i] (uint4 of 4 pairs).
-// MODE_DOWN: rows are down rows (one K chunk per tile); token operand h;
-//   writes the entry's output row part[entry][H] in fp32.
+//   writes h = silu(g) * u of each entry in fp32 in the pair-layout order
+//   hb[entry][dword d < 8][G_i][8].
+// MODE_DOWN: rows are down rows (one K chunk per tile); token operand h scaled
+//   per entry by a power of two and rounded to fp16; writes the entry's output
+//   row part[entry][H] in fp32.
 // ----------------------------------------------------------------------------
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 constexpr int GM_WAVES = 8, GM_ROWS = GM_WAVES * 16, GM_TT = 2, GM_THREADS = GM_WAVES * 64;
@@ -332,7 +334,9 @@ struct GroupedArgs {
     const int32_t* ent_token;
     const uint4* xhl;
     const float* xscale;
-    uint4* hb;
+    float* hb;       // gate/up output: h in fp32, pair-layout order [entry][8][G_i][8]
+    const uint4* hb16;     // down operand: h * 2^-e(entry) as fp16 pairs [entry][8][G_i]
+    const float* hscale;   // 2^e(entry)
     float* part;     // MODE_DOWN output
     float* split;    // MODE_GATEUP partial sums [2 * gridDim.x][2][GM_GROUP][GM_ROWS]
 };
@@ -357,16 +361,16 @@ __device__ inline int gm_blk(int x, int T, int nb)
     return (int)((((uint32_t)x + 1u) * (uint32_t)nb - 1u) / (uint32_t)T);
 }
 
-// h = silu(g * xs) * (u * xs) of entry ent, stored as fp16(h / 256) in the pair layout
+// h = silu(g * xs) * (u * xs) of entry ent at input column `row` of the down
+// GEMM, stored in fp32 in the pair-layout order
 __device__ inline void store_h(const GroupedArgs& A, int ent, int row, float g, float u, float xs)
 {
     g *= xs;
     u *= xs;
     const float h = g / (1.f + __expf(-g)) * u;
-    uint16_t* hrow = reinterpret_cast<uint16_t*>(A.hb + (long long)ent * 8 * A.L.Gi);
+    float* hrow = A.hb + (long long)ent * 64 * A.L.Gi;
     const int grp = row >> 6, cc = row & 63, dd = cc >> 3, r = cc & 7;
-    hrow[((long long)dd * A.L.Gi + grp) * 8 + (r & 3) * 2 + (r >> 2)] =
-        __builtin_bit_cast(uint16_t, (_Float16)(h * (1.f / 256.f)));
+    hrow[((long long)dd * A.L.Gi + grp) * 8 + (r & 3) * 2 + (r >> 2)] = h;
 }
 
 template <int MODE>
@@ -408,7 +412,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         const uint32_t sb_off = (MODE == MODE_GATEUP) ? (uint32_t)(L.off_gu_sb + (long long)row * G * 8)
                                                       : (uint32_t)(L.off_d_sb + (long long)row * G * 4);
         const uint32_t up_off = (uint32_t)L.hb;
-        const char* tok_base = (MODE == MODE_GATEUP) ? (const char*)A.xhl : (const char*)A.hb;
+        const char* tok_base = (MODE == MODE_GATEUP) ? (const char*)A.xhl : (const char*)A.hb16;
 
         // element t = threadIdx.x + GM_THREADS q of a stage holds
         // ((tt*4 + k2)*4 + d)*HL*16 + hl*16 + j; src[q] is its fixed part (token or
@@ -425,15 +429,22 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             const int m = min(tt * 16 + j, n - 1);
             src[q] = (MODE == MODE_GATEUP) ? A.ent_token[ent0 + m] * G * 16 + hl * 8 + d : (ent0 + m) * 8 * G + d * G;
         }
-        auto stage_load = [&](int ks, u4 (&st)[PER_T]) {
+        struct Stage {
+            u4 v[PER_T];
+        };
+        auto stage_load = [&](int ks, Stage& S) {
 #pragma unroll
             for (int q = 0; q < PER_T; ++q) {
                 const int P = min(4 * ks + k2q[q], 2 * G - 1);
                 const int jh = P >= G ? 1 : 0, g = P - jh * G;
                 const uint32_t el = (MODE == MODE_GATEUP) ? (uint32_t)(src[q] + g * 16 + jh * 4)
                                                           : (uint32_t)(src[q] + jh * 4 * G + g);
-                st[q] = *reinterpret_cast<const u4*>(tok_base + el * 16u);
+                S.v[q] = *reinterpret_cast<const u4*>(tok_base + el * 16u);
             }
+        };
+        auto stage_store = [&](int buf, const Stage& S) {
+#pragma unroll
+            for (int q = 0; q < PER_T; ++q) bs[buf][threadIdx.x + GM_THREADS * q] = S.v[q];
         };
         auto weight_load = [&](int ks, WRegs& W) {
             const int P = min(4 * ks + kk, 2 * G - 1), g = P >= G ? P - G : P;
@@ -449,10 +460,14 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             }
         };
 
-        float xs_lane[GM_TT];  // token scale of this lane's output column in each token tile
+        // scale of this lane's output column in each token tile: the token's x scale
+        // (gate/up) or the entry's h scale (down)
+        float xs_lane[GM_TT];
 #pragma unroll
-        for (int tt = 0; tt < GM_TT; ++tt)
-            xs_lane[tt] = (MODE == MODE_GATEUP) ? A.xscale[A.ent_token[ent0 + min(tt * 16 + i, n - 1)]] : 0.f;
+        for (int tt = 0; tt < GM_TT; ++tt) {
+            const int ent = ent0 + min(tt * 16 + i, n - 1);
+            xs_lane[tt] = (MODE == MODE_GATEUP) ? A.xscale[A.ent_token[ent]] : A.hscale[ent];
+        }
 
         f4 acc[NM][GM_TT];
 #pragma unroll
@@ -464,7 +479,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         // ks + RING - 1 -> the ring slot step ks - 1 used (Wp), multiply step ks
         // (weights Wc, token operands in LDS stage ks & 1), then store the token
         // operands of step ks + 1 (Sc, loaded one step earlier) into the other stage.
-        auto step = [&](int ks, const WRegs& Wc, WRegs& Wp, const u4 (&Sc)[PER_T], u4 (&Sp)[PER_T]) {
+        auto step = [&](int ks, const WRegs& Wc, WRegs& Wp, const Stage& Sc, Stage& Sp) {
             if (ks + 2 < k_end) stage_load(ks + 2, Sp);
             __builtin_amdgcn_sched_barrier(0);
             if (ks + RING - 1 < k_end) weight_load(ks + RING - 1, Wp);
@@ -489,14 +504,13 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             }
             __builtin_amdgcn_sched_barrier(0);
             if (ks + 1 < k_end) {
-#pragma unroll
-                for (int q = 0; q < PER_T; ++q) bs[(ks + 1 - k_begin) & 1][threadIdx.x + GM_THREADS * q] = Sc[q];
+                stage_store((ks + 1 - k_begin) & 1, Sc);
                 __syncthreads();
             }
         };
 
         WRegs R0, R1, R2, R3;
-        u4 S0[PER_T], S1[PER_T];
+        Stage S0, S1;
         {
             __syncthreads();  // LDS reads of the previous segment are done
             if (k_begin < k_end) stage_load(k_begin, S0);
@@ -506,9 +520,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             if (k_begin + 1 < k_end) weight_load(k_begin + 1, R1);
             if (RING == 4 && k_begin + 2 < k_end) weight_load(k_begin + 2, R2);
             __builtin_amdgcn_sched_barrier(0);
-            if (k_begin < k_end)
-#pragma unroll
-                for (int q = 0; q < PER_T; ++q) bs[0][threadIdx.x + GM_THREADS * q] = S0[q];
+            if (k_begin < k_end) stage_store(0, S0);
             __syncthreads();
         }
         // token operands alternate between S1 (steps ks + 1 with ks even) and S0
@@ -562,7 +574,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                         sp[(1 * GM_GROUP + m) * GM_ROWS + rl] = acc[NM - 1][tt][v];
                     }
                 } else {
-                    A.part[(long long)ent * L.H + r] = 256.f * acc[0][tt][v];
+                    A.part[(long long)ent * L.H + r] = xs_lane[tt] * acc[0][tt][v];
                 }
             }
         }
@@ -620,6 +632,30 @@ __global__ __launch_bounds__(256) void k_fixup(GroupedArgs A, int nb)
     }
 }
 
+// The down operand: each entry's h scaled by the power of two that puts its
+// largest |h| in [2^14, 2^15), as fp16 pairs, so a token whose h is tiny
+// everywhere (saturated SiLU) keeps its relative precision.  One block per entry.
+__global__ __launch_bounds__(256) void k_hconvert(const float* __restrict__ hb, const int32_t* __restrict__ grp_u,
+                                                  const int32_t* __restrict__ act_off, int I, uint4* __restrict__ hb16,
+                                                  float* __restrict__ hscale)
+{
+    __shared__ float red[4];
+    const int ent = blockIdx.x;
+    if (ent >= act_off[grp_u[0]]) return;  // uniform for the block
+    const int nu = I / 8;                  // pair-layout uint4 of the entry
+    const float4* src = reinterpret_cast<const float4*>(hb) + (long long)ent * nu * 2;
+    float m = 0.f;
+    for (int u = threadIdx.x; u < nu; u += 256) m = fmaxf(m, absmax8(src[2 * u], src[2 * u + 1]));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const int e = h_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    const float inv = exp2i_f(-e);
+    for (int u = threadIdx.x; u < nu; u += 256)
+        hb16[(long long)ent * nu + u] = h_pairs(src[2 * u], src[2 * u + 1], inv);
+    if (threadIdx.x == 0) hscale[ent] = exp2i_f(e);
+}
+
 // y[t][r] = sum_k w[t][k] * part[entry of slot t*K+k][r] + shared_w * part[t][r],
 // in slot order with the shared expert last; a slot whose expert id was invalid
 // makes the token's row NaN.
@@ -663,7 +699,9 @@ size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E)
     add(sizeof(int32_t) * B * K);                      // slot_pos
     add(16ull * B * L.Gh * 16);                        // xhl
     add(sizeof(float) * B);                            // xscale
-    add(2ull * ents * L.I);                            // hb
+    add(4ull * ents * L.I);                            // hb (fp32)
+    add(2ull * ents * L.I);                            // hb16
+    add(sizeof(float) * ents);                         // hscale
     add(sizeof(float) * ents * L.H);                   // part
     add(sizeof(float) * 2ull * GM_MAX_BLOCKS * 2 * GM_GROUP * GM_ROWS);  // split tiles
     return n;
@@ -690,7 +728,9 @@ GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E)
     W.g.slot_pos = (int32_t*)take(sizeof(int32_t) * B * K);
     W.xhl = (uint4*)take(16ull * B * L.Gh * 16);
     W.xscale = (float*)take(sizeof(float) * B);
-    W.hb = (uint4*)take(2ull * ents * L.I);
+    W.hb = (float*)take(4ull * ents * L.I);
+    W.hb16 = (uint4*)take(2ull * ents * L.I);
+    W.hscale = (float*)take(sizeof(float) * ents);
     W.part = (float*)take(sizeof(float) * ents * L.H);
     W.split = (float*)take(sizeof(float) * 2ull * GM_MAX_BLOCKS * 2 * GM_GROUP * GM_ROWS);
     return W;
@@ -727,10 +767,14 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     A.xhl = W.xhl;
     A.xscale = W.xscale;
     A.hb = W.hb;
+    A.hb16 = W.hb16;
+    A.hscale = W.hscale;
     A.part = W.part;
     A.split = W.split;
     hipExtLaunchKernelGGL(k_grouped_mfma<MODE_GATEUP>, dim3(nb_gu), dim3(GM_THREADS), 0, s, tg.start, tg.stop, 0, A);
     hipLaunchKernelGGL(k_fixup, dim3(nb_gu), dim3(256), 0, s, A, nb_gu);
+    hipLaunchKernelGGL(k_hconvert, dim3(B * K + B), dim3(256), 0, s, W.hb, W.g.grp_u, W.g.act_off, L.I, W.hb16,
+                       W.hscale);
     hipExtLaunchKernelGGL(k_grouped_mfma<MODE_DOWN>, dim3(nb_dn), dim3(GM_THREADS), 0, s, td.start, td.stop, 0, A);
     hipLaunchKernelGGL(k_combine, dim3((L.H + 255) / 256, B), dim3(256), 0, s, W.part, W.g.slot_pos, w, K, L.H,
                        shared_w, y);

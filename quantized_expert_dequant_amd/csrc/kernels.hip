@@ -323,13 +323,12 @@ void launch_topk(const double* logits, int B, int E, int K, int renorm, int32_t*
 // shared expert's loads (no routing needed), then selects the token's experts
 // from the logits while those loads are in flight (or takes the caller's
 // routing), then issues the routed experts' loads.  h = silu(g) * u is written
-// as fp16(h / 256) straight into the pair layout the down GEMV reads.
+// in fp32 in the order of the pair layout the down GEMV reads.
 // ----------------------------------------------------------------------------
 constexpr int GU_RPW = 1;   // row passes per wave
 constexpr int GU_SC = 5;    // expert slots held in registers per round
 constexpr int DN_RPW = 1;   // row passes per wave, down
 constexpr int DN_SC = 5;    // expert slots staged per LDS round, down
-constexpr float H_SCALE = 256.f;  // h is carried as fp16(h / 256)
 
 struct FfnArgs {
     const uint8_t* slab;
@@ -342,7 +341,7 @@ struct FfnArgs {
     float* w;
     int K, E;
     float shared_w;
-    uint16_t* hq;          // [B*(K+1)][8][Gi] uint4 viewed as fp16 halves
+    float* hq;             // h in fp32, pair-layout order: [B*(K+1)][8][Gi][8]
     float* y;
     int sc;                // down: slots per LDS round
 };
@@ -363,7 +362,7 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
     const int sub = lane / LPR, gl = lane & (LPR - 1);
     const int row0 = (blockIdx.x * 4 + wave) * GU_RPW * RPP + sub;
     const Masks M = load_masks();
-    uint16_t* hq_tok = A.hq + (long long)b * KS * L.Gi * 64;
+    float* hq_tok = A.hq + (long long)b * KS * L.Gi * 64;
 
     // routing inputs first: they are cache-resident and gate every routed load
     double lv[16];
@@ -462,7 +461,7 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
             if (i >= nr) continue;
             const int pos = r0 + i;
             const int k = pos == 0 ? K : pos - 1;
-            uint16_t* hq = hq_tok + (long long)k * L.Gi * 64;
+            float* hq = hq_tok + (long long)k * L.Gi * 64;
 #pragma unroll
             for (int p = 0; p < GU_RPW; ++p) {
                 const float gg = lane_group_sum(gacc[i][p], LPR);
@@ -480,8 +479,7 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
                         pp = 8 * (cc >> 4) + (cc & 7);
                         hi = (cc >> 3) & 1;
                     }
-                    hq[((long long)(pp >> 2) * L.Gi + grp) * 8 + (pp & 3) * 2 + hi] =
-                        __builtin_bit_cast(uint16_t, (_Float16)(h * (1.f / H_SCALE)));
+                    hq[((long long)(pp >> 2) * L.Gi + grp) * 8 + (pp & 3) * 2 + hi] = h;
                 }
             }
         }
@@ -489,13 +487,76 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
 }
 
 // ----------------------------------------------------------------------------
+// h staging of the down kernels.  An item is one quarter of a (slot s, group g)
+// pair: the pair-layout uint4 j = 2*part and 2*part + 1 of that group, 16 fp32
+// values of h.  The group's four items scale it by a power of two taken from
+// the group's largest |h|, store it as fp16 pairs and derive the group's stats
+// (C, S, scale) in one pass: a group whose h is tiny keeps its relative precision.
+// pairs: uint4 (s, j, g) at pair_base + s * pair_slot + j * G + g
+// stats: uint4 (s, g) at stat_base + s * stat_slot + g
+// ----------------------------------------------------------------------------
+struct HItem {
+    float4 v[4];
+};
+
+__device__ inline void h_item_load(const float4* htok, int G, int it, int n_items, HItem& H)
+{
+    const int itc = it < n_items ? it : 0;
+    const int sg = itc >> 2, part = itc & 3;
+    const int sl = sg / G, g = sg - sl * G;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int u = (sl * 8 + 2 * part + jj) * G + g;
+        H.v[2 * jj] = htok[2 * u];
+        H.v[2 * jj + 1] = htok[2 * u + 1];
+    }
+}
+
+// every lane of a 4-lane group must call this (the group reductions are DPP)
+template <int BITS>
+__device__ inline void h_item_stage(const HItem& H, int G, int it, int n_items, uint4* lds, int pair_slot,
+                                    int stat_base, int stat_slot)
+{
+    const bool ok = it < n_items;
+    const int itc = ok ? it : 0;
+    const int sg = itc >> 2, part = itc & 3;
+    const int sl = sg / G, g = sg - sl * G;
+    float m = fmaxf(absmax8(H.v[0], H.v[1]), absmax8(H.v[2], H.v[3]));
+    m = group_reduce(m, OpMax(), 4);
+    const int e = h_exponent(m);
+    const float inv = exp2i_f(-e);
+    float off = 0.f, sum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * part + jj;
+        const uint4 u = h_pairs(H.v[2 * jj], H.v[2 * jj + 1], inv);
+        if (ok) lds[sl * pair_slot + j * G + g] = u;
+        const uint32_t pr[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int el = 0; el < 4; ++el) {
+            const h2 hh = __builtin_bit_cast(h2, pr[el]);
+            const float ps = (float)hh.x + (float)hh.y;
+            off = fmaf(pair_class_inv(BITS, 4 * j + el), ps, off);
+            sum += ps;
+        }
+    }
+    off = group_reduce(off, OpAdd(), 4);
+    sum = group_reduce(sum, OpAdd(), 4);
+    if (ok && part == 0) {
+        const float sc = exp2i_f(e);
+        lds[stat_base + sl * stat_slot + g] = __builtin_bit_cast(uint4, make_float4(1024.f * off, sc * sum, sc, 0.f));
+    }
+}
+
+// ----------------------------------------------------------------------------
 // down: dequant-GEMV of the down rows + router-weighted combine, one pass.  A
 // block owns output rows of one token for every active expert.  It fetches
-// the token's h pairs (cache-resident) first, then issues its weight loads,
-// stages h in LDS and derives each group's stats there while the weights
+// the token's h (fp32, cache-resident) first, then issues its weight loads,
+// scales each expert's h by a power of two from its largest |h|, stages it in
+// LDS as fp16 pairs and derives each group's stats there while the weights
 // stream in, and writes y = sum_k w_k Wd_k h_k + shared_weight * Wd_s h_s.
 // ----------------------------------------------------------------------------
-constexpr int DN_HREG = 4;  // uint4 of h staged per thread per round
+constexpr int DN_HREG = 4;  // pair-layout uint4 of h staged per thread per round
 
 template <int BITS>
 __global__ __launch_bounds__(256) void k_down(FfnArgs A)
@@ -508,20 +569,20 @@ __global__ __launch_bounds__(256) void k_down(FfnArgs A)
     const int sub = lane / LPR, gl = lane & (LPR - 1);
     const int row0 = (blockIdx.x * 4 + wave) * DN_RPW * RPP + sub;
     const Masks M = load_masks();
-    const uint4* hq4 = reinterpret_cast<const uint4*>(A.hq) + (long long)b * KS * 8 * G;
+    const float4* hq4 = reinterpret_cast<const float4*>(A.hq) + (long long)b * KS * 8 * G * 2;
     float acc[DN_RPW];
 #pragma unroll
     for (int p = 0; p < DN_RPW; ++p) acc[p] = 0.f;
 
     for (int s0 = 0; s0 < KS; s0 += A.sc) {
         const int ns = min(A.sc, KS - s0);
-        const int n = ns * 8 * G;  // <= 256 * DN_HREG
-        // the round's h pairs (cache-resident) first; clamped indices keep every load in bounds
-        static_assert(DN_HREG == 4, "h staging is written out for four loads per thread");
-        const uint4* hsrc = hq4 + (long long)s0 * 8 * G;
-        const int t0 = threadIdx.x, t1 = t0 + 256, t2 = t0 + 512, t3 = t0 + 768;
-        const uint4 hv0 = hsrc[t0 < n ? t0 : 0], hv1 = hsrc[t1 < n ? t1 : 0];
-        const uint4 hv2 = hsrc[t2 < n ? t2 : 0], hv3 = hsrc[t3 < n ? t3 : 0];
+        const int n_items = ns * G * 4;  // <= 512: two items per thread
+        // the round's h (cache-resident) first; clamped indices keep every load in bounds
+        static_assert(DN_HREG == 4, "a round stages at most 1024 pair-layout uint4 of h");
+        const float4* hsrc = hq4 + (long long)s0 * 8 * G * 2;
+        HItem hi0, hi1;
+        h_item_load(hsrc, G, threadIdx.x, n_items, hi0);
+        h_item_load(hsrc, G, threadIdx.x + 256, n_items, hi1);
         const uint8_t* rec[DN_SC];
         float wt[DN_SC];
 #pragma unroll
@@ -579,41 +640,8 @@ __global__ __launch_bounds__(256) void k_down(FfnArgs A)
         };
         if (s0 > 0) __syncthreads();  // the previous round's LDS reads are done
         issue(gl, gl < G);
-        auto stage = [&](int t, uint4 v) {
-            if (t < n) {
-                const int s = t / (8 * G), rem = t - s * 8 * G;
-                lds[s * 9 * G + rem] = v;
-            }
-        };
-        stage(t0, hv0);
-        stage(t1, hv1);
-        stage(t2, hv2);
-        stage(t3, hv3);
-        __syncthreads();
-        // group stats of the staged h: C = 1024 sum_p (pair sum) / t(p), S = sum h
-        for (int t = threadIdx.x; t < ns * G * 4; t += 256) {
-            const int item = t >> 2, part = t & 3;
-            const int s = item / G, gg = item - s * G;
-            float off = 0.f, sum = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j = 2 * part + jj;
-                const uint4 u = lds[s * 9 * G + j * G + gg];
-                const uint32_t pr[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                for (int el = 0; el < 4; ++el) {
-                    const h2 hh = __builtin_bit_cast(h2, pr[el]);
-                    const float ps = (float)hh.x + (float)hh.y;
-                    off = fmaf(pair_class_inv(BITS, 4 * j + el), ps, off);
-                    sum += ps;
-                }
-            }
-            off = group_reduce(off, OpAdd(), 4);
-            sum = group_reduce(sum, OpAdd(), 4);
-            if (part == 0)
-                lds[s * 9 * G + 8 * G + gg] =
-                    __builtin_bit_cast(uint4, make_float4(1024.f * off, H_SCALE * sum, H_SCALE, 0.f));
-        }
+        h_item_stage<BITS>(hi0, G, threadIdx.x, n_items, lds, 9 * G, 8 * G, 9 * G);
+        h_item_stage<BITS>(hi1, G, threadIdx.x + 256, n_items, lds, 9 * G, 8 * G, 9 * G);
         __syncthreads();
         compute(gl, gl < G);
         for (int g0 = LPR; g0 < G; g0 += LPR) {
@@ -714,7 +742,7 @@ __global__ __launch_bounds__(256) void k_gateup_fast(FfnArgs A)
     }
     __builtin_amdgcn_sched_barrier(0);
     // 6. dequant-GEMV of this wave's slots, in arrival order
-    uint16_t* hq_tok = A.hq + (long long)b * KS * L.Gi * 64;
+    float* hq_tok = A.hq + (long long)b * KS * L.Gi * 64;
     const int grp = rc >> 6, cc = rc & 63;
     int pp, hi;
     if (BITS == 4) {
@@ -745,7 +773,7 @@ __global__ __launch_bounds__(256) void k_gateup_fast(FfnArgs A)
         ua = lane_group_sum(gv ? ua : 0.f, LPR);
         const float h = bad[i] ? __builtin_nanf("") : ga / (1.f + __expf(-ga)) * ua;
         if (gl == 0 && rv)
-            hq_tok[(long long)k * L.Gi * 64 + hoff] = __builtin_bit_cast(uint16_t, (_Float16)(h * (1.f / H_SCALE)));
+            hq_tok[(long long)k * L.Gi * 64 + hoff] = h;
     }
 }
 
@@ -765,12 +793,13 @@ __global__ __launch_bounds__(256) void k_down_fast(FfnArgs A)
     const bool rv = r < L.H;
     const int rc = rv ? r : L.H - 1;
     const Masks M = load_masks();
-    const int n = KS * 8 * G;  // <= 1024
-    // 1. the token's h pairs (cache-resident)
-    const uint4* hsrc = reinterpret_cast<const uint4*>(A.hq) + (long long)b * n;
-    const int t0 = threadIdx.x, t1 = t0 + 256, t2 = t0 + 512, t3 = t0 + 768;
-    const uint4 hv0 = hsrc[t0 < n ? t0 : 0], hv1 = hsrc[t1 < n ? t1 : 0];
-    const uint4 hv2 = hsrc[t2 < n ? t2 : 0], hv3 = hsrc[t3 < n ? t3 : 0];
+    const int n = KS * 8 * G;  // pair-layout uint4 of the token's h, <= 1024
+    const int n_items = KS * G * 4;  // <= 512: two items per thread
+    // 1. the token's h (cache-resident)
+    const float4* hsrc = reinterpret_cast<const float4*>(A.hq) + (long long)b * n * 2;
+    HItem hi0, hi1;
+    h_item_load(hsrc, G, threadIdx.x, n_items, hi0);
+    h_item_load(hsrc, G, threadIdx.x + 256, n_items, hi1);
     __builtin_amdgcn_sched_barrier(0);  // keep the h loads ahead of the weight loads
     // 2. the routing and every slot's down rows
     int eid[KS];
@@ -799,34 +828,11 @@ __global__ __launch_bounds__(256) void k_down_fast(FfnArgs A)
         sbv[k] = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)rc * G + g) * 4);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 3. stage h and derive each group's stats while the weights stream in
-    if (t0 < n) lds[t0] = hv0;
-    if (t1 < n) lds[t1] = hv1;
-    if (t2 < n) lds[t2] = hv2;
-    if (t3 < n) lds[t3] = hv3;
-    __syncthreads();
+    // 3. scale h per group, stage it as fp16 pairs and derive each group's stats
+    //    while the weights stream in
     uint4* lst = lds + n;
-    for (int t = threadIdx.x; t < KS * G * 4; t += 256) {
-        const int item = t >> 2, part = t & 3;
-        const int s = item / G, gg = item - s * G;
-        float off = 0.f, sum = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * part + jj;
-            const uint4 u = lds[(s * 8 + j) * G + gg];
-            const uint32_t pr[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int el = 0; el < 4; ++el) {
-                const h2 hh = __builtin_bit_cast(h2, pr[el]);
-                const float ps = (float)hh.x + (float)hh.y;
-                off = fmaf(pair_class_inv(BITS, 4 * j + el), ps, off);
-                sum += ps;
-            }
-        }
-        off = group_reduce(off, OpAdd(), 4);
-        sum = group_reduce(sum, OpAdd(), 4);
-        if (part == 0) lst[item] = __builtin_bit_cast(uint4, make_float4(1024.f * off, H_SCALE * sum, H_SCALE, 0.f));
-    }
+    h_item_stage<BITS>(hi0, G, threadIdx.x, n_items, lds, 8 * G, n, G);
+    h_item_stage<BITS>(hi1, G, threadIdx.x + 256, n_items, lds, 8 * G, n, G);
     __syncthreads();
     // 4. dequant-GEMV and combine
     float acc = 0.f;
@@ -848,7 +854,7 @@ int down_slots_per_round(const Layout& L)
 {
     int sc = (256 * DN_HREG) / (8 * L.Gi);  // h of a round fits the per-thread staging registers
     if (sc > DN_SC) sc = DN_SC;
-    return sc;  // >= 1 for I <= 16384
+    return sc;  // >= 1 for I <= 8192
 }
 
 template <int BITS, int KS>
@@ -890,7 +896,7 @@ void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4
     A.K = K;
     A.E = E;
     A.shared_w = shared_w;
-    A.hq = (uint16_t*)hq;
+    A.hq = (float*)hq;
     A.y = y;
     A.sc = down_slots_per_round(L);
     const int grows = 4 * GU_RPW * (64 / lanes_per_row(L.Gh));

@@ -62,7 +62,7 @@ int check_shape(const char* fn, int bits, int H, int I, int group)
     if (group != 64) return fail(MOE_EUNSUPPORTED, "%s: group=%d (must be 64)", fn, group);
     if (H <= 0 || I <= 0 || H % 64 || I % 64)
         return fail(MOE_EINVAL, "%s: H=%d and I=%d must be positive multiples of 64", fn, H, I);
-    if (H > 65536 || I > 16384) return fail(MOE_EUNSUPPORTED, "%s: H=%d > 65536 or I=%d > 16384", fn, H, I);
+    if (H > 65536 || I > 8192) return fail(MOE_EUNSUPPORTED, "%s: H=%d > 65536 or I=%d > 8192", fn, H, I);
     return MOE_OK;
 }
 
@@ -123,7 +123,7 @@ Work carve(void* ws, int bits, int B, int H, int I, int E, int K)
     W.w = (float*)take((size_t)B * K * 4);
     W.xq = (uint4*)take((size_t)B * Gh * 128);
     W.xst = (float4*)take((size_t)B * Gh * 16);
-    W.hq = take(S * Gi * 128);
+    W.hq = take(S * Gi * 256);  // h in fp32
     const Layout L = make_layout(bits, H, I);
     W.grouped = grouped_supported(L, B, K);
     W.gw = GroupedWork{};

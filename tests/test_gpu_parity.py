@@ -226,3 +226,22 @@ def test_rmsnorm_matches_oracle():
     for b in range(3):
         ref = oracle.rms_renorm(y[b].astype(np.float64), 1e-6)
         np.testing.assert_allclose(x.cpu().numpy()[b], ref, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("c", [2.0, 4.0, 8.0])
+@pytest.mark.parametrize("B", [1, 2])
+def test_saturated_silu_tiny_outputs(layers, c, B):
+    """x = -c everywhere drives every gate row deep into SiLU's negative tail: the exact outputs are
+    1e-10 (c=2), 1e-23 (c=4) and 1e-49 (c=8, below fp32: delivered as zero).  The per-token bar
+    (relative, floored at fp32's smallest normal) must hold on both the single-token (B=1) and the
+    grouped (B=2) path."""
+    L = layers(0)
+    x = np.full((B, L.H), -c, np.float32)
+    if B > 1:
+        x[1] *= 1.1
+    y, idx, w = _decode(L, x)
+    y_ref, idx_ref, w_ref, margin = oracle_layer(WORKLOADS[0], seed_of(0), 0, x)
+    np.testing.assert_array_equal(idx, idx_ref)
+    for b in range(B):
+        assert np.all(np.isfinite(y[b]))
+        assert rel_err(y[b], y_ref[b]) <= TOL, "token %d: max|y_ref| %.3e" % (b, np.max(np.abs(y_ref[b])))
