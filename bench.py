@@ -173,7 +173,47 @@ def traffic_from_profile(workload, launches_per_step):
     return d.get("traffic_bytes_per_launch")
 
 
+def _pmc_per_dispatch(path, kernel_prefix, counter):
+    """Mean per-dispatch value (KiB) of `counter` for kernels whose name starts with kernel_prefix."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and r["Kernel_Name"].replace("void ", "").startswith(kernel_prefix)]
+    if not vals:
+        raise SystemExit("no %s values for %s in %s" % (counter, kernel_prefix, path))
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_pmc_summary(workload, kernel_prefix, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mb):
+    """profiles/pmc_gateup_<workload>.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of the bench
+    and of the plain device copy (--copy-calibration-mb), which scales each counter to bytes."""
+    copy_kib = copy_mb * 1024.0
+    cf, _ = _pmc_per_dispatch(copy_fetch_csv, "__amd_rocclr_copyBuffer", "FETCH_SIZE")
+    cw, _ = _pmc_per_dispatch(copy_write_csv, "__amd_rocclr_copyBuffer", "WRITE_SIZE")
+    f, nf = _pmc_per_dispatch(fetch_csv, kernel_prefix, "FETCH_SIZE")
+    w, nw = _pmc_per_dispatch(write_csv, kernel_prefix, "WRITE_SIZE")
+    kf, kw = copy_kib / cf, copy_kib / cw
+    traffic = (f * kf + w * kw) * 1024.0
+    c = WORKLOADS[workload]
+    algo = gateup_bytes_per_expert(c) * (c["K"] + 1) if c["B"] == 1 else None
+    out = {"workload": workload, "kernel": kernel_prefix, "kernel_source_hash": kernel_source_hash(),
+           "fetch_kib_per_dispatch": round(f, 1), "write_kib_per_dispatch": round(w, 1), "dispatches": [nf, nw],
+           "copy_calibration_mib": copy_mb, "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+           "fetch_scale": round(kf, 4), "write_scale": round(kw, 4),
+           "traffic_bytes_per_launch": round(traffic), "algorithmic_bytes_per_launch": algo,
+           "traffic_over_algorithmic": round(traffic / algo, 4) if algo else None}
+    path = os.path.join(ROOT, "profiles", "pmc_gateup_%s.json" % workload)
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
+        # bench.py --pmc-summary WORKLOAD KERNEL FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv COPY_MIB
+        a = sys.argv[2:]
+        write_pmc_summary(a[0], a[1], a[2], a[3], a[4], a[5], int(a[6]))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
