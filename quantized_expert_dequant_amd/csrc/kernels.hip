@@ -666,119 +666,131 @@ __global__ __launch_bounds__(256) void k_down(FfnArgs A)
 // ----------------------------------------------------------------------------
 constexpr int FAST_NL = 8;  // fast path: E <= 512 logits per token, 8 per lane
 
+constexpr int GUF_WAVES = 8;  // fast gate/up: waves per block
+
+// One (row pass, expert slot) per wave, blocks in slot-major order: the shared
+// expert's blocks (slot 0) come first and need no routing; a routed block's wave
+// 0 selects the token's experts while the block stages the token's operand.
+// Many small waves per SIMD overlap one another's loads and dequant arithmetic.
 template <int BITS, int KS, bool ROUTE>
-__global__ __launch_bounds__(256) void k_gateup_fast(FfnArgs A)
+__global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
 {
     constexpr int K = KS - 1;
-    // a row's K+1 expert slots are split over two waves (the shared expert plus
-    // the first routed ones in half 0), so two waves per SIMD overlap one
-    // another's loads and arithmetic
-    constexpr int S0 = (KS + 1) / 2;  // slots of half 0: positions [0, S0)
-    constexpr int SMAX = S0;
+    __shared__ uint4 xs[64 * 9];  // the token's operand: 8 uint4 of pairs + stats per group (G <= 64)
+    __shared__ int s_id[KS];
     const Layout& L = A.L;
     const int b = blockIdx.y;
     const int G = L.Gh, LPR = lanes_per_row(G), RPP = 64 / LPR;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int half = wave & 1;
     const int sub = lane / LPR, gl = lane & (LPR - 1);
     const bool gv = gl < G;
     const int g = gv ? gl : G - 1;
-    const int r = (blockIdx.x * 2 + (wave >> 1)) * RPP + sub;
+    const int rows_pb = GUF_WAVES * RPP;
+    const int bps = (L.I + rows_pb - 1) / rows_pb;  // blocks per slot
+    const int slot = blockIdx.x / bps;              // 0: shared expert, k + 1: routed expert k
+    const int r = ((blockIdx.x - slot * bps) * GUF_WAVES + wave) * RPP + sub;
     const bool rv = r < L.I;
     const int rc = rv ? r : L.I - 1;
     const Masks M = load_masks();
-    const int p0 = half ? S0 : 0;               // first slot position of this wave
-    const int np = half ? KS - S0 : S0;         // slots of this wave
 
-    // 1. routing inputs (cache-resident, they gate the routed loads)
+    // 1. cache-resident inputs first (so waiting for them never waits for weights):
+    //    a routed block's wave 0 the routing inputs, every thread a share of the operand
     double lv[FAST_NL];
     int my_id = 0;
-    float my_w = 0.f;
-    if (ROUTE) {
-        topk_load<FAST_NL>(A.logits + (long long)b * A.E, A.E, lane, lv);
-    } else {
-        my_id = A.idx[(long long)b * K + min(lane, K - 1)];
+    if (slot > 0 && wave == 0) {
+        if (ROUTE)
+            topk_load<FAST_NL>(A.logits + (long long)b * A.E, A.E, lane, lv);
+        else
+            my_id = A.idx[(long long)b * K + min(lane, K - 1)];
+    }
+    const int nx = G * 9;  // uint4 of pairs ([8][G]) then stats ([G])
+    uint4 xv[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int t = min((int)threadIdx.x + 64 * GUF_WAVES * q, nx - 1);
+        xv[q] = t < 8 * G ? A.xq[(long long)b * 8 * G + t]
+                          : __builtin_bit_cast(uint4, A.xst[(long long)b * G + (t - 8 * G)]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 2. the token's dequant operand
-    uint4 xp[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) xp[j] = A.xq[((long long)b * 8 + j) * G + g];
-    const float4 st = A.xst[(long long)b * G + g];
 
-    SlotRegs<BITS> R[SMAX];
-    auto issue = [&](SlotRegs<BITS>& S, int e) {
+    SlotRegs<BITS> R;
+    auto issue = [&](int e) {
         const uint8_t* rec = A.slab + (long long)e * L.record;
         const uint8_t* base = rec + (long long)rc * 2 * L.hb;
-        S.g0 = ld16(base + g * 16);
-        S.u0 = ld16(base + L.hb + g * 16);
+        R.g0 = ld16(base + g * 16);
+        R.u0 = ld16(base + L.hb + g * 16);
         if (BITS == 4) {
-            S.g1 = ld16(base + (G + g) * 16);
-            S.u1 = ld16(base + L.hb + (G + g) * 16);
+            R.g1 = ld16(base + (G + g) * 16);
+            R.u1 = ld16(base + L.hb + (G + g) * 16);
         }
-        S.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)rc * G + g) * 8);
+        R.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)rc * G + g) * 8);
     };
-    // 3. the shared expert needs no routing: its loads go out first
-    if (half == 0) issue(R[0], A.E);
+    // 2. the shared expert needs no routing: its loads go out now
+    if (slot == 0) issue(A.E);
     __builtin_amdgcn_sched_barrier(0);
-    // 4. select the routed experts while those loads are in flight
-    if (ROUTE) {
-        topk_select<K, FAST_NL>(lv, A.E, K, A.renorm, lane, my_id, my_w);
-        if (blockIdx.x == 0 && wave == 0 && lane < K) {
-            A.idx[(long long)b * K + lane] = my_id;
-            A.w[(long long)b * K + lane] = my_w;
-        }
-    }
-    // 5. this wave's routed loads (an invalid id reads expert 0 and yields NaN)
-    bool bad[SMAX];
+    // 3. stage the token's operand; wave 0 of a routed block selects the experts meanwhile
 #pragma unroll
-    for (int i = 0; i < SMAX; ++i) {
-        bad[i] = false;
-        const int pos = p0 + i;
-        if (i >= np || pos == 0) continue;
-        const int e = __builtin_amdgcn_readlane(my_id, pos - 1);
-        bad[i] = (e < 0 || e >= A.E);
-        issue(R[i], bad[i] ? 0 : e);
+    for (int q = 0; q < 2; ++q) {
+        const int t = threadIdx.x + 64 * GUF_WAVES * q;
+        if (t < nx) xs[t] = xv[q];
+    }
+    if (slot > 0 && wave == 0) {
+        float my_w = 0.f;
+        if (ROUTE) {
+            topk_select<K, FAST_NL>(lv, A.E, K, A.renorm, lane, my_id, my_w);
+            if (blockIdx.x == bps && lane < K) {  // the first routed block publishes the routing
+                A.idx[(long long)b * K + lane] = my_id;
+                A.w[(long long)b * K + lane] = my_w;
+            }
+        }
+        if (lane < K) s_id[lane] = my_id;
+    }
+    __syncthreads();
+    // 4. a routed block's loads (an invalid id reads expert 0 and yields NaN)
+    bool bad = false;
+    if (slot > 0) {
+        const int e = s_id[slot - 1];
+        bad = (e < 0 || e >= A.E);
+        issue(bad ? 0 : e);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 6. dequant-GEMV of this wave's slots, in arrival order
-    float* hq_tok = A.hq + (long long)b * KS * L.Gi * 64;
-    const int grp = rc >> 6, cc = rc & 63;
-    int pp, hi;
+    uint4 xp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xp[j] = xs[j * G + g];
+    const float4 st = __builtin_bit_cast(float4, xs[8 * G + g]);
+    // 5. dequant-GEMV of the row's gate and up, SwiGLU, h into the pair-layout order
+    float dg, du;
     if (BITS == 4) {
-        pp = 4 * (cc >> 3) + (cc & 3);
-        hi = (cc >> 2) & 1;
+        dg = group_dot_q4(M, R.g0, R.g1, xp);
+        du = group_dot_q4(M, R.u0, R.u1, xp);
     } else {
-        pp = 8 * (cc >> 4) + (cc & 7);
-        hi = (cc >> 3) & 1;
+        dg = group_dot_q2(M, R.g0, xp);
+        du = group_dot_q2(M, R.u0, xp);
     }
-    const long long hoff = ((long long)(pp >> 2) * L.Gi + grp) * 8 + (pp & 3) * 2 + hi;
-#pragma unroll
-    for (int i = 0; i < SMAX; ++i) {
-        if (i >= np) break;
-        const int pos = p0 + i;
-        const int k = (pos == 0) ? K : pos - 1;
-        float dg, du;
+    float ga = fmaf(bf16_lo(R.sb.x) * st.z, dg - st.x, bf16_hi(R.sb.x) * st.y);
+    float ua = fmaf(bf16_lo(R.sb.y) * st.z, du - st.x, bf16_hi(R.sb.y) * st.y);
+    ga = lane_group_sum(gv ? ga : 0.f, LPR);
+    ua = lane_group_sum(gv ? ua : 0.f, LPR);
+    if (gl == 0 && rv) {
+        const float h = bad ? __builtin_nanf("") : ga / (1.f + __expf(-ga)) * ua;
+        const int k = (slot == 0) ? K : slot - 1;
+        const int grp = rc >> 6, cc = rc & 63;
+        int pp, hi;
         if (BITS == 4) {
-            dg = group_dot_q4(M, R[i].g0, R[i].g1, xp);
-            du = group_dot_q4(M, R[i].u0, R[i].u1, xp);
+            pp = 4 * (cc >> 3) + (cc & 3);
+            hi = (cc >> 2) & 1;
         } else {
-            dg = group_dot_q2(M, R[i].g0, xp);
-            du = group_dot_q2(M, R[i].u0, xp);
+            pp = 8 * (cc >> 4) + (cc & 7);
+            hi = (cc >> 3) & 1;
         }
-        const uint2 sb = R[i].sb;
-        float ga = fmaf(bf16_lo(sb.x) * st.z, dg - st.x, bf16_hi(sb.x) * st.y);
-        float ua = fmaf(bf16_lo(sb.y) * st.z, du - st.x, bf16_hi(sb.y) * st.y);
-        ga = lane_group_sum(gv ? ga : 0.f, LPR);
-        ua = lane_group_sum(gv ? ua : 0.f, LPR);
-        const float h = bad[i] ? __builtin_nanf("") : ga / (1.f + __expf(-ga)) * ua;
-        if (gl == 0 && rv)
-            hq_tok[(long long)k * L.Gi * 64 + hoff] = h;
+        A.hq[((long long)b * KS + k) * L.Gi * 64 + ((long long)(pp >> 2) * L.Gi + grp) * 8 + (pp & 3) * 2 + hi] = h;
     }
 }
 
+constexpr int DNF_WAVES = 4;  // fast down: waves per block
+
 template <int BITS, int KS>
-__global__ __launch_bounds__(256) void k_down_fast(FfnArgs A)
+__global__ __launch_bounds__(64 * DNF_WAVES) void k_down_fast(FfnArgs A)
 {
     constexpr int K = KS - 1;
     extern __shared__ uint4 lds[];  // h pairs [KS][8][Gi], then stats [KS][Gi]
@@ -789,17 +801,18 @@ __global__ __launch_bounds__(256) void k_down_fast(FfnArgs A)
     const int sub = lane / LPR, gl = lane & (LPR - 1);
     const bool gv = gl < G;
     const int g = gv ? gl : G - 1;
-    const int r = (blockIdx.x * 4 + wave) * RPP + sub;
+    const int r = (blockIdx.x * DNF_WAVES + wave) * RPP + sub;
     const bool rv = r < L.H;
     const int rc = rv ? r : L.H - 1;
     const Masks M = load_masks();
     const int n = KS * 8 * G;  // pair-layout uint4 of the token's h, <= 1024
-    const int n_items = KS * G * 4;  // <= 512: two items per thread
+    const int n_items = KS * G * 4;  // <= 512
+    static_assert(64 * DNF_WAVES * 2 >= 512, "h staging takes two items per thread");
     // 1. the token's h (cache-resident)
     const float4* hsrc = reinterpret_cast<const float4*>(A.hq) + (long long)b * n * 2;
     HItem hi0, hi1;
     h_item_load(hsrc, G, threadIdx.x, n_items, hi0);
-    h_item_load(hsrc, G, threadIdx.x + 256, n_items, hi1);
+    h_item_load(hsrc, G, threadIdx.x + 64 * DNF_WAVES, n_items, hi1);
     __builtin_amdgcn_sched_barrier(0);  // keep the h loads ahead of the weight loads
     // 2. the routing and every slot's down rows
     int eid[KS];
@@ -832,7 +845,7 @@ __global__ __launch_bounds__(256) void k_down_fast(FfnArgs A)
     //    while the weights stream in
     uint4* lst = lds + n;
     h_item_stage<BITS>(hi0, G, threadIdx.x, n_items, lds, 8 * G, n, G);
-    h_item_stage<BITS>(hi1, G, threadIdx.x + 256, n_items, lds, 8 * G, n, G);
+    h_item_stage<BITS>(hi1, G, threadIdx.x + 64 * DNF_WAVES, n_items, lds, 8 * G, n, G);
     __syncthreads();
     // 4. dequant-GEMV and combine
     float acc = 0.f;
@@ -861,10 +874,11 @@ template <int BITS, int KS>
 void launch_fast_ks(bool route, dim3 fg, dim3 fd, size_t flds, const FfnArgs& A, hipStream_t s, Timing tg, Timing td)
 {
     if (route)
-        hipExtLaunchKernelGGL((k_gateup_fast<BITS, KS, true>), fg, dim3(256), 0, s, tg.start, tg.stop, 0, A);
+        hipExtLaunchKernelGGL((k_gateup_fast<BITS, KS, true>), fg, dim3(64 * GUF_WAVES), 0, s, tg.start, tg.stop, 0, A);
     else
-        hipExtLaunchKernelGGL((k_gateup_fast<BITS, KS, false>), fg, dim3(256), 0, s, tg.start, tg.stop, 0, A);
-    hipExtLaunchKernelGGL((k_down_fast<BITS, KS>), fd, dim3(256), flds, s, td.start, td.stop, 0, A);
+        hipExtLaunchKernelGGL((k_gateup_fast<BITS, KS, false>), fg, dim3(64 * GUF_WAVES), 0, s, tg.start, tg.stop, 0,
+                              A);
+    hipExtLaunchKernelGGL((k_down_fast<BITS, KS>), fd, dim3(64 * DNF_WAVES), flds, s, td.start, td.stop, 0, A);
 }
 
 template <int BITS>
@@ -906,8 +920,10 @@ void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4
     const bool fast = L.Gh <= 64 && L.Gi <= 64 && KS * 8 * L.Gi <= 1024 && E <= 64 * FAST_NL &&
                       (KS == 2 || KS == 3 || KS == 5 || KS == 7 || KS == 9);
     if (fast) {
-        const dim3 fg((L.I + 2 * (64 / lanes_per_row(L.Gh)) - 1) / (2 * (64 / lanes_per_row(L.Gh))), B);
-        const dim3 fd((L.H + 4 * (64 / lanes_per_row(L.Gi)) - 1) / (4 * (64 / lanes_per_row(L.Gi))), B);
+        const int grows = GUF_WAVES * (64 / lanes_per_row(L.Gh));
+        const dim3 fg(KS * ((L.I + grows - 1) / grows), B);
+        const int frows = DNF_WAVES * (64 / lanes_per_row(L.Gi));
+        const dim3 fd((L.H + frows - 1) / frows, B);
         const size_t flds = (size_t)KS * 9 * L.Gi * 16;
         if (L.bits == 4)
             launch_fast<4>(KS, logits != nullptr, fg, fd, flds, A, s, t_gateup, t_down);
