@@ -153,11 +153,29 @@ void launch_dequant(const Layout& L, const void* rec, float* W, hipStream_t s)
 // ----------------------------------------------------------------------------
 __device__ inline float exp2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
+// 1 / sqrt(mean(y^2) + eps) of a row of n4 float4, by one wave: lane l sums the
+// squares of float4 l, l+64, ... in fp64 in that order, then the wave adds the
+// lanes.  The standalone RMS renorm and the router that renormalizes its input
+// on the fly both use this, so they produce bit-identical activations.
+__device__ inline float row_inv_rms(const float4* __restrict__ y4, int n4, float eps, int lane)
+{
+    double ss = 0.0;
+    for (int c = lane; c < n4; c += 64) {
+        const float4 v = y4[c];
+        ss = fma((double)v.x, (double)v.x, ss);
+        ss = fma((double)v.y, (double)v.y, ss);
+        ss = fma((double)v.z, (double)v.z, ss);
+        ss = fma((double)v.w, (double)v.w, ss);
+    }
+    ss = wave_sum(ss);
+    return (float)(1.0 / sqrt(ss / (4.0 * n4) + (double)eps));
+}
+
 template <int BITS>
 __device__ void prep_group(const float* __restrict__ v, int G, int vec, int g, int lane, uint4* __restrict__ q,
-                           float4* __restrict__ st)
+                           float4* __restrict__ st, float scale = 1.f)
 {
-    const float val = v[(long long)vec * G * 64 + g * 64 + lane];
+    const float val = v[(long long)vec * G * 64 + g * 64 + lane] * scale;
     const float amax = wave_max(fabsf(val));
     int e = 0;
     if (amax > 0.f && amax <= 3.4e38f) {
@@ -230,8 +248,11 @@ template <int BITS>
 __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int B, int prepB,
                                                 const float* __restrict__ W, const float* __restrict__ bias, int H,
                                                 int E, double* __restrict__ logits, uint4* __restrict__ xq,
-                                                float4* __restrict__ xst)
+                                                float4* __restrict__ xst, float norm_eps)
 {
+    // norm_eps >= 0: x is the previous layer's output y; the token is renormalized
+    // on the fly, x = y / sqrt(mean(y^2) + eps), exactly as k_rmsnorm would
+    const bool norm = norm_eps >= 0.f;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int e = blockIdx.x * 4 + wave;
     const int n4 = H >> 2;
@@ -256,6 +277,22 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
 #pragma unroll
                     for (int i = 0; i < 16; ++i) xv[i] = x4[(long long)b * n4 + min(lane + 64 * i, n4 - 1)];
                 }
+                if (norm) {  // the sum of squares in row_inv_rms's order, from the registers
+                    double ss = 0.0;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (lane + 64 * i < n4) {
+                            ss = fma((double)xv[i].x, (double)xv[i].x, ss);
+                            ss = fma((double)xv[i].y, (double)xv[i].y, ss);
+                            ss = fma((double)xv[i].z, (double)xv[i].z, ss);
+                            ss = fma((double)xv[i].w, (double)xv[i].w, ss);
+                        }
+                    ss = wave_sum(ss);
+                    const float inv = (float)(1.0 / sqrt(ss / (4.0 * n4) + (double)norm_eps));
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        xv[i] = make_float4(xv[i].x * inv, xv[i].y * inv, xv[i].z * inv, xv[i].w * inv);
+                }
                 double acc = 0.0;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc = dot4d(wv[i], xv[i], acc);
@@ -264,8 +301,12 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
             }
         } else {
             for (int b = 0; b < B; ++b) {
+                const float inv = norm ? row_inv_rms(x4 + (long long)b * n4, n4, norm_eps, lane) : 1.f;
                 double acc = 0.0;
-                for (int c = lane; c < n4; c += 64) acc = dot4d(W4[c], x4[(long long)b * n4 + c], acc);
+                for (int c = lane; c < n4; c += 64) {
+                    const float4 v = x4[(long long)b * n4 + c];
+                    acc = dot4d(W4[c], norm ? make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv) : v, acc);
+                }
                 acc = wave_sum(acc);
                 if (lane == 0) logits[(long long)b * E + e] = acc + bb;
             }
@@ -274,12 +315,13 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
     const int Gh = H / 64;
     for (int i = blockIdx.x * 4 + wave; i < prepB * Gh; i += gridDim.x * 4) {
         const int vec = i / Gh, g = i - vec * Gh;
-        prep_group<BITS>(x, Gh, vec, g, lane, xq, xst);
+        const float inv = norm ? row_inv_rms(x4 + (long long)vec * n4, n4, norm_eps, lane) : 1.f;
+        prep_group<BITS>(x, Gh, vec, g, lane, xq, xst, inv);
     }
 }
 
 void launch_router(int bits, const float* x, int B, const float* W, const float* bias, int H, int E, double* logits,
-                   uint4* xq, float4* xst, hipStream_t s, Timing t)
+                   uint4* xq, float4* xst, hipStream_t s, Timing t, float norm_eps)
 {
     int blocks = (E + 3) / 4;
     const int prepB = xq ? B : 0;
@@ -287,10 +329,10 @@ void launch_router(int bits, const float* x, int B, const float* W, const float*
     if (blocks < prep_blocks) blocks = prep_blocks < 1024 ? prep_blocks : 1024;
     if (bits == 2)
         hipExtLaunchKernelGGL(k_router<2>, dim3(blocks), dim3(256), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
-                              H, E, logits, xq, xst);
+                              H, E, logits, xq, xst, norm_eps);
     else
         hipExtLaunchKernelGGL(k_router<4>, dim3(blocks), dim3(256), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
-                              H, E, logits, xq, xst);
+                              H, E, logits, xq, xst, norm_eps);
 }
 
 // one wave per token: logits -> idx, w
@@ -946,17 +988,9 @@ void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ y, int H, float eps, float* __restrict__ x)
 {
-    __shared__ double part[4];
-    const int b = blockIdx.x;
+    const int b = blockIdx.x, lane = threadIdx.x & 63;
     const float* yb = y + (long long)b * H;
-    double ss = 0.0;
-    for (int c = threadIdx.x; c < H; c += 256) ss += (double)yb[c] * (double)yb[c];
-    ss = wave_sum(ss);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const double tot = part[0] + part[1] + part[2] + part[3];
-    const float inv = (float)(1.0 / sqrt(tot / H + (double)eps));
-    __syncthreads();
+    const float inv = row_inv_rms(reinterpret_cast<const float4*>(yb), H / 4, eps, lane);  // every wave alike
     for (int c = threadIdx.x; c < H; c += 256) x[(long long)b * H + c] = yb[c] * inv;
 }
 

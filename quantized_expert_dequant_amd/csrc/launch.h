@@ -18,8 +18,9 @@ void launch_pack(const Layout& L, int n, const uint8_t* gate, const uint8_t* up,
                  const uint16_t* scales, const uint16_t* biases, void* slab, int first, hipStream_t s);
 void launch_dequant(const Layout& L, const void* rec, float* W, hipStream_t s);
 void launch_prep(int bits, const float* v, int n_vec, int len, uint4* q, float4* st, hipStream_t s);
+// norm_eps >= 0: x is the previous layer's output, renormalized on the fly (as launch_rmsnorm)
 void launch_router(int bits, const float* x, int B, const float* W, const float* bias, int H, int E, double* logits,
-                   uint4* xq, float4* xst, hipStream_t s, Timing t = Timing());
+                   uint4* xq, float4* xst, hipStream_t s, Timing t = Timing(), float norm_eps = -1.f);
 void launch_topk(const double* logits, int B, int E, int K, int renorm, int32_t* idx, float* w, hipStream_t s);
 void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4* xst, const double* logits,
                 int renorm, int32_t* idx, float* w, int B, int K, int E, float shared_w, void* hq, float* y,

@@ -278,8 +278,10 @@ int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const i
     return expert_ffn("moe_expert_ffn_q2", 2, desc, x, B, idx, w, y_out, ws, ws_bytes, stream);
 }
 
+// norm_eps >= 0 (per-token path only): x is the previous layer's output, renormalized
+// by the router kernel on the fly
 static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, int B, float* y_out,
-                      int32_t* idx_out, float* w_out, const Work& W, hipStream_t s)
+                      int32_t* idx_out, float* w_out, const Work& W, hipStream_t s, float norm_eps = -1.f)
 {
     int32_t* idx = idx_out ? idx_out : W.idx;
     float* w = w_out ? w_out : W.w;
@@ -293,7 +295,7 @@ static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, i
         return hip_status(fn);
     }
     launch_router(d->bits, x, B, d->w_router, d->logit_bias, d->H, d->E, W.logits, W.xq, W.xst, s,
-                  g_timing[KID_ROUTER]);
+                  g_timing[KID_ROUTER], norm_eps);
     launch_ffn(L, d->experts, W.xq, W.xst, W.logits, d->renormalize ? 1 : 0, idx, w, B, d->K, d->E,
                d->shared_weight, W.hq, y_out, s, g_timing[KID_GATEUP], g_timing[KID_DOWN]);
     return hip_status(fn);
@@ -375,17 +377,26 @@ int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* x,
     float* ybuf = (float*)((char*)ws + W.bytes);
     float* xbuf = (float*)((char*)ws + W.bytes + vec);
     hipStream_t s = (hipStream_t)stream;
+    // Per-token path: each layer's router renormalizes the previous layer's output
+    // itself (no separate pass), and the two buffers alternate so a layer never
+    // writes the y it reads; the grouped path renormalizes ybuf into xbuf.
     const float* xl = x;
+    float norm = -1.f;
     for (int l = 0; l < n_layers; ++l) {
         const bool last = (l == n_layers - 1);
-        float* yl = last ? y_out : ybuf;
+        float* yl = last ? y_out : ((W.grouped || !(l & 1)) ? ybuf : xbuf);
         int32_t* il = idx_out ? idx_out + (size_t)l * B * d0.K : nullptr;
         float* wl = w_out ? w_out + (size_t)l * B * d0.K : nullptr;
-        int rc = layer_impl(fn, &layers[l], xl, B, yl, il, wl, W, s);
+        int rc = layer_impl(fn, &layers[l], xl, B, yl, il, wl, W, s, norm);
         if (rc) return rc;
         if (!last) {
-            launch_rmsnorm(ybuf, B, d0.H, eps, xbuf, s);
-            xl = xbuf;
+            if (W.grouped) {
+                launch_rmsnorm(ybuf, B, d0.H, eps, xbuf, s);
+                xl = xbuf;
+            } else {
+                xl = yl;
+                norm = eps;
+            }
         }
     }
     return hip_status(fn);
