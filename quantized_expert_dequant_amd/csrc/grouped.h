@@ -12,20 +12,26 @@ namespace moe {
 
 // Output of the grouping kernel.  offsets / tokens / slots: the assignments of
 // expert e are positions [offsets[e], offsets[e+1]) of tokens (token id) and
-// slots (slot b*K + k), in slot order.  The rest is the MFMA work list and may
-// be null together: the entries (0 .. B-1: the shared expert's, one per token;
-// B + p: position p of the sort) are cut into V = grp_u[0] groups of at most 32
-// entries of one expert, the shared expert's first, then the routed experts by
-// id; group v is expert act_expert[v] with entries act_off[v] .. act_off[v+1]-1,
-// whose tokens are ent_token[]; slot_pos[b*K + k] = entry of that slot (-1:
-// invalid id).
+// slots (slot b*K + k), in slot order.  The rest is the work list and may be
+// null together.  The entries (0 .. B-1: the shared expert's, one per token;
+// B + p: position p of the sort) of an expert with fewer than gv_t tokens form
+// one GEMV group; a larger expert's are cut into MFMA groups of at most 32
+// entries.  Each list holds the shared expert first (if it falls in it), then
+// the routed experts by id.  MFMA group v (v < grp_u[0]) is expert
+// act_expert[v] with entries act_off[v] .. act_off[v] + act_n[v] - 1, GEMV
+// group v (v < grp_u[1]) likewise with gv_expert / gv_off / gv_n; the entries'
+// tokens are ent_token[]; slot_pos[b*K + k] = entry of that slot (-1: invalid id).
 struct GroupOut {
     int32_t* offsets;     // [E + 1]
     int32_t* tokens;      // [B*K]
     int32_t* slots;       // [B*K]
-    int32_t* grp_u;       // [1]
+    int32_t* grp_u;       // [2]: MFMA groups, GEMV groups
     int32_t* act_expert;  // [V]
-    int32_t* act_off;     // [V + 1]
+    int32_t* act_off;     // [V]
+    int32_t* act_n;       // [V]
+    int32_t* gv_expert;   // [V]
+    int32_t* gv_off;      // [V]
+    int32_t* gv_n;        // [V]
     int32_t* ent_token;   // [B + B*K]
     int32_t* slot_pos;    // [B*K]
 };
@@ -39,6 +45,7 @@ struct GroupedWork {
     float* hb;        // h in fp32, pair-layout order [B + B*K][8][G_i][8]
     uint4* hb16;      // h * 2^-e(entry) as fp16 pairs [B + B*K][8][G_i]
     float* hscale;    // 2^e(entry) [B + B*K]
+    float4* hstats;   // per group of hb16: (C, S, scale, 0) for the dot2 GEMV [B + B*K][G_i]
     float* part;      // down outputs [B + B*K][H]
     float* split;     // partial gate/up sums of tiles split between blocks
 };
@@ -49,8 +56,12 @@ GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E);
 int router_splits(int H);
 void launch_route_batched(const float* x, int B, const float* W, const float* bias, int H, int E, int K, int renorm,
                           double* partial, double* logits, int32_t* idx, float* w, hipStream_t s, Timing t);
-void launch_group(const int32_t* idx, int B, int K, int E, const GroupOut& O, hipStream_t s);
+// experts with fewer tokens than this run as GEMV groups (1: none)
+int gemv_tokens(const Layout& L);
+void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const GroupOut& O, hipStream_t s);
+// xq / xst: room for the B tokens' dot2 operands (fp16 pairs + group stats)
 void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W, const float* x, const float* w,
-                        float shared_w, int B, int K, int E, float* y, hipStream_t s, Timing tg, Timing td);
+                        float shared_w, int B, int K, int E, uint4* xq, float4* xst, float* y, hipStream_t s,
+                        Timing tg, Timing td);
 
 }  // namespace moe

@@ -20,7 +20,9 @@
 //   k_prep_tokens    token activations -> fp16 hi + lo MFMA operands
 //   k_grouped_mfma   gate/up (+ SwiGLU) or down dequant-GEMM over (group, 128 rows, K chunk)
 //   k_fixup          SwiGLU of gate/up tiles whose K chunks two blocks shared
-//   k_hconvert       h of every entry -> fp16 with the entry's power-of-two scale
+//   k_gemv_gateup    gate/up (+ SwiGLU) of the small groups as dot2 GEMVs
+//   k_hconvert       h of every entry -> fp16 with the entry's power-of-two scale + group stats
+//   k_gemv_down      down of the small groups as dot2 GEMVs
 //   k_combine        per-token routing-weighted sum of the down outputs
 #include <hip/hip_ext.h>
 
@@ -33,7 +35,11 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));  // native vector: copies stay in registers
 
-constexpr int GM_GROUP = 32;         // most tokens of one work-list group
+constexpr int GM_GROUP = 32;         // most tokens of one MFMA work-list group
+#ifndef MOE_GV_TOKENS
+#define MOE_GV_TOKENS 3
+#endif
+constexpr int GV_TOKENS = MOE_GV_TOKENS;  // an expert with fewer tokens than this runs as a dot2 GEMV group
 constexpr int GM_MAX_BLOCKS = 1024;  // most blocks of a stream-split launch
 
 __device__ inline f4 mfma16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
@@ -130,11 +136,11 @@ void launch_route_batched(const float* x, int B, const float* W, const float* bi
 // at most GM_GROUP tokens (the shared expert's B entries first, then the routed
 // experts by id), so that every group is one pass of the dequant-GEMM.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx, int B, int K, int E, GroupOut O)
+__global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx, int B, int K, int E, int gv_t, GroupOut O)
 {
     __shared__ int sidx[MOE_MAX_B * MOE_MAX_K];
     __shared__ int cnt[MOE_MAX_E];
-    __shared__ int wsum[2][16];
+    __shared__ int wsum[3][16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int n = B * K;
     const bool work = O.grp_u != nullptr;
@@ -148,49 +154,69 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
     }
     __syncthreads();
     const int c = tid < E ? cnt[tid] : 0;
-    const int f = (c + GM_GROUP - 1) / GM_GROUP;  // groups of this expert
-    // exclusive scans of the counts and of the group counts over the block
-    int sc = c, sf = f;
+    // an expert with fewer than gv_t tokens is one GEMV group, a larger one is
+    // cut into MFMA groups of at most GM_GROUP tokens
+    const int fm = c >= gv_t ? (c + GM_GROUP - 1) / GM_GROUP : 0;
+    const int fg = (c > 0 && c < gv_t) ? 1 : 0;
+    // exclusive scans of the counts and of both group counts over the block
+    int sc = c, sm = fm, sg = fg;
     for (int off = 1; off < 64; off <<= 1) {
-        const int oc = __shfl_up(sc, off, 64), of = __shfl_up(sf, off, 64);
+        const int oc = __shfl_up(sc, off, 64), om = __shfl_up(sm, off, 64), og = __shfl_up(sg, off, 64);
         if (lane >= off) {
             sc += oc;
-            sf += of;
+            sm += om;
+            sg += og;
         }
     }
     if (lane == 63) {
         wsum[0][tid >> 6] = sc;
-        wsum[1][tid >> 6] = sf;
+        wsum[1][tid >> 6] = sm;
+        wsum[2][tid >> 6] = sg;
     }
     __syncthreads();
-    int pc = 0, pf = 0;
+    int pc = 0, pm = 0, pg = 0;
     for (int q = 0; q < (tid >> 6); ++q) {
         pc += wsum[0][q];
-        pf += wsum[1][q];
+        pm += wsum[1][q];
+        pg += wsum[2][q];
     }
-    const int excl_c = pc + sc - c, excl_f = pf + sf - f;
-    const int vs = (B + GM_GROUP - 1) / GM_GROUP;  // groups of the shared expert
+    const int excl_c = pc + sc - c, excl_m = pm + sm - fm, excl_g = pg + sg - fg;
+    // the shared expert (all B tokens, entries 0 .. B-1) leads its list
+    const bool shared_gemv = B < gv_t;
+    const int vsm = shared_gemv ? 0 : (B + GM_GROUP - 1) / GM_GROUP, vsg = shared_gemv ? 1 : 0;
     if (tid < E) {
         O.offsets[tid] = excl_c;
         cnt[tid] = excl_c;  // running position of expert tid
-        if (work)
-            for (int j = 0; j < f; ++j) {
-                O.act_expert[vs + excl_f + j] = tid;
-                O.act_off[vs + excl_f + j] = B + excl_c + j * GM_GROUP;
+        if (work) {
+            for (int j = 0; j < fm; ++j) {
+                O.act_expert[vsm + excl_m + j] = tid;
+                O.act_off[vsm + excl_m + j] = B + excl_c + j * GM_GROUP;
+                O.act_n[vsm + excl_m + j] = min(GM_GROUP, c - j * GM_GROUP);
             }
+            if (fg) {
+                O.gv_expert[vsg + excl_g] = tid;
+                O.gv_off[vsg + excl_g] = B + excl_c;
+                O.gv_n[vsg + excl_g] = c;
+            }
+        }
     }
     if (tid == E - 1) {
-        const int total = excl_c + c, V = vs + excl_f + f;
-        O.offsets[E] = total;
+        O.offsets[E] = excl_c + c;
         if (work) {
-            O.grp_u[0] = V;
-            O.act_off[V] = B + total;
+            O.grp_u[0] = vsm + excl_m + fm;  // MFMA groups
+            O.grp_u[1] = vsg + excl_g + fg;  // GEMV groups
         }
     }
     if (work) {
-        for (int j = tid; j < vs; j += 1024) {
+        for (int j = tid; j < vsm; j += 1024) {
             O.act_expert[j] = E;
             O.act_off[j] = j * GM_GROUP;
+            O.act_n[j] = min(GM_GROUP, B - j * GM_GROUP);
+        }
+        if (shared_gemv && tid == 0) {
+            O.gv_expert[0] = E;
+            O.gv_off[0] = 0;
+            O.gv_n[0] = B;
         }
         for (int b = tid; b < B; b += 1024) O.ent_token[b] = b;
     }
@@ -221,9 +247,11 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
     }
 }
 
-void launch_group(const int32_t* idx, int B, int K, int E, const GroupOut& O, hipStream_t s)
+int gemv_tokens(const Layout& L) { return (L.bits == 4 && L.Gh <= 64 && L.Gi <= 64) ? GV_TOKENS : 1; }
+
+void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const GroupOut& O, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, idx, B, K, E, O);
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, idx, B, K, E, gv_tokens, O);
 }
 
 // ----------------------------------------------------------------------------
@@ -331,6 +359,11 @@ struct GroupedArgs {
     const int32_t* grp_u;
     const int32_t* act_expert;
     const int32_t* act_off;
+    const int32_t* act_n;
+    const int32_t* gv_expert;
+    const int32_t* gv_off;
+    const int32_t* gv_n;
+    const int32_t* n_ent;   // offsets[E]: routed entries placed (entries B .. B + n_ent - 1)
     const int32_t* ent_token;
     const uint4* xhl;
     const float* xscale;
@@ -402,7 +435,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         const int u = tau / tiles, tile = tau - u * tiles;
         const int k_begin = kc0 * nsteps / KC, k_end = kc1 * nsteps / KC;
         const int e = A.act_expert[u];
-        const int ent0 = A.act_off[u], n = A.act_off[u + 1] - ent0;  // 1 <= n <= GM_GROUP
+        const int ent0 = A.act_off[u], n = A.act_n[u];  // 1 <= n <= GM_GROUP
         const int ntt = (n + 15) / 16;
         // addresses: uniform base + 32-bit byte offset (a record, the token and h
         // operands are each far below 4 GiB)
@@ -597,7 +630,7 @@ __global__ __launch_bounds__(256) void k_fixup(GroupedArgs A, int nb)
     const int tau = s0 / KC;
     if (gm_lo(b - 1, T, nb) > tau * KC) return;  // a lower block starts inside this tile
     const int u = tau / tiles, tile = tau - u * tiles;
-    const int ent0 = A.act_off[u], n = A.act_off[u + 1] - ent0;
+    const int ent0 = A.act_off[u], n = A.act_n[u];
     const int b_lo = gm_blk(tau * KC, T, nb), b_hi = gm_blk((tau + 1) * KC - 1, T, nb);
     // the tile's partial slots in K order (at most KC blocks share a tile)
     int slots[KC], ns = 0;
@@ -634,15 +667,18 @@ __global__ __launch_bounds__(256) void k_fixup(GroupedArgs A, int nb)
 
 // The down operand: each entry's h scaled by the power of two that puts its
 // largest |h| in [2^14, 2^15), as fp16 pairs, so a token whose h is tiny
-// everywhere (saturated SiLU) keeps its relative precision.  One block per entry.
-__global__ __launch_bounds__(256) void k_hconvert(const float* __restrict__ hb, const int32_t* __restrict__ grp_u,
-                                                  const int32_t* __restrict__ act_off, int I, uint4* __restrict__ hb16,
-                                                  float* __restrict__ hscale)
+// everywhere (saturated SiLU) keeps its relative precision; and, for the dot2
+// GEMV, each group's stats (C = 1024 * sum_p (pair sum) / t(p), S = sum h, scale)
+// of the rounded values.  One block per entry.
+__global__ __launch_bounds__(256) void k_hconvert(const float* __restrict__ hb, const int32_t* __restrict__ n_ent,
+                                                  int B, int I, uint4* __restrict__ hb16, float* __restrict__ hscale,
+                                                  float4* __restrict__ hstats)
 {
     __shared__ float red[4];
+    __shared__ float poff[1024], psum[1024];  // per pair-layout uint4 (I <= 8192)
     const int ent = blockIdx.x;
-    if (ent >= act_off[grp_u[0]]) return;  // uniform for the block
-    const int nu = I / 8;                  // pair-layout uint4 of the entry
+    if (ent >= B + n_ent[0]) return;  // uniform for the block
+    const int nu = I / 8, Gi = I / 64;  // pair-layout uint4 of the entry: [8][Gi]
     const float4* src = reinterpret_cast<const float4*>(hb) + (long long)ent * nu * 2;
     float m = 0.f;
     for (int u = threadIdx.x; u < nu; u += 256) m = fmaxf(m, absmax8(src[2 * u], src[2 * u + 1]));
@@ -650,10 +686,213 @@ __global__ __launch_bounds__(256) void k_hconvert(const float* __restrict__ hb, 
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     const int e = h_exponent(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
-    const float inv = exp2i_f(-e);
-    for (int u = threadIdx.x; u < nu; u += 256)
-        hb16[(long long)ent * nu + u] = h_pairs(src[2 * u], src[2 * u + 1], inv);
-    if (threadIdx.x == 0) hscale[ent] = exp2i_f(e);
+    const float inv = exp2i_f(-e), sc = exp2i_f(e);
+    for (int u = threadIdx.x; u < nu; u += 256) {
+        const uint4 pv = h_pairs(src[2 * u], src[2 * u + 1], inv);
+        hb16[(long long)ent * nu + u] = pv;
+        const int j = u / Gi;  // uint4 u = j * Gi + g holds pairs 4j .. 4j+3 of group g
+        const uint32_t pr[4] = {pv.x, pv.y, pv.z, pv.w};
+        float off = 0.f, sum = 0.f;
+#pragma unroll
+        for (int el = 0; el < 4; ++el) {
+            const h2 hh = __builtin_bit_cast(h2, pr[el]);
+            const float ps = (float)hh.x + (float)hh.y;
+            off = fmaf(pair_class_inv(4, 4 * j + el), ps, off);
+            sum += ps;
+        }
+        poff[u] = off;
+        psum[u] = sum;
+    }
+    __syncthreads();
+    for (int g = threadIdx.x; g < Gi; g += 256) {
+        float off = 0.f, sum = 0.f;
+        for (int j = 0; j < 8; ++j) {
+            off += poff[j * Gi + g];
+            sum += psum[j * Gi + g];
+        }
+        hstats[(long long)ent * Gi + g] = make_float4(1024.f * off, sc * sum, sc, 0.f);
+    }
+    if (threadIdx.x == 0) hscale[ent] = sc;
+}
+
+// ----------------------------------------------------------------------------
+// Small groups (fewer than GV_TOKENS tokens): dot2 GEMVs, each weight row read
+// once, its fp16 code patterns built once and multiplied by every token of the
+// group; the matrix cores would pad such a group to 16 tokens.  Same operand
+// formats and group fold as the single-token kernels (xq / xst for x, the
+// scaled fp16 pairs + stats for h).  Work items (group, block of rows) are cut
+// into equal contiguous ranges, one per block.
+// ----------------------------------------------------------------------------
+constexpr int GV_WAVES = 4;
+constexpr int GV_META = 32;  // most GEMV groups one block's item range may touch (the grid is sized for it)
+
+// The block's groups (expert, first entry, tokens) in LDS, read once up front so
+// that no wait on them ever drains the weight loads in flight.  Returns the
+// first group of the range.
+__device__ inline int gv_meta(const GroupedArgs& A, int lo, int hi, int rb, int (*meta)[GV_META])
+{
+    const int v0 = lo / rb, nv = min((hi - 1) / rb - v0 + 1, GV_META);
+    if (threadIdx.x < nv) {
+        meta[0][threadIdx.x] = A.gv_expert[v0 + threadIdx.x];
+        meta[1][threadIdx.x] = A.gv_off[v0 + threadIdx.x];
+        meta[2][threadIdx.x] = A.gv_n[v0 + threadIdx.x];
+    }
+    __syncthreads();
+    return v0;
+}
+
+// Stage the group's n operand vectors in LDS: per vector 8*G uint4 of pairs
+// (vector m's pairs at pairs[m*8*G ..]) then G float4 stats.
+__device__ inline void gv_stage(uint4* lds, int n, int G, const int32_t* vec_of, int vec0, const uint4* pairs,
+                                const float4* stats)
+{
+    const int nx = 9 * G;
+    for (int t = threadIdx.x; t < n * nx; t += 64 * GV_WAVES) {
+        const int m = t / nx, k = t - m * nx;
+        const long long vec = vec_of ? vec_of[vec0 + m] : vec0 + m;
+        lds[t] = k < 8 * G ? pairs[vec * 8 * G + k] : __builtin_bit_cast(uint4, stats[vec * G + (k - 8 * G)]);
+    }
+}
+
+// One lane's share of a gate/up row pair (gate codes, up codes, scales) or of a down row.
+struct GvGateUp {
+    uint4 c[4];
+    uint2 sb;
+};
+struct GvDown {
+    uint4 c[2];
+    uint32_t sb;
+};
+
+// gate/up of the small groups: h = silu(W_g x) * (W_u x) per token of the group.
+// Work item = (group, GV_WAVES row passes); each block walks a contiguous range of
+// items, the next item's weights in flight while the current one is computed.
+__global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_gateup(GroupedArgs A, const uint4* __restrict__ xq,
+                                                               const float4* __restrict__ xst)
+{
+    extern __shared__ uint4 xs[];  // [n][9*G]
+    const Layout& L = A.L;
+    const int G = L.Gh, LPR = lanes_per_row(G), RPP = 64 / LPR;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sub = lane / LPR, gl = lane & (LPR - 1);
+    const bool gv = gl < G;
+    const int g = gv ? gl : G - 1;
+    const int rows_pi = GV_WAVES * RPP;
+    const int rb = (L.I + rows_pi - 1) / rows_pi;
+    const int T = A.grp_u[1] * rb;
+    const int lo = gm_lo(blockIdx.x, T, gridDim.x), hi = gm_lo(blockIdx.x + 1, T, gridDim.x);
+    if (lo >= hi) return;  // uniform for the block
+    __shared__ int meta[3][GV_META];
+    const int v0 = gv_meta(A, lo, hi, rb, meta);
+    auto mv = [&](int f, int v) { return __builtin_amdgcn_readfirstlane(meta[f][min(v - v0, GV_META - 1)]); };
+    const Masks M = load_masks();
+    // loads are unconditional (item and row clamped) so that waits stay exact
+    auto load = [&](GvGateUp& w, int it) {
+        it = min(it, hi - 1);
+        const int v = it / rb;
+        const int r = min((it - v * rb) * rows_pi + wave * RPP + sub, L.I - 1);
+        const uint8_t* rec = A.slab + (long long)mv(0, v) * L.record;
+        const uint8_t* base = rec + (long long)r * 2 * L.hb;
+        w.c[0] = *reinterpret_cast<const uint4*>(base + g * 16);
+        w.c[1] = *reinterpret_cast<const uint4*>(base + (G + g) * 16);
+        w.c[2] = *reinterpret_cast<const uint4*>(base + L.hb + g * 16);
+        w.c[3] = *reinterpret_cast<const uint4*>(base + L.hb + (G + g) * 16);
+        w.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)r * G + g) * 8);
+    };
+    int v_prev = -1;
+    auto work = [&](const GvGateUp& w, int it, GvGateUp& next) {
+        const int v = it / rb;
+        const int ent0 = mv(1, v), n = mv(2, v);
+        if (v != v_prev) {    // uniform: every thread walks the same items
+            __syncthreads();  // every wave is done with the previous group's operands
+            gv_stage(xs, n, G, A.ent_token, ent0, xq, xst);
+            __syncthreads();
+            v_prev = v;
+        }
+        load(next, it + 1);
+        const int r = (it - v * rb) * rows_pi + wave * RPP + sub;
+        for (int m = 0; m < n; ++m) {
+            const uint4* xv = xs + m * 9 * G;
+            uint4 xp[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xp[j] = xv[j * G + g];
+            const float4 st = __builtin_bit_cast(float4, xv[8 * G + g]);
+            float ga = fmaf(bf16_lo(w.sb.x) * st.z, group_dot_q4(M, w.c[0], w.c[1], xp) - st.x, bf16_hi(w.sb.x) * st.y);
+            float ua = fmaf(bf16_lo(w.sb.y) * st.z, group_dot_q4(M, w.c[2], w.c[3], xp) - st.x, bf16_hi(w.sb.y) * st.y);
+            ga = lane_group_sum(gv ? ga : 0.f, LPR);
+            ua = lane_group_sum(gv ? ua : 0.f, LPR);
+            if (gl == 0 && r < L.I) store_h(A, ent0 + m, r, ga, ua, 1.f);
+        }
+    };
+    GvGateUp wa, wb;
+    load(wa, lo);
+    for (int it = lo; it < hi; it += 2) {
+        work(wa, it, wb);
+        if (it + 1 >= hi) break;
+        work(wb, it + 1, wa);
+    }
+}
+
+// down of the small groups: part[entry] = W_d h_entry, h as the scaled fp16
+// pairs and per-group stats written by k_hconvert.
+__global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_down(GroupedArgs A, const float4* __restrict__ hstats)
+{
+    extern __shared__ uint4 hs[];  // [n][9*G]
+    const Layout& L = A.L;
+    const int G = L.Gi, LPR = lanes_per_row(G), RPP = 64 / LPR;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sub = lane / LPR, gl = lane & (LPR - 1);
+    const bool gv = gl < G;
+    const int g = gv ? gl : G - 1;
+    const int rows_pi = GV_WAVES * RPP;
+    const int rb = (L.H + rows_pi - 1) / rows_pi;
+    const int T = A.grp_u[1] * rb;
+    const int lo = gm_lo(blockIdx.x, T, gridDim.x), hi = gm_lo(blockIdx.x + 1, T, gridDim.x);
+    if (lo >= hi) return;
+    __shared__ int meta[3][GV_META];
+    const int v0 = gv_meta(A, lo, hi, rb, meta);
+    auto mv = [&](int f, int v) { return __builtin_amdgcn_readfirstlane(meta[f][min(v - v0, GV_META - 1)]); };
+    const Masks M = load_masks();
+    auto load = [&](GvDown& w, int it) {
+        it = min(it, hi - 1);
+        const int v = it / rb;
+        const int r = min((it - v * rb) * rows_pi + wave * RPP + sub, L.H - 1);
+        const uint8_t* rec = A.slab + (long long)mv(0, v) * L.record;
+        const uint8_t* base = rec + L.off_d_codes + (long long)r * L.ib;
+        w.c[0] = *reinterpret_cast<const uint4*>(base + g * 16);
+        w.c[1] = *reinterpret_cast<const uint4*>(base + (G + g) * 16);
+        w.sb = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)r * G + g) * 4);
+    };
+    int v_prev = -1;
+    auto work = [&](const GvDown& w, int it, GvDown& next) {
+        const int v = it / rb;
+        const int ent0 = mv(1, v), n = mv(2, v);
+        if (v != v_prev) {
+            __syncthreads();
+            gv_stage(hs, n, G, nullptr, ent0, A.hb16, hstats);
+            __syncthreads();
+            v_prev = v;
+        }
+        load(next, it + 1);
+        const int r = (it - v * rb) * rows_pi + wave * RPP + sub;
+        for (int m = 0; m < n; ++m) {
+            const uint4* hv = hs + m * 9 * G;
+            uint4 hp[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hp[j] = hv[j * G + g];
+            const float4 sv = __builtin_bit_cast(float4, hv[8 * G + g]);
+            float acc = fmaf(bf16_lo(w.sb) * sv.z, group_dot_q4(M, w.c[0], w.c[1], hp) - sv.x, bf16_hi(w.sb) * sv.y);
+            acc = lane_group_sum(gv ? acc : 0.f, LPR);
+            if (gl == 0 && r < L.H) A.part[(long long)(ent0 + m) * L.H + r] = acc;
+        }
+    };
+    GvDown wa, wb;
+    load(wa, lo);
+    for (int it = lo; it < hi; it += 2) {
+        work(wa, it, wb);
+        if (it + 1 >= hi) break;
+        work(wb, it + 1, wa);
+    }
 }
 
 // y[t][r] = sum_k w[t][k] * part[entry of slot t*K+k][r] + shared_w * part[t][r],
@@ -693,8 +932,7 @@ size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E)
     add(sizeof(int32_t) * B * K);                      // tokens
     add(sizeof(int32_t) * B * K);                      // slots
     add(sizeof(int32_t) * 4);                          // number of groups
-    add(sizeof(int32_t) * V);                          // act_expert
-    add(sizeof(int32_t) * (V + 1));                    // act_off
+    for (int l = 0; l < 6; ++l) add(sizeof(int32_t) * V);  // act_expert, act_off, act_n, gv_expert, gv_off, gv_n
     add(sizeof(int32_t) * ents);                       // ent_token
     add(sizeof(int32_t) * B * K);                      // slot_pos
     add(16ull * B * L.Gh * 16);                        // xhl
@@ -702,6 +940,7 @@ size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E)
     add(4ull * ents * L.I);                            // hb (fp32)
     add(2ull * ents * L.I);                            // hb16
     add(sizeof(float) * ents);                         // hscale
+    add(16ull * ents * L.Gi);                          // hstats
     add(sizeof(float) * ents * L.H);                   // part
     add(sizeof(float) * 2ull * GM_MAX_BLOCKS * 2 * GM_GROUP * GM_ROWS);  // split tiles
     return n;
@@ -723,7 +962,11 @@ GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E)
     W.g.slots = (int32_t*)take(sizeof(int32_t) * B * K);
     W.g.grp_u = (int32_t*)take(sizeof(int32_t) * 4);
     W.g.act_expert = (int32_t*)take(sizeof(int32_t) * V);
-    W.g.act_off = (int32_t*)take(sizeof(int32_t) * (V + 1));
+    W.g.act_off = (int32_t*)take(sizeof(int32_t) * V);
+    W.g.act_n = (int32_t*)take(sizeof(int32_t) * V);
+    W.g.gv_expert = (int32_t*)take(sizeof(int32_t) * V);
+    W.g.gv_off = (int32_t*)take(sizeof(int32_t) * V);
+    W.g.gv_n = (int32_t*)take(sizeof(int32_t) * V);
     W.g.ent_token = (int32_t*)take(sizeof(int32_t) * ents);
     W.g.slot_pos = (int32_t*)take(sizeof(int32_t) * B * K);
     W.xhl = (uint4*)take(16ull * B * L.Gh * 16);
@@ -731,6 +974,7 @@ GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E)
     W.hb = (float*)take(4ull * ents * L.I);
     W.hb16 = (uint4*)take(2ull * ents * L.I);
     W.hscale = (float*)take(sizeof(float) * ents);
+    W.hstats = (float4*)take(16ull * ents * L.Gi);
     W.part = (float*)take(sizeof(float) * ents * L.H);
     W.split = (float*)take(sizeof(float) * 2ull * GM_MAX_BLOCKS * 2 * GM_GROUP * GM_ROWS);
     return W;
@@ -749,20 +993,33 @@ static int resident_blocks(const void* kernel, int threads)
 }
 
 void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W, const float* x, const float* w,
-                        float shared_w, int B, int K, int E, float* y, hipStream_t s, Timing tg, Timing td)
+                        float shared_w, int B, int K, int E, uint4* xq, float4* xst, float* y, hipStream_t s,
+                        Timing tg, Timing td)
 {
-    static int nb_gu = 0, nb_dn = 0;  // per process: one device type
+    static int nb_gu = 0, nb_dn = 0, nb_gvu = 0, nb_gvd = 0;  // per process: one device type
     if (!nb_gu) {
         nb_gu = resident_blocks((const void*)k_grouped_mfma<MODE_GATEUP>, GM_THREADS);
         nb_dn = resident_blocks((const void*)k_grouped_mfma<MODE_DOWN>, GM_THREADS);
+        nb_gvu = resident_blocks((const void*)k_gemv_gateup, 64 * GV_WAVES);
+        nb_gvd = resident_blocks((const void*)k_gemv_down, 64 * GV_WAVES);
     }
+    // a block's item range spans at most ceil(V / nb) + 1 groups: keep that below GV_META
+    const int v_max = max_groups(B, K, E), nb_meta = (v_max + GV_META - 3) / (GV_META - 2);
+    const int nbu = max(nb_gvu, nb_meta), nbd = max(nb_gvd, nb_meta);
+    const int gv_t = gemv_tokens(L);
     hipLaunchKernelGGL(k_prep_tokens, dim3(B), dim3(256), 0, s, x, L.H, W.xhl, W.xscale);
+    if (gv_t > 1) launch_prep(L.bits, x, B, L.H, xq, xst, s);
     GroupedArgs A;
     A.slab = (const uint8_t*)slab;
     A.L = L;
     A.grp_u = W.g.grp_u;
     A.act_expert = W.g.act_expert;
     A.act_off = W.g.act_off;
+    A.act_n = W.g.act_n;
+    A.gv_expert = W.g.gv_expert;
+    A.gv_off = W.g.gv_off;
+    A.gv_n = W.g.gv_n;
+    A.n_ent = W.g.offsets + E;
     A.ent_token = W.g.ent_token;
     A.xhl = W.xhl;
     A.xscale = W.xscale;
@@ -771,11 +1028,18 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     A.hscale = W.hscale;
     A.part = W.part;
     A.split = W.split;
+    // the GEMV groups' operands in LDS: up to gv_t - 1 vectors of 9 * G uint4
+    const size_t lds_gu = 16ull * 9 * L.Gh * (gv_t - 1), lds_dn = 16ull * 9 * L.Gi * (gv_t - 1);
     hipExtLaunchKernelGGL(k_grouped_mfma<MODE_GATEUP>, dim3(nb_gu), dim3(GM_THREADS), 0, s, tg.start, tg.stop, 0, A);
     hipLaunchKernelGGL(k_fixup, dim3(nb_gu), dim3(256), 0, s, A, nb_gu);
-    hipLaunchKernelGGL(k_hconvert, dim3(B * K + B), dim3(256), 0, s, W.hb, W.g.grp_u, W.g.act_off, L.I, W.hb16,
-                       W.hscale);
+    if (gv_t > 1)
+        hipLaunchKernelGGL(k_gemv_gateup, dim3(nbu), dim3(64 * GV_WAVES), lds_gu, s, A, (const uint4*)xq,
+                           (const float4*)xst);
+    hipLaunchKernelGGL(k_hconvert, dim3(B * K + B), dim3(256), 0, s, W.hb, A.n_ent, B, L.I, W.hb16, W.hscale,
+                       W.hstats);
     hipExtLaunchKernelGGL(k_grouped_mfma<MODE_DOWN>, dim3(nb_dn), dim3(GM_THREADS), 0, s, td.start, td.stop, 0, A);
+    if (gv_t > 1)
+        hipLaunchKernelGGL(k_gemv_down, dim3(nbd), dim3(64 * GV_WAVES), lds_dn, s, A, (const float4*)W.hstats);
     hipLaunchKernelGGL(k_combine, dim3((L.H + 255) / 256, B), dim3(256), 0, s, W.part, W.g.slot_pos, w, K, L.H,
                        shared_w, y);
 }

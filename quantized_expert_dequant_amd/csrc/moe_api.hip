@@ -255,8 +255,8 @@ static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, cons
     hipStream_t s = (hipStream_t)stream;
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
     if (W.grouped) {
-        launch_group(idx, B, desc->K, desc->E, W.gw.g, s);
-        launch_ffn_grouped(L, desc->experts, W.gw, x, w, desc->shared_weight, B, desc->K, desc->E, y_out, s,
+        launch_group(idx, B, desc->K, desc->E, gemv_tokens(L), W.gw.g, s);
+        launch_ffn_grouped(L, desc->experts, W.gw, x, w, desc->shared_weight, B, desc->K, desc->E, W.xq, W.xst, y_out, s,
                            g_timing[KID_GATEUP], g_timing[KID_DOWN]);
         return hip_status(fn);
     }
@@ -289,8 +289,8 @@ static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, i
     if (W.grouped) {
         launch_route_batched(x, B, d->w_router, d->logit_bias, d->H, d->E, d->K, d->renormalize ? 1 : 0,
                              W.gw.partial, W.logits, idx, w, s, g_timing[KID_ROUTER]);
-        launch_group(idx, B, d->K, d->E, W.gw.g, s);
-        launch_ffn_grouped(L, d->experts, W.gw, x, w, d->shared_weight, B, d->K, d->E, y_out, s,
+        launch_group(idx, B, d->K, d->E, gemv_tokens(L), W.gw.g, s);
+        launch_ffn_grouped(L, d->experts, W.gw, x, w, d->shared_weight, B, d->K, d->E, W.xq, W.xst, y_out, s,
                            g_timing[KID_GATEUP], g_timing[KID_DOWN]);
         return hip_status(fn);
     }
@@ -333,7 +333,7 @@ int moe_group_tokens(const int32_t* idx, int B, int K, int E, int32_t* offsets_o
     O.offsets = offsets_out;
     O.tokens = tokens_out;
     O.slots = slots_out;
-    launch_group(idx, B, K, E, O, (hipStream_t)stream);
+    launch_group(idx, B, K, E, 1, O, (hipStream_t)stream);
     return hip_status(fn);
 }
 
