@@ -296,29 +296,22 @@ __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x
 }
 
 // ----------------------------------------------------------------------------
-// One 16-byte chunk of a 4-bit row (32 codes) -> fp16 MFMA operands: out[d]
-// holds the 8 weights s*q + b of the chunk's dword d in the order
-// (c0, c4, c1, c5, c2, c6, c3, c7).  OR-ing the fp16 pattern of 1024 into a
-// masked code pair gives (1024 + q_a, 1024 + q_b); subtracting 1024 is exact and
-// one fused multiply-add gives s*q + b, rounded once to fp16.
+// Dword w of a 16-byte chunk of a 4-bit row (8 codes) -> the fp16 MFMA operand
+// of its 8 weights s*q + b in the order (c0, c4, c1, c5, c2, c6, c3, c7).
+// OR-ing the fp16 pattern of 1024 into a masked code pair gives
+// (1024 + q_a, 1024 + q_b); subtracting 1024 is exact and one fused
+// multiply-add gives s*q + b, rounded once to fp16.
 // ----------------------------------------------------------------------------
-__device__ inline void dequant_chunk_q4(u4 c, uint32_t sb, uint32_t mask, uint32_t magic, h8 (&out)[4])
+__device__ inline h8 dequant_dword_q4(uint32_t w, h2 s2, h2 b2, uint32_t mask, uint32_t magic)
 {
-    const _Float16 s = (_Float16)bf16_lo(sb), b = (_Float16)bf16_hi(sb);
-    const h2 s2 = {s, s}, b2 = {b, b};
     const h2 k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-    const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
+    h2 p[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        h2 p[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint32_t bits = ((wd[d] >> (4 * t)) & mask) | magic;  // (1024 + q_a, 1024 + q_b)
-            const h2 q = __builtin_bit_cast(h2, bits) - k1024;
-            p[t] = __builtin_elementwise_fma(q, s2, b2);
-        }
-        out[d] = h8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t bits = ((w >> (4 * t)) & mask) | magic;
+        p[t] = __builtin_elementwise_fma(__builtin_bit_cast(h2, bits) - k1024, s2, b2);
     }
+    return h8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
 }
 
 // ----------------------------------------------------------------------------
@@ -512,27 +505,49 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         // ks + RING - 1 -> the ring slot step ks - 1 used (Wp), multiply step ks
         // (weights Wc, token operands in LDS stage ks & 1), then store the token
         // operands of step ks + 1 (Sc, loaded one step earlier) into the other stage.
+        // The loads are unconditional (past the segment end they repeat its last
+        // step): the waits for them then stay exact, where a skipped load would make
+        // every later wait assume nothing else is in flight and drain the ring.
         auto step = [&](int ks, const WRegs& Wc, WRegs& Wp, const Stage& Sc, Stage& Sp) {
-            if (ks + 2 < k_end) stage_load(ks + 2, Sp);
+            stage_load(min(ks + 2, k_end - 1), Sp);
             __builtin_amdgcn_sched_barrier(0);
-            if (ks + RING - 1 < k_end) weight_load(ks + RING - 1, Wp);
+            weight_load(min(ks + RING - 1, k_end - 1), Wp);
             __builtin_amdgcn_sched_barrier(0);
             const u4* buf = bs[(ks - k_begin) & 1];
             const bool pad = 4 * ks + kk >= 2 * G;  // chunk past the row end: zero weights
-            h8 a[NM][4];
+            h2 s2[NM], b2[NM];
 #pragma unroll
-            for (int mm = 0; mm < NM; ++mm) dequant_chunk_q4(Wc.c[mm], pad ? 0u : Wc.sb[mm], M.m4a, M.magic, a[mm]);
+            for (int mm = 0; mm < NM; ++mm) {
+                const uint32_t sb = pad ? 0u : Wc.sb[mm];
+                const _Float16 sh = (_Float16)bf16_lo(sb), bh = (_Float16)bf16_hi(sb);
+                s2[mm] = h2{sh, sh};
+                b2[mm] = h2{bh, bh};
+            }
+            // dword-major: the token operands of dword d + 1 are read from LDS while
+            // the MFMAs of dword d run, and only one dword's weights are live
+            h8 bv[2][GM_TT][HL];
+            auto bread = [&](int d, h8 (&b)[GM_TT][HL]) {
 #pragma unroll
-            for (int tt = 0; tt < GM_TT; ++tt) {
-                if (tt < ntt) {
+                for (int tt = 0; tt < GM_TT; ++tt)
 #pragma unroll
-                    for (int d = 0; d < 4; ++d)
+                    for (int hl = 0; hl < HL; ++hl)
+                        if (tt < ntt) b[tt][hl] = __builtin_bit_cast(h8, buf[(((tt * 4 + kk) * 4 + d) * HL + hl) * 16 + i]);
+            };
+            bread(0, bv[0]);
 #pragma unroll
-                        for (int hl = 0; hl < HL; ++hl) {
-                            const h8 bv = __builtin_bit_cast(h8, buf[(((tt * 4 + kk) * 4 + d) * HL + hl) * 16 + i]);
+            for (int d = 0; d < 4; ++d) {
+                if (d + 1 < 4) bread(d + 1, bv[(d + 1) & 1]);
+                h8 a[NM];
 #pragma unroll
-                            for (int mm = 0; mm < NM; ++mm) acc[mm][tt] = mfma16(a[mm][d], bv, acc[mm][tt]);
-                        }
+                for (int mm = 0; mm < NM; ++mm) a[mm] = dequant_dword_q4(Wc.c[mm][d], s2[mm], b2[mm], M.m4a, M.magic);
+#pragma unroll
+                for (int tt = 0; tt < GM_TT; ++tt) {
+                    if (tt < ntt) {
+#pragma unroll
+                        for (int hl = 0; hl < HL; ++hl)
+#pragma unroll
+                            for (int mm = 0; mm < NM; ++mm) acc[mm][tt] = mfma16(a[mm], bv[d & 1][tt][hl], acc[mm][tt]);
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -546,14 +561,15 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         Stage S0, S1;
         {
             __syncthreads();  // LDS reads of the previous segment are done
-            if (k_begin < k_end) stage_load(k_begin, S0);
-            if (k_begin + 1 < k_end) stage_load(k_begin + 1, S1);
+            // a segment holds at least one step (grouped_supported: nsteps >= KC)
+            stage_load(k_begin, S0);
+            stage_load(min(k_begin + 1, k_end - 1), S1);
             __builtin_amdgcn_sched_barrier(0);
-            if (k_begin < k_end) weight_load(k_begin, R0);
-            if (k_begin + 1 < k_end) weight_load(k_begin + 1, R1);
-            if (RING == 4 && k_begin + 2 < k_end) weight_load(k_begin + 2, R2);
+            weight_load(k_begin, R0);
+            weight_load(min(k_begin + 1, k_end - 1), R1);
+            if (RING == 4) weight_load(min(k_begin + 2, k_end - 1), R2);
             __builtin_amdgcn_sched_barrier(0);
-            if (k_begin < k_end) stage_store(0, S0);
+            stage_store(0, S0);
             __syncthreads();
         }
         // token operands alternate between S1 (steps ks + 1 with ks even) and S0
@@ -916,7 +932,9 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
 
 bool grouped_supported(const Layout& L, int B, int K)
 {
-    return L.bits == 4 && B >= 2 && B <= MOE_MAX_B && K <= MOE_MAX_K && L.H % 64 == 0 && L.I % 64 == 0;
+    // every gate/up K chunk of a tile must hold at least one step (H >= 448)
+    return L.bits == 4 && B >= 2 && B <= MOE_MAX_B && K <= MOE_MAX_K && L.H % 64 == 0 && L.I % 64 == 0 &&
+           gm_steps(L, MODE_GATEUP) >= GM_KC_GATEUP;
 }
 
 // most work-list groups a call can produce: every expert's entries cut into groups of GM_GROUP
@@ -1003,12 +1021,11 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
         nb_gvu = resident_blocks((const void*)k_gemv_gateup, 64 * GV_WAVES);
         nb_gvd = resident_blocks((const void*)k_gemv_down, 64 * GV_WAVES);
     }
-    // a block's item range spans at most ceil(V / nb) + 1 groups: keep that below GV_META
-    const int v_max = max_groups(B, K, E), nb_meta = (v_max + GV_META - 3) / (GV_META - 2);
-    const int nbu = max(nb_gvu, nb_meta), nbd = max(nb_gvd, nb_meta);
     const int gv_t = gemv_tokens(L);
+    const bool gv = gv_t > 1;
+
     hipLaunchKernelGGL(k_prep_tokens, dim3(B), dim3(256), 0, s, x, L.H, W.xhl, W.xscale);
-    if (gv_t > 1) launch_prep(L.bits, x, B, L.H, xq, xst, s);
+    if (gv) launch_prep(L.bits, x, B, L.H, xq, xst, s);
     GroupedArgs A;
     A.slab = (const uint8_t*)slab;
     A.L = L;
@@ -1030,16 +1047,28 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     A.split = W.split;
     // the GEMV groups' operands in LDS: up to gv_t - 1 vectors of 9 * G uint4
     const size_t lds_gu = 16ull * 9 * L.Gh * (gv_t - 1), lds_dn = 16ull * 9 * L.Gi * (gv_t - 1);
-    hipExtLaunchKernelGGL(k_grouped_mfma<MODE_GATEUP>, dim3(nb_gu), dim3(GM_THREADS), 0, s, tg.start, tg.stop, 0, A);
+    // a block's item range spans at most ceil(V / nb) + 1 groups: keep that below GV_META
+    const int v_max = max_groups(B, K, E), nb_meta = (v_max + GV_META - 3) / (GV_META - 2);
+    const int nbu = max(nb_gvu, nb_meta), nbd = max(nb_gvd, nb_meta);
+
+    // gate/up phase, timed as a whole (MFMA groups, split-tile fixup, GEMV groups):
+    // together they read every active expert's gate/up rows once
+    if (tg.start) hipEventRecord(tg.start, s);
+    hipLaunchKernelGGL(k_grouped_mfma<MODE_GATEUP>, dim3(nb_gu), dim3(GM_THREADS), 0, s, A);
     hipLaunchKernelGGL(k_fixup, dim3(nb_gu), dim3(256), 0, s, A, nb_gu);
-    if (gv_t > 1)
+    if (gv)
         hipLaunchKernelGGL(k_gemv_gateup, dim3(nbu), dim3(64 * GV_WAVES), lds_gu, s, A, (const uint4*)xq,
                            (const float4*)xst);
+    if (tg.stop) hipEventRecord(tg.stop, s);
+
     hipLaunchKernelGGL(k_hconvert, dim3(B * K + B), dim3(256), 0, s, W.hb, A.n_ent, B, L.I, W.hb16, W.hscale,
                        W.hstats);
-    hipExtLaunchKernelGGL(k_grouped_mfma<MODE_DOWN>, dim3(nb_dn), dim3(GM_THREADS), 0, s, td.start, td.stop, 0, A);
-    if (gv_t > 1)
-        hipLaunchKernelGGL(k_gemv_down, dim3(nbd), dim3(64 * GV_WAVES), lds_dn, s, A, (const float4*)W.hstats);
+
+    // down phase, timed as a whole
+    if (td.start) hipEventRecord(td.start, s);
+    hipLaunchKernelGGL(k_grouped_mfma<MODE_DOWN>, dim3(nb_dn), dim3(GM_THREADS), 0, s, A);
+    if (gv) hipLaunchKernelGGL(k_gemv_down, dim3(nbd), dim3(64 * GV_WAVES), lds_dn, s, A, (const float4*)W.hstats);
+    if (td.stop) hipEventRecord(td.stop, s);
     hipLaunchKernelGGL(k_combine, dim3((L.H + 255) / 256, B), dim3(256), 0, s, W.part, W.g.slot_pos, w, K, L.H,
                        shared_w, y);
 }
