@@ -154,9 +154,14 @@ def cpu_baseline(c, budget_s=15.0):
                       "experts' FFNs spread over OpenMP threads; weight generation excluded" % n_tok}
 
 
-def kernel_source_hash():
+def kernel_source_hash(workload):
+    """Hash of the sources the timed gate/up kernels are built from: the single-token
+    kernel lives in kernels.hip; the batched phase also runs grouped.hip's kernels."""
+    files = ["kernels.hip", "common.h", "topk.h"]
+    if WORKLOADS[workload]["B"] > 1:
+        files.append("grouped.hip")
     h = hashlib.sha256()
-    for f in ("kernels.hip", "grouped.hip", "common.h", "topk.h"):
+    for f in files:
         h.update(open(os.path.join(ROOT, "quantized_expert_dequant_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -168,7 +173,7 @@ def traffic_from_profile(workload, launches_per_step):
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -195,7 +200,7 @@ def write_pmc_summary(workload, kernel_prefix, fetch_csv, write_csv, copy_fetch_
     traffic = (f * kf + w * kw) * 1024.0
     c = WORKLOADS[workload]
     algo = gateup_bytes_per_expert(c) * (c["K"] + 1) if c["B"] == 1 else None
-    out = {"workload": workload, "kernel": kernel_prefix, "kernel_source_hash": kernel_source_hash(),
+    out = {"workload": workload, "kernel": kernel_prefix, "kernel_source_hash": kernel_source_hash(workload),
            "fetch_kib_per_dispatch": round(f, 1), "write_kib_per_dispatch": round(w, 1), "dispatches": [nf, nw],
            "copy_calibration_mib": copy_mb, "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
            "fetch_scale": round(kf, 4), "write_scale": round(kw, 4),
@@ -404,7 +409,8 @@ def main():
             **({"distinct_layers": n_distinct} if stack else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "kernel": "k_grouped_mfma<gate/up>" if B > 1 else "k_gateup_fast",
+                     "kernel": ("gate/up phase: k_grouped_mfma<0> + k_fixup + k_gemv_gateup" if B > 1
+                                else "k_gateup_fast"),
                      "bytes_per_launch": round(gu_bytes), "avg_us": round(gu_us, 3)},
         "expert_weight_gbps": round(expert_gbps, 1),
         "expert_weight_frac_of_peak": round(expert_gbps / PEAK_HBM_GBPS, 4),

@@ -55,7 +55,7 @@ size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E);
 GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E);
 int router_splits(int H);
 void launch_route_batched(const float* x, int B, const float* W, const float* bias, int H, int E, int K, int renorm,
-                          double* partial, double* logits, int32_t* idx, float* w, hipStream_t s, Timing t);
+                          double* partial, int32_t* idx, float* w, hipStream_t s, Timing t);
 // experts with fewer tokens than this run as GEMV groups (1: none)
 int gemv_tokens(const Layout& L);
 void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const GroupOut& O, hipStream_t s);

@@ -15,9 +15,9 @@
 //
 // Kernels:
 //   k_router_tiled   fp64-accumulated logits of many tokens, split over H
-//   k_sum_slices     sums the H-slice partials in a fixed order
+//   k_topk_slices    sums the H-slice partials in a fixed order, then softmax / top-K
 //   k_group          stable counting sort of the assignments + the MFMA work list
-//   k_prep_tokens    token activations -> fp16 hi + lo MFMA operands
+//   k_prep_tokens    token activations -> fp16 hi + lo MFMA operands (+ dot2 operands)
 //   k_grouped_mfma   gate/up (+ SwiGLU) or down dequant-GEMM over (group, 128 rows, K chunk)
 //   k_fixup          SwiGLU of gate/up tiles whose K chunks two blocks shared
 //   k_gemv_gateup    gate/up (+ SwiGLU) of the small groups as dot2 GEMVs
@@ -28,6 +28,7 @@
 
 #include "common.h"
 #include "grouped.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -47,7 +48,7 @@ __device__ inline f4 mfma16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32
 // ----------------------------------------------------------------------------
 // Logits of B tokens: a block computes a tile of 32 experts x 32 tokens over a
 // 256-column slice of H; each thread keeps 2 x 2 outputs, accumulating the exact
-// fp32 products in fp64.  partial[slice][b][e]; k_sum_slices adds the slices in
+// fp32 products in fp64.  partial[slice][b][e]; k_topk_slices adds the slices in
 // slice order, so the logits do not depend on the launch.
 // ----------------------------------------------------------------------------
 constexpr int RT_E = 32, RT_B = 32, RT_SLICE = 256, RT_CHUNK = 64, RT_PITCH = RT_E + 2;
@@ -98,29 +99,44 @@ __global__ __launch_bounds__(256) void k_router_tiled(const float* __restrict__ 
     if (e + 1 < E && b + 1 < B) out[(long long)(b + 1) * E + e + 1] = a11;
 }
 
-// logits[b][e] = sum of the slice partials in slice order + bias[e]
-__global__ __launch_bounds__(256) void k_sum_slices(const double* __restrict__ partial, int nslice,
-                                                    const float* __restrict__ bias, int BE, int E,
-                                                    double* __restrict__ logits)
+// One block per token: the token's logits are the H-slice partials added in
+// slice order, then the bias (a fixed order, so they do not depend on the
+// launch); they go to LDS and wave 0 selects the top-K.
+__global__ __launch_bounds__(256) void k_topk_slices(const double* __restrict__ partial, int nslice,
+                                                     const float* __restrict__ bias, int B, int E, int K, int renorm,
+                                                     int32_t* __restrict__ idx, float* __restrict__ w)
 {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= BE) return;
-    double s = 0.0;
-#pragma unroll 8
-    for (int sp = 0; sp < nslice; ++sp) s += partial[(long long)sp * BE + i];
-    logits[i] = s + (bias ? (double)bias[i % E] : 0.0);
+    __shared__ double lg[1024];  // E <= 1024
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const long long BE = (long long)B * E;
+    for (int e = tid; e < E; e += 256) {
+        double s = 0.0;
+        for (int sp = 0; sp < nslice; ++sp) s += partial[sp * BE + (long long)b * E + e];
+        lg[e] = s + (bias ? (double)bias[e] : 0.0);
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    double lv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lv[j] = lg[min(tid + 64 * j, E - 1)];
+    int id;
+    float wt;
+    topk_select<32, 16>(lv, E, K, renorm, tid, id, wt);
+    if (tid < K) {
+        idx[(long long)b * K + tid] = id;
+        w[(long long)b * K + tid] = wt;
+    }
 }
 
 int router_splits(int H) { return (H + RT_SLICE - 1) / RT_SLICE; }
 
 void launch_route_batched(const float* x, int B, const float* W, const float* bias, int H, int E, int K, int renorm,
-                          double* partial, double* logits, int32_t* idx, float* w, hipStream_t s, Timing t)
+                          double* partial, int32_t* idx, float* w, hipStream_t s, Timing t)
 {
     const dim3 grid((E + RT_E - 1) / RT_E, (B + RT_B - 1) / RT_B, router_splits(H));
     hipExtLaunchKernelGGL(k_router_tiled, grid, dim3(256), 0, s, t.start, t.stop, 0, x, B, W, H, E, partial);
-    hipLaunchKernelGGL(k_sum_slices, dim3((B * E + 255) / 256), dim3(256), 0, s, partial, router_splits(H), bias,
-                       B * E, E, logits);
-    launch_topk(logits, B, E, K, renorm, idx, w, s);
+    hipLaunchKernelGGL(k_topk_slices, dim3(B), dim3(256), 0, s, partial, router_splits(H), bias, B, E, K, renorm,
+                       idx, w);
 }
 
 // ----------------------------------------------------------------------------
@@ -261,10 +277,13 @@ void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const 
 //   xhl[(t * G + g) * 16 + hl * 8 + d]: uint4 holding dword d's 8 columns of
 //   group g (d = 0..7; columns 8d + (0,4,1,5,2,6,3,7)), hl = 0 hi, 1 lo.
 // ----------------------------------------------------------------------------
-__device__ inline float exp2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
+// With xq non-null the block also writes the token's dot2 operand (fp16 pairs
+// with a per-group scale + group stats, as the single-token kernels take it)
+// for the GEMV groups, one wave per group.
 __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x, int H, uint4* __restrict__ xhl,
-                                                     float* __restrict__ xscale)
+                                                     float* __restrict__ xscale, uint4* __restrict__ xq,
+                                                     float4* __restrict__ xst)
 {
     __shared__ float red[4];
     const int t = blockIdx.x, tid = threadIdx.x;
@@ -280,8 +299,8 @@ __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x
         e = ilogbf(amax) - 14;
         e = e < -110 ? -110 : (e > 113 ? 113 : e);
     }
-    const float inv = exp2i(-e);
-    if (tid == 0) xscale[t] = exp2i(e);
+    const float inv = exp2i_f(-e);
+    if (tid == 0) xscale[t] = exp2i_f(e);
     const int G = H / 64;
     uint16_t* out = reinterpret_cast<uint16_t*>(xhl + (long long)t * G * 16);
     for (int c = tid; c < H; c += 256) {
@@ -293,6 +312,8 @@ __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x
         out[o] = __builtin_bit_cast(uint16_t, hi);
         out[o + 64] = __builtin_bit_cast(uint16_t, lo);
     }
+    if (xq)
+        for (int g = tid >> 6; g < G; g += 4) prep_group<4>(x, G, t, g, tid & 63, xq, xst);
 }
 
 // ----------------------------------------------------------------------------
@@ -1024,8 +1045,8 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     const int gv_t = gemv_tokens(L);
     const bool gv = gv_t > 1;
 
-    hipLaunchKernelGGL(k_prep_tokens, dim3(B), dim3(256), 0, s, x, L.H, W.xhl, W.xscale);
-    if (gv) launch_prep(L.bits, x, B, L.H, xq, xst, s);
+    hipLaunchKernelGGL(k_prep_tokens, dim3(B), dim3(256), 0, s, x, L.H, W.xhl, W.xscale, gv ? xq : nullptr,
+                       gv ? xst : nullptr);
     GroupedArgs A;
     A.slab = (const uint8_t*)slab;
     A.L = L;
@@ -1053,22 +1074,22 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
 
     // gate/up phase, timed as a whole (MFMA groups, split-tile fixup, GEMV groups):
     // together they read every active expert's gate/up rows once
-    if (tg.start) hipEventRecord(tg.start, s);
+    if (tg.start) (void)hipEventRecord(tg.start, s);
     hipLaunchKernelGGL(k_grouped_mfma<MODE_GATEUP>, dim3(nb_gu), dim3(GM_THREADS), 0, s, A);
     hipLaunchKernelGGL(k_fixup, dim3(nb_gu), dim3(256), 0, s, A, nb_gu);
     if (gv)
         hipLaunchKernelGGL(k_gemv_gateup, dim3(nbu), dim3(64 * GV_WAVES), lds_gu, s, A, (const uint4*)xq,
                            (const float4*)xst);
-    if (tg.stop) hipEventRecord(tg.stop, s);
+    if (tg.stop) (void)hipEventRecord(tg.stop, s);
 
     hipLaunchKernelGGL(k_hconvert, dim3(B * K + B), dim3(256), 0, s, W.hb, A.n_ent, B, L.I, W.hb16, W.hscale,
                        W.hstats);
 
     // down phase, timed as a whole
-    if (td.start) hipEventRecord(td.start, s);
+    if (td.start) (void)hipEventRecord(td.start, s);
     hipLaunchKernelGGL(k_grouped_mfma<MODE_DOWN>, dim3(nb_dn), dim3(GM_THREADS), 0, s, A);
     if (gv) hipLaunchKernelGGL(k_gemv_down, dim3(nbd), dim3(64 * GV_WAVES), lds_dn, s, A, (const float4*)W.hstats);
-    if (td.stop) hipEventRecord(td.stop, s);
+    if (td.stop) (void)hipEventRecord(td.stop, s);
     hipLaunchKernelGGL(k_combine, dim3((L.H + 255) / 256, B), dim3(256), 0, s, W.part, W.g.slot_pos, w, K, L.H,
                        shared_w, y);
 }

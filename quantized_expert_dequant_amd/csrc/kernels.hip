@@ -151,7 +151,6 @@ void launch_dequant(const Layout& L, const void* rec, float* W, hipStream_t s)
 // One wave per (token, group); shared by the standalone prep kernel and the
 // router kernel, which preps the token while it computes the logits.
 // ----------------------------------------------------------------------------
-__device__ inline float exp2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
 // 1 / sqrt(mean(y^2) + eps) of a row of n4 float4, by one wave: lane l sums the
 // squares of float4 l, l+64, ... in fp64 in that order, then the wave adds the
@@ -169,43 +168,6 @@ __device__ inline float row_inv_rms(const float4* __restrict__ y4, int n4, float
     }
     ss = wave_sum(ss);
     return (float)(1.0 / sqrt(ss / (4.0 * n4) + (double)eps));
-}
-
-template <int BITS>
-__device__ void prep_group(const float* __restrict__ v, int G, int vec, int g, int lane, uint4* __restrict__ q,
-                           float4* __restrict__ st, float scale = 1.f)
-{
-    const float val = v[(long long)vec * G * 64 + g * 64 + lane] * scale;
-    const float amax = wave_max(fabsf(val));
-    int e = 0;
-    if (amax > 0.f && amax <= 3.4e38f) {
-        e = ilogbf(amax) - 14;  // amax * 2^-e in [2^14, 2^15)
-        e = e < -110 ? -110 : (e > 113 ? 113 : e);
-    }
-    const float vs = val * exp2i(-e);  // exact power-of-two scaling
-    const _Float16 vh = (_Float16)vs;
-    int p, hi;
-    if (BITS == 4) {
-        const int d = lane >> 3, r = lane & 7;
-        p = 4 * d + (r & 3);
-        hi = r >> 2;
-    } else {
-        const int d = lane >> 4, r = lane & 15;
-        p = 8 * d + (r & 7);
-        hi = r >> 3;
-    }
-    uint16_t* qb = reinterpret_cast<uint16_t*>(q + (long long)vec * 8 * G);
-    qb[((long long)(p >> 2) * G + g) * 8 + (p & 3) * 2 + hi] = __builtin_bit_cast(uint16_t, vh);
-    // C = offset the fp16 code patterns add (1024 * sum_t S_t / t) plus the code
-    // midpoint times the group's fp16 rounding error, so that the kernels compute
-    // sum (q - mid) v_h + mid * sum v: the rounding errors of v then meet only
-    // zero-mean code offsets and do not add up coherently across rows.
-    constexpr float mid = BITS == 4 ? 7.5f : 1.5f;
-    const float off = wave_sum((float)vh * pair_class_inv(BITS, p));
-    const float rnd = wave_sum((float)vh - vs);  // exact per lane
-    const float C = fmaf(off, 1024.f, mid * rnd);
-    const float S = wave_sum(val);
-    if (lane == 0) st[(long long)vec * G + g] = make_float4(C, S, exp2i(e), 0.f);
 }
 
 template <int BITS>

@@ -288,7 +288,7 @@ static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, i
     const Layout L = make_layout(d->bits, d->H, d->I);
     if (W.grouped) {
         launch_route_batched(x, B, d->w_router, d->logit_bias, d->H, d->E, d->K, d->renormalize ? 1 : 0,
-                             W.gw.partial, W.logits, idx, w, s, g_timing[KID_ROUTER]);
+                             W.gw.partial, idx, w, s, g_timing[KID_ROUTER]);
         launch_group(idx, B, d->K, d->E, gemv_tokens(L), W.gw.g, s);
         launch_ffn_grouped(L, d->experts, W.gw, x, w, d->shared_weight, B, d->K, d->E, W.xq, W.xst, y_out, s,
                            g_timing[KID_GATEUP], g_timing[KID_DOWN]);
