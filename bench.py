@@ -194,8 +194,15 @@ def write_pmc_summary(workload, kernel_prefix, fetch_csv, write_csv, copy_fetch_
     copy_kib = copy_mb * 1024.0
     cf, _ = _pmc_per_dispatch(copy_fetch_csv, "__amd_rocclr_copyBuffer", "FETCH_SIZE")
     cw, _ = _pmc_per_dispatch(copy_write_csv, "__amd_rocclr_copyBuffer", "WRITE_SIZE")
-    f, nf = _pmc_per_dispatch(fetch_csv, kernel_prefix, "FETCH_SIZE")
-    w, nw = _pmc_per_dispatch(write_csv, kernel_prefix, "WRITE_SIZE")
+    # "a|b|c": a phase of several kernels, one dispatch of each per step
+    f = w = 0.0
+    nf, nw = [], []
+    for kp in kernel_prefix.split("|"):
+        fk, nfk = _pmc_per_dispatch(fetch_csv, kp, "FETCH_SIZE")
+        wk, nwk = _pmc_per_dispatch(write_csv, kp, "WRITE_SIZE")
+        f, w = f + fk, w + wk
+        nf.append(nfk)
+        nw.append(nwk)
     kf, kw = copy_kib / cf, copy_kib / cw
     traffic = (f * kf + w * kw) * 1024.0
     c = WORKLOADS[workload]

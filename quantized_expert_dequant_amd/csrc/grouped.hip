@@ -102,16 +102,26 @@ __global__ __launch_bounds__(256) void k_router_tiled(const float* __restrict__ 
 // One block per token: the token's logits are the H-slice partials added in
 // slice order, then the bias (a fixed order, so they do not depend on the
 // launch); they go to LDS and wave 0 selects the top-K.
-__global__ __launch_bounds__(256) void k_topk_slices(const double* __restrict__ partial, int nslice,
+constexpr int TS_CHUNK = 16;  // slice loads in flight per thread
+
+__global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ partial, int nslice,
                                                      const float* __restrict__ bias, int B, int E, int K, int renorm,
                                                      int32_t* __restrict__ idx, float* __restrict__ w)
 {
     __shared__ double lg[1024];  // E <= 1024
     const int b = blockIdx.x, tid = threadIdx.x;
     const long long BE = (long long)B * E;
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += 512) {
+        const double* p = partial + (long long)b * E + e;
         double s = 0.0;
-        for (int sp = 0; sp < nslice; ++sp) s += partial[sp * BE + (long long)b * E + e];
+        for (int s0 = 0; s0 < nslice; s0 += TS_CHUNK) {
+            double v[TS_CHUNK];
+#pragma unroll
+            for (int j = 0; j < TS_CHUNK; ++j) v[j] = p[min(s0 + j, nslice - 1) * BE];
+#pragma unroll
+            for (int j = 0; j < TS_CHUNK; ++j)
+                if (s0 + j < nslice) s += v[j];
+        }
         lg[e] = s + (bias ? (double)bias[e] : 0.0);
     }
     __syncthreads();
@@ -135,7 +145,7 @@ void launch_route_batched(const float* x, int B, const float* W, const float* bi
 {
     const dim3 grid((E + RT_E - 1) / RT_E, (B + RT_B - 1) / RT_B, router_splits(H));
     hipExtLaunchKernelGGL(k_router_tiled, grid, dim3(256), 0, s, t.start, t.stop, 0, x, B, W, H, E, partial);
-    hipLaunchKernelGGL(k_topk_slices, dim3(B), dim3(256), 0, s, partial, router_splits(H), bias, B, E, K, renorm,
+    hipLaunchKernelGGL(k_topk_slices, dim3(B), dim3(512), 0, s, partial, router_splits(H), bias, B, E, K, renorm,
                        idx, w);
 }
 
@@ -278,15 +288,22 @@ void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const 
 //   group g (d = 0..7; columns 8d + (0,4,1,5,2,6,3,7)), hl = 0 hi, 1 lo.
 // ----------------------------------------------------------------------------
 
-// With xq non-null the block also writes the token's dot2 operand (fp16 pairs
-// with a per-group scale + group stats, as the single-token kernels take it)
-// for the GEMV groups, one wave per group.
+// Blocks (t, y >= 1) write token t's dot2 operand instead (fp16 pairs with a
+// per-group scale + group stats, as the single-token kernels take it) for the
+// GEMV groups, one wave per group.
+constexpr int PT_DOT2_BLOCKS = 4;
+
 __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x, int H, uint4* __restrict__ xhl,
                                                      float* __restrict__ xscale, uint4* __restrict__ xq,
                                                      float4* __restrict__ xst)
 {
     __shared__ float red[4];
     const int t = blockIdx.x, tid = threadIdx.x;
+    if (blockIdx.y > 0) {
+        const int G = H / 64, step = 4 * (gridDim.y - 1);
+        for (int g = (blockIdx.y - 1) * 4 + (tid >> 6); g < G; g += step) prep_group<4>(x, G, t, g, tid & 63, xq, xst);
+        return;
+    }
     const float* xt = x + (long long)t * H;
     float m = 0.f;
     for (int c = tid; c < H; c += 256) m = fmaxf(m, fabsf(xt[c]));
@@ -312,8 +329,6 @@ __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x
         out[o] = __builtin_bit_cast(uint16_t, hi);
         out[o + 64] = __builtin_bit_cast(uint16_t, lo);
     }
-    if (xq)
-        for (int g = tid >> 6; g < G; g += 4) prep_group<4>(x, G, t, g, tid & 63, xq, xst);
 }
 
 // ----------------------------------------------------------------------------
@@ -1045,8 +1060,8 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     const int gv_t = gemv_tokens(L);
     const bool gv = gv_t > 1;
 
-    hipLaunchKernelGGL(k_prep_tokens, dim3(B), dim3(256), 0, s, x, L.H, W.xhl, W.xscale, gv ? xq : nullptr,
-                       gv ? xst : nullptr);
+    hipLaunchKernelGGL(k_prep_tokens, dim3(B, gv ? 1 + PT_DOT2_BLOCKS : 1), dim3(256), 0, s, x, L.H, W.xhl, W.xscale,
+                       xq, xst);
     GroupedArgs A;
     A.slab = (const uint8_t*)slab;
     A.L = L;
