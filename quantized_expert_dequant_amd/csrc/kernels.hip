@@ -207,10 +207,12 @@ __device__ inline double dot4d(float4 w, float4 x, double acc)
 }
 
 template <int BITS>
+// Blocks [0, rblocks) compute the logits (one wave per expert); blocks from
+// rblocks on prepare the token operand at the same time (one wave per group).
 __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int B, int prepB,
                                                 const float* __restrict__ W, const float* __restrict__ bias, int H,
                                                 int E, double* __restrict__ logits, uint4* __restrict__ xq,
-                                                float4* __restrict__ xst, float norm_eps)
+                                                float4* __restrict__ xst, float norm_eps, int rblocks)
 {
     // norm_eps >= 0: x is the previous layer's output y; the token is renormalized
     // on the fly, x = y / sqrt(mean(y^2) + eps), exactly as k_rmsnorm would
@@ -219,6 +221,15 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
     const int e = blockIdx.x * 4 + wave;
     const int n4 = H >> 2;
     const float4* x4 = reinterpret_cast<const float4*>(x);
+    if ((int)blockIdx.x >= rblocks) {
+        const int Gh = H / 64, nw = ((int)gridDim.x - rblocks) * 4;
+        for (int i = ((int)blockIdx.x - rblocks) * 4 + wave; i < prepB * Gh; i += nw) {
+            const int vec = i / Gh, g = i - vec * Gh;
+            const float inv = norm ? row_inv_rms(x4 + (long long)vec * n4, n4, norm_eps, lane) : 1.f;
+            prep_group<BITS>(x, Gh, vec, g, lane, xq, xst, inv);
+        }
+        return;
+    }
     if (e < E) {
         const float4* W4 = reinterpret_cast<const float4*>(W) + (long long)e * n4;
         const double bb = bias ? (double)bias[e] : 0.0;
@@ -274,27 +285,22 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
             }
         }
     }
-    const int Gh = H / 64;
-    for (int i = blockIdx.x * 4 + wave; i < prepB * Gh; i += gridDim.x * 4) {
-        const int vec = i / Gh, g = i - vec * Gh;
-        const float inv = norm ? row_inv_rms(x4 + (long long)vec * n4, n4, norm_eps, lane) : 1.f;
-        prep_group<BITS>(x, Gh, vec, g, lane, xq, xst, inv);
-    }
 }
 
 void launch_router(int bits, const float* x, int B, const float* W, const float* bias, int H, int E, double* logits,
                    uint4* xq, float4* xst, hipStream_t s, Timing t, float norm_eps)
 {
-    int blocks = (E + 3) / 4;
+    const int rblocks = (E + 3) / 4;
     const int prepB = xq ? B : 0;
-    const int prep_blocks = (prepB * (H / 64) + 3) / 4;
-    if (blocks < prep_blocks) blocks = prep_blocks < 1024 ? prep_blocks : 1024;
+    int prep_blocks = (prepB * (H / 64) + 3) / 4;
+    if (prep_blocks > 1024) prep_blocks = 1024;
+    const int blocks = rblocks + prep_blocks;
     if (bits == 2)
         hipExtLaunchKernelGGL(k_router<2>, dim3(blocks), dim3(256), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
-                              H, E, logits, xq, xst, norm_eps);
+                              H, E, logits, xq, xst, norm_eps, rblocks);
     else
         hipExtLaunchKernelGGL(k_router<4>, dim3(blocks), dim3(256), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
-                              H, E, logits, xq, xst, norm_eps);
+                              H, E, logits, xq, xst, norm_eps, rblocks);
 }
 
 // one wave per token: logits -> idx, w
