@@ -818,37 +818,39 @@ __global__ __launch_bounds__(64 * DNF_WAVES) void k_down_fast(FfnArgs A)
     const int n = KS * 8 * G;  // pair-layout uint4 of the token's h, <= 1024
     const int n_items = KS * G * 4;  // <= 512
     static_assert(64 * DNF_WAVES * 2 >= 512, "h staging takes two items per thread");
-    // 1. the token's h (cache-resident)
+    // Issue order matters: gfx9 counts outstanding vector loads in order, so each
+    // wait below covers only what was issued before the data it needs.
+    // 1. the routing (cache-resident, one slot per lane): the routed rows wait for it
+    const int my_id = A.idx[b * K + min(lane, K - 1)];
+    const float my_w = A.w[b * K + min(lane, K - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    // 2. the token's h (cache-resident): the staging waits for it
     const float4* hsrc = reinterpret_cast<const float4*>(A.hq) + (long long)b * n * 2;
     HItem hi0, hi1;
     h_item_load(hsrc, G, threadIdx.x, n_items, hi0);
     h_item_load(hsrc, G, threadIdx.x + 64 * DNF_WAVES, n_items, hi1);
-    __builtin_amdgcn_sched_barrier(0);  // keep the h loads ahead of the weight loads
-    // 2. the routing and every slot's down rows
-    int eid[KS];
-    float wt[KS];
-#pragma unroll
-    for (int k = 0; k < K; ++k) {  // all routing loads first, then one wait
-        eid[k] = A.idx[b * K + k];
-        wt[k] = A.w[b * K + k];
-    }
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const bool bad = (eid[k] < 0 || eid[k] >= A.E);
-        eid[k] = bad ? 0 : eid[k];
-        wt[k] = bad ? __builtin_nanf("") : wt[k];
-    }
-    eid[K] = A.E;
-    wt[K] = A.shared_w;
+    __builtin_amdgcn_sched_barrier(0);
+    // 3. the shared expert's rows need no routing: they go out before the routing returns
     uint4 c0[KS], c1[KS];
     uint32_t sbv[KS];
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-        const uint8_t* rec = A.slab + (long long)eid[k] * L.record;
+    auto issue = [&](int k, int e) {
+        const uint8_t* rec = A.slab + (long long)e * L.record;
         const uint8_t* base = rec + L.off_d_codes + (long long)rc * L.ib;
         c0[k] = ld16(base + g * 16);
         if (BITS == 4) c1[k] = ld16(base + (G + g) * 16);
         sbv[k] = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)rc * G + g) * 4);
+    };
+    issue(K, A.E);
+    float wt[KS];
+    wt[K] = A.shared_w;
+    __builtin_amdgcn_sched_barrier(0);
+    // 4. the routed rows
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int e = __builtin_amdgcn_readlane(my_id, k);
+        const bool bad = (e < 0 || e >= A.E);
+        wt[k] = bad ? __builtin_nanf("") : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k));
+        issue(k, bad ? 0 : e);
     }
     __builtin_amdgcn_sched_barrier(0);
     // 3. scale h per group, stage it as fp16 pairs and derive each group's stats
