@@ -18,6 +18,9 @@ MOE_OK = 0
 MOE_EINVAL = -1
 MOE_EUNSUPPORTED = -2
 MOE_EHIP = -3
+MOE_MAX_K = 32      # largest top-K (include/moe.h)
+MOE_MAX_E = 1024    # most routed experts
+MOE_MAX_B = 256     # most tokens per call
 
 KERNEL_ROUTER = 1
 KERNEL_GATEUP = 2

@@ -118,3 +118,12 @@ def test_product_path_has_no_oracle_dependency():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text and "oracle.c" not in text, f
+
+
+def test_binding_limits_match_header():
+    """The binding's MOE_MAX_* mirror include/moe.h."""
+    import re
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "moe.h")).read()
+    for name in ("MOE_MAX_K", "MOE_MAX_E", "MOE_MAX_B"):
+        m = re.search(r"#define %s (\d+)" % name, hdr)
+        assert m and int(m.group(1)) == getattr(moe, name), name

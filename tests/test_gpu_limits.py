@@ -1,0 +1,84 @@
+"""GPU parity at the limits of the boundary: the largest batch, the most experts and
+the largest K the library takes, and K = E (every expert active).
+
+Bars as everywhere: expert indices bit-exact, routing weights within 1e-6
+relative, each token's output within max|dy| / max|y_ref| <= 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+import quantized_expert_dequant_amd as moe
+from quantized_expert_dequant_amd.slab import workspace
+
+from helpers import TOL, W_RTOL, WORKLOADS, build_layer, oracle_layer, oracle_route, rel_err, seed_of
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    moe.lib()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _decode(layer, x):
+    B = x.shape[0]
+    ws, n = workspace(layer.desc, B)
+    y = torch.empty((B, layer.H), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, layer.K), dtype=torch.int32, device=DEV)
+    w = torch.empty((B, layer.K), dtype=torch.float32, device=DEV)
+    moe.layer_decode(layer.desc, torch.from_numpy(np.ascontiguousarray(x)).to(DEV), B, y, idx, w, ws, n)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+def test_batched_largest_batch():
+    """B = 256 (the most tokens per call) on the full-size batched layer: the routing of
+    every token, the outputs of sampled tokens (experts shared by dozens of tokens are cut
+    into several 32-token groups)."""
+    cfg, seed = dict(WORKLOADS[4]), seed_of(4)
+    assert moe.MOE_MAX_B == 256
+    L = build_layer(cfg, seed)
+    x = synth.tokens(seed, 40, moe.MOE_MAX_B, L.H)
+    y, idx, w = _decode(L, x)
+    _, _, _, sel = oracle_route(cfg, seed, 0, x)
+    assert min(s[2] for s in sel) > 1e-9
+    np.testing.assert_array_equal(idx, np.stack([s[0] for s in sel]))
+    np.testing.assert_allclose(w, np.stack([s[1] for s in sel]), rtol=W_RTOL)
+    counts = np.bincount(idx.ravel(), minlength=cfg["E"])
+    assert counts.max() > 64  # the hottest expert spans more than two MFMA groups
+    sample = [0, 77, 128, 201, 255]
+    y_ref, _, _, _ = oracle_layer(cfg, seed, 0, x[sample])
+    for j, b in enumerate(sample):
+        assert rel_err(y[b], y_ref[j]) <= TOL, "token %d" % b
+    del L
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("E,K,B", [(moe.MOE_MAX_E, moe.MOE_MAX_K, 1), (moe.MOE_MAX_E, moe.MOE_MAX_K, 5),
+                                   (16, 16, 1), (16, 16, 3)])
+def test_most_experts_and_largest_k(E, K, B):
+    """E = 1024 with K = 32 (the library's maxima), and K = E = 16 (every expert active),
+    through the per-token path (B = 1) and the grouped path (B > 1); every output checked."""
+    cfg = dict(H=512, I=128, E=E, K=K, bits=4, B=B, layers=1, zipf=None)
+    seed = 1100 + E + K
+    L = build_layer(cfg, seed)
+    x = synth.tokens(seed, B, B, L.H)
+    y, idx, w = _decode(L, x)
+    y_ref, idx_ref, w_ref, margin = oracle_layer(cfg, seed, 0, x)
+    assert np.all(margin > 1e-9)  # infinite when K = E
+    if K == E:  # every expert is selected; the rank order still has to match
+        assert np.all(np.sort(idx, axis=1) == np.arange(E))
+    np.testing.assert_array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
+    for b in range(B):
+        assert rel_err(y[b], y_ref[b]) <= TOL, "token %d" % b
+    del L
+    torch.cuda.empty_cache()
