@@ -43,7 +43,8 @@ struct GroupedWork {
     uint4* xhl;       // token operands [B][G_h][16] uint4
     float* xscale;    // [B]
     float* hb;        // h in fp32, pair-layout order [B + B*K][8][G_i][8]
-    uint4* hb16;      // h * 2^-e(entry) as fp16 pairs [B + B*K][8][G_i]
+    uint4* hb16;      // h * 2^-e(entry) as fp16 pairs in chunk order [B + B*K][2 G_i][4]:
+                      // uint4 (c, d) holds pairs 4(4(c / G_i) + d) .. +3 of group c % G_i
     float* hscale;    // 2^e(entry) [B + B*K]
     float4* hstats;   // per group of hb16: (C, S, scale, 0) for the dot2 GEMV [B + B*K][G_i]
     float* part;      // down outputs [B + B*K][H]

@@ -284,8 +284,9 @@ void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const 
 // Token operands of the gate/up GEMM: x * 2^-e (one power-of-two scale per
 // token, so that the largest |x| lands in [2^14, 2^15)) split into fp16 hi and
 // lo = fp16(v - hi), in the pair order the packed codes unpack to.
-//   xhl[(t * G + g) * 16 + hl * 8 + d]: uint4 holding dword d's 8 columns of
-//   group g (d = 0..7; columns 8d + (0,4,1,5,2,6,3,7)), hl = 0 hi, 1 lo.
+//   xhl[(t * G + g) * 16 + (d / 4) * 8 + hl * 4 + d % 4]: uint4 holding dword d's
+//   8 columns of group g (d = 0..7; columns 8d + (0,4,1,5,2,6,3,7)), hl = 0 hi,
+//   1 lo.  One half of a group (d / 4), hi and lo, is one 128-byte line.
 // ----------------------------------------------------------------------------
 
 // Blocks (t, y >= 1) write token t's dot2 operand instead (fp16 pairs with a
@@ -325,29 +326,33 @@ __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x
         const _Float16 hi = (_Float16)v;
         const _Float16 lo = (_Float16)(v - (float)hi);
         const int g = c >> 6, cc = c & 63, d = cc >> 3, r = cc & 7;
-        const long long o = ((long long)g * 16 + d) * 8 + (r & 3) * 2 + (r >> 2);
+        const long long o = ((long long)g * 16 + (d >> 2) * 8 + (d & 3)) * 8 + (r & 3) * 2 + (r >> 2);
         out[o] = __builtin_bit_cast(uint16_t, hi);
-        out[o + 64] = __builtin_bit_cast(uint16_t, lo);
+        out[o + 32] = __builtin_bit_cast(uint16_t, lo);
     }
 }
 
 // ----------------------------------------------------------------------------
 // Dword w of a 16-byte chunk of a 4-bit row (8 codes) -> the fp16 MFMA operand
 // of its 8 weights s*q + b in the order (c0, c4, c1, c5, c2, c6, c3, c7).
-// OR-ing the fp16 pattern of 1024 into a masked code pair gives
-// (1024 + q_a, 1024 + q_b); subtracting 1024 is exact and one fused
-// multiply-add gives s*q + b, rounded once to fp16.
+// OR-ing the fp16 pattern of 1024 into the masked code pair (c_t, c_t+4) gives
+// (1024 + q_a, 1024 + q_b) for t = 0, 2 (mask 0x000F000F on w, on w >> 8) and
+// (1024 + 16 q_a, 1024 + 16 q_b) for t = 1, 3 (mask 0x00F000F0): subtracting 1024,
+// or scaling by 1/16 and subtracting 64, gives q exactly; one fused multiply-add
+// gives s*q + b, rounded once to fp16.
 // ----------------------------------------------------------------------------
-__device__ inline h8 dequant_dword_q4(uint32_t w, h2 s2, h2 b2, uint32_t mask, uint32_t magic)
+__device__ inline h8 dequant_dword_q4(uint32_t w, h2 s2, h2 b2, const Masks& M)
 {
     const h2 k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-    h2 p[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const uint32_t bits = ((w >> (4 * t)) & mask) | magic;
-        p[t] = __builtin_elementwise_fma(__builtin_bit_cast(h2, bits) - k1024, s2, b2);
-    }
-    return h8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
+    const h2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f}, k64 = {(_Float16)-64.f, (_Float16)-64.f};
+    const uint32_t w8 = w >> 8;
+    const h2 q0 = __builtin_bit_cast(h2, (w & M.m4a) | M.magic) - k1024;
+    const h2 q1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w & M.m4b) | M.magic), k16, k64);
+    const h2 q2 = __builtin_bit_cast(h2, (w8 & M.m4a) | M.magic) - k1024;
+    const h2 q3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w8 & M.m4b) | M.magic), k16, k64);
+    const h2 p0 = __builtin_elementwise_fma(q0, s2, b2), p1 = __builtin_elementwise_fma(q1, s2, b2);
+    const h2 p2 = __builtin_elementwise_fma(q2, s2, b2), p3 = __builtin_elementwise_fma(q3, s2, b2);
+    return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 // ----------------------------------------------------------------------------
@@ -411,6 +416,9 @@ struct GmShape {
     static constexpr int RING = (MODE == MODE_GATEUP) ? 3 : 4;  // weight ring slots (loads run RING-1 steps ahead)
     static constexpr int NSTG = GM_TT * 4 * 4 * HL * 16;     // 16-byte elements staged per step
     static constexpr int PER_T = NSTG / GM_THREADS;
+    // LDS of a stage: rows (tt, k2, token) of 8 (gate/up: hi, lo) or 4 (down) elements,
+    // padded to 9 or 5 so that the MFMA's reads of 16 tokens are free of bank conflicts
+    static constexpr int NLDS = (MODE == MODE_GATEUP) ? GM_TT * 4 * 16 * 9 : GM_TT * 4 * 16 * 5;
 };
 
 __host__ __device__ inline int gm_tiles(const Layout& L, int mode) { return ((mode == MODE_GATEUP ? L.I : L.H) + GM_ROWS - 1) / GM_ROWS; }
@@ -440,7 +448,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
 {
     using S = GmShape<MODE>;
     constexpr int NM = S::NM, HL = S::HL, KC = S::KC, NSTG = S::NSTG, PER_T = S::PER_T, RING = S::RING;
-    __shared__ u4 bs[2][NSTG];
+    __shared__ u4 bs[2][S::NLDS];
 
     const Layout& L = A.L;
     const int G = (MODE == MODE_GATEUP) ? L.Gh : L.Gi;
@@ -476,20 +484,30 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         const uint32_t up_off = (uint32_t)L.hb;
         const char* tok_base = (MODE == MODE_GATEUP) ? (const char*)A.xhl : (const char*)A.hb16;
 
-        // element t = threadIdx.x + GM_THREADS q of a stage holds
-        // ((tt*4 + k2)*4 + d)*HL*16 + hl*16 + j; src[q] is its fixed part (token or
-        // entry row, hl, d), the step adds the chunk's group and half.  Chunks past the
-        // row end (2G not a multiple of 4) read a valid chunk and get zero weights.
-        int src[PER_T], k2q[PER_T];
+        // Element t = threadIdx.x + GM_THREADS q of a stage.  Gate/up: t = ((tt*4 + k2)*16
+        // + j)*8 + hl*4 + d, so 8 consecutive lanes read one 128-byte line of a token's
+        // operand.  Down: t = ((tt*16 + j)*4 + k2)*4 + d, so 16 consecutive lanes read the
+        // step's 256 contiguous bytes of an entry's h.  Either lands in LDS row
+        // (tt*4 + k2)*16 + j.  src[q] is the fixed part of the source index (token or entry
+        // row, hl, d), the step adds the chunk.  Chunks past the row end (2G not a
+        // multiple of 4) read a valid chunk and get zero weights.
+        int src[PER_T], k2q[PER_T], dst[PER_T];
 #pragma unroll
         for (int q = 0; q < PER_T; ++q) {
             const int t = threadIdx.x + GM_THREADS * q;
-            const int j = t & 15, r1 = t >> 4;
-            const int hl = (HL == 2) ? (r1 & 1) : 0, r2 = r1 / HL;
-            const int d = r2 & 3, tt = r2 >> 4;
-            k2q[q] = (r2 >> 2) & 3;
-            const int m = min(tt * 16 + j, n - 1);
-            src[q] = (MODE == MODE_GATEUP) ? A.ent_token[ent0 + m] * G * 16 + hl * 8 + d : (ent0 + m) * 8 * G + d * G;
+            if (MODE == MODE_GATEUP) {
+                const int d = t & 3, hl = (t >> 2) & 1, j = (t >> 3) & 15, k2 = (t >> 7) & 3, tt = t >> 9;
+                const int m = min(tt * 16 + j, n - 1);
+                k2q[q] = k2;
+                src[q] = A.ent_token[ent0 + m] * G * 16 + hl * 4 + d;
+                dst[q] = ((tt * 4 + k2) * 16 + j) * 9 + hl * 4 + d;
+            } else {
+                const int d = t & 3, k2 = (t >> 2) & 3, j = (t >> 4) & 15, tt = t >> 8;
+                const int m = min(tt * 16 + j, n - 1);
+                k2q[q] = k2;
+                src[q] = (ent0 + m) * 8 * G + d;
+                dst[q] = ((tt * 4 + k2) * 16 + j) * 5 + d;
+            }
         }
         struct Stage {
             u4 v[PER_T];
@@ -499,14 +517,14 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             for (int q = 0; q < PER_T; ++q) {
                 const int P = min(4 * ks + k2q[q], 2 * G - 1);
                 const int jh = P >= G ? 1 : 0, g = P - jh * G;
-                const uint32_t el = (MODE == MODE_GATEUP) ? (uint32_t)(src[q] + g * 16 + jh * 4)
-                                                          : (uint32_t)(src[q] + jh * 4 * G + g);
+                const uint32_t el = (MODE == MODE_GATEUP) ? (uint32_t)(src[q] + g * 16 + jh * 8)
+                                                          : (uint32_t)(src[q] + P * 4);
                 S.v[q] = *reinterpret_cast<const u4*>(tok_base + el * 16u);
             }
         };
         auto stage_store = [&](int buf, const Stage& S) {
 #pragma unroll
-            for (int q = 0; q < PER_T; ++q) bs[buf][threadIdx.x + GM_THREADS * q] = S.v[q];
+            for (int q = 0; q < PER_T; ++q) bs[buf][dst[q]] = S.v[q];
         };
         auto weight_load = [&](int ks, WRegs& W) {
             const int P = min(4 * ks + kk, 2 * G - 1), g = P >= G ? P - G : P;
@@ -567,7 +585,10 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                 for (int tt = 0; tt < GM_TT; ++tt)
 #pragma unroll
                     for (int hl = 0; hl < HL; ++hl)
-                        if (tt < ntt) b[tt][hl] = __builtin_bit_cast(h8, buf[(((tt * 4 + kk) * 4 + d) * HL + hl) * 16 + i]);
+                        if (tt < ntt)
+                            b[tt][hl] = __builtin_bit_cast(
+                                h8, buf[(MODE == MODE_GATEUP) ? ((tt * 4 + kk) * 16 + i) * 9 + hl * 4 + d
+                                                              : ((tt * 4 + kk) * 16 + i) * 5 + d]);
             };
             bread(0, bv[0]);
 #pragma unroll
@@ -575,7 +596,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                 if (d + 1 < 4) bread(d + 1, bv[(d + 1) & 1]);
                 h8 a[NM];
 #pragma unroll
-                for (int mm = 0; mm < NM; ++mm) a[mm] = dequant_dword_q4(Wc.c[mm][d], s2[mm], b2[mm], M.m4a, M.magic);
+                for (int mm = 0; mm < NM; ++mm) a[mm] = dequant_dword_q4(Wc.c[mm][d], s2[mm], b2[mm], M);
 #pragma unroll
                 for (int tt = 0; tt < GM_TT; ++tt) {
                     if (tt < ntt) {
@@ -718,7 +739,9 @@ __global__ __launch_bounds__(256) void k_fixup(GroupedArgs A, int nb)
 }
 
 // The down operand: each entry's h scaled by the power of two that puts its
-// largest |h| in [2^14, 2^15), as fp16 pairs, so a token whose h is tiny
+// largest |h| in [2^14, 2^15), as fp16 pairs in chunk order (the 4 dwords of
+// code chunk c = j * G_i + g, j = 0, 1, are the uint4 of pairs 16j .. 16j+15 of
+// group g, so a down step's 4 chunks are contiguous), so a token whose h is tiny
 // everywhere (saturated SiLU) keeps its relative precision; and, for the dot2
 // GEMV, each group's stats (C = 1024 * sum_p (pair sum) / t(p), S = sum h, scale)
 // of the rounded values.  One block per entry.
@@ -741,8 +764,8 @@ __global__ __launch_bounds__(256) void k_hconvert(const float* __restrict__ hb, 
     const float inv = exp2i_f(-e), sc = exp2i_f(e);
     for (int u = threadIdx.x; u < nu; u += 256) {
         const uint4 pv = h_pairs(src[2 * u], src[2 * u + 1], inv);
-        hb16[(long long)ent * nu + u] = pv;
-        const int j = u / Gi;  // uint4 u = j * Gi + g holds pairs 4j .. 4j+3 of group g
+        const int j = u / Gi, gg = u - j * Gi;  // uint4 u = j * Gi + g holds pairs 4j .. 4j+3 of group g
+        hb16[(long long)ent * nu + ((j >> 2) * Gi + gg) * 4 + (j & 3)] = pv;  // chunk order
         const uint32_t pr[4] = {pv.x, pv.y, pv.z, pv.w};
         float off = 0.f, sum = 0.f;
 #pragma unroll
@@ -931,7 +954,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_down(GroupedArgs A, cons
             const uint4* hv = hs + m * 9 * G;
             uint4 hp[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) hp[j] = hv[j * G + g];
+            for (int j = 0; j < 8; ++j) hp[j] = hv[((j >> 2) * G + g) * 4 + (j & 3)];
             const float4 sv = __builtin_bit_cast(float4, hv[8 * G + g]);
             float acc = fmaf(bf16_lo(w.sb) * sv.z, group_dot_q4(M, w.c[0], w.c[1], hp) - sv.x, bf16_hi(w.sb) * sv.y);
             acc = lane_group_sum(gv ? acc : 0.f, LPR);
