@@ -365,10 +365,10 @@ __device__ inline h8 dequant_dword_q4(uint32_t w, h2 s2, h2 b2, const Masks& M)
 // columns, staged in LDS as [tt][kk][d][hl][token].
 //
 // Work split: the units (group, tile, K chunk) in that order are cut into
-// gridDim.x equal contiguous ranges, one per block, so every block streams the
-// same number of weight bytes (groups of <= 32 tokens keep the matrix work
-// below the memory time).  A tile whose K chunks fall into two blocks is
-// finished by k_fixup from the blocks' partial sums.
+// gridDim.x equal contiguous ranges, one per block.  Gate/up tiles are whole
+// units while they number at most one per block; beyond that each is cut into
+// GM_KC_GATEUP K chunks so the ranges still balance, and a tile whose K chunks
+// fall into two blocks is finished by k_fixup from the blocks' partial sums.
 //
 // Pipelining: each step first loads the next step's token operands (cache-
 // resident) into registers, then the weights of step + 3 (HBM) into a 4-slot
@@ -385,7 +385,12 @@ __device__ inline h8 dequant_dword_q4(uint32_t w, h2 s2, h2 b2, const Masks& M)
 // ----------------------------------------------------------------------------
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 constexpr int GM_WAVES = 8, GM_ROWS = GM_WAVES * 16, GM_TT = 2, GM_THREADS = GM_WAVES * 64;
-constexpr int GM_KC_GATEUP = 4;  // K chunks per gate/up tile
+constexpr int GM_KC_GATEUP = 4;  // K chunks per gate/up tile when tiles outnumber the blocks
+
+// K chunks per gate/up tile of a launch: whole tiles when every block gets at
+// most one (no partial sums, nothing for k_fixup), else GM_KC_GATEUP so that the
+// equal ranges still balance.  Uniform for the launch: both kernels derive it alike.
+__device__ inline int gm_kc(int tiles_total, int nb) { return tiles_total <= nb ? 1 : GM_KC_GATEUP; }
 
 struct GroupedArgs {
     const uint8_t* slab;
@@ -402,7 +407,7 @@ struct GroupedArgs {
     const uint4* xhl;
     const float* xscale;
     float* hb;       // gate/up output: h in fp32, pair-layout order [entry][8][G_i][8]
-    const uint4* hb16;     // down operand: h * 2^-e(entry) as fp16 pairs [entry][8][G_i]
+    const uint4* hb16;     // down operand: h * 2^-e(entry) as fp16 pairs in chunk order [entry][2 G_i][4]
     const float* hscale;   // 2^e(entry)
     float* part;     // MODE_DOWN output
     float* split;    // MODE_GATEUP partial sums [2 * gridDim.x][2][GM_GROUP][GM_ROWS]
@@ -412,7 +417,6 @@ template <int MODE>
 struct GmShape {
     static constexpr int NM = (MODE == MODE_GATEUP) ? 2 : 1;  // matrices per row: gate + up | down
     static constexpr int HL = (MODE == MODE_GATEUP) ? 2 : 1;  // token operand parts: hi + lo | h
-    static constexpr int KC = (MODE == MODE_GATEUP) ? GM_KC_GATEUP : 1;
     static constexpr int RING = (MODE == MODE_GATEUP) ? 3 : 4;  // weight ring slots (loads run RING-1 steps ahead)
     static constexpr int NSTG = GM_TT * 4 * 4 * HL * 16;     // 16-byte elements staged per step
     static constexpr int PER_T = NSTG / GM_THREADS;
@@ -447,7 +451,7 @@ template <int MODE>
 __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void k_grouped_mfma(GroupedArgs A)
 {
     using S = GmShape<MODE>;
-    constexpr int NM = S::NM, HL = S::HL, KC = S::KC, NSTG = S::NSTG, PER_T = S::PER_T, RING = S::RING;
+    constexpr int NM = S::NM, HL = S::HL, NSTG = S::NSTG, PER_T = S::PER_T, RING = S::RING;
     __shared__ u4 bs[2][S::NLDS];
 
     const Layout& L = A.L;
@@ -455,8 +459,9 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
     const int NR = (MODE == MODE_GATEUP) ? L.I : L.H;
     const int tiles = gm_tiles(L, MODE);
     const int nsteps = gm_steps(L, MODE);
-    const int T = A.grp_u[0] * tiles * KC;
     const int nb = gridDim.x, blk = blockIdx.x;
+    const int KC = (MODE == MODE_GATEUP) ? gm_kc(A.grp_u[0] * tiles, nb) : 1;
+    const int T = A.grp_u[0] * tiles * KC;
     const int lo = gm_lo(blk, T, nb), hi = gm_lo(blk + 1, T, nb);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int i = lane & 15, kk = lane >> 4;
@@ -694,8 +699,9 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
 // inside the same tile.
 __global__ __launch_bounds__(256) void k_fixup(GroupedArgs A, int nb)
 {
-    constexpr int KC = GM_KC_GATEUP;
     const int tiles = gm_tiles(A.L, MODE_GATEUP);
+    const int KC = gm_kc(A.grp_u[0] * tiles, nb);
+    if (KC == 1) return;  // whole tiles: nothing was split
     const int T = A.grp_u[0] * tiles * KC;
     const int b = blockIdx.x;
     const int s0 = gm_lo(b, T, nb);
@@ -706,7 +712,7 @@ __global__ __launch_bounds__(256) void k_fixup(GroupedArgs A, int nb)
     const int ent0 = A.act_off[u], n = A.act_n[u];
     const int b_lo = gm_blk(tau * KC, T, nb), b_hi = gm_blk((tau + 1) * KC - 1, T, nb);
     // the tile's partial slots in K order (at most KC blocks share a tile)
-    int slots[KC], ns = 0;
+    int slots[GM_KC_GATEUP], ns = 0;
     for (int bb = b_lo; bb <= b_hi && ns < KC; ++bb) {
         const int l0 = gm_lo(bb, T, nb);
         if (l0 == gm_lo(bb + 1, T, nb)) continue;  // empty range
