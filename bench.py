@@ -348,6 +348,7 @@ def main():
     kinds = [moe.KERNEL_ROUTER, moe.KERNEL_GATEUP, moe.KERNEL_DOWN]
     dur = {k: None for k in kinds}
     eager_ms = None
+    eager_pct = None
     if not args.no_eager:
         hip = Hip()
         ev = {k: [(hip.event(), hip.event()) for _ in range(K)] for k in kinds}
@@ -366,6 +367,11 @@ def main():
         # so each pair times the step's last launch of that kernel
         dur = {k: sum(hip.elapsed_ms(a, b) for a, b in ev[k]) / K for k in kinds}
         eager_ms = hip.elapsed_ms(ev[moe.KERNEL_ROUTER][0][0], ev[moe.KERNEL_DOWN][K - 1][1]) / K
+        if not stack:  # per-step spread: router start to down end of each step
+            st = np.array([hip.elapsed_ms(ev[moe.KERNEL_ROUTER][i][0], ev[moe.KERNEL_DOWN][i][1]) * 1e3
+                           for i in range(K)])
+            eager_pct = {"p10": round(float(np.percentile(st, 10)), 3), "p50": round(float(np.percentile(st, 50)), 3),
+                         "p90": round(float(np.percentile(st, 90)), 3)}
         for k in kinds:
             for a, b in ev[k]:
                 hip.destroy(a)
@@ -423,6 +429,7 @@ def main():
         "expert_weight_frac_of_peak": round(expert_gbps / PEAK_HBM_GBPS, 4),
         "kernel_us": {"router": round(rt_us, 3), "gateup": round(gu_us, 3), "down": round(dn_us, 3)},
         "eager_ms_per_step": round(eager_ms, 6),
+        **({"eager_step_us": eager_pct} if eager_pct else {}),
         "parity_rel_err": err,
     }
     if B > 1:
