@@ -187,13 +187,10 @@ __device__ inline float absmax8(float4 a, float4 b)
 template <int CTRL>
 __device__ inline uint32_t dpp32(uint32_t v)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    // every pattern used here reads inside the lane's row, so every lane is
+    // written and the destination needs no initial value
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
-
-struct ArgMax {  // (value, id): larger value first, equal values -> lower id first
-    double v;
-    int id;
-};
 
 template <int CTRL>
 __device__ inline float xchg(float v) { return __uint_as_float(dpp32<CTRL>(__float_as_uint(v))); }
@@ -204,30 +201,6 @@ __device__ inline double xchg(double v)
     u.x = dpp32<CTRL>(u.x);
     u.y = dpp32<CTRL>(u.y);
     return __builtin_bit_cast(double, u);
-}
-template <int CTRL>
-__device__ inline ArgMax xchg(ArgMax a) { return ArgMax{xchg<CTRL>(a.v), (int)dpp32<CTRL>((uint32_t)a.id)}; }
-
-template <int CTRL>
-__device__ inline uint64_t xchg(uint64_t v)
-{
-    uint2 u = __builtin_bit_cast(uint2, v);
-    u.x = dpp32<CTRL>(u.x);
-    u.y = dpp32<CTRL>(u.y);
-    return __builtin_bit_cast(uint64_t, u);
-}
-
-struct KeyId {  // (key, id): larger key first, equal keys -> lower id first
-    uint64_t key;
-    int id;
-};
-template <int CTRL>
-__device__ inline KeyId xchg(KeyId a)
-{
-    uint2 u = __builtin_bit_cast(uint2, a.key);
-    u.x = dpp32<CTRL>(u.x);
-    u.y = dpp32<CTRL>(u.y);
-    return KeyId{__builtin_bit_cast(uint64_t, u), (int)dpp32<CTRL>((uint32_t)a.id)};
 }
 
 template <bool ROW32>
@@ -260,35 +233,6 @@ __device__ inline void swap(double v, double& a, double& b)
     a = __builtin_bit_cast(double, p);
     b = __builtin_bit_cast(double, q);
 }
-template <bool ROW32>
-__device__ inline void swap(uint64_t v, uint64_t& a, uint64_t& b)
-{
-    uint2 u = __builtin_bit_cast(uint2, v), p, q;
-    swap_u32<ROW32>(u.x, p.x, q.x);
-    swap_u32<ROW32>(u.y, p.y, q.y);
-    a = __builtin_bit_cast(uint64_t, p);
-    b = __builtin_bit_cast(uint64_t, q);
-}
-template <bool ROW32>
-__device__ inline void swap(KeyId v, KeyId& a, KeyId& b)
-{
-    uint2 u = __builtin_bit_cast(uint2, v.key), p, q;
-    swap_u32<ROW32>(u.x, p.x, q.x);
-    swap_u32<ROW32>(u.y, p.y, q.y);
-    uint32_t x, y;
-    swap_u32<ROW32>((uint32_t)v.id, x, y);
-    a = KeyId{__builtin_bit_cast(uint64_t, p), (int)x};
-    b = KeyId{__builtin_bit_cast(uint64_t, q), (int)y};
-}
-template <bool ROW32>
-__device__ inline void swap(ArgMax v, ArgMax& a, ArgMax& b)
-{
-    swap<ROW32>(v.v, a.v, b.v);
-    uint32_t x, y;
-    swap_u32<ROW32>((uint32_t)v.id, x, y);
-    a.id = (int)x;
-    b.id = (int)y;
-}
 
 // all-reduce over aligned groups of `width` lanes (a power of two <= 64)
 template <typename T, typename Op>
@@ -317,18 +261,6 @@ struct OpAdd {
 };
 struct OpMax {
     __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
-};
-struct OpKeyMax {
-    __device__ KeyId operator()(KeyId a, KeyId b) const
-    {
-        return (b.key > a.key || (b.key == a.key && b.id < a.id)) ? b : a;
-    }
-};
-struct OpArgMax {
-    __device__ ArgMax operator()(ArgMax a, ArgMax b) const
-    {
-        return (b.v > a.v || (b.v == a.v && b.id < a.id)) ? b : a;
-    }
 };
 
 template <typename T>

@@ -6,22 +6,24 @@
 
 namespace moe {
 
-// Selection key of a logit: an order-preserving map of the double onto a
-// 64-bit integer (larger logit, larger key) whose lowest 10 bits are replaced
-// by 1023 - id.  One unsigned compare then ranks (logit desc, id asc); logits
-// that agree to 2^-43 relative (below what fp64 summation order fixes) count
-// as equal and go to the lower id.  Needs E <= 1024.
-__device__ inline uint64_t select_key(double d, int id)
+// Selection value of a logit: the double itself with its lowest 10 mantissa
+// bits replaced by a code of the id, so that fp64 max/min alone rank
+// (logit desc, id asc): 1023 - id for a non-negative logit, id for a negative
+// one (there a larger magnitude is a smaller value).  Logits that agree but for
+// those bits (2^-43 relative, below what the fp64 summation order fixes) count
+// as equal and go to the lower id.  -0 is made +0 first, so the two zeros are
+// one logit.  The value is the logit to within 2^-42 relative.  Needs E <= 1024.
+__device__ inline double select_val(double d, int id)
 {
-    const uint64_t u = (uint64_t)__double_as_longlong(d);
-    const uint64_t k = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-    return (k & ~1023ull) | (uint64_t)(1023 - id);
+    const uint64_t u = (uint64_t)__double_as_longlong(d + 0.0);
+    const uint64_t t = (u >> 63) ? (uint64_t)id : (uint64_t)(1023 - id);
+    return __longlong_as_double((long long)((u & ~1023ull) | t));
 }
-__device__ inline int key_id(uint64_t k) { return 1023 - (int)(k & 1023ull); }
-__device__ inline double key_value(uint64_t k)  // the logit to within 2^-42 relative
+__device__ inline int val_id(double v)
 {
-    const uint64_t u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
-    return __longlong_as_double((long long)u);
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const int t = (int)(u & 1023ull);
+    return (u >> 63) ? t : 1023 - t;
 }
 
 // Load the logits a wave selects from: lane l holds ids l + 64 j, j < NL
@@ -33,44 +35,101 @@ __device__ inline void topk_load(const double* __restrict__ lg, int E, int lane,
     for (int j = 0; j < NL; ++j) lv[j] = lg[min(lane + 64 * j, E - 1)];
 }
 
-struct OpU64Max {
-    __device__ uint64_t operator()(uint64_t a, uint64_t b) const { return b > a ? b : a; }
+// fp64 max / min of selection values: one v_max_f64 / v_min_f64 each (the
+// compiler adds a quieting max only for inputs it cannot prove NaN-free: the
+// built values and the values taken from other lanes)
+__device__ inline double sel_max(double a, double b) { return fmax(a, b); }
+__device__ inline double sel_min(double a, double b) { return fmin(a, b); }
+constexpr double SEL_NONE = -1.7976931348623157e308;  // below every selection value of a real logit
+
+struct OpSelMax {
+    __device__ double operator()(double a, double b) const { return sel_max(a, b); }
 };
+
+// compare-exchange: a takes the larger value (DESC) or the smaller one
+template <bool DESC>
+__device__ inline void cmp_xchg(double& a, double& b)
+{
+    const double hi = sel_max(a, b), lo = sel_min(a, b);
+    a = DESC ? hi : lo;
+    b = DESC ? lo : hi;
+}
+
+// bitonic sort of v[0..N) into descending order (N a power of two)
+template <int N>
+__device__ inline void sort_desc(double* v)
+{
+#pragma unroll
+    for (int k = 2; k <= N; k *= 2)
+#pragma unroll
+        for (int j = k / 2; j > 0; j /= 2)
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    if ((i & k) == 0)
+                        cmp_xchg<true>(v[i], v[l]);
+                    else
+                        cmp_xchg<false>(v[i], v[l]);
+                }
+            }
+}
+
+// a[0..P) and b[0..P) sorted descending -> a = the P largest of both, sorted
+// descending: max(a_i, b_{P-1-i}) is bitonic, then one bitonic merge
+template <int P>
+__device__ inline void merge_top(double* a, const double* b)
+{
+#pragma unroll
+    for (int i = 0; i < P; ++i) a[i] = sel_max(a[i], b[P - 1 - i]);
+#pragma unroll
+    for (int j = P / 2; j > 0; j /= 2)
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int l = i ^ j;
+            if (l > i) cmp_xchg<true>(a[i], a[l]);
+        }
+}
 
 // Top-K of one token's E <= 64 * NL logits by one wave.  Lane k < K returns
 // the k-th expert (rank order) and its routing weight; every lane sees the
-// same selection.  All loops have compile-time trip counts, so the keys stay
-// in registers.
+// same selection.  Each lane first sorts its own candidates (it can give at
+// most P = min(KMAX, NL) of the K), then every round takes the wave maximum
+// of the lanes' heads and the lane that held it drops its head.  All loops have
+// compile-time trip counts, so the values stay in registers.
 template <int KMAX, int NL>
 __device__ void topk_select(const double (&lv)[NL], int E, int K, int renorm, int lane, int& my_id, float& my_w)
 {
-    uint64_t key[NL];
+    constexpr int P = KMAX < NL ? KMAX : NL;
+    constexpr int PP = (P <= 1) ? 1 : (P <= 2) ? 2 : (P <= 4) ? 4 : (P <= 8) ? 8 : 16;  // power of two >= P
+    static_assert(NL % PP == 0, "candidates per lane: a multiple of the sorted run");
+    double v[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
         const int id = lane + 64 * j;
-        key[j] = (id < E) ? select_key(lv[j], id) : 0ull;
+        const double s = select_val(lv[j], id);
+        v[j] = (id < E) ? s : SEL_NONE;
     }
-    uint64_t mine = 0ull, top = 0ull;
+    // this lane's P best, descending: sorted runs of PP merged pairwise
+#pragma unroll
+    for (int r = 0; r < NL; r += PP) sort_desc<PP>(v + r);
+#pragma unroll
+    for (int r = PP; r < NL; r += PP) merge_top<PP>(v, v + r);
+    double mine = 0.0, top = 0.0;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         if (k >= K) break;
-        uint64_t t[NL];  // this lane's best remaining key: a tree over its candidates
+        const double best = group_reduce(v[0], OpSelMax(), 64);
+        const bool win = __double_as_longlong(v[0]) == __double_as_longlong(best);  // values are unique
 #pragma unroll
-        for (int j = 0; j < NL; ++j) t[j] = key[j];
-#pragma unroll
-        for (int w = 1; w < NL; w *= 2)
-#pragma unroll
-            for (int j = 0; j + w < NL; j += 2 * w) t[j] = t[j + w] > t[j] ? t[j + w] : t[j];
-        const uint64_t best = group_reduce(t[0], OpU64Max(), 64);
-#pragma unroll
-        for (int j = 0; j < NL; ++j) key[j] = (key[j] == best) ? 0ull : key[j];  // keys are unique
+        for (int i = 0; i + 1 < P; ++i) v[i] = win ? v[i + 1] : v[i];
+        v[P - 1] = win ? SEL_NONE : v[P - 1];
         if (k == 0) top = best;
         if (lane == k) mine = best;
     }
-    my_id = (lane < K) ? key_id(mine) : 0x7FFFFFFF;
-    const double lmax = key_value(top);
+    my_id = (lane < K) ? val_id(mine) : 0x7FFFFFFF;
     // softmax weights in fp32: exp of logit differences, renormalized over the K
-    const float ew = (lane < K) ? __expf((float)(key_value(mine) - lmax)) : 0.f;
+    const float ew = (lane < K) ? __expf((float)(mine - top)) : 0.f;
     float denom;
     if (renorm) {
         denom = wave_sum(ew);
@@ -78,7 +137,7 @@ __device__ void topk_select(const double (&lv)[NL], int E, int K, int renorm, in
         float part = 0.f;
 #pragma unroll
         for (int j = 0; j < NL; ++j)
-            if (lane + 64 * j < E) part += __expf((float)(lv[j] - lmax));
+            if (lane + 64 * j < E) part += __expf((float)(lv[j] - top));
         denom = wave_sum(part);
     }
     my_w = ew / denom;
