@@ -677,6 +677,7 @@ __global__ __launch_bounds__(256) void k_down(FfnArgs A)
 constexpr int FAST_NL = 8;  // fast path: E <= 512 logits per token, 8 per lane
 
 constexpr int GUF_WAVES = 8;  // fast gate/up: waves per block
+constexpr int GUF_XQ = (64 * 9 + 64 * GUF_WAVES - 1) / (64 * GUF_WAVES);  // operand uint4 per thread (G <= 64)
 
 // One (row pass, expert slot) per wave, blocks in slot-major order: the shared
 // expert's blocks (slot 0) come first and need no routing; a routed block's wave
@@ -714,9 +715,9 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
             my_id = A.idx[(long long)b * K + min(lane, K - 1)];
     }
     const int nx = G * 9;  // uint4 of pairs ([8][G]) then stats ([G])
-    uint4 xv[2];
+    uint4 xv[GUF_XQ];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < GUF_XQ; ++q) {
         const int t = min((int)threadIdx.x + 64 * GUF_WAVES * q, nx - 1);
         xv[q] = t < 8 * G ? A.xq[(long long)b * 8 * G + t]
                           : __builtin_bit_cast(uint4, A.xst[(long long)b * G + (t - 8 * G)]);
@@ -740,7 +741,7 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
     __builtin_amdgcn_sched_barrier(0);
     // 3. stage the token's operand; wave 0 of a routed block selects the experts meanwhile
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < GUF_XQ; ++q) {
         const int t = threadIdx.x + 64 * GUF_WAVES * q;
         if (t < nx) xs[t] = xv[q];
     }

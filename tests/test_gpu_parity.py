@@ -85,9 +85,7 @@ def test_router_raw_softmax_and_ties():
     Wr = rng.normal(0, 1 / 16, (E, H)).astype(np.float32)
     x = rng.normal(0, 1, (4, H)).astype(np.float32)
     lg = oracle.router_logits(x, Wr)
-    for b in range(4):               # make expert 33 an exact twin of each token's best expert
-        pass
-    top = int(np.argmax(lg[0]))
+    top = int(np.argmax(lg[0]))      # experts 33 and 35 become exact twins of token 0's best
     Wr[33] = Wr[top]
     Wr[35] = Wr[top]
     lg = oracle.router_logits(x, Wr)
@@ -99,6 +97,50 @@ def test_router_raw_softmax_and_ties():
     i0 = list(idx[0])
     assert i0[:3] == sorted([top, 33, 35])
 
+
+
+@pytest.mark.parametrize("bias", [None, -100.0])
+def test_layer_exact_ties_in_fused_selection(bias):
+    """Exact logit ties inside the single-token gate/up kernel, which selects the experts
+    itself: twin router rows tie at the top (positive logits, or negative ones under a
+    constant -100 logit bias), and a zero token ties every logit at the bias (+0 without
+    one).  Ties go to the lower id, as in the oracle; weights and outputs as everywhere."""
+    H, I, E, K, bits, seed = 512, 128, 64, 4, 4, 1207
+    rng = np.random.default_rng(seed)
+    Wr = rng.normal(0, 1 / np.sqrt(H), (E, H)).astype(np.float32)
+    x = rng.normal(0, 1, (3, H)).astype(np.float32)
+    x[2] = 0.0
+    prior = None if bias is None else np.full(E, bias, np.float32)
+    lg = oracle.router_logits(x, Wr, prior)
+    t0, t1 = int(np.argmax(lg[0])), int(np.argsort(lg[1])[-1])
+    for twin in (9, 40, 63):
+        Wr[twin] = Wr[t0]
+    Wr[3] = Wr[t1]
+    src = lambda first, n: synth.experts(seed, 0, first, n, bits, H, I)
+    slab = upload_experts(src, E + 1, bits, H, I, device=DEV)
+    L = DeviceLayer(H, I, E, K, bits, slab, _t(Wr), None if prior is None else _t(prior))
+    ws, n = workspace(L.desc, 1)
+    experts = {e: synth.experts(seed, 0, e, 1, bits, H, I) for e in range(E + 1)}
+    lg = oracle.router_logits(x, Wr, prior)
+    for b in range(3):
+        y = torch.empty((1, H), dtype=torch.float32, device=DEV)
+        idx = torch.empty((1, K), dtype=torch.int32, device=DEV)
+        w = torch.empty((1, K), dtype=torch.float32, device=DEV)
+        moe.layer_decode(L.desc, _t(x[b:b + 1]), 1, y, idx, w, ws, n)
+        torch.cuda.synchronize()
+        y_ref, idx_ref, w_ref, _ = oracle.layer_decode(bits, H, I, E, K, x[b:b + 1], Wr, experts, prior=prior)
+        got = idx.cpu().numpy()[0]
+        np.testing.assert_array_equal(got, idx_ref[0])
+        np.testing.assert_allclose(w.cpu().numpy()[0], w_ref[0], rtol=W_RTOL)
+        assert rel_err(y.cpu().numpy()[0], y_ref[0]) <= TOL, "token %d" % b
+        if b == 0:
+            assert list(got[:4]) == sorted([t0, 9, 40, 63])
+        pos = {int(e): i for i, e in enumerate(got)}
+        if 3 in pos and t1 in pos:  # twins sit side by side, the lower id first
+            assert abs(pos[3] - pos[t1]) == 1 and (pos[3] < pos[t1]) == (3 < t1)
+        if b == 2:
+            assert list(got) == [0, 1, 2, 3]
+            np.testing.assert_allclose(w.cpu().numpy()[0], 0.25, rtol=W_RTOL)
 
 # ------------------------------------------------------------------ layer ----
 
