@@ -55,14 +55,26 @@ bool grouped_supported(const Layout& L, int B, int K);
 size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E);
 GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E);
 int router_splits(int H);
+// Token operands the batched top-K kernel writes beside the selection (xhl
+// nullptr: none; xq nullptr: no dot2 operand).  x and H are filled in by
+// launch_route_batched.
+struct TokenPrep {
+    const float* x;
+    int H;
+    uint4* xhl;
+    float* xscale;
+    uint4* xq;
+    float4* xst;
+};
 void launch_route_batched(const float* x, int B, const float* W, const float* bias, int H, int E, int K, int renorm,
-                          double* partial, int32_t* idx, float* w, hipStream_t s, Timing t);
+                          double* partial, int32_t* idx, float* w, const TokenPrep& P, hipStream_t s, Timing t);
 // experts with fewer tokens than this run as GEMV groups (1: none)
 int gemv_tokens(const Layout& L);
 void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const GroupOut& O, hipStream_t s);
 // xq / xst: room for the B tokens' dot2 operands (fp16 pairs + group stats)
+// prepped: the token operands are already written (by the batched top-K kernel)
 void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W, const float* x, const float* w,
-                        float shared_w, int B, int K, int E, uint4* xq, float4* xst, float* y, hipStream_t s,
-                        Timing tg, Timing td);
+                        float shared_w, int B, int K, int E, uint4* xq, float4* xst, bool prepped, float* y,
+                        hipStream_t s, Timing tg, Timing td);
 
 }  // namespace moe

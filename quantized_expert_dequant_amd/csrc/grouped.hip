@@ -45,6 +45,34 @@ constexpr int GM_MAX_BLOCKS = 1024;  // most blocks of a stream-split launch
 
 __device__ inline f4 mfma16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
+
+// ----------------------------------------------------------------------------
+// The MFMA token operand: x scaled by the power of two that puts the token's
+// largest |x| in [2^14, 2^15), split into fp16 hi + lo; element c of group g
+// lands in the 128-byte line of its group half, hi at o and lo at o + 32 (in
+// fp16 units), o = ((g * 16 + (d / 4) * 8 + d % 4) * 8 + (r % 4) * 2 + r / 4)
+// for d = (c % 64) / 8, r = c % 8.
+// ----------------------------------------------------------------------------
+__device__ inline int token_exponent(float amax)
+{
+    int e = 0;
+    if (amax > 0.f && amax <= 3.4e38f) {
+        e = ilogbf(amax) - 14;
+        e = e < -110 ? -110 : (e > 113 ? 113 : e);
+    }
+    return e;
+}
+__device__ inline void token_operand_elem(const float* __restrict__ xt, int c, float inv, uint16_t* __restrict__ out)
+{
+    const float v = xt[c] * inv;
+    const _Float16 hi = (_Float16)v;
+    const _Float16 lo = (_Float16)(v - (float)hi);
+    const int g = c >> 6, cc = c & 63, d = cc >> 3, r = cc & 7;
+    const long long o = ((long long)g * 16 + (d >> 2) * 8 + (d & 3)) * 8 + (r & 3) * 2 + (r >> 2);
+    out[o] = __builtin_bit_cast(uint16_t, hi);
+    out[o + 32] = __builtin_bit_cast(uint16_t, lo);
+}
+
 // ----------------------------------------------------------------------------
 // Logits of B tokens: a block computes a tile of 32 experts x 32 tokens over a
 // 256-column slice of H; each thread keeps 2 x 2 outputs, accumulating the exact
@@ -106,10 +134,19 @@ constexpr int TS_CHUNK = 16;  // slice loads in flight per thread
 
 __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ partial, int nslice,
                                                      const float* __restrict__ bias, int B, int E, int K, int renorm,
-                                                     int32_t* __restrict__ idx, float* __restrict__ w)
+                                                     int32_t* __restrict__ idx, float* __restrict__ w, TokenPrep P)
 {
     __shared__ double lg[1024];  // E <= 1024
+    __shared__ float red[8];
     const int b = blockIdx.x, tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const float* xt = P.x + (long long)b * P.H;
+    if (P.xhl) {  // the token's largest |x|, for the MFMA operand's scale
+        float m = 0.f;
+        for (int c = tid; c < P.H; c += 512) m = fmaxf(m, fabsf(xt[c]));
+        m = wave_max(m);
+        if (lane == 0) red[wave] = m;
+    }
     const long long BE = (long long)B * E;
     for (int e = tid; e < E; e += 512) {
         const double* p = partial + (long long)b * E + e;
@@ -125,7 +162,23 @@ __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ 
         lg[e] = s + (bias ? (double)bias[e] : 0.0);
     }
     __syncthreads();
-    if (tid >= 64) return;
+    if (tid >= 64) {
+        // waves 1..7 write the token's operands while wave 0 selects: the MFMA
+        // operand (as k_prep_tokens) and, for the GEMV groups, the dot2 operand
+        if (!P.xhl) return;
+        float amax = red[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) amax = fmaxf(amax, red[i]);
+        const int e = token_exponent(amax);
+        const float inv = exp2i_f(-e);
+        if (tid == 64) P.xscale[b] = exp2i_f(e);
+        const int G = P.H / 64;
+        uint16_t* out = reinterpret_cast<uint16_t*>(P.xhl + (long long)b * G * 16);
+        for (int c = tid - 64; c < P.H; c += 448) token_operand_elem(xt, c, inv, out);
+        if (P.xq)
+            for (int g = wave - 1; g < G; g += 7) prep_group<4>(P.x, G, b, g, lane, P.xq, P.xst);
+        return;
+    }
     double lv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) lv[j] = lg[min(tid + 64 * j, E - 1)];
@@ -141,12 +194,15 @@ __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ 
 int router_splits(int H) { return (H + RT_SLICE - 1) / RT_SLICE; }
 
 void launch_route_batched(const float* x, int B, const float* W, const float* bias, int H, int E, int K, int renorm,
-                          double* partial, int32_t* idx, float* w, hipStream_t s, Timing t)
+                          double* partial, int32_t* idx, float* w, const TokenPrep& P, hipStream_t s, Timing t)
 {
     const dim3 grid((E + RT_E - 1) / RT_E, (B + RT_B - 1) / RT_B, router_splits(H));
     hipExtLaunchKernelGGL(k_router_tiled, grid, dim3(256), 0, s, t.start, t.stop, 0, x, B, W, H, E, partial);
+    TokenPrep Q = P;
+    Q.x = x;
+    Q.H = H;
     hipLaunchKernelGGL(k_topk_slices, dim3(B), dim3(512), 0, s, partial, router_splits(H), bias, B, E, K, renorm,
-                       idx, w);
+                       idx, w, Q);
 }
 
 // ----------------------------------------------------------------------------
@@ -312,24 +368,12 @@ __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
     const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    int e = 0;
-    if (amax > 0.f && amax <= 3.4e38f) {
-        e = ilogbf(amax) - 14;
-        e = e < -110 ? -110 : (e > 113 ? 113 : e);
-    }
+    const int e = token_exponent(amax);
     const float inv = exp2i_f(-e);
     if (tid == 0) xscale[t] = exp2i_f(e);
     const int G = H / 64;
     uint16_t* out = reinterpret_cast<uint16_t*>(xhl + (long long)t * G * 16);
-    for (int c = tid; c < H; c += 256) {
-        const float v = xt[c] * inv;
-        const _Float16 hi = (_Float16)v;
-        const _Float16 lo = (_Float16)(v - (float)hi);
-        const int g = c >> 6, cc = c & 63, d = cc >> 3, r = cc & 7;
-        const long long o = ((long long)g * 16 + (d >> 2) * 8 + (d & 3)) * 8 + (r & 3) * 2 + (r >> 2);
-        out[o] = __builtin_bit_cast(uint16_t, hi);
-        out[o + 32] = __builtin_bit_cast(uint16_t, lo);
-    }
+    for (int c = tid; c < H; c += 256) token_operand_elem(xt, c, inv, out);
 }
 
 // ----------------------------------------------------------------------------
@@ -697,13 +741,13 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
 // partial sums in K order, then SwiGLU.  Block b handles the tile in which its
 // range starts, when that start is inside a tile and no lower block starts
 // inside the same tile.
-__global__ __launch_bounds__(256) void k_fixup(GroupedArgs A, int nb)
+// Block-uniform; 256 threads.
+__device__ inline void fixup_block(const GroupedArgs& A, int nb, int b)
 {
     const int tiles = gm_tiles(A.L, MODE_GATEUP);
     const int KC = gm_kc(A.grp_u[0] * tiles, nb);
     if (KC == 1) return;  // whole tiles: nothing was split
     const int T = A.grp_u[0] * tiles * KC;
-    const int b = blockIdx.x;
     const int s0 = gm_lo(b, T, nb);
     if (s0 >= T || s0 % KC == 0) return;
     const int tau = s0 / KC;
@@ -742,7 +786,10 @@ __global__ __launch_bounds__(256) void k_fixup(GroupedArgs A, int nb)
             if (t < n * GM_ROWS && r < A.L.I) store_h(A, ent0 + m, r, g[q], up[q], xs_tok[m]);
         }
     }
+    __syncthreads();  // xs_tok is free for the block's next tile
 }
+
+__global__ __launch_bounds__(256) void k_fixup(GroupedArgs A, int nb) { fixup_block(A, nb, blockIdx.x); }
 
 // The down operand: each entry's h scaled by the power of two that puts its
 // largest |h| in [2^14, 2^15), as fp16 pairs in chunk order (the 4 dwords of
@@ -849,8 +896,11 @@ struct GvDown {
 // Work item = (group, GV_WAVES row passes); each block walks a contiguous range of
 // items, the next item's weights in flight while the current one is computed.
 __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_gateup(GroupedArgs A, const uint4* __restrict__ xq,
-                                                               const float4* __restrict__ xst)
+                                                               const float4* __restrict__ xst, int nb_fix)
 {
+    static_assert(64 * GV_WAVES == 256, "the split-tile fixup runs on 256-thread blocks");
+    // first the MFMA launch's split-tile fixups (nothing when its tiles were whole)
+    for (int fb = blockIdx.x; fb < nb_fix; fb += gridDim.x) fixup_block(A, nb_fix, fb);
     extern __shared__ uint4 xs[];  // [n][9*G]
     const Layout& L = A.L;
     const int G = L.Gh, LPR = lanes_per_row(G), RPP = 64 / LPR;
@@ -1076,8 +1126,8 @@ static int resident_blocks(const void* kernel, int threads)
 }
 
 void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W, const float* x, const float* w,
-                        float shared_w, int B, int K, int E, uint4* xq, float4* xst, float* y, hipStream_t s,
-                        Timing tg, Timing td)
+                        float shared_w, int B, int K, int E, uint4* xq, float4* xst, bool prepped, float* y,
+                        hipStream_t s, Timing tg, Timing td)
 {
     static int nb_gu = 0, nb_dn = 0, nb_gvu = 0, nb_gvd = 0;  // per process: one device type
     if (!nb_gu) {
@@ -1089,8 +1139,9 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     const int gv_t = gemv_tokens(L);
     const bool gv = gv_t > 1;
 
-    hipLaunchKernelGGL(k_prep_tokens, dim3(B, gv ? 1 + PT_DOT2_BLOCKS : 1), dim3(256), 0, s, x, L.H, W.xhl, W.xscale,
-                       xq, xst);
+    if (!prepped)
+        hipLaunchKernelGGL(k_prep_tokens, dim3(B, gv ? 1 + PT_DOT2_BLOCKS : 1), dim3(256), 0, s, x, L.H, W.xhl,
+                           W.xscale, xq, xst);
     GroupedArgs A;
     A.slab = (const uint8_t*)slab;
     A.L = L;
@@ -1120,10 +1171,11 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     // together they read every active expert's gate/up rows once
     if (tg.start) (void)hipEventRecord(tg.start, s);
     hipLaunchKernelGGL(k_grouped_mfma<MODE_GATEUP>, dim3(nb_gu), dim3(GM_THREADS), 0, s, A);
-    hipLaunchKernelGGL(k_fixup, dim3(nb_gu), dim3(256), 0, s, A, nb_gu);
-    if (gv)
+    if (gv)  // the GEMV kernel runs the split-tile fixups first
         hipLaunchKernelGGL(k_gemv_gateup, dim3(nbu), dim3(64 * GV_WAVES), lds_gu, s, A, (const uint4*)xq,
-                           (const float4*)xst);
+                           (const float4*)xst, nb_gu);
+    else
+        hipLaunchKernelGGL(k_fixup, dim3(nb_gu), dim3(256), 0, s, A, nb_gu);
     if (tg.stop) (void)hipEventRecord(tg.stop, s);
 
     hipLaunchKernelGGL(k_hconvert, dim3(B * K + B), dim3(256), 0, s, W.hb, A.n_ent, B, L.I, W.hb16, W.hscale,

@@ -256,8 +256,8 @@ static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, cons
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
     if (W.grouped) {
         launch_group(idx, B, desc->K, desc->E, gemv_tokens(L), W.gw.g, s);
-        launch_ffn_grouped(L, desc->experts, W.gw, x, w, desc->shared_weight, B, desc->K, desc->E, W.xq, W.xst, y_out, s,
-                           g_timing[KID_GATEUP], g_timing[KID_DOWN]);
+        launch_ffn_grouped(L, desc->experts, W.gw, x, w, desc->shared_weight, B, desc->K, desc->E, W.xq, W.xst, false,
+                           y_out, s, g_timing[KID_GATEUP], g_timing[KID_DOWN]);
         return hip_status(fn);
     }
     launch_prep(desc->bits, x, B, desc->H, W.xq, W.xst, s);
@@ -287,10 +287,11 @@ static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, i
     float* w = w_out ? w_out : W.w;
     const Layout L = make_layout(d->bits, d->H, d->I);
     if (W.grouped) {
+        const TokenPrep P{x, d->H, W.gw.xhl, W.gw.xscale, gemv_tokens(L) > 1 ? W.xq : nullptr, W.xst};
         launch_route_batched(x, B, d->w_router, d->logit_bias, d->H, d->E, d->K, d->renormalize ? 1 : 0,
-                             W.gw.partial, idx, w, s, g_timing[KID_ROUTER]);
+                             W.gw.partial, idx, w, P, s, g_timing[KID_ROUTER]);
         launch_group(idx, B, d->K, d->E, gemv_tokens(L), W.gw.g, s);
-        launch_ffn_grouped(L, d->experts, W.gw, x, w, d->shared_weight, B, d->K, d->E, W.xq, W.xst, y_out, s,
+        launch_ffn_grouped(L, d->experts, W.gw, x, w, d->shared_weight, B, d->K, d->E, W.xq, W.xst, true, y_out, s,
                            g_timing[KID_GATEUP], g_timing[KID_DOWN]);
         return hip_status(fn);
     }
