@@ -681,14 +681,14 @@ constexpr int GUF_XQ = (64 * 9 + 64 * GUF_WAVES - 1) / (64 * GUF_WAVES);  // ope
 
 // One (row pass, expert slot) per wave, blocks in slot-major order: the shared
 // expert's blocks (slot 0) come first and need no routing; a routed block's wave
-// 0 selects the token's experts while the block stages the token's operand.
+// 0 selects its expert while the block stages the token's operand.
 // Many small waves per SIMD overlap one another's loads and dequant arithmetic.
 template <int BITS, int KS, bool ROUTE>
 __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
 {
     constexpr int K = KS - 1;
     __shared__ uint4 xs[64 * 9];  // the token's operand: 8 uint4 of pairs + stats per group (G <= 64)
-    __shared__ int s_id[KS];
+    __shared__ int s_id;          // a routed block's expert
     const Layout& L = A.L;
     const int b = blockIdx.y;
     const int G = L.Gh, LPR = lanes_per_row(G), RPP = 64 / LPR;
@@ -698,8 +698,12 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
     const int g = gv ? gl : G - 1;
     const int rows_pb = GUF_WAVES * RPP;
     const int bps = (L.I + rows_pb - 1) / rows_pb;  // blocks per slot
-    const int slot = blockIdx.x / bps;              // 0: shared expert, k + 1: routed expert k
-    const int r = ((blockIdx.x - slot * bps) * GUF_WAVES + wave) * RPP + sub;
+    // block groups: the shared expert's first, then the routed experts from the
+    // last rank to the first, so that the blocks dispatched last need the fewest
+    // selection rounds (a block selects only up to its own rank)
+    const int sg = blockIdx.x / bps;
+    const int slot = (sg > 0) ? KS - sg : 0;  // 0: shared expert, k + 1: routed expert of rank k
+    const int r = ((blockIdx.x - sg * bps) * GUF_WAVES + wave) * RPP + sub;
     const bool rv = r < L.I;
     const int rc = rv ? r : L.I - 1;
     const Masks M = load_masks();
@@ -746,21 +750,27 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
         if (t < nx) xs[t] = xv[q];
     }
     if (slot > 0 && wave == 0) {
-        float my_w = 0.f;
-        if (ROUTE) {
-            topk_select<K, FAST_NL>(lv, A.E, K, A.renorm, lane, my_id, my_w);
-            if (blockIdx.x == bps && lane < K) {  // the first routed block publishes the routing
-                A.idx[(long long)b * K + lane] = my_id;
-                A.w[(long long)b * K + lane] = my_w;
+        int id;
+        if (ROUTE && blockIdx.x != bps) {
+            id = __builtin_amdgcn_readfirstlane(topk_nth<K, FAST_NL>(lv, A.E, slot - 1, lane));
+        } else {
+            if (ROUTE) {  // the first routed block (rank K - 1) selects all K and publishes the routing
+                float my_w;
+                topk_select<K, FAST_NL>(lv, A.E, K, A.renorm, lane, my_id, my_w);
+                if (lane < K) {
+                    A.idx[(long long)b * K + lane] = my_id;
+                    A.w[(long long)b * K + lane] = my_w;
+                }
             }
+            id = __builtin_amdgcn_readlane(my_id, slot - 1);
         }
-        if (lane < K) s_id[lane] = my_id;
+        if (lane == 0) s_id = id;
     }
     __syncthreads();
     // 4. a routed block's loads (an invalid id reads expert 0 and yields NaN)
     bool bad = false;
     if (slot > 0) {
-        const int e = s_id[slot - 1];
+        const int e = s_id;
         bad = (e < 0 || e >= A.E);
         issue(bad ? 0 : e);
     }

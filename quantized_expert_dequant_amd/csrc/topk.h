@@ -91,14 +91,16 @@ __device__ inline void merge_top(double* a, const double* b)
         }
 }
 
-// Top-K of one token's E <= 64 * NL logits by one wave.  Lane k < K returns
-// the k-th expert (rank order) and its routing weight; every lane sees the
-// same selection.  Each lane first sorts its own candidates (it can give at
-// most P = min(KMAX, NL) of the K), then every round takes the wave maximum
-// of the lanes' heads and the lane that held it drops its head.  All loops have
-// compile-time trip counts, so the values stay in registers.
+// The rounds of the top-K of one token's E <= 64 * NL logits by one wave.  Each
+// lane first sorts its own candidates (it can give at most P = min(KMAX, NL) of
+// the K), then every round takes the wave maximum of the lanes' heads and the
+// lane that held it drops its head.  After `rounds` (<= KMAX) rounds every lane
+// has `top` (the largest value) and `last` (the value of the last round), and
+// lane k < rounds has `mine`, the value of round k.  All loops have compile-time
+// trip counts, so the values stay in registers.
 template <int KMAX, int NL>
-__device__ void topk_select(const double (&lv)[NL], int E, int K, int renorm, int lane, int& my_id, float& my_w)
+__device__ inline void topk_rounds(const double (&lv)[NL], int E, int rounds, int lane, double& mine, double& top,
+                                   double& last)
 {
     constexpr int P = KMAX < NL ? KMAX : NL;
     constexpr int PP = (P <= 1) ? 1 : (P <= 2) ? 2 : (P <= 4) ? 4 : (P <= 8) ? 8 : 16;  // power of two >= P
@@ -115,10 +117,12 @@ __device__ void topk_select(const double (&lv)[NL], int E, int K, int renorm, in
     for (int r = 0; r < NL; r += PP) sort_desc<PP>(v + r);
 #pragma unroll
     for (int r = PP; r < NL; r += PP) merge_top<PP>(v, v + r);
-    double mine = 0.0, top = 0.0;
+    mine = 0.0;
+    top = 0.0;
+    last = 0.0;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-        if (k >= K) break;
+        if (k >= rounds) break;
         const double best = group_reduce(v[0], OpSelMax(), 64);
         const bool win = __double_as_longlong(v[0]) == __double_as_longlong(best);  // values are unique
 #pragma unroll
@@ -126,7 +130,17 @@ __device__ void topk_select(const double (&lv)[NL], int E, int K, int renorm, in
         v[P - 1] = win ? SEL_NONE : v[P - 1];
         if (k == 0) top = best;
         if (lane == k) mine = best;
+        last = best;
     }
+}
+
+// Top-K of one token's logits by one wave.  Lane k < K returns the k-th expert
+// (rank order) and its routing weight; every lane sees the same selection.
+template <int KMAX, int NL>
+__device__ void topk_select(const double (&lv)[NL], int E, int K, int renorm, int lane, int& my_id, float& my_w)
+{
+    double mine, top, last;
+    topk_rounds<KMAX, NL>(lv, E, K, lane, mine, top, last);
     my_id = (lane < K) ? val_id(mine) : 0x7FFFFFFF;
     // softmax weights in fp32: exp of logit differences, renormalized over the K
     const float ew = (lane < K) ? __expf((float)(mine - top)) : 0.f;
@@ -141,6 +155,15 @@ __device__ void topk_select(const double (&lv)[NL], int E, int K, int renorm, in
         denom = wave_sum(part);
     }
     my_w = ew / denom;
+}
+
+// The expert of rank r < KMAX (0: the largest logit) alone: r + 1 rounds.
+template <int KMAX, int NL>
+__device__ inline int topk_nth(const double (&lv)[NL], int E, int r, int lane)
+{
+    double mine, top, last;
+    topk_rounds<KMAX, NL>(lv, E, r + 1, lane, mine, top, last);
+    return val_id(last);
 }
 
 }  // namespace moe
