@@ -422,7 +422,7 @@ def main():
             **({"distinct_layers": n_distinct} if stack else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "kernel": ("gate/up phase: k_grouped_mfma<0> + k_fixup + k_gemv_gateup" if B > 1
+                     "kernel": ("gate/up phase: k_grouped_mfma<0> + k_gemv_gateup" if B > 1
                                 else "k_gateup_fast"),
                      "bytes_per_launch": round(gu_bytes), "avg_us": round(gu_us, 3)},
         "expert_weight_gbps": round(expert_gbps, 1),
