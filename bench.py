@@ -413,7 +413,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4" if c["bits"] == 4 else "u2",
+        "dtype": "f16",  # fp16 x fp16 products (codes turned exactly into fp16), fp32 accumulation
         "data": "synthetic",
         "config": {"workload": "%s: H=%d I=%d E=%d+1 shared K=%d %d-bit group 64 bf16 scale+bias, B=%d%s" % (
             args.workload, H, c["I"], c["E"], c["K"], c["bits"], B,
