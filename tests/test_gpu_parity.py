@@ -260,6 +260,25 @@ def test_ragged_shapes_and_batch():
             assert rel_err(y[b], y_ref[b]) <= TOL
 
 
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("K", [1, 2, 6, 8])
+def test_single_token_every_fused_k(K, bits):
+    """Every K the fused single-token kernels are built for besides 4 (1 + K expert slots of
+    2, 3, 7, 9): each routed block selects up to its own rank, the rank K - 1 block publishes
+    idx and w; routing bit-exact and outputs within the bar, over several tokens."""
+    cfg = dict(H=512, I=128, E=64, K=K, bits=bits, zipf=None)
+    seed = 1300 + 10 * K + bits
+    L = build_layer(cfg, seed)
+    for t in range(3):
+        x = synth.tokens(seed, t, 1, cfg["H"])
+        y, idx, w = _decode(L, x)
+        y_ref, idx_ref, w_ref, margin = oracle_layer(cfg, seed, 0, x)
+        assert np.all(margin > 1e-9)
+        np.testing.assert_array_equal(idx, idx_ref)
+        np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
+        assert rel_err(y[0], y_ref[0]) <= TOL, "token %d" % t
+
 def test_rmsnorm_matches_oracle():
     y = synth.tokens(5, 0, 3, 4096) * 7.0
     x = torch.empty((3, 4096), dtype=torch.float32, device=DEV)
