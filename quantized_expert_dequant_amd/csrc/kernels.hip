@@ -743,7 +743,7 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
     // 2. the shared expert needs no routing: its loads go out now
     if (slot == 0) issue(A.E);
     __builtin_amdgcn_sched_barrier(0);
-    // 3. stage the token's operand; wave 0 of a routed block selects the experts meanwhile
+    // 3. stage the token's operand; wave 0 of a routed block selects its expert meanwhile
 #pragma unroll
     for (int q = 0; q < GUF_XQ; ++q) {
         const int t = threadIdx.x + 64 * GUF_WAVES * q;
