@@ -166,9 +166,15 @@ def kernel_source_hash(workload):
     return h.hexdigest()[:16]
 
 
+# the stack's layers have the layer workload's shape and run the same gate/up kernel,
+# so its per-launch traffic is the layer workload's
+PMC_RECORD = {"stack": "layer"}
+
+
 def traffic_from_profile(workload, launches_per_step):
     """HBM bytes per launch of the dominant kernel from committed rocprofv3 PMC results,
     only while the kernel sources still match the ones the counters were taken on."""
+    workload = PMC_RECORD.get(workload, workload)
     p = os.path.join(ROOT, "profiles", "pmc_gateup_%s.json" % workload)
     if not os.path.exists(p):
         return None
