@@ -279,6 +279,47 @@ def test_single_token_every_fused_k(K, bits):
         np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
         assert rel_err(y[0], y_ref[0]) <= TOL, "token %d" % t
 
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_layer_raw_softmax_and_shared_weight(B):
+    """renormalize = 0 (the K weights are the softmax over all E, not renormalized) and a shared
+    expert weight of 0.5, through the fused single-token kernels (B = 1) and the batched top-K and
+    combine (B = 3); routing bit-exact, weights to 1e-6, outputs within the bar."""
+    cfg = dict(H=512, I=128, E=64, K=4, bits=4, zipf=None)
+    seed = 1410 + B
+    src = lambda first, n: synth.experts(seed, 0, first, n, cfg["bits"], cfg["H"], cfg["I"])
+    slab = upload_experts(src, cfg["E"] + 1, cfg["bits"], cfg["H"], cfg["I"], device=DEV)
+    Wr = synth.router(seed, 0, cfg["E"], cfg["H"])
+    L = DeviceLayer(cfg["H"], cfg["I"], cfg["E"], cfg["K"], cfg["bits"], slab, _t(Wr), None, shared_weight=0.5,
+                    renormalize=False)
+    x = synth.tokens(seed, 0, B, cfg["H"])
+    y, idx, w = _decode(L, x)
+    experts = {e: synth.experts(seed, 0, e, 1, cfg["bits"], cfg["H"], cfg["I"]) for e in range(cfg["E"] + 1)}
+    y_ref, idx_ref, w_ref, margin = oracle.layer_decode(cfg["bits"], cfg["H"], cfg["I"], cfg["E"], cfg["K"], x, Wr,
+                                                        experts, renormalize=False, shared_weight=0.5)
+    assert np.all(margin > 1e-9)
+    np.testing.assert_array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
+    assert np.all(w.sum(axis=1) < 1.0)  # raw probabilities of K of 64 experts
+    for b in range(B):
+        assert rel_err(y[b], y_ref[b]) <= TOL, "token %d" % b
+
+
+def test_route_topk_most_experts_and_largest_k():
+    """The route-only entry point at the library's maxima: E = 1024, K = 32, B = 3, with a logit
+    bias; idx bit-exact and weights against the oracle."""
+    E, H, K, B = moe.MOE_MAX_E, 512, moe.MOE_MAX_K, 3
+    Wr = synth.router(1501, 0, E, H)
+    prior = synth.zipf_bias(E, 1.1)
+    x = synth.tokens(1501, 0, B, H)
+    idx, w = _gpu_route(x, Wr, prior, K)
+    lg = oracle.router_logits(x, Wr, prior)
+    for b in range(B):
+        ref_idx, ref_w, margin = oracle.topk(lg[b], K)
+        assert margin > 1e-9
+        np.testing.assert_array_equal(idx[b], ref_idx)
+        np.testing.assert_allclose(w[b], ref_w, rtol=W_RTOL)
+
 def test_rmsnorm_matches_oracle():
     y = synth.tokens(5, 0, 3, 4096) * 7.0
     x = torch.empty((3, 4096), dtype=torch.float32, device=DEV)
