@@ -4,12 +4,18 @@
 // byte-for-byte the same size as the canonical expert:
 //   [gu_codes]  I row pairs, each [gate row codes (H*bits/8 B) | up row codes (H*bits/8 B)]
 //   [gu_sb]     I x G_h entries of 8 B: bf16 (gate scale, gate bias, up scale, up bias)
-//   [d_codes]   H rows of I*bits/8 B
+//   [d_codes]   H rows of I*bits/8 B, in panels of 16 rows (d_chunk_off below)
 //   [d_sb]      H x G_i entries of 4 B: bf16 (scale, bias)
 // Inside a row the codes of group g are split into 16-byte chunks; chunk j of
 // group g sits at chunk position j*G + g (4-bit: 2 chunks per group, 2-bit: 1),
 // so that 64 lanes working on 64 consecutive groups issue fully contiguous
-// 16-byte loads.  Within a chunk the codes keep the canonical order (low bits =
+// 16-byte loads.  A gate/up row's chunks are contiguous.  The down rows are
+// stored in panels of 16 rows: each row's chunks are cut into units of 4 chunks
+// (64 bytes), and unit u of the panel's 16 rows is stored as 16 consecutive runs,
+// row 0 first, so that 64 bytes of 16 consecutive rows (a step of the grouped
+// MFMA kernel) are one contiguous kilobyte and 4 consecutive rows (a wave of the
+// single-token down kernel) are contiguous per unit.  A row shorter than 64
+// bytes leaves the panel row-major.  Within a chunk the codes keep the canonical order (low bits =
 // lower column), which puts columns (c, c+4) (4-bit) or (c, c+8) (2-bit) in the
 // two 16-bit halves of a dword: masking one field of each half and OR-ing in the
 // fp16 pattern of 1024 turns two codes into the fp16 pair (1024 + t*q_a, 1024 + t*q_b)
@@ -56,6 +62,16 @@ __host__ __device__ inline Layout make_layout(int bits, int H, int I)
     L.off_d_sb = L.off_d_codes + (long long)H * L.ib;
     L.record = L.off_d_sb + 4LL * H * L.Gi;
     return L;
+}
+
+// Byte offset, from the start of d_codes, of chunk position P of down row r:
+// panel r / 16, unit P / 4 (the units before it are full, 16 x 64 bytes), then the
+// row's run in the unit (64 bytes, or what is left of a shorter row), then the chunk.
+__host__ __device__ inline long long d_chunk_off(const Layout& L, int r, int P)
+{
+    const int u = P >> 2;
+    const long long w = (L.ib - 64LL * u) < 64 ? (L.ib - 64LL * u) : 64;
+    return (long long)(r >> 4) * 16 * L.ib + (long long)u * 1024 + (long long)(r & 15) * w + (P & 3) * 16;
 }
 
 // lanes cooperating on one row: G rounded up to a power of two, at most 64

@@ -527,7 +527,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         // operands are each far below 4 GiB)
         const uint8_t* rec = A.slab + (long long)e * L.record;
         const int row = min(tile * GM_ROWS + wave * 16 + i, NR - 1);
-        const uint32_t row_off = (MODE == MODE_GATEUP) ? (uint32_t)(row * 2 * L.hb) : (uint32_t)(L.off_d_codes + row * L.ib);
+        const uint32_t row_off = (uint32_t)(row * 2 * L.hb);  // gate/up; down chunks go through d_chunk_off
         const uint32_t sb_off = (MODE == MODE_GATEUP) ? (uint32_t)(L.off_gu_sb + (long long)row * G * 8)
                                                       : (uint32_t)(L.off_d_sb + (long long)row * G * 4);
         const uint32_t up_off = (uint32_t)L.hb;
@@ -577,7 +577,8 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         };
         auto weight_load = [&](int ks, WRegs& W) {
             const int P = min(4 * ks + kk, 2 * G - 1), g = P >= G ? P - G : P;
-            const uint32_t co = row_off + (uint32_t)P * 16u;
+            const uint32_t co = (MODE == MODE_GATEUP) ? row_off + (uint32_t)P * 16u
+                                                      : (uint32_t)(L.off_d_codes + d_chunk_off(L, row, P));
             W.c[0] = *reinterpret_cast<const u4*>(rec + co);
             if (MODE == MODE_GATEUP) {
                 W.c[NM - 1] = *reinterpret_cast<const u4*>(rec + (co + up_off));
@@ -989,9 +990,9 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_down(GroupedArgs A, cons
         const int v = it / rb;
         const int r = min((it - v * rb) * rows_pi + wave * RPP + sub, L.H - 1);
         const uint8_t* rec = A.slab + (long long)mv(0, v) * L.record;
-        const uint8_t* base = rec + L.off_d_codes + (long long)r * L.ib;
-        w.c[0] = *reinterpret_cast<const uint4*>(base + g * 16);
-        w.c[1] = *reinterpret_cast<const uint4*>(base + (G + g) * 16);
+        const uint8_t* base = rec + L.off_d_codes;
+        w.c[0] = *reinterpret_cast<const uint4*>(base + d_chunk_off(L, r, g));
+        w.c[1] = *reinterpret_cast<const uint4*>(base + d_chunk_off(L, r, G + g));
         w.sb = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)r * G + g) * 4);
     };
     int v_prev = -1;

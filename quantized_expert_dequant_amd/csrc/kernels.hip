@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_pack(Layout L, const uint8_t* __restric
             const int pos = (int)(c - r * per_row);
             const int half = pos / L.Gi, g = pos - half * L.Gi;
             const uint8_t* src = down + j * ((long long)L.H * L.ib) + r * L.ib + (long long)(g * cpg + half) * 16;
-            *reinterpret_cast<uint4*>(rec + L.off_d_codes + r * L.ib + (long long)pos * 16) =
+            *reinterpret_cast<uint4*>(rec + L.off_d_codes + d_chunk_off(L, (int)r, pos)) =
                 *reinterpret_cast<const uint4*>(src);
         } else {
             const long long i = t - n_gu_chunks - n_gu_sb - n_d_chunks;  // r * Gi + g
@@ -98,12 +98,17 @@ void launch_pack(const Layout& L, int n, const uint8_t* gate, const uint8_t* up,
 // ----------------------------------------------------------------------------
 // dequant of one packed record (layout check)
 // ----------------------------------------------------------------------------
-__device__ inline int packed_code(const uint8_t* row, int bits, int G, int c)
+// chunk position of column c of a row with G groups, and c's place in the chunk
+__device__ inline int packed_pos(int bits, int G, int c, int& k)
 {
     const int g = c >> 6, cc = c & 63;
     const int per_chunk = 128 / bits;  // codes per 16-byte chunk
-    const int half = cc / per_chunk, k = cc - half * per_chunk;
-    const uint8_t* chunk = row + (long long)(half * G + g) * 16;
+    const int half = cc / per_chunk;
+    k = cc - half * per_chunk;
+    return half * G + g;
+}
+__device__ inline int chunk_code(const uint8_t* chunk, int bits, int k)
+{
     if (bits == 4) return (chunk[k >> 1] >> ((k & 1) * 4)) & 15;
     return (chunk[k >> 2] >> ((k & 3) * 2)) & 3;
 }
@@ -122,14 +127,18 @@ __global__ __launch_bounds__(256) void k_dequant(Layout L, const uint8_t* __rest
             const long long i = t - m * n_gu;
             const int r = (int)(i / L.H), c = (int)(i - (long long)r * L.H);
             const uint8_t* row = rec + (long long)r * 2 * L.hb + m * L.hb;
-            q = packed_code(row, L.bits, L.Gh, c);
+            int k;
+            const int P = packed_pos(L.bits, L.Gh, c, k);
+            q = chunk_code(row + (long long)P * 16, L.bits, k);
             const uint16_t* sb = reinterpret_cast<const uint16_t*>(rec + L.off_gu_sb + ((long long)r * L.Gh + (c >> 6)) * 8);
             s = __uint_as_float((uint32_t)sb[2 * m] << 16);
             b = __uint_as_float((uint32_t)sb[2 * m + 1] << 16);
         } else {
             const long long i = t - 2 * n_gu;
             const int r = (int)(i / L.I), c = (int)(i - (long long)r * L.I);
-            q = packed_code(rec + L.off_d_codes + (long long)r * L.ib, L.bits, L.Gi, c);
+            int k;
+            const int P = packed_pos(L.bits, L.Gi, c, k);
+            q = chunk_code(rec + L.off_d_codes + d_chunk_off(L, r, P), L.bits, k);
             const uint16_t* sb = reinterpret_cast<const uint16_t*>(rec + L.off_d_sb + ((long long)r * L.Gi + (c >> 6)) * 4);
             s = __uint_as_float((uint32_t)sb[0] << 16);
             b = __uint_as_float((uint32_t)sb[1] << 16);
@@ -616,9 +625,9 @@ __global__ __launch_bounds__(256) void k_down(FfnArgs A)
                 for (int p = 0; p < DN_RPW; ++p) {
                     const int r = row0 + p * RPP;
                     if (rec[s] && gv && r < L.H) {
-                        const uint8_t* base = rec[s] + L.off_d_codes + (long long)r * L.ib;
-                        c0[s][p] = ld16(base + g * 16);
-                        if (BITS == 4) c1[s][p] = ld16(base + (G + g) * 16);
+                        const uint8_t* base = rec[s] + L.off_d_codes;
+                        c0[s][p] = ld16(base + d_chunk_off(L, r, g));
+                        if (BITS == 4) c1[s][p] = ld16(base + d_chunk_off(L, r, G + g));
                         sbv[s][p] = *reinterpret_cast<const uint32_t*>(rec[s] + L.off_d_sb + ((long long)r * G + g) * 4);
                     }
                 }
@@ -844,11 +853,11 @@ __global__ __launch_bounds__(64 * DNF_WAVES) void k_down_fast(FfnArgs A)
     // 3. the shared expert's rows need no routing: they go out before the routing returns
     uint4 c0[KS], c1[KS];
     uint32_t sbv[KS];
+    const long long o0 = L.off_d_codes + d_chunk_off(L, rc, g), o1 = L.off_d_codes + d_chunk_off(L, rc, G + g);
     auto issue = [&](int k, int e) {
         const uint8_t* rec = A.slab + (long long)e * L.record;
-        const uint8_t* base = rec + L.off_d_codes + (long long)rc * L.ib;
-        c0[k] = ld16(base + g * 16);
-        if (BITS == 4) c1[k] = ld16(base + (G + g) * 16);
+        c0[k] = ld16(rec + o0);
+        if (BITS == 4) c1[k] = ld16(rec + o1);
         sbv[k] = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)rc * G + g) * 4);
     };
     issue(K, A.E);
