@@ -215,6 +215,14 @@ __device__ inline double dot4d(float4 w, float4 x, double acc)
     return fma((double)w.w, (double)x.w, acc);
 }
 
+// router: waves (experts or prep groups) per block.  A token as given: one, so the
+// 512 logit waves of a layer land on every CU instead of on half of them (measured
+// at H=4096, E=512: step 18.05 -> 17.47 us; two per block 17.6-17.9).  A token
+// renormalized on the fly (stacked layers): four (60-layer step 1088 us, against
+// 1126 with one and 1130 with two).
+constexpr int RT_WAVES = 1;
+constexpr int RT_NORM_WAVES = 4;
+
 template <int BITS>
 // Blocks [0, rblocks) compute the logits (one wave per expert); blocks from
 // rblocks on prepare the token operand at the same time (one wave per group).
@@ -227,12 +235,13 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
     // on the fly, x = y / sqrt(mean(y^2) + eps), exactly as k_rmsnorm would
     const bool norm = norm_eps >= 0.f;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + wave;
+    const int rw = (int)(blockDim.x >> 6);  // waves per block
+    const int e = blockIdx.x * rw + wave;
     const int n4 = H >> 2;
     const float4* x4 = reinterpret_cast<const float4*>(x);
     if ((int)blockIdx.x >= rblocks) {
-        const int Gh = H / 64, nw = ((int)gridDim.x - rblocks) * 4;
-        for (int i = ((int)blockIdx.x - rblocks) * 4 + wave; i < prepB * Gh; i += nw) {
+        const int Gh = H / 64, nw = ((int)gridDim.x - rblocks) * rw;
+        for (int i = ((int)blockIdx.x - rblocks) * rw + wave; i < prepB * Gh; i += nw) {
             const int vec = i / Gh, g = i - vec * Gh;
             const float inv = norm ? row_inv_rms(x4 + (long long)vec * n4, n4, norm_eps, lane) : 1.f;
             prep_group<BITS>(x, Gh, vec, g, lane, xq, xst, inv);
@@ -299,16 +308,17 @@ __global__ __launch_bounds__(256) void k_router(const float* __restrict__ x, int
 void launch_router(int bits, const float* x, int B, const float* W, const float* bias, int H, int E, double* logits,
                    uint4* xq, float4* xst, hipStream_t s, Timing t, float norm_eps)
 {
-    const int rblocks = (E + 3) / 4;
+    const int rw = norm_eps >= 0.f ? RT_NORM_WAVES : RT_WAVES;
+    const int rblocks = (E + rw - 1) / rw;
     const int prepB = xq ? B : 0;
-    int prep_blocks = (prepB * (H / 64) + 3) / 4;
+    int prep_blocks = (prepB * (H / 64) + rw - 1) / rw;
     if (prep_blocks > 1024) prep_blocks = 1024;
     const int blocks = rblocks + prep_blocks;
     if (bits == 2)
-        hipExtLaunchKernelGGL(k_router<2>, dim3(blocks), dim3(256), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
+        hipExtLaunchKernelGGL(k_router<2>, dim3(blocks), dim3(64 * rw), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
                               H, E, logits, xq, xst, norm_eps, rblocks);
     else
-        hipExtLaunchKernelGGL(k_router<4>, dim3(blocks), dim3(256), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
+        hipExtLaunchKernelGGL(k_router<4>, dim3(blocks), dim3(64 * rw), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
                               H, E, logits, xq, xst, norm_eps, rblocks);
 }
 
