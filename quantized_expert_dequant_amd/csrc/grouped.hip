@@ -378,35 +378,45 @@ __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x
 
 // ----------------------------------------------------------------------------
 // Dword w of a 16-byte chunk of a 4-bit row (8 codes) -> the fp16 MFMA operand
-// of its 8 weights s*q + b in the order (c0, c4, c1, c5, c2, c6, c3, c7).
+// s * (q - 8) of its 8 weights in the order (c0, c4, c1, c5, c2, c6, c3, c7).
 // OR-ing the fp16 pattern of 1024 into the masked code pair (c_t, c_t+4) gives
 // (1024 + q_a, 1024 + q_b) for t = 0, 2 (mask 0x000F000F on w, on w >> 8) and
-// (1024 + 16 q_a, 1024 + 16 q_b) for t = 1, 3 (mask 0x00F000F0): subtracting 1024,
-// or scaling by 1/16 and subtracting 64, gives q exactly; one fused multiply-add
-// gives s*q + b, rounded once to fp16.
+// (1024 + 16 q_a, 1024 + 16 q_b) for t = 1, 3 (mask 0x00F000F0): subtracting 1032,
+// or scaling by 1/16 and subtracting 72, gives q - 8 exactly.  |q - 8| <= 8 has at
+// most 3 significant bits and a bf16 scale at most 8, so the product fits fp16's
+// 11 and is exact (for 2^-14 <= |s| < 2^13): the weights s*q + b = s*(q - 8) +
+// (b + 8 s) reach the MFMA unrounded, the group's b + 8 s being added apart, times
+// the token operand's chunk sum.
 // ----------------------------------------------------------------------------
-__device__ inline h8 dequant_dword_q4(uint32_t w, h2 s2, h2 b2, const Masks& M)
+__device__ inline h8 dequant_dword_q4(uint32_t w, h2 s2, const Masks& M)
 {
-    const h2 k1024 = {(_Float16)1024.f, (_Float16)1024.f};
-    const h2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f}, k64 = {(_Float16)-64.f, (_Float16)-64.f};
+    const h2 k1032 = {(_Float16)1032.f, (_Float16)1032.f};
+    const h2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f}, k72 = {(_Float16)-72.f, (_Float16)-72.f};
     const uint32_t w8 = w >> 8;
-    const h2 q0 = __builtin_bit_cast(h2, (w & M.m4a) | M.magic) - k1024;
-    const h2 q1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w & M.m4b) | M.magic), k16, k64);
-    const h2 q2 = __builtin_bit_cast(h2, (w8 & M.m4a) | M.magic) - k1024;
-    const h2 q3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w8 & M.m4b) | M.magic), k16, k64);
-    const h2 p0 = __builtin_elementwise_fma(q0, s2, b2), p1 = __builtin_elementwise_fma(q1, s2, b2);
-    const h2 p2 = __builtin_elementwise_fma(q2, s2, b2), p3 = __builtin_elementwise_fma(q3, s2, b2);
+    const h2 q0 = __builtin_bit_cast(h2, (w & M.m4a) | M.magic) - k1032;
+    const h2 q1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w & M.m4b) | M.magic), k16, k72);
+    const h2 q2 = __builtin_bit_cast(h2, (w8 & M.m4a) | M.magic) - k1032;
+    const h2 q3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (w8 & M.m4b) | M.magic), k16, k72);
+    const h2 p0 = q0 * s2, p1 = q1 * s2, p2 = q2 * s2, p3 = q3 * s2;
     return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
+
+// The chunk term (b + 8 s) * sum: one MFMA per tile and step whose K slots of a
+// lane's chunk hold (b', b', s', s') against (X_hi, X_lo, X_hi, X_lo), with
+// b' = 2^5 b and s' = 2^5 * 8 s (exact in fp16 for |b| < 2^11 and |s| < 2^8) and
+// X = 2^-5 * the token operand's sum over the chunk's 32 columns (below 2^15 for
+// operands below 2^15), split into fp16 hi + lo.
+constexpr float GM_CT = 32.f;
 
 // ----------------------------------------------------------------------------
 // Grouped dequant-GEMM.  A block of 8 waves owns a tile of 128 rows of one
 // group's expert (16 rows per wave) and multiplies it by the group's tokens
 // (at most 32: two 16-token MFMA tiles).  K advances 128 columns (4 chunks of
 // 16 bytes) per step: lane (i, kk) of a wave holds chunk 4*step + kk of its
-// row i, dequantizes it to fp16 (s*q + b), and MFMA d (16 x 16 x 32) takes
-// dword d of the four lanes' chunks against the token operands of the same 32
-// columns, staged in LDS as [tt][kk][d][hl][token].
+// row i, turns it into the exact fp16 operand s*(q - 8), and MFMA d (16 x 16 x
+// 32) takes dword d of the four lanes' chunks against the token operands of the
+// same 32 columns, staged in LDS as [tt][kk][token][d]; one more MFMA per step
+// adds (b + 8 s) times each chunk's token-operand sum, staged beside them.
 //
 // Work split: the units (group, tile, K chunk) in that order are cut into
 // gridDim.x equal contiguous ranges, one per block.  Gate/up tiles are whole
@@ -420,7 +430,8 @@ __device__ inline h8 dequant_dword_q4(uint32_t w, h2 s2, h2 b2, const Masks& M)
 // LDS hand-over waits only for the token operands and the weight loads stay in
 // flight across the barrier.
 //
-// MODE_GATEUP: rows are gate/up row pairs; token operand x as fp16 hi + lo;
+// MODE_GATEUP: rows are gate/up row pairs; token operand x as fp16 hi + lo (the
+//   codes multiply hi, the chunk sums take hi + lo);
 //   writes h = silu(g) * u of each entry in fp32 in the pair-layout order
 //   hb[entry][dword d < 8][G_i][8].
 // MODE_DOWN: rows are down rows (one K chunk per tile); token operand h scaled
@@ -461,11 +472,18 @@ template <int MODE>
 struct GmShape {
     static constexpr int NM = (MODE == MODE_GATEUP) ? 2 : 1;  // matrices per row: gate + up | down
     static constexpr int HL = (MODE == MODE_GATEUP) ? 2 : 1;  // token operand parts: hi + lo | h
+    // token operand parts the codes are multiplied with: x's hi alone.  The codes
+    // q - 8 average about zero, so x's rounding adds no error of one sign to every
+    // row; the part of each weight that does not average out, b + 8 s, meets the
+    // chunk sums of hi + lo.
+    static constexpr int HM = 1;
     static constexpr int RING = (MODE == MODE_GATEUP) ? 3 : 4;  // weight ring slots (loads run RING-1 steps ahead)
     static constexpr int NSTG = GM_TT * 4 * 4 * HL * 16;     // 16-byte elements staged per step
     static constexpr int PER_T = NSTG / GM_THREADS;
-    // LDS of a stage: rows (tt, k2, token) of 8 (gate/up: hi, lo) or 4 (down) elements,
-    // padded to 9 or 5 so that the MFMA's reads of 16 tokens are free of bank conflicts
+    // LDS of a stage: rows (tt, k2, token) of 9 (gate/up) or 5 (down) elements: the 4
+    // dwords' operands the MFMAs read (gate/up: x's hi; slots 4-7 stay unused), then
+    // the chunk sum in the last slot; the odd pitch keeps the reads of 16 tokens free
+    // of bank conflicts
     static constexpr int NLDS = (MODE == MODE_GATEUP) ? GM_TT * 4 * 16 * 9 : GM_TT * 4 * 16 * 5;
 };
 
@@ -495,7 +513,7 @@ template <int MODE>
 __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void k_grouped_mfma(GroupedArgs A)
 {
     using S = GmShape<MODE>;
-    constexpr int NM = S::NM, HL = S::HL, NSTG = S::NSTG, PER_T = S::PER_T, RING = S::RING;
+    constexpr int NM = S::NM, HL = S::HL, HM = S::HM, NSTG = S::NSTG, PER_T = S::PER_T, RING = S::RING;
     __shared__ u4 bs[2][S::NLDS];
 
     const Layout& L = A.L;
@@ -540,7 +558,10 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         // (tt*4 + k2)*16 + j.  src[q] is the fixed part of the source index (token or entry
         // row, hl, d), the step adds the chunk.  Chunks past the row end (2G not a
         // multiple of 4) read a valid chunk and get zero weights.
-        int src[PER_T], k2q[PER_T], dst[PER_T];
+        // The row's last slot (the padding) takes the chunk sum of the row's token
+        // operand for the bias MFMA; the 8 (gate/up: hi, lo x 4 dwords) or 4 (down)
+        // consecutive threads of a row add their elements and the first writes it.
+        int src[PER_T], k2q[PER_T], dst[PER_T], sdst[PER_T];
 #pragma unroll
         for (int q = 0; q < PER_T; ++q) {
             const int t = threadIdx.x + GM_THREADS * q;
@@ -550,12 +571,14 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                 k2q[q] = k2;
                 src[q] = A.ent_token[ent0 + m] * G * 16 + hl * 4 + d;
                 dst[q] = ((tt * 4 + k2) * 16 + j) * 9 + hl * 4 + d;
+                sdst[q] = ((tt * 4 + k2) * 16 + j) * 9 + 8;
             } else {
                 const int d = t & 3, k2 = (t >> 2) & 3, j = (t >> 4) & 15, tt = t >> 8;
                 const int m = min(tt * 16 + j, n - 1);
                 k2q[q] = k2;
                 src[q] = (ent0 + m) * 8 * G + d;
                 dst[q] = ((tt * 4 + k2) * 16 + j) * 5 + d;
+                sdst[q] = ((tt * 4 + k2) * 16 + j) * 5 + 4;
             }
         }
         struct Stage {
@@ -572,8 +595,24 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             }
         };
         auto stage_store = [&](int buf, const Stage& S) {
+            const bool mul_part = HM == HL || ((threadIdx.x >> 2) & 1) == 0;  // an element the MFMAs read
 #pragma unroll
-            for (int q = 0; q < PER_T; ++q) bs[buf][dst[q]] = S.v[q];
+            for (int q = 0; q < PER_T; ++q)
+                if (mul_part) bs[buf][dst[q]] = S.v[q];
+            constexpr int RL = (MODE == MODE_GATEUP) ? 8 : 4;  // threads per LDS row
+            const uint32_t one2 = 0x3C003C00u;                 // fp16 (1, 1)
+#pragma unroll
+            for (int q = 0; q < PER_T; ++q) {
+                float sum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum = dot2(S.v[q][e], one2, sum);
+                sum = group_reduce(sum, OpAdd(), RL);
+                if ((threadIdx.x & (RL - 1)) == 0) {
+                    const float v = sum * (1.f / GM_CT);
+                    const _Float16 vh = (_Float16)v, vl = (_Float16)(v - (float)vh);
+                    bs[buf][sdst[q]] = u4{__builtin_bit_cast(uint32_t, h2{vh, vl}), 0u, 0u, 0u};
+                }
+            }
         };
         auto weight_load = [&](int ks, WRegs& W) {
             const int P = min(4 * ks + kk, 2 * G - 1), g = P >= G ? P - G : P;
@@ -619,22 +658,35 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             __builtin_amdgcn_sched_barrier(0);
             const u4* buf = bs[(ks - k_begin) & 1];
             const bool pad = 4 * ks + kk >= 2 * G;  // chunk past the row end: zero weights
-            h2 s2[NM], b2[NM];
+            h2 s2[NM];
+            h8 cw[NM];  // the chunk term's weight operand
 #pragma unroll
             for (int mm = 0; mm < NM; ++mm) {
                 const uint32_t sb = pad ? 0u : Wc.sb[mm];
-                const _Float16 sh = (_Float16)bf16_lo(sb), bh = (_Float16)bf16_hi(sb);
+                const float s = bf16_lo(sb);
+                const _Float16 sh = (_Float16)s, bh = (_Float16)(bf16_hi(sb) * GM_CT), s8 = (_Float16)(s * (8.f * GM_CT));
                 s2[mm] = h2{sh, sh};
-                b2[mm] = h2{bh, bh};
+                cw[mm] = h8{bh, bh, s8, s8, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+            }
+            // (b + 8 s) of each lane's chunk times the token operand's chunk sum
+#pragma unroll
+            for (int tt = 0; tt < GM_TT; ++tt) {
+                if (tt < ntt) {
+                    const int r = (tt * 4 + kk) * 16 + i;
+                    const uint32_t xsum = (MODE == MODE_GATEUP) ? buf[r * 9 + 8].x : buf[r * 5 + 4].x;
+                    const h8 bx = __builtin_bit_cast(h8, u4{xsum, xsum, 0u, 0u});
+#pragma unroll
+                    for (int mm = 0; mm < NM; ++mm) acc[mm][tt] = mfma16(cw[mm], bx, acc[mm][tt]);
+                }
             }
             // dword-major: the token operands of dword d + 1 are read from LDS while
             // the MFMAs of dword d run, and only one dword's weights are live
-            h8 bv[2][GM_TT][HL];
-            auto bread = [&](int d, h8 (&b)[GM_TT][HL]) {
+            h8 bv[2][GM_TT][HM];
+            auto bread = [&](int d, h8 (&b)[GM_TT][HM]) {
 #pragma unroll
                 for (int tt = 0; tt < GM_TT; ++tt)
 #pragma unroll
-                    for (int hl = 0; hl < HL; ++hl)
+                    for (int hl = 0; hl < HM; ++hl)
                         if (tt < ntt)
                             b[tt][hl] = __builtin_bit_cast(
                                 h8, buf[(MODE == MODE_GATEUP) ? ((tt * 4 + kk) * 16 + i) * 9 + hl * 4 + d
@@ -646,12 +698,12 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                 if (d + 1 < 4) bread(d + 1, bv[(d + 1) & 1]);
                 h8 a[NM];
 #pragma unroll
-                for (int mm = 0; mm < NM; ++mm) a[mm] = dequant_dword_q4(Wc.c[mm][d], s2[mm], b2[mm], M);
+                for (int mm = 0; mm < NM; ++mm) a[mm] = dequant_dword_q4(Wc.c[mm][d], s2[mm], M);
 #pragma unroll
                 for (int tt = 0; tt < GM_TT; ++tt) {
                     if (tt < ntt) {
 #pragma unroll
-                        for (int hl = 0; hl < HL; ++hl)
+                        for (int hl = 0; hl < HM; ++hl)
 #pragma unroll
                             for (int mm = 0; mm < NM; ++mm) acc[mm][tt] = mfma16(a[mm], bv[d & 1][tt][hl], acc[mm][tt]);
                     }
