@@ -141,8 +141,8 @@ int moe_route_topk(const float* x, int B, const float* w_router, const float* lo
  * _q4 requires desc->bits == 4, _q2 requires desc->bits == 2.
  * With 4-bit codes and B > 1 the tokens are grouped by expert (as
  * moe_group_tokens) so each active expert's weights are read once per call and
- * multiplied against all of its tokens on the matrix cores; 2-bit batches run
- * token by token.
+ * multiplied against all of its tokens on the matrix cores (value range as
+ * for moe_layer_decode); 2-bit batches run token by token.
  */
 int moe_expert_ffn_q4(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx,
                       const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
@@ -153,6 +153,11 @@ int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const i
  * Whole layer: route, then expert FFNs and combine, as above.
  *   x: fp32 [B][H]; y_out: fp32 [B][H]; idx_out: int32 [B][K] or NULL;
  *   w_out: fp32 [B][K] or NULL.
+ * Value range: with 4-bit codes and B >= 2 the experts that several tokens
+ * share run on the matrix cores, which take each group's scale s as fp16 and
+ * (b + 8 s) through fp16 operands 2^5 b and 2^8 s: there |s| < 256 and
+ * |b| < 2048 per group (larger values overflow to inf in y).  The other paths
+ * apply scale and bias in fp32.
  */
 int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y_out,
                      int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream);
