@@ -219,3 +219,42 @@ def test_batched_expert_with_more_than_32_tokens(layers):
     for b in range(B):
         ref = ffn(E, x[b]) + sum(float(w[b, k]) * ffn(int(idx[b, k]), x[b]) for k in range(K))
         assert rel_err(yh[b], ref) <= TOL, "token %d" % b
+
+
+def _bf16_times_pow2(a, k):
+    """bf16 bit patterns times 2^k, exactly (exponent shift of every nonzero normal value)."""
+    v = a.astype(np.int32)
+    nz = (v & 0x7F80) != 0
+    v[nz] += k << 7
+    return v.astype(np.uint16)
+
+
+@pytest.mark.parametrize("B", [1, 16])
+def test_large_scales_and_biases(B):
+    """Scales and biases 2^10 times the usual (|s| up to about 90, |b| up to about 50): the
+    matrix-core path takes s as fp16 and b + 8 s through fp16 operands 2^5 b and 2^8 s, which
+    must stay finite and exact inside the range the header states (|s| < 256, |b| < 2048).
+    B = 16 runs the grouped path with MFMA groups, B = 1 the single-token kernels."""
+    H, I, E, K, bits, seed = 512, 128, 16, 4, 4, 1501
+
+    def src(first, n):
+        c = synth.experts(seed, 0, first, n, bits, H, I)
+        c.scales[...] = _bf16_times_pow2(c.scales, 10)
+        c.biases[...] = _bf16_times_pow2(c.biases, 10)
+        return c
+
+    from quantized_expert_dequant_amd.slab import DeviceLayer, upload_experts
+    slab = upload_experts(src, E + 1, bits, H, I, device=DEV)
+    Wr = synth.router(seed, 0, E, H)
+    L = DeviceLayer(H, I, E, K, bits, slab, _t(Wr), None)
+    experts = {e: src(e, 1) for e in range(E + 1)}
+    assert max(float(np.abs(oracle.bf16_to_double(int(v)))) for v in experts[E].scales.reshape(-1)[:512]) > 16
+    x = synth.tokens(seed, 3, B, H)
+    y, idx, w = _decode(L, x)
+    y_ref, idx_ref, w_ref, margin = oracle.layer_decode(bits, H, I, E, K, x, Wr, experts)
+    assert np.all(margin > 1e-9)
+    np.testing.assert_array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
+    assert np.all(np.isfinite(y))
+    for b in range(B):
+        assert rel_err(y[b], y_ref[b]) <= TOL, "token %d" % b
