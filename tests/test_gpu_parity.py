@@ -195,6 +195,28 @@ def test_layer_decode_tiny_several_tokens(layers):
     _check_layer(0, y, idx, w, x)
 
 
+@pytest.mark.parametrize("bits", [4, 2])
+def test_single_token_many_tokens_tiny(bits):
+    """128 tokens of the tiny layer decoded one at a time (the fused single-token kernels),
+    every token against the oracle: the shape with 128 intermediate units is where one
+    token's output can rest on a few rows, so a per-token error tail shows here first."""
+    cfg = dict(WORKLOADS[0], bits=bits)
+    seed = seed_of(0) + bits
+    L = build_layer(cfg, seed)
+    x = synth.tokens(seed, 9, 128, L.H)
+    ys, idxs, ws_ = [], [], []
+    for b in range(x.shape[0]):
+        y, idx, w = _decode(L, x[b:b + 1])
+        ys.append(y[0]); idxs.append(idx[0]); ws_.append(w[0])
+    y_ref, idx_ref, w_ref, margin = oracle_layer(cfg, seed, 0, x)
+    assert np.all(margin > 1e-9)
+    np.testing.assert_array_equal(np.stack(idxs), idx_ref)
+    np.testing.assert_allclose(np.stack(ws_), w_ref, rtol=W_RTOL)
+    errs = np.array([rel_err(ys[b], y_ref[b]) for b in range(x.shape[0])])
+    print("single token, %d-bit tiny: max rel err %.2e, median %.2e" % (bits, errs.max(), np.median(errs)))
+    assert errs.max() <= TOL, "token %d" % int(errs.argmax())
+
+
 @pytest.mark.parametrize("n", [1, 2])
 @pytest.mark.parametrize("step", range(3))
 def test_layer_decode_full_size(layers, n, step):
