@@ -40,7 +40,8 @@ struct GroupOut {
 struct GroupedWork {
     double* partial;  // router partial logits [splits][B][E]
     GroupOut g;
-    uint4* xhl;       // token operands [B][G_h][16] uint4
+    uint4* xh;        // MFMA token operands: x * 2^-e as fp16 in chunk order [B][2 G_h][4] uint4
+    uint32_t* xsum;   // their chunk sums: 2^-5 * sum, fp16 (hi, lo) [B][2 G_h]
     float* xscale;    // [B]
     float* hb;        // h in fp32, pair-layout order [B + B*K][8][G_i][8]
     uint4* hb16;      // h * 2^-e(entry) as fp16 pairs in chunk order [B + B*K][2 G_i][4]:
@@ -55,13 +56,14 @@ bool grouped_supported(const Layout& L, int B, int K);
 size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E);
 GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E);
 int router_splits(int H);
-// Token operands the batched top-K kernel writes beside the selection (xhl
+// Token operands the batched top-K kernel writes beside the selection (xh
 // nullptr: none; xq nullptr: no dot2 operand).  x and H are filled in by
 // launch_route_batched.
 struct TokenPrep {
     const float* x;
     int H;
-    uint4* xhl;
+    uint4* xh;
+    uint32_t* xsum;
     float* xscale;
     uint4* xq;
     float4* xst;

@@ -17,7 +17,7 @@
 //   k_router_tiled   fp64-accumulated logits of many tokens, split over H
 //   k_topk_slices    sums the H-slice partials in a fixed order, then softmax / top-K
 //   k_group          stable counting sort of the assignments + the MFMA work list
-//   k_prep_tokens    token activations -> fp16 hi + lo MFMA operands (+ dot2 operands)
+//   k_prep_tokens    token activations -> fp16 MFMA operands + chunk sums (+ dot2 operands)
 //   k_grouped_mfma   gate/up (+ SwiGLU) or down dequant-GEMM over (group, 128 rows, K chunk)
 //   k_fixup          SwiGLU of gate/up tiles whose K chunks two blocks shared
 //   k_gemv_gateup    gate/up (+ SwiGLU) of the small groups as dot2 GEMVs
@@ -47,12 +47,17 @@ __device__ inline f4 mfma16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32
 
 
 // ----------------------------------------------------------------------------
-// The MFMA token operand: x scaled by the power of two that puts the token's
-// largest |x| in [2^14, 2^15), split into fp16 hi + lo; element c of group g
-// lands in the 128-byte line of its group half, hi at o and lo at o + 32 (in
-// fp16 units), o = ((g * 16 + (d / 4) * 8 + d % 4) * 8 + (r % 4) * 2 + r / 4)
-// for d = (c % 64) / 8, r = c % 8.
+// The MFMA token operand: v = x scaled by the power of two that puts the token's
+// largest |x| in [2^14, 2^15), rounded to fp16, in chunk order: element c lands
+// in chunk P = (c / 32 % 2) * G + c / 64 (the code chunks' order in a row), dword
+// dd = c % 32 / 8, at xh[(t * 2G + P) * 4 + dd] element (r % 4) * 2 + r / 4 for
+// r = c % 8 (the pair order the packed codes unpack to), so a step's 4 chunks are
+// 256 contiguous bytes; and, for the MFMA kernel's chunk term, each chunk's sum
+// of the unrounded v, as fp16 hi + lo of 2^-5 times it, at xsum[t * 2G + P].
 // ----------------------------------------------------------------------------
+// 2^5: the chunk term's fp16 operands are 2^5 b, 2^5 * 8 s and 2^-5 * chunk sum
+constexpr float GM_CT = 32.f;
+
 __device__ inline int token_exponent(float amax)
 {
     int e = 0;
@@ -62,15 +67,21 @@ __device__ inline int token_exponent(float amax)
     }
     return e;
 }
-__device__ inline void token_operand_elem(const float* __restrict__ xt, int c, float inv, uint16_t* __restrict__ out)
+__device__ inline uint32_t hi_lo_pair(float v)
+{
+    const _Float16 h = (_Float16)v, l = (_Float16)(v - (float)h);
+    return __builtin_bit_cast(uint32_t, h2{h, l});
+}
+// Element c of token row xt; the 32 columns of a chunk must be 32 consecutive
+// lanes of one wave, all calling together (c % 32 == lane % 32).
+__device__ inline void token_operand(const float* __restrict__ xt, int c, float inv, int G, uint16_t* __restrict__ out,
+                                     uint32_t* __restrict__ sums)
 {
     const float v = xt[c] * inv;
-    const _Float16 hi = (_Float16)v;
-    const _Float16 lo = (_Float16)(v - (float)hi);
-    const int g = c >> 6, cc = c & 63, d = cc >> 3, r = cc & 7;
-    const long long o = ((long long)g * 16 + (d >> 2) * 8 + (d & 3)) * 8 + (r & 3) * 2 + (r >> 2);
-    out[o] = __builtin_bit_cast(uint16_t, hi);
-    out[o + 32] = __builtin_bit_cast(uint16_t, lo);
+    const int P = ((c >> 5) & 1) * G + (c >> 6), dd = (c >> 3) & 3, r = c & 7;
+    out[((long long)P * 4 + dd) * 8 + (r & 3) * 2 + (r >> 2)] = __builtin_bit_cast(uint16_t, (_Float16)v);
+    const float sum = group_reduce(v, OpAdd(), 32);
+    if ((c & 31) == 0) sums[P] = hi_lo_pair(sum * (1.f / GM_CT));
 }
 
 // ----------------------------------------------------------------------------
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ 
     const int b = blockIdx.x, tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const float* xt = P.x + (long long)b * P.H;
-    if (P.xhl) {  // the token's largest |x|, for the MFMA operand's scale
+    if (P.xh) {  // the token's largest |x|, for the MFMA operand's scale
         float m = 0.f;
         for (int c = tid; c < P.H; c += 512) m = fmaxf(m, fabsf(xt[c]));
         m = wave_max(m);
@@ -165,7 +176,7 @@ __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ 
     if (tid >= 64) {
         // waves 1..7 write the token's operands while wave 0 selects: the MFMA
         // operand (as k_prep_tokens) and, for the GEMV groups, the dot2 operand
-        if (!P.xhl) return;
+        if (!P.xh) return;
         float amax = red[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) amax = fmaxf(amax, red[i]);
@@ -173,8 +184,8 @@ __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ 
         const float inv = exp2i_f(-e);
         if (tid == 64) P.xscale[b] = exp2i_f(e);
         const int G = P.H / 64;
-        uint16_t* out = reinterpret_cast<uint16_t*>(P.xhl + (long long)b * G * 16);
-        for (int c = tid - 64; c < P.H; c += 448) token_operand_elem(xt, c, inv, out);
+        uint16_t* out = reinterpret_cast<uint16_t*>(P.xh + (long long)b * 2 * G * 4);
+        for (int c = tid - 64; c < P.H; c += 448) token_operand(xt, c, inv, G, out, P.xsum + (long long)b * 2 * G);
         if (P.xq)
             for (int g = wave - 1; g < G; g += 7) prep_group<4>(P.x, G, b, g, lane, P.xq, P.xst);
         return;
@@ -337,12 +348,8 @@ void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const 
 }
 
 // ----------------------------------------------------------------------------
-// Token operands of the gate/up GEMM: x * 2^-e (one power-of-two scale per
-// token, so that the largest |x| lands in [2^14, 2^15)) split into fp16 hi and
-// lo = fp16(v - hi), in the pair order the packed codes unpack to.
-//   xhl[(t * G + g) * 16 + (d / 4) * 8 + hl * 4 + d % 4]: uint4 holding dword d's
-//   8 columns of group g (d = 0..7; columns 8d + (0,4,1,5,2,6,3,7)), hl = 0 hi,
-//   1 lo.  One half of a group (d / 4), hi and lo, is one 128-byte line.
+// Token operands of the gate/up GEMM (token_operand: x * 2^-e in fp16, chunk
+// order, and the chunk sums) when the caller brings the routing.
 // ----------------------------------------------------------------------------
 
 // Blocks (t, y >= 1) write token t's dot2 operand instead (fp16 pairs with a
@@ -350,9 +357,9 @@ void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const 
 // GEMV groups, one wave per group.
 constexpr int PT_DOT2_BLOCKS = 4;
 
-__global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x, int H, uint4* __restrict__ xhl,
-                                                     float* __restrict__ xscale, uint4* __restrict__ xq,
-                                                     float4* __restrict__ xst)
+__global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x, int H, uint4* __restrict__ xh,
+                                                     uint32_t* __restrict__ xsum, float* __restrict__ xscale,
+                                                     uint4* __restrict__ xq, float4* __restrict__ xst)
 {
     __shared__ float red[4];
     const int t = blockIdx.x, tid = threadIdx.x;
@@ -372,8 +379,8 @@ __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x
     const float inv = exp2i_f(-e);
     if (tid == 0) xscale[t] = exp2i_f(e);
     const int G = H / 64;
-    uint16_t* out = reinterpret_cast<uint16_t*>(xhl + (long long)t * G * 16);
-    for (int c = tid; c < H; c += 256) token_operand_elem(xt, c, inv, out);
+    uint16_t* out = reinterpret_cast<uint16_t*>(xh + (long long)t * 2 * G * 4);
+    for (int c = tid; c < H; c += 256) token_operand(xt, c, inv, G, out, xsum + (long long)t * 2 * G);
 }
 
 // ----------------------------------------------------------------------------
@@ -405,8 +412,10 @@ __device__ inline h8 dequant_dword_q4(uint32_t w, h2 s2, const Masks& M)
 // lane's chunk hold (b', b', s', s') against (X_hi, X_lo, X_hi, X_lo), with
 // b' = 2^5 b and s' = 2^5 * 8 s (exact in fp16 for |b| < 2^11 and |s| < 2^8) and
 // X = 2^-5 * the token operand's sum over the chunk's 32 columns (below 2^15 for
-// operands below 2^15), split into fp16 hi + lo.
-constexpr float GM_CT = 32.f;
+// operands below 2^15), split into fp16 hi + lo.  The codes q - 8 average about
+// zero, so the rounding of the token operand they multiply adds no error of one
+// sign to every row; the part of each weight that does not average out, b + 8 s,
+// meets the sum of the unrounded x (gate/up) or of the operand itself (down).
 
 // ----------------------------------------------------------------------------
 // Grouped dequant-GEMM.  A block of 8 waves owns a tile of 128 rows of one
@@ -416,7 +425,9 @@ constexpr float GM_CT = 32.f;
 // row i, turns it into the exact fp16 operand s*(q - 8), and MFMA d (16 x 16 x
 // 32) takes dword d of the four lanes' chunks against the token operands of the
 // same 32 columns, staged in LDS as [tt][kk][token][d]; one more MFMA per step
-// adds (b + 8 s) times each chunk's token-operand sum, staged beside them.
+// adds (b + 8 s) times each chunk's token-operand sum, staged beside them.  Both
+// operands are stored in chunk order, so a step's 4 chunks of one token (x) or
+// entry (h) are 256 contiguous bytes.
 //
 // Work split: the units (group, tile, K chunk) in that order are cut into
 // gridDim.x equal contiguous ranges, one per block.  Gate/up tiles are whole
@@ -430,8 +441,8 @@ constexpr float GM_CT = 32.f;
 // LDS hand-over waits only for the token operands and the weight loads stay in
 // flight across the barrier.
 //
-// MODE_GATEUP: rows are gate/up row pairs; token operand x as fp16 hi + lo (the
-//   codes multiply hi, the chunk sums take hi + lo);
+// MODE_GATEUP: rows are gate/up row pairs; token operand x scaled per token by a
+//   power of two and rounded to fp16, with the chunk sums of the unrounded x;
 //   writes h = silu(g) * u of each entry in fp32 in the pair-layout order
 //   hb[entry][dword d < 8][G_i][8].
 // MODE_DOWN: rows are down rows (one K chunk per tile); token operand h scaled
@@ -459,7 +470,8 @@ struct GroupedArgs {
     const int32_t* gv_n;
     const int32_t* n_ent;   // offsets[E]: routed entries placed (entries B .. B + n_ent - 1)
     const int32_t* ent_token;
-    const uint4* xhl;
+    const uint4* xh;        // gate/up operand: x * 2^-e(token) as fp16 in chunk order [token][2 G_h][4]
+    const uint32_t* xsum;   // its chunk sums: 2^-5 * sum of x * 2^-e over each chunk, fp16 (hi, lo)
     const float* xscale;
     float* hb;       // gate/up output: h in fp32, pair-layout order [entry][8][G_i][8]
     const uint4* hb16;     // down operand: h * 2^-e(entry) as fp16 pairs in chunk order [entry][2 G_i][4]
@@ -471,20 +483,12 @@ struct GroupedArgs {
 template <int MODE>
 struct GmShape {
     static constexpr int NM = (MODE == MODE_GATEUP) ? 2 : 1;  // matrices per row: gate + up | down
-    static constexpr int HL = (MODE == MODE_GATEUP) ? 2 : 1;  // token operand parts: hi + lo | h
-    // token operand parts the codes are multiplied with: x's hi alone.  The codes
-    // q - 8 average about zero, so x's rounding adds no error of one sign to every
-    // row; the part of each weight that does not average out, b + 8 s, meets the
-    // chunk sums of hi + lo.
-    static constexpr int HM = 1;
     static constexpr int RING = (MODE == MODE_GATEUP) ? 3 : 4;  // weight ring slots (loads run RING-1 steps ahead)
-    static constexpr int NSTG = GM_TT * 4 * 4 * HL * 16;     // 16-byte elements staged per step
-    static constexpr int PER_T = NSTG / GM_THREADS;
-    // LDS of a stage: rows (tt, k2, token) of 9 (gate/up) or 5 (down) elements: the 4
-    // dwords' operands the MFMAs read (gate/up: x's hi; slots 4-7 stay unused), then
-    // the chunk sum in the last slot; the odd pitch keeps the reads of 16 tokens free
-    // of bank conflicts
-    static constexpr int NLDS = (MODE == MODE_GATEUP) ? GM_TT * 4 * 16 * 9 : GM_TT * 4 * 16 * 5;
+    static constexpr int NSTG = GM_TT * 4 * 4 * 16;           // 16-byte token-operand elements staged per step
+    static_assert(NSTG == GM_THREADS, "one staged element per thread");
+    // LDS of a stage: rows (tt, k2, token) of 5 elements: the 4 dwords' operands, then
+    // the chunk sum; the odd pitch keeps the reads of 16 tokens free of bank conflicts
+    static constexpr int NLDS = GM_TT * 4 * 16 * 5;
 };
 
 __host__ __device__ inline int gm_tiles(const Layout& L, int mode) { return ((mode == MODE_GATEUP ? L.I : L.H) + GM_ROWS - 1) / GM_ROWS; }
@@ -513,7 +517,7 @@ template <int MODE>
 __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void k_grouped_mfma(GroupedArgs A)
 {
     using S = GmShape<MODE>;
-    constexpr int NM = S::NM, HL = S::HL, HM = S::HM, NSTG = S::NSTG, PER_T = S::PER_T, RING = S::RING;
+    constexpr int NM = S::NM, RING = S::RING;
     __shared__ u4 bs[2][S::NLDS];
 
     const Layout& L = A.L;
@@ -549,70 +553,45 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         const uint32_t sb_off = (MODE == MODE_GATEUP) ? (uint32_t)(L.off_gu_sb + (long long)row * G * 8)
                                                       : (uint32_t)(L.off_d_sb + (long long)row * G * 4);
         const uint32_t up_off = (uint32_t)L.hb;
-        const char* tok_base = (MODE == MODE_GATEUP) ? (const char*)A.xhl : (const char*)A.hb16;
+        const char* tok_base = (MODE == MODE_GATEUP) ? (const char*)A.xh : (const char*)A.hb16;
 
-        // Element t = threadIdx.x + GM_THREADS q of a stage.  Gate/up: t = ((tt*4 + k2)*16
-        // + j)*8 + hl*4 + d, so 8 consecutive lanes read one 128-byte line of a token's
-        // operand.  Down: t = ((tt*16 + j)*4 + k2)*4 + d, so 16 consecutive lanes read the
-        // step's 256 contiguous bytes of an entry's h.  Either lands in LDS row
-        // (tt*4 + k2)*16 + j.  src[q] is the fixed part of the source index (token or entry
-        // row, hl, d), the step adds the chunk.  Chunks past the row end (2G not a
-        // multiple of 4) read a valid chunk and get zero weights.
-        // The row's last slot (the padding) takes the chunk sum of the row's token
-        // operand for the bias MFMA; the 8 (gate/up: hi, lo x 4 dwords) or 4 (down)
-        // consecutive threads of a row add their elements and the first writes it.
-        int src[PER_T], k2q[PER_T], dst[PER_T], sdst[PER_T];
-#pragma unroll
-        for (int q = 0; q < PER_T; ++q) {
-            const int t = threadIdx.x + GM_THREADS * q;
-            if (MODE == MODE_GATEUP) {
-                const int d = t & 3, hl = (t >> 2) & 1, j = (t >> 3) & 15, k2 = (t >> 7) & 3, tt = t >> 9;
-                const int m = min(tt * 16 + j, n - 1);
-                k2q[q] = k2;
-                src[q] = A.ent_token[ent0 + m] * G * 16 + hl * 4 + d;
-                dst[q] = ((tt * 4 + k2) * 16 + j) * 9 + hl * 4 + d;
-                sdst[q] = ((tt * 4 + k2) * 16 + j) * 9 + 8;
-            } else {
-                const int d = t & 3, k2 = (t >> 2) & 3, j = (t >> 4) & 15, tt = t >> 8;
-                const int m = min(tt * 16 + j, n - 1);
-                k2q[q] = k2;
-                src[q] = (ent0 + m) * 8 * G + d;
-                dst[q] = ((tt * 4 + k2) * 16 + j) * 5 + d;
-                sdst[q] = ((tt * 4 + k2) * 16 + j) * 5 + 4;
-            }
+        // Stage element t = threadIdx.x = ((tt*16 + j)*4 + k2)*4 + d: dword d of chunk
+        // 4 * step + k2 of the tile's token j (gate/up: x of the entry's token, down: h
+        // of the entry), so 16 consecutive lanes read a step's 256 contiguous bytes of
+        // one operand row.  It lands in LDS row (tt*4 + k2)*16 + j, whose last slot takes
+        // the chunk sum for the chunk-term MFMA: gate/up loads the one the token-operand
+        // writer stored; down adds the row's 4 elements across its 4 threads.  Chunks
+        // past the row end (2G not a multiple of 4) read a valid chunk and get zero weights.
+        const int st_d = threadIdx.x & 3, st_k2 = (threadIdx.x >> 2) & 3;
+        const int st_row = (((threadIdx.x >> 8) * 4 + st_k2) * 16 + ((threadIdx.x >> 4) & 15)) * 5;
+        int st_src, st_sum;
+        {
+            const int m = min((threadIdx.x >> 8) * 16 + ((threadIdx.x >> 4) & 15), n - 1);
+            const int orow = (MODE == MODE_GATEUP) ? A.ent_token[ent0 + m] : ent0 + m;
+            st_src = orow * 8 * G + st_d;
+            st_sum = orow * 2 * G;
         }
         struct Stage {
-            u4 v[PER_T];
+            u4 v;
+            uint32_t cs;  // gate/up: the row's chunk sum
         };
         auto stage_load = [&](int ks, Stage& S) {
-#pragma unroll
-            for (int q = 0; q < PER_T; ++q) {
-                const int P = min(4 * ks + k2q[q], 2 * G - 1);
-                const int jh = P >= G ? 1 : 0, g = P - jh * G;
-                const uint32_t el = (MODE == MODE_GATEUP) ? (uint32_t)(src[q] + g * 16 + jh * 8)
-                                                          : (uint32_t)(src[q] + P * 4);
-                S.v[q] = *reinterpret_cast<const u4*>(tok_base + el * 16u);
-            }
+            const int P = min(4 * ks + st_k2, 2 * G - 1);
+            S.v = *reinterpret_cast<const u4*>(tok_base + (uint32_t)(st_src + P * 4) * 16u);
+            if (MODE == MODE_GATEUP) S.cs = A.xsum[st_sum + P];
         };
         auto stage_store = [&](int buf, const Stage& S) {
-            const bool mul_part = HM == HL || ((threadIdx.x >> 2) & 1) == 0;  // an element the MFMAs read
-#pragma unroll
-            for (int q = 0; q < PER_T; ++q)
-                if (mul_part) bs[buf][dst[q]] = S.v[q];
-            constexpr int RL = (MODE == MODE_GATEUP) ? 8 : 4;  // threads per LDS row
-            const uint32_t one2 = 0x3C003C00u;                 // fp16 (1, 1)
-#pragma unroll
-            for (int q = 0; q < PER_T; ++q) {
+            bs[buf][st_row + st_d] = S.v;
+            uint32_t cs;
+            if (MODE == MODE_GATEUP) {
+                cs = S.cs;
+            } else {
                 float sum = 0.f;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sum = dot2(S.v[q][e], one2, sum);
-                sum = group_reduce(sum, OpAdd(), RL);
-                if ((threadIdx.x & (RL - 1)) == 0) {
-                    const float v = sum * (1.f / GM_CT);
-                    const _Float16 vh = (_Float16)v, vl = (_Float16)(v - (float)vh);
-                    bs[buf][sdst[q]] = u4{__builtin_bit_cast(uint32_t, h2{vh, vl}), 0u, 0u, 0u};
-                }
+                for (int e = 0; e < 4; ++e) sum = dot2(S.v[e], 0x3C003C00u, sum);  // fp16 (1, 1)
+                cs = hi_lo_pair(group_reduce(sum, OpAdd(), 4) * (1.f / GM_CT));
             }
+            if (st_d == 0) bs[buf][st_row + 4] = u4{cs, 0u, 0u, 0u};
         };
         auto weight_load = [&](int ks, WRegs& W) {
             const int P = min(4 * ks + kk, 2 * G - 1), g = P >= G ? P - G : P;
@@ -673,7 +652,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             for (int tt = 0; tt < GM_TT; ++tt) {
                 if (tt < ntt) {
                     const int r = (tt * 4 + kk) * 16 + i;
-                    const uint32_t xsum = (MODE == MODE_GATEUP) ? buf[r * 9 + 8].x : buf[r * 5 + 4].x;
+                    const uint32_t xsum = buf[r * 5 + 4].x;
                     const h8 bx = __builtin_bit_cast(h8, u4{xsum, xsum, 0u, 0u});
 #pragma unroll
                     for (int mm = 0; mm < NM; ++mm) acc[mm][tt] = mfma16(cw[mm], bx, acc[mm][tt]);
@@ -681,16 +660,11 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             }
             // dword-major: the token operands of dword d + 1 are read from LDS while
             // the MFMAs of dword d run, and only one dword's weights are live
-            h8 bv[2][GM_TT][HM];
-            auto bread = [&](int d, h8 (&b)[GM_TT][HM]) {
+            h8 bv[2][GM_TT];
+            auto bread = [&](int d, h8 (&b)[GM_TT]) {
 #pragma unroll
                 for (int tt = 0; tt < GM_TT; ++tt)
-#pragma unroll
-                    for (int hl = 0; hl < HM; ++hl)
-                        if (tt < ntt)
-                            b[tt][hl] = __builtin_bit_cast(
-                                h8, buf[(MODE == MODE_GATEUP) ? ((tt * 4 + kk) * 16 + i) * 9 + hl * 4 + d
-                                                              : ((tt * 4 + kk) * 16 + i) * 5 + d]);
+                    if (tt < ntt) b[tt] = __builtin_bit_cast(h8, buf[((tt * 4 + kk) * 16 + i) * 5 + d]);
             };
             bread(0, bv[0]);
 #pragma unroll
@@ -703,9 +677,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                 for (int tt = 0; tt < GM_TT; ++tt) {
                     if (tt < ntt) {
 #pragma unroll
-                        for (int hl = 0; hl < HM; ++hl)
-#pragma unroll
-                            for (int mm = 0; mm < NM; ++mm) acc[mm][tt] = mfma16(a[mm], bv[d & 1][tt][hl], acc[mm][tt]);
+                        for (int mm = 0; mm < NM; ++mm) acc[mm][tt] = mfma16(a[mm], bv[d & 1][tt], acc[mm][tt]);
                     }
                 }
             }
@@ -1121,7 +1093,8 @@ size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E)
     for (int l = 0; l < 6; ++l) add(sizeof(int32_t) * V);  // act_expert, act_off, act_n, gv_expert, gv_off, gv_n
     add(sizeof(int32_t) * ents);                       // ent_token
     add(sizeof(int32_t) * B * K);                      // slot_pos
-    add(16ull * B * L.Gh * 16);                        // xhl
+    add(16ull * B * 2 * L.Gh * 4);                     // xh
+    add(4ull * B * 2 * L.Gh);                          // xsum
     add(sizeof(float) * B);                            // xscale
     add(4ull * ents * L.I);                            // hb (fp32)
     add(2ull * ents * L.I);                            // hb16
@@ -1155,7 +1128,8 @@ GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E)
     W.g.gv_n = (int32_t*)take(sizeof(int32_t) * V);
     W.g.ent_token = (int32_t*)take(sizeof(int32_t) * ents);
     W.g.slot_pos = (int32_t*)take(sizeof(int32_t) * B * K);
-    W.xhl = (uint4*)take(16ull * B * L.Gh * 16);
+    W.xh = (uint4*)take(16ull * B * 2 * L.Gh * 4);
+    W.xsum = (uint32_t*)take(4ull * B * 2 * L.Gh);
     W.xscale = (float*)take(sizeof(float) * B);
     W.hb = (float*)take(4ull * ents * L.I);
     W.hb16 = (uint4*)take(2ull * ents * L.I);
@@ -1193,8 +1167,8 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     const bool gv = gv_t > 1;
 
     if (!prepped)
-        hipLaunchKernelGGL(k_prep_tokens, dim3(B, gv ? 1 + PT_DOT2_BLOCKS : 1), dim3(256), 0, s, x, L.H, W.xhl,
-                           W.xscale, xq, xst);
+        hipLaunchKernelGGL(k_prep_tokens, dim3(B, gv ? 1 + PT_DOT2_BLOCKS : 1), dim3(256), 0, s, x, L.H, W.xh,
+                           W.xsum, W.xscale, xq, xst);
     GroupedArgs A;
     A.slab = (const uint8_t*)slab;
     A.L = L;
@@ -1207,7 +1181,8 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     A.gv_n = W.g.gv_n;
     A.n_ent = W.g.offsets + E;
     A.ent_token = W.g.ent_token;
-    A.xhl = W.xhl;
+    A.xh = W.xh;
+    A.xsum = W.xsum;
     A.xscale = W.xscale;
     A.hb = W.hb;
     A.hb16 = W.hb16;

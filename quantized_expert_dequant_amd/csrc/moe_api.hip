@@ -287,7 +287,7 @@ static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, i
     float* w = w_out ? w_out : W.w;
     const Layout L = make_layout(d->bits, d->H, d->I);
     if (W.grouped) {
-        const TokenPrep P{x, d->H, W.gw.xhl, W.gw.xscale, gemv_tokens(L) > 1 ? W.xq : nullptr, W.xst};
+        const TokenPrep P{x, d->H, W.gw.xh, W.gw.xsum, W.gw.xscale, gemv_tokens(L) > 1 ? W.xq : nullptr, W.xst};
         launch_route_batched(x, B, d->w_router, d->logit_bias, d->H, d->E, d->K, d->renormalize ? 1 : 0,
                              W.gw.partial, idx, w, P, s, g_timing[KID_ROUTER]);
         launch_group(idx, B, d->K, d->E, gemv_tokens(L), W.gw.g, s);
