@@ -6,9 +6,11 @@ input and output buffers, then replays it several times.  Before each replay a
 fresh token is copied into the static input, the outputs are poisoned, and the
 same entry point runs eagerly on its own workspace and outputs (the program's
 own work between replays).  Every replay must equal that eager call bit for bit
-(the same kernels with fixed summation orders) and, for a single layer, the
-oracle within the bar.  The cases cover the fused single-token path, the
-grouped path with and without matrix-core groups, and the stack on both.
+(the same kernels with fixed summation orders) and, for a single routed layer,
+the oracle within the bar; the given-routing entry point's parity with the
+oracle is tested in test_gpu_parity.py.  The cases cover the fused single-token
+path, the grouped path with and without matrix-core groups, the stack on both,
+and the given-routing entry point on the grouped path.
 """
 import numpy as np
 import pytest
@@ -85,8 +87,9 @@ class _Bufs:
 # (entry point, workload, tokens): workload 1 is the full single-token layer (fused
 # selection); workload 0 at B = 16 has experts with >= 3 tokens (matrix-core groups),
 # at B = 2 only GEMV groups; the stack renormalizes inside the next router at B = 1
-# and with the separate renorm kernel on the grouped path.
-CASES = [("layer", 1, 1), ("layer", 0, 16), ("layer", 0, 2), ("stack", 0, 1), ("stack", 0, 3)]
+# and with the separate renorm kernel on the grouped path; the given-routing entry point
+# at B = 16 writes its own token operands (k_prep_tokens) before the grouped FFNs.
+CASES = [("layer", 1, 1), ("layer", 0, 16), ("layer", 0, 2), ("stack", 0, 1), ("stack", 0, 3), ("ffn", 0, 16)]
 
 
 @pytest.mark.parametrize("kind,n,B", CASES)
@@ -99,9 +102,16 @@ def test_graph_replay_matches_eager(layers, kind, n, B):
     Ls = [layers(n, l) for l in range(nl)]
     descs = [L.desc for L in Ls]
 
+    # fixed routing for the given-routing entry point: K distinct experts per token
+    rng = np.random.default_rng(seed)
+    idx_in = _t(np.stack([rng.choice(cfg["E"], K, replace=False) for _ in range(B)]).astype(np.int32))
+    w_in = _t(rng.dirichlet(np.ones(K), size=B).astype(np.float32))
+
     def call(b):
         if stack:
             moe.stack_decode(descs, b.x, B, RMS_EPS, b.y, b.idx, b.w, b.ws, b.n)
+        elif kind == "ffn":
+            moe.expert_ffn(descs[0], b.x, B, idx_in, w_in, b.y, b.ws, b.n)
         else:
             moe.layer_decode(descs[0], b.x, B, b.y, b.idx[0], b.w[0], b.ws, b.n)
 
@@ -120,10 +130,11 @@ def test_graph_replay_matches_eager(layers, kind, n, B):
             g.replay()
             torch.cuda.synchronize()
             case = "replay %d" % r
-            torch.testing.assert_close(gb.idx, eb.idx, rtol=0, atol=0, msg=case)
-            torch.testing.assert_close(gb.w, eb.w, rtol=0, atol=0, msg=case)
+            if kind != "ffn":  # routing outputs (the given-routing call has none)
+                torch.testing.assert_close(gb.idx, eb.idx, rtol=0, atol=0, msg=case)
+                torch.testing.assert_close(gb.w, eb.w, rtol=0, atol=0, msg=case)
             torch.testing.assert_close(gb.y, eb.y, rtol=0, atol=0, equal_nan=False, msg=case)
-            if not stack:
+            if kind == "layer":
                 y_ref, idx_ref, w_ref, margin = oracle_layer(cfg, seed, 0, xh)
                 assert np.all(margin > 1e-9), case + ": routing margin below 1e-9"
                 np.testing.assert_array_equal(gb.idx[0].cpu().numpy(), idx_ref, err_msg=case)
