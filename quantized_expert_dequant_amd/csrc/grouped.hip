@@ -15,7 +15,8 @@
 //
 // Kernels:
 //   k_router_tiled   fp64-accumulated logits of many tokens, split over H
-//   k_topk_slices    sums the H-slice partials in a fixed order, then softmax / top-K
+//   k_topk_slices    sums the H-slice partials in a fixed order, then softmax / top-K;
+//                    blocks beside the selecting ones write the token operands
 //   k_group          stable counting sort of the assignments + the MFMA work list
 //   k_prep_tokens    token activations -> fp16 MFMA operands + chunk sums (+ dot2 operands)
 //   k_grouped_mfma   gate/up (+ SwiGLU) or down dequant-GEMM over (group, 128 rows, K chunk)
@@ -138,10 +139,14 @@ __global__ __launch_bounds__(256) void k_router_tiled(const float* __restrict__ 
     if (e + 1 < E && b + 1 < B) out[(long long)(b + 1) * E + e + 1] = a11;
 }
 
-// One block per token: the token's logits are the H-slice partials added in
-// slice order, then the bias (a fixed order, so they do not depend on the
-// launch); they go to LDS and wave 0 selects the top-K.
-constexpr int TS_CHUNK = 16;  // slice loads in flight per thread
+// Blocks (t, 0), one per token: the token's logits are the H-slice partials
+// added in slice order, then the bias (a fixed order, so they do not depend on
+// the launch); they go to LDS and wave 0 selects the top-K.  Beside them, when
+// the FFNs need token operands: block (t, 1) writes token t's MFMA operand and
+// chunk sums (as k_prep_tokens), blocks (t, y >= 2) its dot2 operand for the GEMV
+// groups, one wave per group.  The selecting blocks alone would hold 64 CUs.
+constexpr int TS_CHUNK = 16;       // slice loads in flight per thread
+constexpr int TS_DOT2_BLOCKS = 4;  // blocks per token writing the dot2 operand
 
 __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ partial, int nslice,
                                                      const float* __restrict__ bias, int B, int E, int K, int renorm,
@@ -152,11 +157,27 @@ __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ 
     const int b = blockIdx.x, tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const float* xt = P.x + (long long)b * P.H;
-    if (P.xh) {  // the token's largest |x|, for the MFMA operand's scale
+    if (blockIdx.y == 1) {  // the MFMA operand and its chunk sums
         float m = 0.f;
         for (int c = tid; c < P.H; c += 512) m = fmaxf(m, fabsf(xt[c]));
         m = wave_max(m);
         if (lane == 0) red[wave] = m;
+        __syncthreads();
+        float amax = red[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) amax = fmaxf(amax, red[i]);
+        const int e = token_exponent(amax);
+        const float inv = exp2i_f(-e);
+        if (tid == 0) P.xscale[b] = exp2i_f(e);
+        const int G = P.H / 64;
+        uint16_t* out = reinterpret_cast<uint16_t*>(P.xh + (long long)b * 2 * G * 4);
+        for (int c = tid; c < P.H; c += 512) token_operand(xt, c, inv, G, out, P.xsum + (long long)b * 2 * G);
+        return;
+    }
+    if (blockIdx.y >= 2) {  // the dot2 operand of the GEMV groups
+        const int G = P.H / 64, step = 8 * (gridDim.y - 2);
+        for (int g = (blockIdx.y - 2) * 8 + wave; g < G; g += step) prep_group<4>(P.x, G, b, g, lane, P.xq, P.xst);
+        return;
     }
     const long long BE = (long long)B * E;
     for (int e = tid; e < E; e += 512) {
@@ -173,23 +194,7 @@ __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ 
         lg[e] = s + (bias ? (double)bias[e] : 0.0);
     }
     __syncthreads();
-    if (tid >= 64) {
-        // waves 1..7 write the token's operands while wave 0 selects: the MFMA
-        // operand (as k_prep_tokens) and, for the GEMV groups, the dot2 operand
-        if (!P.xh) return;
-        float amax = red[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) amax = fmaxf(amax, red[i]);
-        const int e = token_exponent(amax);
-        const float inv = exp2i_f(-e);
-        if (tid == 64) P.xscale[b] = exp2i_f(e);
-        const int G = P.H / 64;
-        uint16_t* out = reinterpret_cast<uint16_t*>(P.xh + (long long)b * 2 * G * 4);
-        for (int c = tid - 64; c < P.H; c += 448) token_operand(xt, c, inv, G, out, P.xsum + (long long)b * 2 * G);
-        if (P.xq)
-            for (int g = wave - 1; g < G; g += 7) prep_group<4>(P.x, G, b, g, lane, P.xq, P.xst);
-        return;
-    }
+    if (tid >= 64) return;
     double lv[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) lv[j] = lg[min(tid + 64 * j, E - 1)];
@@ -212,7 +217,8 @@ void launch_route_batched(const float* x, int B, const float* W, const float* bi
     TokenPrep Q = P;
     Q.x = x;
     Q.H = H;
-    hipLaunchKernelGGL(k_topk_slices, dim3(B), dim3(512), 0, s, partial, router_splits(H), bias, B, E, K, renorm,
+    const int ny = 1 + (P.xh ? 1 + (P.xq ? TS_DOT2_BLOCKS : 0) : 0);  // selection, MFMA operand, dot2 operand
+    hipLaunchKernelGGL(k_topk_slices, dim3(B, ny), dim3(512), 0, s, partial, router_splits(H), bias, B, E, K, renorm,
                        idx, w, Q);
 }
 
