@@ -227,6 +227,17 @@ def test_layer_decode_full_size(layers, n, step):
     print("workload %d step %d: max rel err %.2e" % (n, step, err))
 
 
+def test_layer_decode_full_size_2bit_several_tokens(layers):
+    """Four tokens through the full 2-bit layer in one call: 2-bit batches run token by
+    token through the fused single-token kernels, each token's routing its own."""
+    n = 2
+    L = layers(n)
+    x = synth.tokens(seed_of(n), 30, 4, L.H)
+    y, idx, w = _decode(L, x)
+    err = _check_layer(n, y, idx, w, x)
+    print("workload %d, 4 tokens: max rel err %.2e" % (n, err))
+
+
 def test_layer_decode_is_deterministic(layers):
     L = layers(1)
     x = synth.tokens(seed_of(1), 9, 1, L.H)
