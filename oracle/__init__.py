@@ -50,6 +50,8 @@ def lib():
         L.oracle_layer_decode.restype = i32
         L.oracle_layer_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, dbl, vp, i32, vp, vp,
                                           vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_layer_decode_par.restype = i32
+        L.oracle_layer_decode_par.argtypes = list(L.oracle_layer_decode.argtypes)
         L.oracle_layer_decode_mt.restype = i32
         L.oracle_layer_decode_mt.argtypes = [i32, i32, i32, i32, i32, i32, i32, dbl, vp, vp, vp,
                                              vp, vp, vp, vp, vp, vp, vp, vp]
@@ -162,9 +164,12 @@ class _Table:
 
 
 def layer_decode(bits, H, I, E, K, x, Wr, experts, prior=None, renormalize=True,
-                 shared_weight=1.0, group=64):
+                 shared_weight=1.0, group=64, parallel=False):
     """Decode B tokens through one layer.
 
+    parallel=True spreads the tokens over OpenMP threads (oracle_layer_decode_par:
+    each token decoded by the serial function on its own, so the results are the
+    serial ones bit for bit).
     Returns (y float64 [B][H], idx int32 [B][K], w float64 [B][K], margin [B]).
     """
     x = _c(np.atleast_2d(x), np.float32)
@@ -176,8 +181,9 @@ def layer_decode(bits, H, I, E, K, x, Wr, experts, prior=None, renormalize=True,
     idx = np.empty((B, K), np.int32)
     w = np.empty((B, K), np.float64)
     m = np.empty(B, np.float64)
-    rc = lib().oracle_layer_decode(bits, H, I, E, K, group, int(bool(renormalize)), shared_weight,
-                                   _p(x), B, _p(Wr), _p(pr), *t.args(), _p(y), _p(idx), _p(w), _p(m))
+    fn = lib().oracle_layer_decode_par if parallel else lib().oracle_layer_decode
+    rc = fn(bits, H, I, E, K, group, int(bool(renormalize)), shared_weight,
+            _p(x), B, _p(Wr), _p(pr), *t.args(), _p(y), _p(idx), _p(w), _p(m))
     if rc == -2:
         raise KeyError("oracle_layer_decode: a selected expert was not provided")
     if rc != 0:

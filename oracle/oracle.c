@@ -42,7 +42,9 @@
  * bias widen to double exactly.
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
- * (OpenMP is used only by oracle_layer_decode_mt, the timed baseline.)
+ * (OpenMP is used only by oracle_layer_decode_mt, the timed baseline, and by
+ * oracle_layer_decode_par, which runs the serial per-token decode on many
+ * tokens at once.)
  */
 #include <math.h>
 #include <stdint.h>
@@ -306,6 +308,35 @@ int oracle_layer_decode_mt(int bits, int H, int I, int E, int K, int group, int 
             y[c] = acc + shared_weight * ys[(long)K * H + c];
         }
     free(logits); free(xd); free(ys);
+    return rc;
+}
+
+/*
+ * oracle_layer_decode over B tokens with the tokens spread over OpenMP
+ * threads: each token is decoded by oracle_layer_decode on its own, so every
+ * token's result is the serial one bit for bit.  Used where many tokens of a
+ * full-size batch are checked.  Same outputs and return codes as
+ * oracle_layer_decode (the first failing token's code).
+ */
+int oracle_layer_decode_par(int bits, int H, int I, int E, int K, int group, int renormalize,
+                            double shared_weight, const float* x, int B, const float* Wr,
+                            const float* prior, const uint8_t* const* gate, const uint8_t* const* up,
+                            const uint8_t* const* down, const uint16_t* const* scales,
+                            const uint16_t* const* biases, double* y, int32_t* idx, double* w,
+                            double* margin)
+{
+    int rc = 0;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        int r = oracle_layer_decode(bits, H, I, E, K, group, renormalize, shared_weight,
+                                    x + (long)b * H, 1, Wr, prior, gate, up, down, scales, biases,
+                                    y + (long)b * H, idx + (long)b * K, w + (long)b * K,
+                                    margin ? margin + b : NULL);
+        if (r) {
+            #pragma omp critical
+            if (rc == 0) rc = r;
+        }
+    }
     return rc;
 }
 

@@ -335,3 +335,47 @@ def test_rms_renorm_closed_form():
     ms = np.mean(y * y)
     assert abs(math.sqrt(np.mean(x * x)) - 1 / math.sqrt(1 + eps / ms)) < 1e-14
     np.testing.assert_allclose(x / y, x[0] / y[0], rtol=1e-15)   # pure rescale, no shift
+
+
+# -------------------- threaded forms of the layer decode ------------------------
+# oracle_layer_decode_mt (the timed CPU baseline: router rows and the active experts'
+# FFNs over OpenMP threads) and oracle_layer_decode_par (many tokens of a batch at
+# once) must give the serial decode's results bit for bit, since every floating-point
+# sum keeps its order; a slip in their indexing (w[k], the shared slot, the token
+# offsets) would show as a difference.
+
+def _assert_same_decode(a, b):
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    np.testing.assert_array_equal(a[2], b[2])
+
+
+@pytest.mark.parametrize("bits,K,prior_s,shared_w", [(4, 4, None, 1.0), (2, 3, 1.1, 0.5), (4, 16, None, 1.0)])
+def test_layer_decode_mt_and_par_equal_serial(bits, K, prior_s, shared_w):
+    experts, Wr, _ = _tiny_layer(40 + K, bits=bits)
+    x = np.random.default_rng(K).normal(0, 1, (5, H_T)).astype(np.float32)
+    prior = synth.zipf_bias(E_T, prior_s) if prior_s else None
+    kw = dict(prior=prior, shared_weight=shared_w)
+    ser = oracle.layer_decode(bits, H_T, I_T, E_T, K, x, Wr, Stack(experts), **kw)
+    par = oracle.layer_decode(bits, H_T, I_T, E_T, K, x, Wr, Stack(experts), parallel=True, **kw)
+    _assert_same_decode(ser, par)
+    np.testing.assert_array_equal(ser[3], par[3])
+    for b in range(x.shape[0]):
+        mt = oracle.layer_decode_mt(bits, H_T, I_T, E_T, K, x[b], Wr, Stack(experts), **kw)
+        _assert_same_decode((ser[0][b], ser[1][b], ser[2][b]), mt)
+
+
+@pytest.mark.slow
+def test_layer_decode_mt_and_par_equal_serial_full_shape():
+    """One token of the full layer shape (H=4096, I=1024, E=512, K=4), generated experts."""
+    H, I, E, K, seed = 4096, 1024, 512, 4, 1001
+    Wr = synth.router(seed, 0, E, H)
+    x = synth.tokens(seed, 0, 2, H)
+    lg = oracle.router_logits(x, Wr)
+    need = sorted({int(e) for b in range(2) for e in oracle.topk(lg[b], K)[0]} | {E})
+    experts = {e: synth.experts(seed, 0, e, 1, 4, H, I) for e in need}
+    ser = oracle.layer_decode(4, H, I, E, K, x, Wr, experts)
+    par = oracle.layer_decode(4, H, I, E, K, x, Wr, experts, parallel=True)
+    _assert_same_decode(ser, par)
+    mt = oracle.layer_decode_mt(4, H, I, E, K, x[1], Wr, experts)
+    _assert_same_decode((ser[0][1], ser[1][1], ser[2][1]), mt)
