@@ -13,14 +13,19 @@ reads were last touched R-1 steps (>600 MB of traffic) earlier and cannot be
 served from the 256 MB Infinity Cache or the L2s.
 
 Timed regions:
-  * graph: K steps captured once into a HIP graph (launch-bound loop) and
-    replayed; gives ms_per_step and the headline tokens/s.
+  * graph: K steps captured once into a HIP graph (launch-bound loop); each of
+    --replays replays is bracketed by GPU events recorded on the replay stream,
+    and the median replay gives ms_per_step and the headline tokens/s (host
+    launch latency is outside the events, so the figure does not depend on K).
+    The same steps replayed on one layer copy give the warm-cache figure.
   * eager: the same K steps launched one by one with start/stop HIP events
     recorded around the router, gate/up and down kernels on their stream;
     gives each kernel's average duration, hence achieved GB/s.
+The other workloads (2-bit layer, 64-token batch, 60-layer stack) are timed the
+same way with fewer steps and reported under "configs" in the same JSON line.
 The float64 oracle is timed on the host cores on a small sample of tokens
-(cpu_baseline).  One token is checked against the oracle before timing; a
-mismatch reports no throughput.
+(cpu_baseline).  Each workload's first step is checked against the oracle
+before timing; a mismatch reports no throughput.
 
     python bench.py [--steps K] [--warmup W] [--workload layer|layer2|batched|stack]
 """
@@ -130,30 +135,6 @@ def oracle_check(c, x_host, y_dev, idx_dev, layer_id=0):
     return bool(np.array_equal(idx_dev, idx_ref)) and err <= 2e-3, err
 
 
-def cpu_baseline(c, budget_s=15.0):
-    """The float64 oracle as it stands, on the host cores, on a bounded sample of tokens."""
-    import oracle
-    import synth
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or min(os.cpu_count() or 1, 16)
-    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
-    E, K, H = c["E"], c["K"], c["H"]
-    Wr = synth.router(c["seed"], 0, E, H)
-    prior = synth.zipf_bias(E, c["zipf"]) if c["zipf"] else None
-    n_tok, elapsed = 0, 0.0
-    while elapsed < budget_s and n_tok < 64:
-        x = synth.tokens(c["seed"], 10_000 + n_tok, 1, H)[0]
-        lg = oracle.router_logits(x, Wr, prior)[0]
-        sel = oracle.topk(lg, K)[0]
-        experts = {e: synth.experts(c["seed"], 0, e, 1, c["bits"], H, c["I"]) for e in sorted(set(sel) | {E})}
-        t0 = time.perf_counter()
-        oracle.layer_decode_mt(c["bits"], H, c["I"], E, K, x, Wr, experts, prior=prior)
-        elapsed += time.perf_counter() - t0
-        n_tok += 1
-    return {"value": n_tok / elapsed, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%d tokens of the timed layer (one token per decode step), float64 oracle with the active "
-                      "experts' FFNs spread over OpenMP threads; weight generation excluded" % n_tok}
-
-
 def kernel_source_hash(workload):
     """Hash of the sources the timed gate/up kernels are built from: the single-token
     kernel lives in kernels.hip; the batched phase also runs grouped.hip's kernels."""
@@ -226,6 +207,225 @@ def write_pmc_summary(workload, kernel_prefix, fetch_csv, write_csv, copy_fetch_
     print(json.dumps(out))
 
 
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def _workload_name(name, c, n_copies, n_distinct, stack):
+    return "%s: H=%d I=%d E=%d+1 shared K=%d %d-bit group 64 bf16 scale+bias, B=%d%s" % (
+        name, c["H"], c["I"], c["E"], c["K"], c["bits"], c["B"],
+        ", %d layers with RMS renorm" % c["layers"] if stack else "")
+
+
+def measure(name, steps, warmup, dev, rotate=16, distinct=0, graph=True, eager=True, warm=False, replays=5,
+            lead_ms=30.0):
+    """Time one workload: parity spot check, graph replays (GPU events around each replay on
+    the replay stream, median over `replays`), optionally the same steps on one layer copy
+    (warm caches), and an eager pass with per-kernel events.  Returns a dict of numbers."""
+    import torch
+    import synth
+    import quantized_expert_dequant_amd as moe
+    from quantized_expert_dequant_amd.slab import workspace
+
+    c = dict(WORKLOADS[name])
+    K, W, B, H = steps, warmup, c["B"], c["H"]
+    stack = c["layers"] > 1
+    n_distinct = min(distinct or c["layers"], c["layers"]) if stack else 1
+    n_copies = c["layers"] if stack else max(1, rotate)
+    log("workload %s: building %d layer(s) (%d distinct)" % (name, n_copies, n_distinct))
+    layers = build_layers(c, n_distinct, n_copies, dev)
+
+    xs_host = np.stack([synth.tokens(c["seed"], t, B, H) for t in range(W + K)])
+    xs = torch.from_numpy(xs_host).to(dev)
+    ws, ws_n = workspace(layers[0].desc, B, stack=stack)
+    y = torch.empty((W + K, B, H), dtype=torch.float32, device=dev)
+    nL = c["layers"]
+    idx = torch.empty((W + K, nL, B, c["K"]), dtype=torch.int32, device=dev)
+    wts = torch.empty((W + K, nL, B, c["K"]), dtype=torch.float32, device=dev)
+    descs = [L.desc for L in layers]
+
+    def step(t, copy=None):
+        if stack:
+            moe.stack_decode(descs, xs[t], B, RMS_EPS, y[t], idx[t], wts[t], ws, ws_n)
+        else:
+            L = layers[t % n_copies if copy is None else copy]
+            moe.layer_decode(L.desc, xs[t], B, y[t], idx[t, 0], wts[t, 0], ws, ws_n)
+
+    # parity spot check on the first step's tokens (layer copy 0 == distinct layer 0)
+    step(0)
+    torch.cuda.synchronize()
+    if stack:
+        y0 = torch.empty((B, H), dtype=torch.float32, device=dev)
+        i0 = torch.empty((B, c["K"]), dtype=torch.int32, device=dev)
+        w0 = torch.empty((B, c["K"]), dtype=torch.float32, device=dev)
+        moe.layer_decode(layers[0].desc, xs[0], B, y0, i0, w0, ws, ws_n)
+        torch.cuda.synchronize()
+        ok, err = oracle_check(c, xs_host[0], y0.cpu().numpy(), i0.cpu().numpy())
+        ok = ok and bool(torch.equal(i0, idx[0, 0]))
+    else:
+        ok, err = oracle_check(c, xs_host[0], y[0].cpu().numpy(), idx[0, 0].cpu().numpy())
+    log("%s parity spot check: ok=%s max rel err %.3e" % (name, ok, err))
+    res = {"workload": name, "config": _workload_name(name, c, n_copies, n_distinct, stack), "parity_ok": ok,
+           "parity_rel_err": err, "steps": K, "rotation_copies": n_copies}
+    if stack:
+        res["distinct_layers"] = n_distinct
+    if not ok:
+        return res
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+
+    def graph_time(copy=None):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for t in range(W, W + K):
+                    step(t, copy)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g.replay()  # one untimed replay, checked against eager
+        torch.cuda.synchronize()
+        y_graph = y[W + K - 1].clone()
+        step(W + K - 1, copy)
+        torch.cuda.synchronize()
+        if not torch.equal(y_graph, y[W + K - 1]):
+            log("graph replay differs from eager: graph timing disabled")
+            return None
+        times = []
+        for _ in range(replays):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) / K)
+        del g
+        return times
+
+    graph_ms = None
+    if graph:
+        times = graph_time()
+        if times:
+            graph_ms = _median(times)
+            res["graph_replays_ms_per_step"] = [round(v, 6) for v in times]
+        if warm and not stack:
+            wt = graph_time(copy=0)
+            if wt:
+                res["warm_ms_per_step"] = round(_median(wt), 6)
+
+    kinds = [moe.KERNEL_ROUTER, moe.KERNEL_GATEUP, moe.KERNEL_DOWN]
+    dur = {k: None for k in kinds}
+    eager_ms = None
+    if eager:
+        hip = Hip()
+        ev = {k: [(hip.event(), hip.event()) for _ in range(K)] for k in kinds}
+        torch.cuda.synchronize()
+        # a bounded delay kernel first, so the host has enqueued the steps before the
+        # GPU reaches them and the kernels run back to back, as they do in the graph
+        torch.cuda._sleep(int(lead_ms * 2.4e6))
+        for i, t in enumerate(range(W, W + K)):
+            for k in kinds:
+                moe.set_timing_events(k, *ev[k][i])
+            step(t)
+        torch.cuda.synchronize()
+        for k in kinds:
+            moe.set_timing_events(k, None, None)
+        # with several layers per step the hook re-records each pair on every layer,
+        # so each pair times the step's last launch of that kernel
+        dur = {k: sum(hip.elapsed_ms(a, b) for a, b in ev[k]) / K for k in kinds}
+        eager_ms = hip.elapsed_ms(ev[moe.KERNEL_ROUTER][0][0], ev[moe.KERNEL_DOWN][K - 1][1]) / K
+        if not stack:
+            st = np.array([hip.elapsed_ms(ev[moe.KERNEL_ROUTER][i][0], ev[moe.KERNEL_DOWN][i][1]) * 1e3
+                           for i in range(K)])
+            res["eager_step_us"] = {"p10": round(float(np.percentile(st, 10)), 3),
+                                    "p50": round(float(np.percentile(st, 50)), 3),
+                                    "p90": round(float(np.percentile(st, 90)), 3)}
+        for k in kinds:
+            for a, b in ev[k]:
+                hip.destroy(a)
+                hip.destroy(b)
+
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
+    res["timing"] = "graph" if graph_ms is not None else "eager"
+    idx_h = idx[W:W + K].cpu().numpy()
+    if B > 1:
+        # the grouped path reads each distinct routed expert once per step, plus the shared one
+        uniq = [len(np.unique(idx_h[i, 0][(idx_h[i, 0] >= 0) & (idx_h[i, 0] < c["E"])])) for i in range(K)]
+        n_act = float(np.mean(uniq)) + 1
+        res["distinct_experts_per_step"] = n_act
+    else:
+        n_act = c["K"] + 1
+    gu_bytes = gateup_bytes_per_expert(c) * n_act
+    dn_bytes = down_bytes_per_expert(c) * n_act
+    router_bytes = 4 * c["E"] * H
+    expert_bytes_step = (gu_bytes + dn_bytes) * nL
+    res.update({
+        "ms_per_step": round(ms_per_step, 6),
+        "tokens_per_s": round(B / (ms_per_step / 1e3), 2),
+        "expert_bytes_per_token": round(expert_bytes_step / B),
+        "step_frac": round((expert_bytes_step + router_bytes * nL) / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+    })
+    if eager_ms is not None:
+        rt_us, gu_us, dn_us = (dur[k] * 1e3 for k in kinds)
+        res["eager_ms_per_step"] = round(eager_ms, 6)
+        res["kernel_us"] = {"router": round(rt_us, 3), "gateup": round(gu_us, 3), "down": round(dn_us, 3)}
+        res["gateup_gbps"] = round(gu_bytes / (gu_us * 1e-6) / 1e9, 1)
+        res["gateup_bytes_per_launch"] = round(gu_bytes)
+        # expert bytes over the summed time of every kernel that reads expert bytes
+        eg = (gu_bytes + dn_bytes) / ((gu_us + dn_us) * 1e-6) / 1e9
+        res["expert_weight_gbps"] = round(eg, 1)
+        res["expert_weight_frac_of_peak"] = round(eg / PEAK_HBM_GBPS, 4)
+    del layers, xs, ws, y, idx, wts, descs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(c, budget_s=15.0):
+    """The float64 oracle as it stands on the host cores, on a bounded sample of tokens of the
+    timed layer: tokens decoded on OpenMP threads (oracle_layer_decode_par, each token by the
+    serial oracle), and the serial oracle on one thread."""
+    import oracle
+    import synth
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    ncpu = os.cpu_count() or 1
+    threads = int(omp) if omp.isdigit() and int(omp) > 0 else ncpu
+    E, K, H, I = c["E"], c["K"], c["H"], c["I"]
+    Wr = synth.router(c["seed"], 0, E, H)
+    prior = synth.zipf_bias(E, c["zipf"]) if c["zipf"] else None
+
+    def batch(first, n):
+        x = synth.tokens(c["seed"], 10_000 + first, n, H)
+        lg = oracle.router_logits(x, Wr, prior)
+        need = {E} | {int(e) for b in range(n) for e in oracle.topk(lg[b], K)[0]}
+        ex = {e: synth.experts(c["seed"], 0, e, 1, c["bits"], H, I) for e in sorted(need)}
+        return x, ex
+
+    # one thread: the serial oracle on two tokens
+    x, ex = batch(0, 2)
+    t0 = time.perf_counter()
+    oracle.layer_decode(c["bits"], H, I, E, K, x, Wr, ex, prior=prior)
+    one = 2 / (time.perf_counter() - t0)
+    # all threads: tokens decoded in parallel, until the budget is spent
+    n_tok, elapsed, first = 0, 0.0, 2
+    while elapsed < budget_s and n_tok < 512:
+        x, ex = batch(first, threads)
+        t0 = time.perf_counter()
+        oracle.layer_decode(c["bits"], H, I, E, K, x, Wr, ex, prior=prior, parallel=True)
+        elapsed += time.perf_counter() - t0
+        n_tok += threads
+        first += threads
+    return {"value": round(n_tok / elapsed, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d tokens of the timed layer, %d at a time on %d OpenMP threads (float64 oracle, each token "
+                      "decoded by the serial oracle; weight generation excluded); nproc=%d OMP_NUM_THREADS=%s"
+                      % (n_tok, threads, threads, ncpu, omp or "unset"),
+            "one_thread_tokens_per_s": round(one, 3)}
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
         # bench.py --pmc-summary WORKLOAD KERNEL FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv COPY_MIB
@@ -241,8 +441,10 @@ def main():
     ap.add_argument("--distinct", type=int, default=0,
                     help="stack: generate this many distinct layers and fill the rest with device copies "
                          "(0 = every layer distinct)")
+    ap.add_argument("--replays", type=int, default=5, help="graph replays timed (median reported)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-eager", action="store_true", help="skip the per-kernel event pass (profiling runs)")
+    ap.add_argument("--no-configs", action="store_true", help="time the named workload only")
     ap.add_argument("--lead-ms", type=float, default=30.0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -255,9 +457,7 @@ def main():
         sys.exit(2)
 
     import torch
-    import synth
     import quantized_expert_dequant_amd as moe
-    from quantized_expert_dequant_amd.slab import workspace
 
     dev = "cuda"
     torch.cuda.init()
@@ -275,178 +475,77 @@ def main():
         return
 
     c = dict(WORKLOADS[args.workload])
-    K, W, B, H = args.steps, args.warmup, c["B"], c["H"]
-    stack = c["layers"] > 1
-    n_distinct = min(args.distinct or c["layers"], c["layers"]) if stack else 1
-    n_copies = c["layers"] if stack else max(1, args.rotate)
-    log("workload %s: building %d layer(s) (%d distinct)" % (args.workload, n_copies, n_distinct))
-    layers = build_layers(c, n_distinct, n_copies, dev)
-
-    # tokens for every warmup + timed step, resident in HBM before timing
-    xs_host = np.stack([synth.tokens(c["seed"], t, B, H) for t in range(W + K)])
-    xs = torch.from_numpy(xs_host).to(dev)
-    ws, ws_n = workspace(layers[0].desc, B, stack=stack)
-    y = torch.empty((W + K, B, H), dtype=torch.float32, device=dev)
-    nL = c["layers"]
-    idx = torch.empty((W + K, nL, B, c["K"]), dtype=torch.int32, device=dev)
-    wts = torch.empty((W + K, nL, B, c["K"]), dtype=torch.float32, device=dev)
-    descs = [L.desc for L in layers]
-
-    def step(t):
-        if stack:
-            moe.stack_decode(descs, xs[t], B, RMS_EPS, y[t], idx[t], wts[t], ws, ws_n)
-        else:
-            L = layers[t % n_copies]
-            moe.layer_decode(L.desc, xs[t], B, y[t], idx[t, 0], wts[t, 0], ws, ws_n)
-
-    # parity spot check on the first token (layer copy 0 == distinct layer 0)
-    step(0)
-    torch.cuda.synchronize()
-    if stack:
-        # layer 0 of the first token, decoded on its own, against the oracle (every layer of a
-        # short stack is checked teacher-forced in the GPU tests)
-        y0 = torch.empty((B, H), dtype=torch.float32, device=dev)
-        i0 = torch.empty((B, c["K"]), dtype=torch.int32, device=dev)
-        w0 = torch.empty((B, c["K"]), dtype=torch.float32, device=dev)
-        moe.layer_decode(layers[0].desc, xs[0], B, y0, i0, w0, ws, ws_n)
-        torch.cuda.synchronize()
-        ok, err = oracle_check(c, xs_host[0], y0.cpu().numpy(), i0.cpu().numpy())
-        ok = ok and bool(torch.equal(i0, idx[0, 0]))
-    else:
-        ok, err = oracle_check(c, xs_host[0], y[0].cpu().numpy(), idx[0, 0].cpu().numpy())
-    log("parity spot check: ok=%s max rel err %.3e" % (ok, err))
-    if not ok:
-        print(json.dumps({"metric": METRIC, "value": None, "error": "parity check failed", "rel_err": err}))
+    r = measure(args.workload, args.steps, args.warmup, dev, rotate=args.rotate, distinct=args.distinct,
+                graph=not args.no_graph, eager=not args.no_eager, warm=True, replays=args.replays,
+                lead_ms=args.lead_ms)
+    if not r["parity_ok"]:
+        print(json.dumps({"metric": METRIC, "value": None, "error": "parity check failed",
+                          "rel_err": r["parity_rel_err"]}))
         sys.exit(1)
-
-    for t in range(W):
-        step(t)
-    torch.cuda.synchronize()
-
-    # ---- timed region 1: graph replay of K steps -----------------------------
-    graph_ms = None
-    if not args.no_graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                for t in range(W, W + K):
-                    step(t)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        g.replay()                      # one untimed replay, then check it against eager
-        torch.cuda.synchronize()
-        y_graph = y[W + K - 1].clone()
-        step(W + K - 1)
-        torch.cuda.synchronize()
-        if not torch.equal(y_graph, y[W + K - 1]):
-            log("graph replay differs from eager: graph timing disabled")
-        else:
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            g.replay()
-            torch.cuda.synchronize()
-            graph_ms = (time.perf_counter() - t0) * 1e3 / K
-        del g
-
-    # ---- timed region 2: eager steps with kernel events ------------------------
-    kinds = [moe.KERNEL_ROUTER, moe.KERNEL_GATEUP, moe.KERNEL_DOWN]
-    dur = {k: None for k in kinds}
-    eager_ms = None
-    eager_pct = None
-    if not args.no_eager:
-        hip = Hip()
-        ev = {k: [(hip.event(), hip.event()) for _ in range(K)] for k in kinds}
-        torch.cuda.synchronize()
-        # a bounded delay kernel first, so the host has enqueued the steps before the
-        # GPU reaches them and the kernels run back to back, as they do in the graph
-        torch.cuda._sleep(int(args.lead_ms * 2.4e6))
-        for i, t in enumerate(range(W, W + K)):
-            for k in kinds:
-                moe.set_timing_events(k, *ev[k][i])
-            step(t)
-        torch.cuda.synchronize()
-        for k in kinds:
-            moe.set_timing_events(k, None, None)
-        # with several layers per step the hook re-records each pair on every layer,
-        # so each pair times the step's last launch of that kernel
-        dur = {k: sum(hip.elapsed_ms(a, b) for a, b in ev[k]) / K for k in kinds}
-        eager_ms = hip.elapsed_ms(ev[moe.KERNEL_ROUTER][0][0], ev[moe.KERNEL_DOWN][K - 1][1]) / K
-        if not stack:  # per-step spread: router start to down end of each step
-            st = np.array([hip.elapsed_ms(ev[moe.KERNEL_ROUTER][i][0], ev[moe.KERNEL_DOWN][i][1]) * 1e3
-                           for i in range(K)])
-            eager_pct = {"p10": round(float(np.percentile(st, 10)), 3), "p50": round(float(np.percentile(st, 50)), 3),
-                         "p90": round(float(np.percentile(st, 90)), 3)}
-        for k in kinds:
-            for a, b in ev[k]:
-                hip.destroy(a)
-                hip.destroy(b)
-    launches = nL
-
-    # ---- numbers ---------------------------------------------------------------
-    ms_per_step = graph_ms if graph_ms is not None else eager_ms
-    tokens_per_step = B
-    value = tokens_per_step / (ms_per_step / 1e3)
-    idx_h = idx[W:W + K].cpu().numpy()
-    if B > 1:
-        # the grouped path reads each distinct routed expert once per step, plus the shared one
-        uniq = [len(np.unique(idx_h[i, 0][(idx_h[i, 0] >= 0) & (idx_h[i, 0] < c["E"])])) for i in range(K)]
-        n_experts = float(np.mean(uniq)) + 1
-    else:
-        n_experts = c["K"] + 1
-    n_act = n_experts
-    gu_bytes = gateup_bytes_per_expert(c) * n_act
-    dn_bytes = down_bytes_per_expert(c) * n_act
-    if dur[moe.KERNEL_GATEUP] is None:
-        print(json.dumps({"metric": METRIC, "value": round(value, 2), "unit": "tokens/s",
-                          "ms_per_step": round(ms_per_step, 6), "note": "kernel event pass skipped"}), flush=True)
+    if "kernel_us" not in r:
+        print(json.dumps({"metric": METRIC, "value": r["tokens_per_s"], "unit": "tokens/s",
+                          "ms_per_step": r["ms_per_step"], "note": "kernel event pass skipped"}), flush=True)
         return
-    gu_us = dur[moe.KERNEL_GATEUP] * 1e3
-    dn_us = dur[moe.KERNEL_DOWN] * 1e3
-    rt_us = dur[moe.KERNEL_ROUTER] * 1e3
-    achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-    expert_gbps = (gu_bytes + dn_bytes) / ((gu_us + dn_us) * 1e-6) / 1e9
-    traffic = traffic_from_profile(args.workload, launches)
+    B, stack = c["B"], c["layers"] > 1
+    traffic = traffic_from_profile(args.workload, c["layers"])
+    gu_us = r["kernel_us"]["gateup"]
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 6),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",  # fp16 x fp16 products (codes turned exactly into fp16), fp32 accumulation
         "data": "synthetic",
-        "config": {"workload": "%s: H=%d I=%d E=%d+1 shared K=%d %d-bit group 64 bf16 scale+bias, B=%d%s" % (
-            args.workload, H, c["I"], c["E"], c["K"], c["bits"], B,
-            ", %d layers with RMS renorm" % nL if stack else ""),
-            "global_batch": B, "rotation_copies": n_copies, "timing": "graph" if graph_ms else "eager",
-            **({"distinct_layers": n_distinct} if stack else {})},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "kernel": ("gate/up phase: k_grouped_mfma<0> + k_gemv_gateup" if B > 1
-                                else "k_gateup_fast"),
-                     "bytes_per_launch": round(gu_bytes), "avg_us": round(gu_us, 3)},
-        "expert_weight_gbps": round(expert_gbps, 1),
-        "expert_weight_frac_of_peak": round(expert_gbps / PEAK_HBM_GBPS, 4),
-        "kernel_us": {"router": round(rt_us, 3), "gateup": round(gu_us, 3), "down": round(dn_us, 3)},
-        "eager_ms_per_step": round(eager_ms, 6),
-        **({"eager_step_us": eager_pct} if eager_pct else {}),
-        "parity_rel_err": err,
+        "config": {"workload": r["config"], "global_batch": B, "rotation_copies": r["rotation_copies"],
+                   "timing": r["timing"] + (" (median of %d replays, GPU events)" % args.replays
+                                            if r["timing"] == "graph" else ""),
+                   **({"distinct_layers": r["distinct_layers"]} if stack else {})},
+        "roofline": {"bound": "hbm", "achieved": r["gateup_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(r["gateup_gbps"] / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                     "kernel": ("gate/up phase: k_grouped_mfma<0> + k_gemv_gateup" if B > 1 else "k_gateup_fast"),
+                     "bytes_per_launch": r["gateup_bytes_per_launch"], "avg_us": gu_us,
+                     "step_frac": r["step_frac"]},
+        "expert_weight_gbps": r["expert_weight_gbps"],
+        "expert_weight_frac_of_peak": r["expert_weight_frac_of_peak"],
+        "kernel_us": r["kernel_us"],
+        "graph_replays_ms_per_step": r.get("graph_replays_ms_per_step"),
+        "eager_ms_per_step": r["eager_ms_per_step"],
+        **({"warm_ms_per_step": r["warm_ms_per_step"]} if "warm_ms_per_step" in r else {}),
+        **({"eager_step_us": r["eager_step_us"]} if "eager_step_us" in r else {}),
+        **({"distinct_experts_per_step": r["distinct_experts_per_step"]} if B > 1 else {}),
+        "parity_rel_err": r["parity_rel_err"],
     }
-    if B > 1:
-        out["distinct_experts_per_step"] = n_experts
+    if not args.no_configs:
+        # every other workload at its own shape, fewer steps, same measurement
+        extra = {"layer2": dict(steps=100, warmup=10), "batched": dict(steps=40, warmup=5),
+                 "stack": dict(steps=10, warmup=2, distinct=4), "layer": dict(steps=100, warmup=10)}
+        cfgs = {}
+        for name, kw in extra.items():
+            if name == args.workload:
+                continue
+            e = measure(name, kw["steps"], kw["warmup"], dev, rotate=args.rotate, distinct=kw.get("distinct", 0),
+                        warm=False, replays=3, lead_ms=args.lead_ms)
+            keep = ("config", "parity_ok", "parity_rel_err", "steps", "ms_per_step", "tokens_per_s",
+                    "expert_bytes_per_token", "expert_weight_gbps", "expert_weight_frac_of_peak", "gateup_gbps",
+                    "step_frac", "kernel_us", "distinct_experts_per_step", "distinct_layers")
+            e = {k: e[k] for k in keep if k in e}
+            if "gateup_gbps" in e:
+                e["gateup_frac"] = round(e["gateup_gbps"] / PEAK_HBM_GBPS, 4)
+            cfgs[name] = e
+        out["configs"] = cfgs
     if not args.cpu_seconds <= 0:
         log("timing the oracle on the host ...")
         if stack:
-            # one layer of the stack's shape timed on the host, per token through nL layers
-            cb = cpu_baseline(dict(c, layers=1, seed=c["seed"]), args.cpu_seconds)
-            cb["value"] = cb["value"] / nL
-            cb["sample"] += "; per-layer time extrapolated to %d layers (one layer timed)" % nL
+            cb = cpu_baseline(dict(c, layers=1), args.cpu_seconds)
+            cb["value"] = round(cb["value"] / c["layers"], 4)
+            cb["one_thread_tokens_per_s"] = round(cb["one_thread_tokens_per_s"] / c["layers"], 5)
+            cb["sample"] += "; per-layer time extrapolated to %d layers (one layer timed)" % c["layers"]
             out["cpu_baseline"] = cb
         else:
             out["cpu_baseline"] = cpu_baseline(c, args.cpu_seconds)

@@ -90,11 +90,19 @@ typedef struct moe_layer_desc {
  */
 size_t moe_expert_record_bytes(int bits, int H, int I, int group);
 
-/* Workspace bytes needed by moe_layer_decode / moe_expert_ffn_* for B tokens
- * (and by moe_stack_decode, which needs the same).  0 on invalid desc/B. */
+/*
+ * Workspace bytes needed by moe_layer_decode / moe_expert_ffn_* for B tokens
+ * (and by moe_stack_decode, which needs the same).  The workspace holds what
+ * passes between the steps of the layer ([LLMAPIS] section 深度分析: routing,
+ * reading, dequantization, local compute, combine): the logits and routing, the
+ * token's dequant operand (scale*x / bias*x folded per group), h of every
+ * active expert and, for batches, the grouping and per-expert partial outputs.
+ * 0 on an invalid desc or B (moe_last_error says why).
+ */
 size_t moe_workspace_bytes(const moe_layer_desc* desc, int B);
 
-/* Workspace bytes needed by moe_route_topk. 0 on invalid arguments. */
+/* Workspace bytes needed by moe_route_topk: the fp64 logits of B tokens over E
+ * experts ([LLMAPIS] section 深度分析, the routing step).  0 on invalid arguments. */
 size_t moe_route_workspace_bytes(int B, int E, int K);
 
 /*
@@ -135,8 +143,12 @@ int moe_route_topk(const float* x, int B, const float* w_router, const float* lo
                    size_t ws_bytes, void* stream);
 
 /*
- * Expert FFNs and combine for given routing: y[b] = sum_k w[b][k] *
- * FFN_{idx[b][k]}(x[b]) + shared_weight * FFN_shared(x[b]).
+ * Expert FFNs and combine for given routing ([LLMAPIS] section 深度分析: read the
+ * selected experts, dequantize, compute, combine with the routing weights, the
+ * dequant folding precomputed scale*x and bias*x into fused multiply-adds; 4-bit
+ * or 2-bit experts, [LLMAPIS] section 为什么值得关注; one always-on shared expert,
+ * [LLMAPIS] section 数据和技术细节):
+ * y[b] = sum_k w[b][k] * FFN_{idx[b][k]}(x[b]) + shared_weight * FFN_shared(x[b]).
  *   x: fp32 [B][H]; idx: int32 [B][K]; w: fp32 [B][K]; y_out: fp32 [B][H].
  * _q4 requires desc->bits == 4, _q2 requires desc->bits == 2.
  * With 4-bit codes and B > 1 the tokens are grouped by expert (as
@@ -150,7 +162,9 @@ int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const i
                       const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Whole layer: route, then expert FFNs and combine, as above.
+ * Whole layer ([LLMAPIS] section 深度分析: routing + reading + dequantization +
+ * local compute + result combine; [CLAUDAY]: K of 512 experts active, router at
+ * full precision): route, then expert FFNs and combine, as above.
  *   x: fp32 [B][H]; y_out: fp32 [B][H]; idx_out: int32 [B][K] or NULL;
  *   w_out: fp32 [B][K] or NULL.
  * Value range: with 4-bit codes and B >= 2 the experts that several tokens
@@ -179,7 +193,11 @@ int moe_group_tokens(const int32_t* idx, int B, int K, int E, int32_t* offsets_o
 
 /*
  * x_out[b] = y[b] / sqrt(mean(y[b]^2) + eps), no gain, no residual: the
- * normalization between stacked layers.  y, x_out: fp32 [B][H]; may alias.
+ * normalization between stacked MoE layers ([LLMAPIS] section 数据和技术细节 gives
+ * the 60-layer stack; the pages do not print the normalization, this RMS form
+ * without gain or residual is the reading the library fixes).
+ * y, x_out: fp32 [B][H]; may alias.  MOE_EINVAL for B outside [1, 256], H <= 0,
+ * eps < 0 or a NULL / misaligned pointer.
  */
 int moe_rmsnorm(const float* y, int B, int H, float eps, float* x_out, void* stream);
 
@@ -210,6 +228,23 @@ int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* x,
 #define MOE_KERNEL_GATEUP 2
 #define MOE_KERNEL_DOWN 3
 int moe_set_timing_events(int kernel, void* start_event, void* stop_event);
+
+/*
+ * Launch shape of the batched path for B tokens of this layer on the calling
+ * thread's current device, for inspection (no device work, no synchronization).
+ * info_out: host int32 [8]:
+ *   [0] 1 if B tokens take the grouped path (each active expert read once per
+ *       call, [LLMAPIS] section 深度分析), else 0 (token by token)
+ *   [1] blocks of the gate/up matrix-core launch (its work units are cut into
+ *       that many equal ranges)
+ *   [2] matrix-core tiles per work-list group in the gate/up phase
+ *   [3] K chunks per gate/up tile when tiles outnumber the blocks of [1] (the
+ *       partial sums of a tile shared by two blocks are added in K order)
+ *   [4] blocks of the down matrix-core launch   [5] tiles per group, down
+ *   [6] experts with fewer tokens than this run as dot2 GEMV groups
+ *   [7] most tokens of one matrix-core work-list group
+ */
+int moe_grouped_launch_info(const moe_layer_desc* desc, int B, int32_t* info_out);
 
 /* Text of the last error on the calling thread ("" if none). */
 const char* moe_last_error(void);

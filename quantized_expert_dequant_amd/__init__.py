@@ -69,6 +69,7 @@ def lib():
             "moe_rmsnorm": (i32, [vp, i32, i32, f32, vp, vp]),
             "moe_stack_decode": (i32, [dp, i32, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
             "moe_set_timing_events": (i32, [i32, vp, vp]),
+            "moe_grouped_launch_info": (i32, [dp, i32, vp]),
             "moe_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -179,6 +180,15 @@ def stack_decode(descs, x, B, eps, y_out, idx_out, w_out, ws, ws_bytes, stream=N
     arr = (LayerDesc * len(descs))(*descs)
     return _check(lib().moe_stack_decode(arr, len(descs), _p(x), B, eps, _p(y_out), _p(idx_out), _p(w_out), _p(ws),
                                          ws_bytes, _stream(stream)))
+
+
+def grouped_launch_info(desc, B):
+    """Launch shape of the batched path (dict); see moe_grouped_launch_info."""
+    info = (ctypes.c_int32 * 8)()
+    _check(lib().moe_grouped_launch_info(ctypes.byref(desc), B, info))
+    keys = ("grouped", "gateup_blocks", "gateup_tiles_per_group", "gateup_k_chunks", "down_blocks",
+            "down_tiles_per_group", "gemv_below_tokens", "group_tokens")
+    return dict(zip(keys, list(info)))
 
 
 def set_timing_events(kernel, start_event, stop_event):

@@ -53,6 +53,17 @@ struct GroupedWork {
 };
 
 bool grouped_supported(const Layout& L, int B, int K);
+// blocks of the batched launches on the current device (each as many as stay resident)
+struct GroupedBlocks {
+    int gateup, down, gemv_gateup, gemv_down;
+};
+GroupedBlocks grouped_blocks();
+// MFMA tiles of one work-list group (128 output rows) in the gate/up and the down phase
+int grouped_tiles(const Layout& L, int down);
+// K chunks a gate/up tile is cut into when the tiles outnumber the gate/up blocks
+int grouped_gateup_chunks();
+// most tokens of one matrix-core work-list group
+int grouped_group_tokens();
 size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E);
 GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E);
 int router_splits(int H);

@@ -27,6 +27,8 @@
 //   k_combine        per-token routing-weighted sum of the down outputs
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "grouped.h"
 #include "topk.h"
@@ -43,6 +45,7 @@ constexpr int GM_GROUP = 32;         // most tokens of one MFMA work-list group
 #endif
 constexpr int GV_TOKENS = MOE_GV_TOKENS;  // an expert with fewer tokens than this runs as a dot2 GEMV group
 constexpr int GM_MAX_BLOCKS = 1024;  // most blocks of a stream-split launch
+constexpr int GM_MAX_DEVICES = 64;   // devices whose launch shapes are cached
 
 __device__ inline f4 mfma16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
@@ -499,6 +502,9 @@ struct GmShape {
 
 __host__ __device__ inline int gm_tiles(const Layout& L, int mode) { return ((mode == MODE_GATEUP ? L.I : L.H) + GM_ROWS - 1) / GM_ROWS; }
 __host__ __device__ inline int gm_steps(const Layout& L, int mode) { return (2 * (mode == MODE_GATEUP ? L.Gh : L.Gi) + 3) / 4; }
+int grouped_tiles(const Layout& L, int down) { return gm_tiles(L, down ? MODE_DOWN : MODE_GATEUP); }
+int grouped_gateup_chunks() { return GM_KC_GATEUP; }
+int grouped_group_tokens() { return GM_GROUP; }
 // first unit of block b when T units are cut into nb ranges (T * nb < 2^32)
 __device__ inline int gm_lo(int b, int T, int nb) { return (int)(((uint32_t)b * (uint32_t)T) / (uint32_t)nb); }
 // the block whose range holds unit x
@@ -1148,27 +1154,47 @@ GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E)
 
 // blocks of the stream split: as many as stay resident together (the work is cut
 // into equal ranges, so all of them must run at once), at most GM_MAX_BLOCKS
-static int resident_blocks(const void* kernel, int threads)
+static int resident_blocks(int dev, const void* kernel, int threads)
 {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return GM_MAX_BLOCKS / 2;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
         per_cu = 1;
     return max(1, min(GM_MAX_BLOCKS, cus * per_cu));
+}
+
+// Block counts of the four stream-split launches on the calling thread's current
+// device.  Computed once per device under a lock and only then published, so a
+// thread never sees a partly filled entry; callers on several threads and devices
+// are safe.
+GroupedBlocks grouped_blocks()
+{
+    static std::mutex mu;
+    static GroupedBlocks cache[GM_MAX_DEVICES];
+    static bool filled[GM_MAX_DEVICES];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    const int slot = dev < GM_MAX_DEVICES ? dev : -1;
+    std::lock_guard<std::mutex> lock(mu);
+    if (slot >= 0 && filled[slot]) return cache[slot];
+    GroupedBlocks n;
+    n.gateup = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_GATEUP>, GM_THREADS);
+    n.down = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_DOWN>, GM_THREADS);
+    n.gemv_gateup = resident_blocks(dev, (const void*)k_gemv_gateup, 64 * GV_WAVES);
+    n.gemv_down = resident_blocks(dev, (const void*)k_gemv_down, 64 * GV_WAVES);
+    if (slot >= 0) {
+        cache[slot] = n;
+        filled[slot] = true;
+    }
+    return n;
 }
 
 void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W, const float* x, const float* w,
                         float shared_w, int B, int K, int E, uint4* xq, float4* xst, bool prepped, float* y,
                         hipStream_t s, Timing tg, Timing td)
 {
-    static int nb_gu = 0, nb_dn = 0, nb_gvu = 0, nb_gvd = 0;  // per process: one device type
-    if (!nb_gu) {
-        nb_gu = resident_blocks((const void*)k_grouped_mfma<MODE_GATEUP>, GM_THREADS);
-        nb_dn = resident_blocks((const void*)k_grouped_mfma<MODE_DOWN>, GM_THREADS);
-        nb_gvu = resident_blocks((const void*)k_gemv_gateup, 64 * GV_WAVES);
-        nb_gvd = resident_blocks((const void*)k_gemv_down, 64 * GV_WAVES);
-    }
+    const GroupedBlocks nb = grouped_blocks();
+    const int nb_gu = nb.gateup, nb_dn = nb.down, nb_gvu = nb.gemv_gateup, nb_gvd = nb.gemv_down;
     const int gv_t = gemv_tokens(L);
     const bool gv = gv_t > 1;
 

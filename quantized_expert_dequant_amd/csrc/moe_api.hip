@@ -320,6 +320,26 @@ int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y
     return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, (hipStream_t)stream);
 }
 
+int moe_grouped_launch_info(const moe_layer_desc* desc, int B, int32_t* info_out)
+{
+    const char* fn = "moe_grouped_launch_info";
+    int rc = check_desc(fn, desc, B);
+    if (rc) return rc;
+    if (!info_out) return fail(MOE_EINVAL, "%s: info_out is NULL", fn);
+    const Layout L = make_layout(desc->bits, desc->H, desc->I);
+    const bool grouped = grouped_supported(L, B, desc->K);
+    const GroupedBlocks nb = grouped_blocks();
+    info_out[0] = grouped ? 1 : 0;
+    info_out[1] = nb.gateup;
+    info_out[2] = grouped_tiles(L, 0);
+    info_out[3] = grouped_gateup_chunks();
+    info_out[4] = nb.down;
+    info_out[5] = grouped_tiles(L, 1);
+    info_out[6] = gemv_tokens(L);
+    info_out[7] = grouped_group_tokens();
+    return ok();
+}
+
 int moe_group_tokens(const int32_t* idx, int B, int K, int E, int32_t* offsets_out, int32_t* tokens_out,
                      int32_t* slots_out, void* stream)
 {

@@ -66,11 +66,23 @@ def oracle_route(cfg, seed, layer, x):
     return Wr, prior, lg, sel
 
 
-def oracle_layer(cfg, seed, layer, x, shared_weight=1.0):
-    """Oracle decode of tokens x through one layer, generating only the experts it selects."""
+def oracle_layer(cfg, seed, layer, x, shared_weight=1.0, parallel=False):
+    """Oracle decode of tokens x through one layer, generating only the experts it selects.
+    parallel=True decodes the tokens on OpenMP threads (each token by the serial oracle)."""
     x = np.atleast_2d(np.asarray(x, np.float32))
     Wr, prior, lg, sel = oracle_route(cfg, seed, layer, x)
     need = sorted({int(e) for s in sel for e in s[0]} | {cfg["E"]})
     experts = {e: synth.experts(seed, layer, e, 1, cfg["bits"], cfg["H"], cfg["I"]) for e in need}
     return oracle.layer_decode(cfg["bits"], cfg["H"], cfg["I"], cfg["E"], cfg["K"], x, Wr, experts, prior=prior,
-                               shared_weight=shared_weight)
+                               shared_weight=shared_weight, parallel=parallel)
+
+
+def mfma_tiles(idx, E, info):
+    """Gate/up matrix-core tiles of a batch's routing, by the grouping rule the library states
+    (moe_grouped_launch_info): the shared expert's B tokens and every routed expert with at
+    least gemv_below_tokens tokens are cut into groups of at most group_tokens."""
+    B = idx.shape[0]
+    counts = np.bincount(idx[(idx >= 0) & (idx < E)].ravel(), minlength=E)
+    g, lo = info["group_tokens"], info["gemv_below_tokens"]
+    groups = (-(-B // g) if B >= lo else 0) + sum(-(-int(c) // g) for c in counts if c >= lo)
+    return groups * info["gateup_tiles_per_group"]

@@ -136,23 +136,21 @@ def test_batched_tiny_many_tokens(layers, step):
 
 @pytest.mark.parametrize("step", range(2))
 def test_batched_full_size(layers, step):
-    """B=64, K=10 with the Zipf(1.1) prior: routing of all 64 tokens, outputs of sampled tokens."""
+    """B=64, K=10 with the Zipf(1.1) prior: routing and output of every one of the 64 tokens
+    against the oracle (both GEMV and MFMA groups; the gate/up tiles are whole here)."""
     n = 4
     L = layers(n)
     cfg, seed = WORKLOADS[n], seed_of(n)
     x = synth.tokens(seed, step, cfg["B"], L.H)
     y, idx, w = _decode(L, x)
-    _, _, _, sel = oracle_route(cfg, seed, 0, x)
-    idx_ref = np.stack([s[0] for s in sel])
-    w_ref = np.stack([s[1] for s in sel])
-    assert min(s[2] for s in sel) > 1e-9
+    y_ref, idx_ref, w_ref, margin = oracle_layer(cfg, seed, 0, x, parallel=True)
+    assert margin.min() > 1e-9
     np.testing.assert_array_equal(idx, idx_ref)
     np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
-    sample = [0, 13, 31, 42, 63]
-    y_ref, _, _, _ = oracle_layer(cfg, seed, 0, x[sample])
-    errs = [rel_err(y[b], y_ref[j]) for j, b in enumerate(sample)]
-    print("batched step %d: distinct experts %d, max rel err %.2e" % (step, len(np.unique(idx)), max(errs)))
-    assert max(errs) <= TOL
+    errs = np.array([rel_err(y[b], y_ref[b]) for b in range(cfg["B"])])
+    print("batched step %d: distinct experts %d, max rel err %.2e (token %d), median %.2e"
+          % (step, len(np.unique(idx)), errs.max(), int(errs.argmax()), np.median(errs)))
+    assert errs.max() <= TOL, "token %d" % int(errs.argmax())
 
 
 def test_batched_is_deterministic(layers):

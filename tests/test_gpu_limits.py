@@ -12,7 +12,7 @@ import synth
 import quantized_expert_dequant_amd as moe
 from quantized_expert_dequant_amd.slab import workspace
 
-from helpers import TOL, W_RTOL, WORKLOADS, build_layer, oracle_layer, oracle_route, rel_err, seed_of
+from helpers import TOL, W_RTOL, WORKLOADS, build_layer, mfma_tiles, oracle_layer, oracle_route, rel_err, seed_of
 
 pytestmark = pytest.mark.gpu
 
@@ -40,24 +40,32 @@ def _decode(layer, x):
 
 
 def test_batched_largest_batch():
-    """B = 256 (the most tokens per call) on the full-size batched layer: the routing of
-    every token, the outputs of sampled tokens (experts shared by dozens of tokens are cut
-    into several 32-token groups)."""
+    """B = 256 (the most tokens per call) on the full-size batched layer: routing and output
+    of every token against the oracle.  Experts shared by dozens of tokens are cut into
+    several 32-token groups, and the gate/up tiles outnumber the blocks of the matrix-core
+    launch, so tiles are cut into K chunks and the tiles two blocks share are finished by
+    adding their partial sums in K order: every output of those tiles is compared here."""
     cfg, seed = dict(WORKLOADS[4]), seed_of(4)
     assert moe.MOE_MAX_B == 256
     L = build_layer(cfg, seed)
-    x = synth.tokens(seed, 40, moe.MOE_MAX_B, L.H)
+    B = moe.MOE_MAX_B
+    info = moe.grouped_launch_info(L.desc, B)
+    assert info["grouped"] == 1 and info["gateup_k_chunks"] > 1
+    x = synth.tokens(seed, 40, B, L.H)
     y, idx, w = _decode(L, x)
-    _, _, _, sel = oracle_route(cfg, seed, 0, x)
-    assert min(s[2] for s in sel) > 1e-9
-    np.testing.assert_array_equal(idx, np.stack([s[0] for s in sel]))
-    np.testing.assert_allclose(w, np.stack([s[1] for s in sel]), rtol=W_RTOL)
+    tiles = mfma_tiles(idx, cfg["E"], info)
+    assert tiles > info["gateup_blocks"], "the K-chunk split is not taken (%d tiles, %d blocks)" % (
+        tiles, info["gateup_blocks"])
     counts = np.bincount(idx.ravel(), minlength=cfg["E"])
     assert counts.max() > 64  # the hottest expert spans more than two MFMA groups
-    sample = [0, 77, 128, 201, 255]
-    y_ref, _, _, _ = oracle_layer(cfg, seed, 0, x[sample])
-    for j, b in enumerate(sample):
-        assert rel_err(y[b], y_ref[j]) <= TOL, "token %d" % b
+    y_ref, idx_ref, w_ref, margin = oracle_layer(cfg, seed, 0, x, parallel=True)
+    assert margin.min() > 1e-9
+    np.testing.assert_array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
+    errs = np.array([rel_err(y[b], y_ref[b]) for b in range(B)])
+    print("B=256: %d tiles on %d blocks, max rel err %.2e (token %d)" % (tiles, info["gateup_blocks"], errs.max(),
+                                                                       int(errs.argmax())))
+    assert errs.max() <= TOL, "token %d" % int(errs.argmax())
     del L
     torch.cuda.empty_cache()
 
