@@ -177,6 +177,25 @@ int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y
                      int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_layer_decode without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory during a call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, results and kernels as moe_layer_decode; its scratch is a
+ * library-owned array of MOE_NOALLOC_SCRATCH_BYTES in each GPU's memory, held
+ * until the process ends.  Calls whose workspace (moe_workspace_bytes) would
+ * exceed it return MOE_EUNSUPPORTED: at H = 4096, I = 1024, E = 512, K = 4
+ * single tokens and 2-bit batches up to about 240 tokens fit, 4-bit batches of
+ * two or more tokens (the grouped path) do not.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (different streams or
+ * threads without ordering) race and must not be issued.  The array's contents
+ * need no initialization.  MOE_EHIP if the array's device address cannot be
+ * obtained.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (8 << 20)
+int moe_layer_decode_noalloc(const moe_layer_desc* desc, const float* x, int B, float* y_out,
+                             int32_t* idx_out, float* w_out, void* stream);
+
+/*
  * Token -> expert grouping of a batch's routing ([LLMAPIS] section 深度分析: only
  * the selected experts are read; with B tokens each selected expert is read
  * once for all the tokens that chose it).  A stable counting sort of the B*K

@@ -21,6 +21,7 @@ MOE_EHIP = -3
 MOE_MAX_K = 32      # largest top-K (include/moe.h)
 MOE_MAX_E = 1024    # most routed experts
 MOE_MAX_B = 256     # most tokens per call
+MOE_NOALLOC_SCRATCH_BYTES = 8 << 20  # scratch of moe_layer_decode_noalloc per GPU
 
 KERNEL_ROUTER = 1
 KERNEL_GATEUP = 2
@@ -65,6 +66,7 @@ def lib():
             "moe_expert_ffn_q4": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_expert_ffn_q2": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_layer_decode": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_layer_decode_noalloc": (i32, [dp, vp, i32, vp, vp, vp, vp]),
             "moe_group_tokens": (i32, [vp, i32, i32, i32, vp, vp, vp, vp]),
             "moe_rmsnorm": (i32, [vp, i32, i32, f32, vp, vp]),
             "moe_stack_decode": (i32, [dp, i32, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
@@ -165,6 +167,11 @@ def expert_ffn_q2(desc, x, B, idx, w, y_out, ws, ws_bytes, stream=None):
 def layer_decode(desc, x, B, y_out, idx_out, w_out, ws, ws_bytes, stream=None):
     return _check(lib().moe_layer_decode(ctypes.byref(desc), _p(x), B, _p(y_out), _p(idx_out), _p(w_out), _p(ws),
                                          ws_bytes, _stream(stream)))
+
+
+def layer_decode_noalloc(desc, x, B, y_out, idx_out, w_out, stream=None):
+    return _check(lib().moe_layer_decode_noalloc(ctypes.byref(desc), _p(x), B, _p(y_out), _p(idx_out), _p(w_out),
+                                                 _stream(stream)))
 
 
 def group_tokens(idx, B, K, E, offsets_out, tokens_out, slots_out, stream=None):

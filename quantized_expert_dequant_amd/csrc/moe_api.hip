@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "grouped.h"
 #include "launch.h"
@@ -141,6 +143,39 @@ int hip_status(const char* fn)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", fn, hipGetErrorString(e));
     return ok();
+}
+
+// Workspace of moe_layer_decode_noalloc: one array per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+// Device address of `scratch` on the current device, looked up on the first call
+// per device (with that device current) under a lock; nullptr if the lookup fails.
+void* scratch_ptr(const char* fn, int& rc)
+{
+    static std::mutex mu;
+    static void* ptrs[NOALLOC_MAX_DEVICES];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) {
+        rc = fail(MOE_EHIP, "%s: no current HIP device (or device id >= %d)", fn, NOALLOC_MAX_DEVICES);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            rc = fail(MOE_EHIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev,
+                      hipGetErrorString(e));
+            return nullptr;
+        }
+        ptrs[dev] = p;
+    }
+    rc = MOE_OK;
+    return ptrs[dev];
 }
 
 }  // namespace
@@ -338,6 +373,28 @@ int moe_grouped_launch_info(const moe_layer_desc* desc, int B, int32_t* info_out
     info_out[6] = gemv_tokens(L);
     info_out[7] = grouped_group_tokens();
     return ok();
+}
+
+int moe_layer_decode_noalloc(const moe_layer_desc* desc, const float* x, int B, float* y_out, int32_t* idx_out,
+                             float* w_out, void* stream)
+{
+    const char* fn = "moe_layer_decode_noalloc";
+    int rc = check_desc(fn, desc, B);
+    if (rc) return rc;
+    CHECK_PTR(desc->w_router);
+    CHECK_OPT_PTR4(desc->logit_bias);
+    CHECK_PTR(x);
+    CHECK_PTR(y_out);
+    CHECK_OPT_PTR4(idx_out);
+    CHECK_OPT_PTR4(w_out);
+    const Work need = carve(nullptr, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
+    if (need.bytes > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_EUNSUPPORTED, "%s: B=%d needs %zu bytes of scratch, more than the %d this entry point holds "
+                    "per GPU (use moe_layer_decode with a workspace)", fn, B, need.bytes, MOE_NOALLOC_SCRATCH_BYTES);
+    void* ws = scratch_ptr(fn, rc);
+    if (!ws) return rc;
+    const Work W = carve(ws, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
+    return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, (hipStream_t)stream);
 }
 
 int moe_group_tokens(const int32_t* idx, int B, int K, int E, int32_t* offsets_out, int32_t* tokens_out,
