@@ -81,6 +81,14 @@ class Hip:
             raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
         return f.value
 
+    def recorded(self, a, b):
+        """True if the pair was recorded (the elapsed time of a never-recorded pair is an error)."""
+        f = ctypes.c_float()
+        ok = self.h.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        if not ok:
+            self.h.hipGetLastError()  # the failed query leaves a sticky error: clear it
+        return ok
+
     def destroy(self, e):
         self.h.hipEventDestroy(e)
 
@@ -336,10 +344,15 @@ def measure(name, steps, warmup, dev, rotate=16, distinct=0, graph=True, eager=T
             moe.set_timing_events(k, None, None)
         # with several layers per step the hook re-records each pair on every layer,
         # so each pair times the step's last launch of that kernel
-        dur = {k: sum(hip.elapsed_ms(a, b) for a, b in ev[k]) / K for k in kinds}
-        eager_ms = hip.elapsed_ms(ev[moe.KERNEL_ROUTER][0][0], ev[moe.KERNEL_DOWN][K - 1][1]) / K
+        # the fused single-token expert kernel (gate/up and down in one launch) records
+        # no separate down events: its down time is part of the gate/up launch
+        recorded = {k: hip.recorded(*ev[k][0]) for k in kinds}
+        dur = {k: (sum(hip.elapsed_ms(a, b) for a, b in ev[k]) / K if recorded[k] else 0.0) for k in kinds}
+        last = moe.KERNEL_DOWN if recorded[moe.KERNEL_DOWN] else moe.KERNEL_GATEUP
+        res["expert_launches"] = "gate/up + down" if recorded[moe.KERNEL_DOWN] else "fused gate/up + down"
+        eager_ms = hip.elapsed_ms(ev[moe.KERNEL_ROUTER][0][0], ev[last][K - 1][1]) / K
         if not stack:
-            st = np.array([hip.elapsed_ms(ev[moe.KERNEL_ROUTER][i][0], ev[moe.KERNEL_DOWN][i][1]) * 1e3
+            st = np.array([hip.elapsed_ms(ev[moe.KERNEL_ROUTER][i][0], ev[last][i][1]) * 1e3
                            for i in range(K)])
             res["eager_step_us"] = {"p10": round(float(np.percentile(st, 10)), 3),
                                     "p50": round(float(np.percentile(st, 50)), 3),
@@ -373,8 +386,10 @@ def measure(name, steps, warmup, dev, rotate=16, distinct=0, graph=True, eager=T
         rt_us, gu_us, dn_us = (dur[k] * 1e3 for k in kinds)
         res["eager_ms_per_step"] = round(eager_ms, 6)
         res["kernel_us"] = {"router": round(rt_us, 3), "gateup": round(gu_us, 3), "down": round(dn_us, 3)}
-        res["gateup_gbps"] = round(gu_bytes / (gu_us * 1e-6) / 1e9, 1)
-        res["gateup_bytes_per_launch"] = round(gu_bytes)
+        # the dominant launch: the gate/up kernel, or the fused kernel that also does the down phase
+        dom_bytes = gu_bytes + (dn_bytes if dn_us == 0.0 else 0.0)
+        res["gateup_gbps"] = round(dom_bytes / (gu_us * 1e-6) / 1e9, 1)
+        res["gateup_bytes_per_launch"] = round(dom_bytes)
         # expert bytes over the summed time of every kernel that reads expert bytes
         eg = (gu_bytes + dn_bytes) / ((gu_us + dn_us) * 1e-6) / 1e9
         res["expert_weight_gbps"] = round(eg, 1)
