@@ -58,6 +58,10 @@ def lib():
         L.oracle_group_by_expert.restype = i32
         L.oracle_group_by_expert.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.oracle_rms_renorm.argtypes = [i32, vp, dbl, vp]
+        L.oracle_bf16_round.restype = ctypes.c_uint16
+        L.oracle_bf16_round.argtypes = [dbl]
+        L.oracle_requant_group.argtypes = [i32, vp, ctypes.c_uint16, ctypes.c_uint16, vp, vp, vp]
+        L.oracle_requant_expert.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -224,3 +228,33 @@ def rms_renorm(y, eps=1e-6):
     x = np.empty_like(y)
     lib().oracle_rms_renorm(y.shape[0], _p(y), eps, _p(x))
     return x
+
+
+def bf16_round(v):
+    """Bit pattern of the nearest bf16 value of a double (ties to even)."""
+    return int(lib().oracle_bf16_round(float(v)))
+
+
+def requant_group(q4, s4, b4):
+    """(q2 [n], s2 bits, b2 bits) of one group of 4-bit codes with bf16 bit patterns s4, b4."""
+    q4 = _c(q4, np.int32)
+    q2 = np.empty_like(q4)
+    s2 = np.zeros(1, np.uint16)
+    b2 = np.zeros(1, np.uint16)
+    lib().oracle_requant_group(q4.shape[0], _p(q4), int(s4), int(b4), _p(q2), _p(s2), _p(b2))
+    return q2, int(s2[0]), int(b2[0])
+
+
+def requant_expert(H, I, gate, up, down, scales, biases, group=64):
+    """Canonical 4-bit expert -> canonical 2-bit expert: (gate2, up2, down2, scales2, biases2)."""
+    g4, u4, d4 = _c(gate, np.uint8), _c(up, np.uint8), _c(down, np.uint8)
+    s4, b4 = _c(scales, np.uint16).reshape(-1), _c(biases, np.uint16).reshape(-1)
+    g2 = np.empty((I, H // 4), np.uint8)
+    u2 = np.empty((I, H // 4), np.uint8)
+    d2 = np.empty((H, I // 4), np.uint8)
+    s2 = np.empty_like(s4)
+    b2 = np.empty_like(b4)
+    lib().oracle_requant_expert(H, I, group, _p(g4), _p(u4), _p(d4), _p(s4), _p(b4), _p(g2), _p(u2), _p(d2),
+                                _p(s2), _p(b2))
+    return g2, u2, d2, s2, b2
+

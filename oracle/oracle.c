@@ -378,3 +378,109 @@ void oracle_rms_renorm(int H, const double* y, double eps, double* x)
     double inv = 1.0 / sqrt(ss / H + eps);
     for (int c = 0; c < H; ++c) x[c] = y[c] * inv;
 }
+
+/* ---- offline 4-bit -> 2-bit requantization ------------------------------------- */
+
+/*
+ * The pages report that the experts were requantized from 4-bit to 2-bit,
+ * shrinking the expert files from 209 GB to 120 GB ([CLAUDAY]; [LLMAPIS]
+ * section 数据和技术细节), without giving the procedure.  The reading used here is
+ * a per-group min/max affine refit of the dequantized 4-bit weights:
+ *   w_c = s4 * q4_c + b4 for the 64 weights c of a group (exact in double),
+ *   b2  = bf16(min_c w_c), s2 = bf16((max_c w_c - min_c w_c) / 3),
+ *   q2_c = clamp(rint((w_c - b2) / s2), 0, 3)   (q2_c = 0 when s2 == 0),
+ * every step in IEEE double (rint: to nearest, ties to even) and bf16() a single
+ * rounding of the double to the nearest bf16 value, ties to even.
+ */
+
+/* Nearest bf16 value of a finite double, ties to even, as a bit pattern: one
+ * rounding of the 53-bit mantissa to bf16's 8 bits, with fp32's exponent range
+ * (subnormals in steps of 2^-133); magnitudes that round past the largest bf16
+ * become infinity. */
+uint16_t oracle_bf16_round(double v)
+{
+    if (v != v) return 0x7FC0;
+    uint16_t sign = (v < 0 || (v == 0 && 1.0 / v < 0)) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                      /* a = m * 2^e, 0.5 <= m < 1 */
+    int q = e - 8;                     /* a normal bf16 keeps 8 significant bits: quantum 2^(e-8) */
+    if (q < -133) q = -133;            /* below 2^-126: the subnormal quantum */
+    double r = nearbyint(ldexp(a, -q));   /* multiple of the quantum, ties to even */
+    double rv = ldexp(r, q);
+    if (rv > 3.3895313892515355e38) return (uint16_t)(sign | 0x7F80);   /* past the largest bf16 */
+    float f = (float)rv;               /* exact: rv is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | ((u >> 16) & 0x7FFF));
+}
+
+/* One group of n weights given as 4-bit codes q4[c] with bf16 s4, b4 -> 2-bit codes q2[c]
+ * and bf16 s2, b2 (bit patterns), as defined above. */
+void oracle_requant_group(int n, const int* q4, uint16_t s4, uint16_t b4, int* q2, uint16_t* s2_out,
+                          uint16_t* b2_out)
+{
+    double s = oracle_bf16_to_double(s4), b = oracle_bf16_to_double(b4);
+    double lo = s * q4[0] + b, hi = lo;
+    for (int c = 1; c < n; ++c) {
+        double w = s * q4[c] + b;
+        if (w < lo) lo = w;
+        if (w > hi) hi = w;
+    }
+    uint16_t b2 = oracle_bf16_round(lo);
+    uint16_t s2 = oracle_bf16_round((hi - lo) / 3.0);
+    double bd = oracle_bf16_to_double(b2), sd = oracle_bf16_to_double(s2);
+    for (int c = 0; c < n; ++c) {
+        if (sd == 0.0) {
+            q2[c] = 0;
+            continue;
+        }
+        double t = nearbyint((s * q4[c] + b - bd) / sd);
+        q2[c] = t < 0.0 ? 0 : (t > 3.0 ? 3 : (int)t);
+    }
+    *s2_out = s2;
+    *b2_out = b2;
+}
+
+/* A [rows][cols] matrix of canonical 4-bit codes with per-group bf16 scales and
+ * biases -> canonical 2-bit codes [rows][cols/4 bytes] and new scales / biases. */
+static void requant_matrix(int rows, int cols, int group, const uint8_t* codes4, const uint16_t* s4,
+                           const uint16_t* b4, uint8_t* codes2, uint16_t* s2, uint16_t* b2)
+{
+    int gpr = cols / group;
+    int* q4 = (int*)malloc(sizeof(int) * (size_t)group);
+    int* q2 = (int*)malloc(sizeof(int) * (size_t)group);
+    if (!q4 || !q2) {
+        free(q4);
+        free(q2);
+        return;
+    }
+    memset(codes2, 0, (size_t)rows * cols / 4);
+    for (int r = 0; r < rows; ++r)
+        for (int g = 0; g < gpr; ++g) {
+            const uint8_t* row = codes4 + (long)r * cols / 2;
+            for (int c = 0; c < group; ++c) q4[c] = oracle_code_at(row, 4, (long)g * group + c);
+            long gi = (long)r * gpr + g;
+            oracle_requant_group(group, q4, s4[gi], b4[gi], q2, s2 + gi, b2 + gi);
+            for (int c = 0; c < group; ++c) {
+                long col = (long)g * group + c;
+                codes2[(long)r * cols / 4 + col / 4] |= (uint8_t)(q2[c] << (2 * (col % 4)));
+            }
+        }
+    free(q4);
+    free(q2);
+}
+
+/* One canonical 4-bit expert -> the canonical 2-bit expert (same H, I, group). */
+void oracle_requant_expert(int H, int I, int group, const uint8_t* gate4, const uint8_t* up4,
+                           const uint8_t* down4, const uint16_t* scales4, const uint16_t* biases4,
+                           uint8_t* gate2, uint8_t* up2, uint8_t* down2, uint16_t* scales2,
+                           uint16_t* biases2)
+{
+    long ngu = (long)I * (H / group);
+    requant_matrix(I, H, group, gate4, scales4, biases4, gate2, scales2, biases2);
+    requant_matrix(I, H, group, up4, scales4 + ngu, biases4 + ngu, up2, scales2 + ngu, biases2 + ngu);
+    requant_matrix(H, I, group, down4, scales4 + 2 * ngu, biases4 + 2 * ngu, down2, scales2 + 2 * ngu,
+                   biases2 + 2 * ngu);
+}

@@ -45,6 +45,10 @@ int oracle_layer_decode_mt(int bits, int H, int I, int E, int K, int group, int 
 int oracle_group_by_expert(int B, int K, int E, const int32_t* idx, int32_t* offsets, int32_t* tokens,
                            int32_t* slots);
 void oracle_rms_renorm(int H, const double* y, double eps, double* x);
+uint16_t oracle_bf16_round(double v);
+void oracle_requant_expert(int H, int I, int group, const uint8_t* gate4, const uint8_t* up4, const uint8_t* down4,
+                           const uint16_t* scales4, const uint16_t* biases4, uint8_t* gate2, uint8_t* up2,
+                           uint8_t* down2, uint16_t* scales2, uint16_t* biases2);
 
 /* synth.c */
 size_t synth_codes_bytes(int bits, int rows, int cols);
@@ -117,6 +121,26 @@ static int run_layer(int bits, int H, int I, int E, int K, int B, int with_prior
             EXPECT(W[(long)r * H + c] == want, "dequant r=%d c=%d", r, c);
         }
     free(W);
+
+    /* 4-bit -> 2-bit requantization of expert 1: every requantized weight lies within
+     * the refit's range [b2, b2 + 3 s2] and every code is one of the four levels */
+    if (bits == 4) {
+        uint8_t* g2 = xmalloc(cb / 2);
+        uint8_t* u2 = xmalloc(cb / 2);
+        uint8_t* d2 = xmalloc(db / 2);
+        uint16_t* s2 = xmalloc(ng * 2);
+        uint16_t* b2 = xmalloc(ng * 2);
+        oracle_requant_expert(H, I, group, pg[1], pu[1], pd[1], ps[1], pb[1], g2, u2, d2, s2, b2);
+        double* W2 = xmalloc(sizeof(double) * (size_t)I * H);
+        oracle_dequant_matrix(2, I, H, group, g2, s2, b2, W2);
+        for (int r = 0; r < I; r += 5)
+            for (int c = 0; c < H; c += 3) {
+                const long gi = (long)r * (H / group) + c / group;
+                const double lo = oracle_bf16_to_double(b2[gi]), st = oracle_bf16_to_double(s2[gi]);
+                EXPECT(W2[(long)r * H + c] >= lo && W2[(long)r * H + c] <= lo + 3 * st, "requant r=%d c=%d", r, c);
+            }
+        free(W2); free(g2); free(u2); free(d2); free(s2); free(b2);
+    }
 
     /* one expert's FFN, h returned */
     double* xd = xmalloc(sizeof(double) * H);
@@ -205,6 +229,9 @@ int main(void)
     for (int t = 0; t < 4; ++t) EXPECT(oracle_code_at(&be4, 2, t) == t, "crumb %d of 0xE4", t);
     EXPECT(oracle_code_at(&b21, 3, 0) == -1, "bits=3 rejected");
     EXPECT(oracle_bf16_to_double(0x3F00) == 0.5 && oracle_bf16_to_double(0xBF80) == -1.0, "bf16 widening");
+    EXPECT(oracle_bf16_round(1.0 + 1.0 / 256) == 0x3F80 && oracle_bf16_round(1.0 + 3.0 / 256) == 0x3F82,
+           "bf16 rounding ties to even");
+    EXPECT(oracle_bf16_round(3.4e38) == 0x7F80 && oracle_bf16_round(-0.0) == 0x8000, "bf16 rounding edges");
     run_layer(4, 128, 64, 16, 4, 3, 0);
     run_layer(2, 128, 64, 16, 4, 3, 1);
     run_layer(4, 192, 128, 37, 5, 4, 1);

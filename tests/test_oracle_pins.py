@@ -379,3 +379,105 @@ def test_layer_decode_mt_and_par_equal_serial_full_shape():
     _assert_same_decode(ser, par)
     mt = oracle.layer_decode_mt(4, H, I, E, K, x[1], Wr, experts)
     _assert_same_decode((ser[0][1], ser[1][1], ser[2][1]), mt)
+
+
+# ------------------------ 4-bit -> 2-bit requantization -------------------------
+# Reading (the pages give only the result, 209 GB -> 120 GB): per group of 64, the
+# dequantized 4-bit weights are refit by b2 = bf16(min w), s2 = bf16((max - min) / 3),
+# q2 = clamp(rint((w - b2) / s2), 0, 3), every step in IEEE double.
+
+from fractions import Fraction
+
+
+def _bf16_exact(bits16):
+    return Fraction(bf16_value(bits16)) if (bits16 & 0x7F80) != 0x7F80 else None
+
+
+def _nearest_bf16_bruteforce(v):
+    """The nearest bf16 to a finite double by exact rational search over the two candidates
+    around it (bit patterns are monotone in value for a fixed sign), ties to even."""
+    x = Fraction(v)
+    sign = 0x8000 if v < 0 or (v == 0 and math.copysign(1, v) < 0) else 0
+    a = abs(x)
+    lo, hi = 0, 0x7F80  # largest pattern with value <= a, searched by bisection
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if _bf16_exact(mid) <= a:
+            lo = mid
+        else:
+            hi = mid - 1
+    below = lo
+    above = lo + 1
+    vb = _bf16_exact(below)
+    if vb == a:
+        return sign | below
+    va = Fraction(2) ** 128 if above == 0x7F80 else _bf16_exact(above)
+    db, da = a - vb, va - a
+    pick = below if db < da or (db == da and below % 2 == 0) else above
+    return sign | pick
+
+
+def test_bf16_round_matches_exact_nearest():
+    rng = np.random.default_rng(3)
+    vals = [0.0, -0.0, 1.0, -1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 3e38, 1e-40, 2 ** -133, 1.5 * 2 ** -133, 2 ** -127]
+    vals += list(rng.normal(0, 0.02, 300)) + list(rng.normal(0, 1, 100) * 10.0 ** rng.integers(-30, 30, 100))
+    for v in vals:
+        assert oracle.bf16_round(v) == _nearest_bf16_bruteforce(v), v
+    assert oracle.bf16_round(3.4e38) == 0x7F80  # past the largest bf16: infinity
+
+
+def test_requant_group_closed_forms():
+    # s4 = 0.5, b4 = 0, codes 0..6: w = 0, 0.5, ..., 3 -> b2 = 0, s2 = 1, q2 = rint(w) (ties to even)
+    q2, s2, b2 = oracle.requant_group([0, 1, 2, 3, 4, 5, 6], 0x3F00, 0x0000)
+    assert (s2, b2) == (0x3F80, 0x0000)
+    assert list(q2) == [0, 0, 1, 2, 2, 2, 3]
+    # a constant group: s2 = 0, every code 0, b2 = the weight
+    q2, s2, b2 = oracle.requant_group([9] * 64, 0x3F00, 0xBF80)  # w = 0.5 * 9 - 1 = 3.5
+    assert s2 == 0 and b2 == 0x4060 and not any(q2)
+    # s4 = 1, b4 = 0, codes 0..15: b2 = 0, s2 = 5, q2 = rint(w / 5) clamped
+    q2, s2, b2 = oracle.requant_group(list(range(16)), 0x3F80, 0x0000)
+    assert (s2, b2) == (0x40A0, 0x0000)
+    assert list(q2) == [0, 0, 0, 1, 1, 1, 1, 1, 2, 2, 2, 2, 2, 3, 3, 3]
+    # a negative scale reverses the order: w = 1 - q, min at q = 15
+    q2, s2, b2 = oracle.requant_group([0, 15, 6, 9], 0xBF80, 0x3F80)
+    assert (s2, b2) == (0x40A0, 0xC160)  # (1 - (-14)) / 3 = 5, min = -14
+    assert list(q2) == [3, 0, 2, 1]
+
+
+def test_requant_group_nearest_level_property():
+    """For random groups: b2, s2 are the exact nearest bf16 of min and of (max - min) / 3 (the
+    division rounded once in double), and every code is the nearest of the four levels."""
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        q4 = rng.integers(0, 16, 64)
+        s4 = synth.bf16_from_double(abs(rng.normal(0, 0.02)))
+        b4 = synth.bf16_from_double(rng.normal(0, 0.01))
+        q2, s2, b2 = oracle.requant_group(q4, s4, b4)
+        w = [Fraction(bf16_value(s4)) * int(q) + Fraction(bf16_value(b4)) for q in q4]
+        lo, hi = min(w), max(w)
+        assert b2 == _nearest_bf16_bruteforce(float(lo))
+        assert s2 == _nearest_bf16_bruteforce((float(hi) - float(lo)) / 3.0)
+        S, Bv = Fraction(bf16_value(s2)), Fraction(bf16_value(b2))
+        for wc, qc in zip(w, q2):
+            d = abs(wc - (Bv + S * int(qc)))
+            assert all(d <= abs(wc - (Bv + S * j)) for j in range(4)), (wc, qc)
+
+
+def test_requant_expert_group_and_row_indexing():
+    """Every weight of the requantized expert equals b2 + s2 * q2 of its own group as the
+    group function gives it (rows, groups and the gate | up | down split all line up)."""
+    rng = np.random.default_rng(5)
+    H, I = 192, 128
+    ex = random_expert(rng, 4, H, I)
+    g2, u2, d2, s2, b2 = oracle.requant_expert(H, I, ex["gate"], ex["up"], ex["down"], ex["s"], ex["b"])
+    ngu = I * (H // 64)
+    for name, q4, codes2, rows, cols, off in (("gate", ex["qg"], g2, I, H, 0), ("up", ex["qu"], u2, I, H, ngu),
+                                              ("down", ex["qd"], d2, H, I, 2 * ngu)):
+        W2 = oracle.dequant_matrix(2, rows, cols, codes2, s2[off:off + rows * cols // 64], b2[off:off + rows * cols // 64])
+        for r in range(0, rows, 7):
+            for g in range(cols // 64):
+                gi = off + r * (cols // 64) + g
+                q2, ss, bb = oracle.requant_group(q4[r, 64 * g:64 * g + 64], ex["s"][gi], ex["b"][gi])
+                assert (ss, bb) == (int(s2[gi]), int(b2[gi])), (name, r, g)
+                np.testing.assert_array_equal(W2[r, 64 * g:64 * g + 64],
+                                              bf16_value(ss) * q2.astype(np.float64) + bf16_value(bb))
