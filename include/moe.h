@@ -124,6 +124,23 @@ int moe_pack_experts(int bits, int H, int I, int group, int n_experts, const uin
                      int first_expert, void* stream);
 
 /*
+ * Offline requantization of n_experts canonical 4-bit experts to canonical 2-bit
+ * experts of the same shape ([CLAUDAY] and [LLMAPIS] section 数据和技术细节: the
+ * experts were requantized from 4-bit to 2-bit, 209 GB -> 120 GB; the pages give no
+ * procedure).  Per group of 64 weights w_c = s4 q4_c + b4: b2 = bf16(min w),
+ * s2 = bf16((max w - min w) / 3), q2_c = clamp(rint((w_c - b2) / s2), 0, 3) (0 when
+ * s2 = 0 or the quotient is not a number), every operation in IEEE double and bf16() the nearest bf16, ties to even.
+ * Inputs: the canonical 4-bit tensors as for moe_pack_experts (device, stacked
+ * over the n experts); outputs: gate2, up2 uint8 [n][I][H/4], down2 [n][H][I/4],
+ * scales2, biases2 uint16 [n][ng] in the same order as the inputs' scales.  The
+ * result is packed with moe_pack_experts(bits = 2).  MOE_EINVAL / MOE_EUNSUPPORTED
+ * as for moe_pack_experts (group must be 64).
+ */
+int moe_requant_4to2(int H, int I, int group, int n_experts, const uint8_t* gate4, const uint8_t* up4,
+                     const uint8_t* down4, const uint16_t* scales4, const uint16_t* biases4, uint8_t* gate2,
+                     uint8_t* up2, uint8_t* down2, uint16_t* scales2, uint16_t* biases2, void* stream);
+
+/*
  * Dequantize one packed record back to dense fp32, reading it exactly as the
  * compute kernels do: W_out = [Wg (I x H) | Wu (I x H) | Wd (H x I)] row-major,
  * each element fmaf(s, q, b).  A check of the packed layout, not a hot path.

@@ -388,7 +388,8 @@ void oracle_rms_renorm(int H, const double* y, double eps, double* x)
  * a per-group min/max affine refit of the dequantized 4-bit weights:
  *   w_c = s4 * q4_c + b4 for the 64 weights c of a group (exact in double),
  *   b2  = bf16(min_c w_c), s2 = bf16((max_c w_c - min_c w_c) / 3),
- *   q2_c = clamp(rint((w_c - b2) / s2), 0, 3)   (q2_c = 0 when s2 == 0),
+ *   q2_c = clamp(rint((w_c - b2) / s2), 0, 3)   (q2_c = 0 when s2 == 0, and when the
+ *   quotient is not a number, as with a scale or bias beyond the bf16 range),
  * every step in IEEE double (rint: to nearest, ties to even) and bf16() a single
  * rounding of the double to the nearest bf16 value, ties to even.
  */
@@ -437,7 +438,7 @@ void oracle_requant_group(int n, const int* q4, uint16_t s4, uint16_t b4, int* q
             continue;
         }
         double t = nearbyint((s * q4[c] + b - bd) / sd);
-        q2[c] = t < 0.0 ? 0 : (t > 3.0 ? 3 : (int)t);
+        q2[c] = t >= 3.0 ? 3 : (t > 0.0 ? (int)t : 0);   /* a quotient that is not a number gives 0 */
     }
     *s2_out = s2;
     *b2_out = b2;

@@ -62,6 +62,7 @@ def lib():
             "moe_stack_extra_bytes": (sz, [i32, i32]),
             "moe_pack_experts": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]),
             "moe_dequant_expert": (i32, [i32, i32, i32, i32, vp, vp, vp]),
+            "moe_requant_4to2": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "moe_route_topk": (i32, [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]),
             "moe_expert_ffn_q4": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_expert_ffn_q2": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
@@ -138,6 +139,12 @@ def stack_extra_bytes(B, H):
 def pack_experts(bits, H, I, n, gate, up, down, scales, biases, slab, first, stream=None, group=64):
     return _check(lib().moe_pack_experts(bits, H, I, group, n, _p(gate), _p(up), _p(down), _p(scales), _p(biases),
                                          _p(slab), first, _stream(stream)))
+
+
+def requant_4to2(H, I, n, gate4, up4, down4, scales4, biases4, gate2, up2, down2, scales2, biases2, stream=None,
+                 group=64):
+    return _check(lib().moe_requant_4to2(H, I, group, n, _p(gate4), _p(up4), _p(down4), _p(scales4), _p(biases4),
+                                         _p(gate2), _p(up2), _p(down2), _p(scales2), _p(biases2), _stream(stream)))
 
 
 def dequant_expert(bits, H, I, record, W_out, stream=None, group=64):

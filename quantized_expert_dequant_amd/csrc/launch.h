@@ -26,5 +26,9 @@ void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4
                 int renorm, int32_t* idx, float* w, int B, int K, int E, float shared_w, void* hq, float* y,
                 hipStream_t s, Timing t_gateup = Timing(), Timing t_down = Timing());
 void launch_rmsnorm(const float* y, int B, int H, float eps, float* x, hipStream_t s);
+// canonical 4-bit experts -> canonical 2-bit experts (requant.hip)
+void launch_requant_4to2(int H, int I, int n, const uint8_t* gate4, const uint8_t* up4, const uint8_t* down4,
+                         const uint16_t* s4, const uint16_t* b4, uint8_t* gate2, uint8_t* up2, uint8_t* down2,
+                         uint16_t* s2, uint16_t* b2, hipStream_t s);
 
 }  // namespace moe

@@ -242,6 +242,29 @@ int moe_pack_experts(int bits, int H, int I, int group, int n_experts, const uin
     return hip_status(fn);
 }
 
+int moe_requant_4to2(int H, int I, int group, int n_experts, const uint8_t* gate4, const uint8_t* up4,
+                     const uint8_t* down4, const uint16_t* scales4, const uint16_t* biases4, uint8_t* gate2,
+                     uint8_t* up2, uint8_t* down2, uint16_t* scales2, uint16_t* biases2, void* stream)
+{
+    const char* fn = "moe_requant_4to2";
+    int rc = check_shape(fn, 4, H, I, group);
+    if (rc) return rc;
+    if (n_experts < 1 || n_experts > 65535) return fail(MOE_EINVAL, "%s: n_experts=%d", fn, n_experts);
+    CHECK_PTR(gate4);
+    CHECK_PTR(up4);
+    CHECK_PTR(down4);
+    CHECK_PTR(scales4);
+    CHECK_PTR(biases4);
+    CHECK_PTR(gate2);
+    CHECK_PTR(up2);
+    CHECK_PTR(down2);
+    CHECK_PTR4(scales2);
+    CHECK_PTR4(biases2);
+    launch_requant_4to2(H, I, n_experts, gate4, up4, down4, scales4, biases4, gate2, up2, down2, scales2, biases2,
+                        (hipStream_t)stream);
+    return hip_status(fn);
+}
+
 int moe_dequant_expert(int bits, int H, int I, int group, const void* record, float* W_out, void* stream)
 {
     const char* fn = "moe_dequant_expert";

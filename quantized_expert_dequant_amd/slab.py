@@ -11,7 +11,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import make_desc, pack_experts, record_bytes, workspace_bytes, stack_extra_bytes
+from . import make_desc, pack_experts, record_bytes, requant_4to2, workspace_bytes, stack_extra_bytes
 
 
 def upload_experts(source, n_total, bits, H, I, device="cuda", chunk=32, slab=None):
@@ -31,6 +31,28 @@ def upload_experts(source, n_total, bits, H, I, device="cuda", chunk=32, slab=No
         for d, a in zip(dev, arrays):
             d.copy_(a)
         pack_experts(bits, H, I, n, *dev, slab, first)
+    torch.cuda.synchronize()
+    return slab
+
+
+def upload_requantized(source4, n_total, H, I, device="cuda", chunk=32, slab=None):
+    """A 2-bit slab from canonical 4-bit experts: each chunk is uploaded, requantized on the
+    GPU (moe_requant_4to2) and packed as 2-bit records.  source4(first, n) as for
+    upload_experts, with 4-bit tensors."""
+    rb = record_bytes(2, H, I)
+    if slab is None:
+        slab = torch.empty(n_total * rb, dtype=torch.uint8, device=device)
+    for first in range(0, n_total, chunk):
+        n = min(chunk, n_total - first)
+        c = source4(first, n)
+        g4, u4, d4, s4, b4 = [torch.from_numpy(a.reshape(n, -1)).to(device)
+                              for a in (c.gate, c.up, c.down, c.scales, c.biases)]
+        g2 = torch.empty((n, I * H // 4), dtype=torch.uint8, device=device)
+        u2 = torch.empty_like(g2)
+        d2 = torch.empty((n, H * I // 4), dtype=torch.uint8, device=device)
+        s2, b2 = torch.empty_like(s4), torch.empty_like(b4)
+        requant_4to2(H, I, n, g4, u4, d4, s4, b4, g2, u2, d2, s2, b2)
+        pack_experts(2, H, I, n, g2, u2, d2, s2, b2, slab, first)
     torch.cuda.synchronize()
     return slab
 
