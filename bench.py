@@ -50,6 +50,8 @@ WORKLOADS = {
     "layer2": dict(H=4096, I=1024, E=512, K=4, bits=2, B=1, layers=1, zipf=None, seed=1002),
     "stack": dict(H=4096, I=1024, E=512, K=4, bits=4, B=1, layers=60, zipf=None, seed=1003),
     "batched": dict(H=4096, I=1024, E=512, K=10, bits=4, B=64, layers=1, zipf=1.1, seed=1004),
+    # the layer workload's 4-bit experts requantized to 2-bit on the GPU (moe_requant_4to2)
+    "requant": dict(H=4096, I=1024, E=512, K=4, bits=2, B=1, layers=1, zipf=None, seed=1001, requant=True),
 }
 RMS_EPS = 1e-6
 
@@ -109,8 +111,13 @@ def build_layers(c, n_distinct, n_copies, dev):
     base = []
     for l in range(n_distinct):
         t0 = time.time()
-        src = lambda first, n, l=l: synth.experts(c["seed"], l, first, n, bits, H, I)
-        slab = upload_experts(src, E + 1, bits, H, I, device=dev)
+        if c.get("requant"):
+            from quantized_expert_dequant_amd.slab import upload_requantized
+            src = lambda first, n, l=l: synth.experts(c["seed"], l, first, n, 4, H, I)
+            slab = upload_requantized(src, E + 1, H, I, device=dev)
+        else:
+            src = lambda first, n, l=l: synth.experts(c["seed"], l, first, n, bits, H, I)
+            slab = upload_experts(src, E + 1, bits, H, I, device=dev)
         wr = torch.from_numpy(synth.router(c["seed"], l, E, H)).to(dev)
         bias = torch.from_numpy(synth.zipf_bias(E, c["zipf"])).to(dev) if c["zipf"] else None
         base.append(DeviceLayer(H, I, E, K, bits, slab, wr, bias))
@@ -135,7 +142,13 @@ def oracle_check(c, x_host, y_dev, idx_dev, layer_id=0):
     need = {E}
     for b in range(x_host.shape[0]):
         need |= {int(e) for e in oracle.topk(lg[b], K)[0]}
-    experts = {e: synth.experts(c["seed"], layer_id, e, 1, c["bits"], c["H"], c["I"]) for e in sorted(need)}
+    experts = {e: synth.experts(c["seed"], layer_id, e, 1, 4 if c.get("requant") else c["bits"], c["H"], c["I"])
+               for e in sorted(need)}
+    if c.get("requant"):
+        for e, x4 in experts.items():
+            g2, u2, d2, s2, b2 = oracle.requant_expert(c["H"], c["I"], x4.gate[0], x4.up[0], x4.down[0],
+                                                       x4.scales[0], x4.biases[0])
+            experts[e] = synth.Canonical(2, c["H"], c["I"], 64, g2[None], u2[None], d2[None], s2[None], b2[None])
     y_ref, idx_ref, _, _ = oracle.layer_decode(c["bits"], c["H"], c["I"], E, K, x_host, Wr, experts, prior=prior)
     # per token max|dy| / max|y_ref|, the denominator floored where fp32 cannot represent the tolerance
     err = max(float(np.max(np.abs(y_dev[b] - y_ref[b])) / max(np.max(np.abs(y_ref[b])), 2.0 ** -126 / 2e-3))
@@ -221,9 +234,10 @@ def _median(v):
 
 
 def _workload_name(name, c, n_copies, n_distinct, stack):
-    return "%s: H=%d I=%d E=%d+1 shared K=%d %d-bit group 64 bf16 scale+bias, B=%d%s" % (
+    return "%s: H=%d I=%d E=%d+1 shared K=%d %d-bit group 64 bf16 scale+bias, B=%d%s%s" % (
         name, c["H"], c["I"], c["E"], c["K"], c["bits"], c["B"],
-        ", %d layers with RMS renorm" % c["layers"] if stack else "")
+        ", %d layers with RMS renorm" % c["layers"] if stack else "",
+        ", experts requantized from the layer workload's 4-bit ones on the GPU" if c.get("requant") else "")
 
 
 def measure(name, steps, warmup, dev, rotate=16, distinct=0, graph=True, eager=True, warm=False, replays=5,
@@ -400,6 +414,36 @@ def measure(name, steps, warmup, dev, rotate=16, distinct=0, graph=True, eager=T
     return res
 
 
+def requant_throughput(dev, n=64, reps=5):
+    """GB/s of moe_requant_4to2 over n full-shape experts (4-bit bytes read + 2-bit bytes written),
+    GPU events around each call, median."""
+    import torch
+    import synth
+    import quantized_expert_dequant_amd as moe
+    H, I = 4096, 1024
+    c = synth.experts(1001, 0, 0, n, 4, H, I)
+    ins = [torch.from_numpy(np.ascontiguousarray(a.reshape(n, -1))).to(dev)
+           for a in (c.gate, c.up, c.down, c.scales, c.biases)]
+    g2 = torch.empty((n, I * H // 4), dtype=torch.uint8, device=dev)
+    u2 = torch.empty_like(g2)
+    d2 = torch.empty((n, H * I // 4), dtype=torch.uint8, device=dev)
+    s2, b2 = torch.empty_like(ins[3]), torch.empty_like(ins[4])
+    moe.requant_4to2(H, I, n, *ins, g2, u2, d2, s2, b2)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        moe.requant_4to2(H, I, n, *ins, g2, u2, d2, s2, b2)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = _median(times)
+    nbytes = n * (moe.record_bytes(4, H, I) + moe.record_bytes(2, H, I))
+    return {"experts": n, "ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "bytes_4bit_per_expert": moe.record_bytes(4, H, I), "bytes_2bit_per_expert": moe.record_bytes(2, H, I)}
+
+
 def cpu_baseline(c, budget_s=15.0):
     """The float64 oracle as it stands on the host cores, on a bounded sample of tokens of the
     timed layer: tokens decoded on OpenMP threads (oracle_layer_decode_par, each token by the
@@ -538,8 +582,9 @@ def main():
     }
     if not args.no_configs:
         # every other workload at its own shape, fewer steps, same measurement
-        extra = {"layer2": dict(steps=100, warmup=10), "batched": dict(steps=40, warmup=5),
-                 "stack": dict(steps=10, warmup=2, distinct=4), "layer": dict(steps=100, warmup=10)}
+        extra = {"layer2": dict(steps=100, warmup=10), "requant": dict(steps=100, warmup=10),
+                 "batched": dict(steps=40, warmup=5), "stack": dict(steps=10, warmup=2, distinct=4),
+                 "layer": dict(steps=100, warmup=10)}
         cfgs = {}
         for name, kw in extra.items():
             if name == args.workload:
@@ -552,6 +597,8 @@ def main():
             e = {k: e[k] for k in keep if k in e}
             if "gateup_gbps" in e:
                 e["gateup_frac"] = round(e["gateup_gbps"] / PEAK_HBM_GBPS, 4)
+            if name == "requant":
+                e["requant_kernel"] = requant_throughput(dev)
             cfgs[name] = e
         out["configs"] = cfgs
     if not args.cpu_seconds <= 0:
