@@ -213,6 +213,54 @@ int moe_layer_decode_noalloc(const moe_layer_desc* desc, const float* x, int B, 
                              int32_t* idx_out, float* w_out, void* stream);
 
 /*
+ * Tiered expert residency ([LLMAPIS] section 深度分析: only the K selected
+ * experts of a layer are brought near the processor, and the OS page cache decides
+ * what stays; [ACGFAV] section 到底做了什么).  Here the layer's packed records live
+ * in a backing store, normally pinned host memory (allocated with hipHostMalloc,
+ * e.g. torch's pin_memory=True), and `slots` of them plus the shared expert in an
+ * HBM cache.  Each cached decode routes on the GPU, maps the selected experts onto
+ * slots (a hit refreshes its slot; each miss evicts the least recently used slot
+ * that the call does not use, ties to the lowest slot, misses taken in ascending
+ * expert id), copies the missing records from the store with a GPU kernel that reads
+ * the host memory directly, and runs the expert FFNs on the cache.  Nothing waits
+ * on the host, so a call can be captured in a HIP graph.
+ *   slab:  device, (slots + 1) records of moe_expert_record_bytes; the last holds
+ *          the shared expert.
+ *   state: device, moe_cache_state_bytes(E, slots) bytes, set up by moe_cache_init
+ *          and updated by every cached decode (calls on one cache must be ordered
+ *          on one stream).  Its first 32 bytes are uint64 counters: hits, misses,
+ *          bytes copied from the store, calls.
+ * With the cache the results are those of moe_layer_decode on the same records.
+ */
+#define MOE_MAX_CACHE_SLOTS 65536
+typedef struct moe_expert_cache {
+    int32_t slots;
+    void* slab;
+    void* state;
+} moe_expert_cache;
+
+/* Bytes of the cache state for E routed experts and `slots` slots (0 if invalid). */
+size_t moe_cache_state_bytes(int E, int slots);
+
+/* Empties every slot, zeroes the counters and copies the shared expert (record E of
+ * desc->experts, the store) into its slot.  MOE_EINVAL for a bad desc or cache, or a
+ * store that is neither device memory nor pinned host memory. */
+int moe_cache_init(const moe_layer_desc* desc, const moe_expert_cache* cache, void* stream);
+
+/* Workspace bytes of moe_layer_decode_cached for B tokens (0 if invalid). */
+size_t moe_cache_workspace_bytes(const moe_layer_desc* desc, int slots, int B);
+
+/*
+ * moe_layer_decode with desc->experts a store of E + 1 packed records (pinned host
+ * memory or device memory) and the experts computed from `cache`.  idx_out / w_out
+ * (nullable) receive the routing in expert ids.  MOE_EINVAL if slots < min(E, B*K)
+ * (a call's distinct experts must fit) or the workspace is too small.
+ */
+int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* cache, const float* x, int B,
+                            float* y_out, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/*
  * Token -> expert grouping of a batch's routing ([LLMAPIS] section 深度分析: only
  * the selected experts are read; with B tokens each selected expert is read
  * once for all the tokens that chose it).  A stable counting sort of the B*K

@@ -22,6 +22,7 @@ MOE_MAX_K = 32      # largest top-K (include/moe.h)
 MOE_MAX_E = 1024    # most routed experts
 MOE_MAX_B = 256     # most tokens per call
 MOE_NOALLOC_SCRATCH_BYTES = 8 << 20  # scratch of moe_layer_decode_noalloc per GPU
+MOE_MAX_CACHE_SLOTS = 65536  # most slots of an expert cache
 
 KERNEL_ROUTER = 1
 KERNEL_GATEUP = 2
@@ -32,6 +33,11 @@ class MoeError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__("%s (code %d)" % (msg, code))
         self.code = code
+
+
+class ExpertCache(ctypes.Structure):
+    """moe_expert_cache (include/moe.h)."""
+    _fields_ = [("slots", ctypes.c_int32), ("slab", ctypes.c_void_p), ("state", ctypes.c_void_p)]
 
 
 class LayerDesc(ctypes.Structure):
@@ -73,6 +79,10 @@ def lib():
             "moe_stack_decode": (i32, [dp, i32, vp, i32, f32, vp, vp, vp, vp, sz, vp]),
             "moe_set_timing_events": (i32, [i32, vp, vp]),
             "moe_grouped_launch_info": (i32, [dp, i32, vp]),
+            "moe_cache_state_bytes": (sz, [i32, i32]),
+            "moe_cache_init": (i32, [dp, ctypes.POINTER(ExpertCache), vp]),
+            "moe_cache_workspace_bytes": (sz, [dp, i32, i32]),
+            "moe_layer_decode_cached": (i32, [dp, ctypes.POINTER(ExpertCache), vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -203,6 +213,27 @@ def grouped_launch_info(desc, B):
     keys = ("grouped", "gateup_blocks", "gateup_tiles_per_group", "gateup_k_chunks", "down_blocks",
             "down_tiles_per_group", "gemv_below_tokens", "group_tokens")
     return dict(zip(keys, list(info)))
+
+
+def make_cache(slots, slab, state):
+    return ExpertCache(slots, _p(slab), _p(state))
+
+
+def cache_state_bytes(E, slots):
+    return lib().moe_cache_state_bytes(E, slots)
+
+
+def cache_workspace_bytes(desc, slots, B):
+    return lib().moe_cache_workspace_bytes(ctypes.byref(desc), slots, B)
+
+
+def cache_init(desc, cache, stream=None):
+    return _check(lib().moe_cache_init(ctypes.byref(desc), ctypes.byref(cache), _stream(stream)))
+
+
+def layer_decode_cached(desc, cache, x, B, y_out, idx_out, w_out, ws, ws_bytes, stream=None):
+    return _check(lib().moe_layer_decode_cached(ctypes.byref(desc), ctypes.byref(cache), _p(x), B, _p(y_out),
+                                                _p(idx_out), _p(w_out), _p(ws), ws_bytes, _stream(stream)))
 
 
 def set_timing_events(kernel, start_event, stop_event):

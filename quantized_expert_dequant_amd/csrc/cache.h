@@ -1,0 +1,23 @@
+// cache.h - host-side interface of the HBM expert cache (cache.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// bytes of the cache state for E routed experts and `slots` HBM slots
+size_t cache_state_bytes(int E, int slots);
+// every slot empty, counters zero
+void launch_cache_reset(void* state, int E, int slots, hipStream_t s);
+// the call's plan from the selected ids idx [n]: slot ids idx_slot [n] (-1 for ids
+// outside [0, E)) and the copy list plan = [count, (expert, slot) x count]
+void launch_cache_plan(const int32_t* idx, int n, int E, int slots, void* state, int32_t* idx_slot, int32_t* plan,
+                       long long record, hipStream_t s);
+// copy the planned records (at most max_copies) from src (device-accessible) into slab
+void launch_cache_copy(const int32_t* plan, int max_copies, const void* src, void* slab, long long record,
+                       hipStream_t s);
+
+}  // namespace moe

@@ -5,9 +5,11 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/moe.h"
+#include "cache.h"
 #include "grouped.h"
 #include "launch.h"
 
@@ -418,6 +420,137 @@ int moe_layer_decode_noalloc(const moe_layer_desc* desc, const float* x, int B, 
     if (!ws) return rc;
     const Work W = carve(ws, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
     return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, (hipStream_t)stream);
+}
+
+size_t moe_cache_state_bytes(int E, int slots)
+{
+    if (E < 1 || E > MOE_MAX_E || slots < 1 || slots > MOE_MAX_CACHE_SLOTS) return 0;
+    return cache_state_bytes(E, slots);
+}
+
+// Workspace of a cached decode: the layer's workspace carved for max(E, slots)
+// experts (the router works on E ids, the expert FFNs on slot ids), then the slot
+// ids of the selection and the copy plan.
+static size_t cached_extra_bytes(int B, int K, int E)
+{
+    return up256((size_t)B * K * 4) + up256(4 * (1 + 2 * (size_t)std::min(E, B * K)));
+}
+
+size_t moe_cache_workspace_bytes(const moe_layer_desc* desc, int slots, int B)
+{
+    if (!desc || check_shape("moe_cache_workspace_bytes", desc->bits, desc->H, desc->I, desc->group) ||
+        check_routing("moe_cache_workspace_bytes", B, desc->E, desc->K) || slots < 1 || slots > MOE_MAX_CACHE_SLOTS)
+        return 0;
+    const int Eb = std::max(desc->E, slots);
+    return carve(nullptr, desc->bits, B, desc->H, desc->I, Eb, desc->K).bytes + cached_extra_bytes(B, desc->K, desc->E);
+}
+
+// The backing store as a device address: pinned host memory is translated, device
+// memory is used as it is.
+static const void* backing_device_ptr(const void* p)
+{
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (a.type == hipMemoryTypeHost) {
+        void* d = nullptr;
+        if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        return d;
+    }
+    return p;
+}
+
+static int check_cache(const char* fn, const moe_layer_desc* d, const moe_expert_cache* c)
+{
+    if (!c) return fail(MOE_EINVAL, "%s: cache is NULL", fn);
+    if (c->slots < 1 || c->slots > MOE_MAX_CACHE_SLOTS)
+        return fail(MOE_EINVAL, "%s: cache->slots=%d (must be in [1, %d])", fn, c->slots, MOE_MAX_CACHE_SLOTS);
+    if (!c->slab || misaligned(c->slab)) return fail(MOE_EINVAL, "%s: cache->slab is NULL or not 16-byte aligned", fn);
+    if (!c->state || misaligned(c->state))
+        return fail(MOE_EINVAL, "%s: cache->state is NULL or not 16-byte aligned", fn);
+    return MOE_OK;
+}
+
+int moe_cache_init(const moe_layer_desc* desc, const moe_expert_cache* cache, void* stream)
+{
+    const char* fn = "moe_cache_init";
+    int rc = check_desc(fn, desc, 1);
+    if (rc) return rc;
+    rc = check_cache(fn, desc, cache);
+    if (rc) return rc;
+    const void* src = backing_device_ptr(desc->experts);
+    if (!src) return fail(MOE_EINVAL, "%s: desc->experts is neither device memory nor pinned host memory", fn);
+    const Layout L = make_layout(desc->bits, desc->H, desc->I);
+    hipStream_t s = (hipStream_t)stream;
+    launch_cache_reset(cache->state, desc->E, cache->slots, s);
+    // the shared expert (record E of the store) has a slot of its own, after the routed ones
+    const hipError_t e = hipMemcpyAsync((char*)cache->slab + (size_t)cache->slots * L.record,
+                                        (const char*)desc->experts + (size_t)desc->E * L.record, L.record,
+                                        hipMemcpyDefault, s);
+    if (e != hipSuccess) return fail(MOE_EHIP, "%s: copy of the shared expert: %s", fn, hipGetErrorString(e));
+    return hip_status(fn);
+}
+
+int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* cache, const float* x, int B,
+                            float* y_out, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream)
+{
+    const char* fn = "moe_layer_decode_cached";
+    int rc = check_desc(fn, desc, B);
+    if (rc) return rc;
+    rc = check_cache(fn, desc, cache);
+    if (rc) return rc;
+    CHECK_PTR(desc->w_router);
+    CHECK_OPT_PTR4(desc->logit_bias);
+    CHECK_PTR(x);
+    CHECK_PTR(y_out);
+    CHECK_OPT_PTR4(idx_out);
+    CHECK_OPT_PTR4(w_out);
+    CHECK_PTR(ws);
+    const int E = desc->E, K = desc->K, S = cache->slots;
+    if (S < std::min(E, B * K))
+        return fail(MOE_EINVAL, "%s: %d slots cannot hold the up to %d distinct experts of %d tokens x K=%d", fn, S,
+                    std::min(E, B * K), B, K);
+    const void* src = backing_device_ptr(desc->experts);
+    if (!src) return fail(MOE_EINVAL, "%s: desc->experts is neither device memory nor pinned host memory", fn);
+    const int Eb = std::max(E, S);
+    const Work W = carve(ws, desc->bits, B, desc->H, desc->I, Eb, K);
+    const size_t need = W.bytes + cached_extra_bytes(B, K, E);
+    if (ws_bytes < need) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+    int32_t* idx_slot = (int32_t*)((char*)ws + W.bytes);
+    int32_t* plan = (int32_t*)((char*)ws + W.bytes + up256((size_t)B * K * 4));
+    int32_t* idx = idx_out ? idx_out : W.idx;
+    float* w = w_out ? w_out : W.w;
+    const Layout L = make_layout(desc->bits, desc->H, desc->I);
+    hipStream_t s = (hipStream_t)stream;
+    const int renorm = desc->renormalize ? 1 : 0;
+    // 1. route on the E expert ids
+    if (W.grouped) {
+        const TokenPrep P{x, desc->H, W.gw.xh, W.gw.xsum, W.gw.xscale, gemv_tokens(L) > 1 ? W.xq : nullptr, W.xst};
+        launch_route_batched(x, B, desc->w_router, desc->logit_bias, desc->H, E, K, renorm, W.gw.partial, idx, w, P,
+                             s, g_timing[KID_ROUTER]);
+    } else {
+        launch_router(desc->bits, x, B, desc->w_router, desc->logit_bias, desc->H, E, W.logits, W.xq, W.xst, s,
+                      g_timing[KID_ROUTER]);
+        launch_topk(W.logits, B, E, K, renorm, idx, w, s);
+    }
+    // 2. map the selection onto slots and bring in the missing records
+    launch_cache_plan(idx, B * K, E, S, cache->state, idx_slot, plan, L.record, s);
+    launch_cache_copy(plan, std::min(E, B * K), src, cache->slab, L.record, s);
+    // 3. the expert FFNs on the cache, by slot id (the shared expert at slot S)
+    if (W.grouped) {
+        launch_group(idx_slot, B, K, S, gemv_tokens(L), W.gw.g, s);
+        launch_ffn_grouped(L, cache->slab, W.gw, x, w, desc->shared_weight, B, K, S, W.xq, W.xst, true, y_out, s,
+                           g_timing[KID_GATEUP], g_timing[KID_DOWN]);
+    } else {
+        launch_ffn(L, cache->slab, W.xq, W.xst, nullptr, 0, idx_slot, w, B, K, S, desc->shared_weight, W.hq, y_out,
+                   s, g_timing[KID_GATEUP], g_timing[KID_DOWN]);
+    }
+    return hip_status(fn);
 }
 
 int moe_group_tokens(const int32_t* idx, int B, int K, int E, int32_t* offsets_out, int32_t* tokens_out,

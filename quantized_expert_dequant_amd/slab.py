@@ -35,6 +35,23 @@ def upload_experts(source, n_total, bits, H, I, device="cuda", chunk=32, slab=No
     return slab
 
 
+def host_store(source, n_total, bits, H, I, device="cuda", chunk=32):
+    """The packed records of n_total experts in pinned host memory (the backing store of an
+    expert cache): each chunk is packed on the GPU into a small device buffer and copied out,
+    so the whole layer never has to fit in device memory."""
+    rb = record_bytes(bits, H, I)
+    store = torch.empty(n_total * rb, dtype=torch.uint8, pin_memory=True)
+    buf = torch.empty(chunk * rb, dtype=torch.uint8, device=device)
+    for first in range(0, n_total, chunk):
+        n = min(chunk, n_total - first)
+        c = source(first, n)
+        arrays = [torch.from_numpy(a.reshape(n, -1)).to(device) for a in (c.gate, c.up, c.down, c.scales, c.biases)]
+        pack_experts(bits, H, I, n, *arrays, buf, 0)
+        store[first * rb:(first + n) * rb].copy_(buf[:n * rb])
+    torch.cuda.synchronize()
+    return store
+
+
 def upload_requantized(source4, n_total, H, I, device="cuda", chunk=32, slab=None):
     """A 2-bit slab from canonical 4-bit experts: each chunk is uploaded, requantized on the
     GPU (moe_requant_4to2) and packed as 2-bit records.  source4(first, n) as for
