@@ -414,6 +414,67 @@ def measure(name, steps, warmup, dev, rotate=16, distinct=0, graph=True, eager=T
     return res
 
 
+def measure_tiered(dev, steps=200, warmup=20, slots=64, zipf=1.1):
+    """The layer workload's 4-bit layer with its E + 1 records in pinned host memory and an HBM
+    cache of `slots` records (moe_layer_decode_cached), routing biased by a Zipf(zipf) prior so
+    that hot experts recur: tokens/s, hit rate, bytes pulled from host memory per second and
+    expert bytes per second; GPU events around the timed steps (eager: the cache state changes
+    from call to call)."""
+    import torch
+    import synth
+    import quantized_expert_dequant_amd as moe
+    from quantized_expert_dequant_amd.slab import DeviceLayer, host_store
+    c = dict(WORKLOADS["layer"])
+    H, I, E, K, bits, seed = c["H"], c["I"], c["E"], c["K"], c["bits"], c["seed"]
+    t0 = time.time()
+    store = host_store(lambda f, n: synth.experts(seed, 0, f, n, bits, H, I), E + 1, bits, H, I, device=dev)
+    log("tiered: %d records (%.1f GB) in pinned host memory in %.1fs" % (E + 1, store.numel() / 1e9, time.time() - t0))
+    wr = torch.from_numpy(synth.router(seed, 0, E, H)).to(dev)
+    bias = torch.from_numpy(synth.zipf_bias(E, zipf)).to(dev)
+    L = DeviceLayer(H, I, E, K, bits, store, wr, bias)
+    rb = moe.record_bytes(bits, H, I)
+    slab = torch.empty((slots + 1) * rb, dtype=torch.uint8, device=dev)
+    state = torch.empty(moe.cache_state_bytes(E, slots), dtype=torch.uint8, device=dev)
+    cache = moe.make_cache(slots, slab, state)
+    moe.cache_init(L.desc, cache)
+    n = moe.cache_workspace_bytes(L.desc, slots, 1)
+    ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+    xs = torch.from_numpy(np.stack([synth.tokens(seed, 20_000 + t, 1, H) for t in range(warmup + steps)])).to(dev)
+    y = torch.empty((warmup + steps, 1, H), dtype=torch.float32, device=dev)
+    idx = torch.empty((warmup + steps, 1, K), dtype=torch.int32, device=dev)
+    w = torch.empty((warmup + steps, 1, K), dtype=torch.float32, device=dev)
+    for t in range(warmup):
+        moe.layer_decode_cached(L.desc, cache, xs[t], 1, y[t], idx[t], w[t], ws, n)
+    torch.cuda.synchronize()
+    before = state[:32].cpu().numpy().view(np.uint64).copy()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(30 * 2.4e6))
+    a.record()
+    for t in range(warmup, warmup + steps):
+        moe.layer_decode_cached(L.desc, cache, xs[t], 1, y[t], idx[t], w[t], ws, n)
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / steps
+    after = state[:32].cpu().numpy().view(np.uint64).copy()
+    hits, misses, copied = (int(after[i] - before[i]) for i in range(3))
+    # parity: the last token against the oracle (same records, prior on the logits)
+    ok, err = oracle_check(dict(c, zipf=zipf), xs[warmup + steps - 1].cpu().numpy(), y[warmup + steps - 1].cpu().numpy(),
+                           idx[warmup + steps - 1].cpu().numpy())
+    expert_bytes = (gateup_bytes_per_expert(c) + down_bytes_per_expert(c)) * (K + 1)
+    res = {"config": "tiered: layer workload (H=%d I=%d E=%d+1 K=%d %d-bit) with a Zipf(%.1f) prior, all records in "
+                     "pinned host memory, %d routed slots + the shared expert in HBM, B=1" % (H, I, E, K, bits, zipf,
+                                                                                              slots),
+           "parity_ok": ok, "parity_rel_err": err, "steps": steps, "timing": "eager, GPU events",
+           "ms_per_step": round(ms, 6), "tokens_per_s": round(1e3 / ms, 2),
+           "hit_rate": round(hits / max(1, hits + misses), 4), "misses_per_token": round(misses / steps, 3),
+           "host_gbps": round(copied / (ms * steps * 1e-3) / 1e9, 2),
+           "expert_weight_gbps": round(expert_bytes / (ms * 1e-3) / 1e9, 1)}
+    del L, store, slab, state, ws, xs, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def requant_throughput(dev, n=64, reps=5):
     """GB/s of moe_requant_4to2 over n full-shape experts (4-bit bytes read + 2-bit bytes written),
     GPU events around each call, median."""
@@ -600,6 +661,7 @@ def main():
             if name == "requant":
                 e["requant_kernel"] = requant_throughput(dev)
             cfgs[name] = e
+        cfgs["tiered"] = measure_tiered(dev)
         out["configs"] = cfgs
     if not args.cpu_seconds <= 0:
         log("timing the oracle on the host ...")
