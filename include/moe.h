@@ -71,6 +71,10 @@ extern "C" {
  *   shared_weight: factor of the shared expert in the combine (1.0 = plain sum).
  *   renormalize: 1 = routing weights renormalized over the kept K; 0 = raw
  *            softmax probabilities over all E.
+ *   expert_flags: int32 [E + 1] as written by moe_expert_ranges, or NULL.  With
+ *            it, batches route experts flagged as holding scales or biases beyond
+ *            the matrix cores' range to the fp32-scaled GEMV path; without it the
+ *            range limit of moe_layer_decode applies.
  */
 typedef struct moe_layer_desc {
     int32_t H, I, E, K, bits, group;
@@ -79,6 +83,7 @@ typedef struct moe_layer_desc {
     const float* logit_bias;
     float shared_weight;
     int32_t renormalize;
+    const int32_t* expert_flags;
 } moe_layer_desc;
 
 /*
@@ -149,6 +154,16 @@ int moe_dequant_expert(int bits, int H, int I, int group, const void* record, fl
                        void* stream);
 
 /*
+ * Range flags of records [0, n_experts) of a packed slab, for
+ * moe_layer_desc.expert_flags: flags_out[e] = 1 if record e holds a group whose
+ * scale or bias the batched matrix-core path cannot take (|s| >= 256,
+ * |b| >= 2048 or not finite), else 0.  Reads only the records' scales and biases
+ * (1/9 of a 4-bit record).  flags_out: device int32 [n_experts].
+ */
+int moe_expert_ranges(int bits, int H, int I, int group, const void* slab, int n_experts, int32_t* flags_out,
+                      void* stream);
+
+/*
  * Router ([LLMAPIS] section 深度分析; [CLAUDAY]): logits = W_r x (+ bias),
  * each fp32 product accumulated in fp64; keep the K largest (ties to the
  * lower id), in rank order; w = softmax weights (renormalized over the K if
@@ -187,8 +202,9 @@ int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const i
  * Value range: with 4-bit codes and B >= 2 the experts that several tokens
  * share run on the matrix cores, which take each group's scale s as fp16 and
  * (b + 8 s) through fp16 operands 2^5 b and 2^8 s: there |s| < 256 and
- * |b| < 2048 per group (larger values overflow to inf in y).  The other paths
- * apply scale and bias in fp32.
+ * |b| < 2048 per group (larger values overflow to inf in y) unless
+ * desc->expert_flags (moe_expert_ranges) marks such experts, which then run on
+ * the GEMV path (at H, I <= 4096).  The other paths apply scale and bias in fp32.
  */
 int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y_out,
                      int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream);

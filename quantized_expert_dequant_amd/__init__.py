@@ -46,7 +46,7 @@ class LayerDesc(ctypes.Structure):
                 ("K", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("experts", ctypes.c_void_p), ("w_router", ctypes.c_void_p),
                 ("logit_bias", ctypes.c_void_p), ("shared_weight", ctypes.c_float),
-                ("renormalize", ctypes.c_int32)]
+                ("renormalize", ctypes.c_int32), ("expert_flags", ctypes.c_void_p)]
 
 
 _lib = None
@@ -68,6 +68,7 @@ def lib():
             "moe_stack_extra_bytes": (sz, [i32, i32]),
             "moe_pack_experts": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]),
             "moe_dequant_expert": (i32, [i32, i32, i32, i32, vp, vp, vp]),
+            "moe_expert_ranges": (i32, [i32, i32, i32, i32, vp, i32, vp, vp]),
             "moe_requant_4to2": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "moe_route_topk": (i32, [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]),
             "moe_expert_ffn_q4": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
@@ -125,9 +126,10 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_desc(H, I, E, K, bits, experts, w_router, logit_bias=None, shared_weight=1.0, renormalize=True, group=64):
+def make_desc(H, I, E, K, bits, experts, w_router, logit_bias=None, shared_weight=1.0, renormalize=True, group=64,
+              expert_flags=None):
     return LayerDesc(H, I, E, K, bits, group, _p(experts), _p(w_router), _p(logit_bias), float(shared_weight),
-                     int(bool(renormalize)))
+                     int(bool(renormalize)), _p(expert_flags))
 
 
 def record_bytes(bits, H, I, group=64):
@@ -155,6 +157,10 @@ def requant_4to2(H, I, n, gate4, up4, down4, scales4, biases4, gate2, up2, down2
                  group=64):
     return _check(lib().moe_requant_4to2(H, I, group, n, _p(gate4), _p(up4), _p(down4), _p(scales4), _p(biases4),
                                          _p(gate2), _p(up2), _p(down2), _p(scales2), _p(biases2), _stream(stream)))
+
+
+def expert_ranges(bits, H, I, slab, n, flags_out, stream=None, group=64):
+    return _check(lib().moe_expert_ranges(bits, H, I, group, _p(slab), n, _p(flags_out), _stream(stream)))
 
 
 def dequant_expert(bits, H, I, record, W_out, stream=None, group=64):

@@ -14,8 +14,10 @@ size_t cache_state_bytes(int E, int slots);
 void launch_cache_reset(void* state, int E, int slots, hipStream_t s);
 // the call's plan from the selected ids idx [n]: slot ids idx_slot [n] (-1 for ids
 // outside [0, E)) and the copy list plan = [count, (expert, slot) x count]
+// flags (nullable): per expert range flags [E + 1]; then slot_flags [slots + 1] receives
+// them by slot (slot `slots`: the shared expert's)
 void launch_cache_plan(const int32_t* idx, int n, int E, int slots, void* state, int32_t* idx_slot, int32_t* plan,
-                       long long record, hipStream_t s);
+                       long long record, const int32_t* flags, int32_t* slot_flags, hipStream_t s);
 // copy the planned records (at most max_copies) from src (device-accessible) into slab
 void launch_cache_copy(const int32_t* plan, int max_copies, const void* src, void* slab, long long record,
                        hipStream_t s);

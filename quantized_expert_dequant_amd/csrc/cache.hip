@@ -84,7 +84,9 @@ constexpr int CP_THREADS = 1024;
 
 __global__ __launch_bounds__(CP_THREADS) void k_cache_plan(const int32_t* __restrict__ idx, int n, int E, int slots,
                                                           void* state, int32_t* __restrict__ idx_slot,
-                                                          int32_t* __restrict__ plan, unsigned long long record)
+                                                          int32_t* __restrict__ plan, unsigned long long record,
+                                                          const int32_t* __restrict__ flags,
+                                                          int32_t* __restrict__ slot_flags)
 {
     __shared__ uint32_t sel[MOE_MAX_E / 32];
     __shared__ int miss[MOE_MAX_E];
@@ -162,6 +164,12 @@ __global__ __launch_bounds__(CP_THREADS) void k_cache_plan(const int32_t* __rest
         const int e = idx[i];
         idx_slot[i] = (e >= 0 && e < E) ? v.slot_of[e] : -1;
     }
+    if (flags) {  // the range flags by slot, the shared expert's last
+        for (int sl = tid; sl <= slots; sl += CP_THREADS) {
+            const int e = sl < slots ? v.expert_of[sl] : E;
+            slot_flags[sl] = e >= 0 ? flags[e] : 0;
+        }
+    }
     if (tid == 0) {
         plan[0] = nm;
         v.counters[0] += (unsigned long long)n_hit;
@@ -191,10 +199,10 @@ __global__ __launch_bounds__(256) void k_cache_copy(const int32_t* __restrict__ 
 }
 
 void launch_cache_plan(const int32_t* idx, int n, int E, int slots, void* state, int32_t* idx_slot, int32_t* plan,
-                       long long record, hipStream_t s)
+                       long long record, const int32_t* flags, int32_t* slot_flags, hipStream_t s)
 {
     hipLaunchKernelGGL(k_cache_plan, dim3(1), dim3(CP_THREADS), 0, s, idx, n, E, slots, state, idx_slot, plan,
-                       (unsigned long long)record);
+                       (unsigned long long)record, flags, slot_flags);
 }
 
 void launch_cache_copy(const int32_t* plan, int max_copies, const void* src, void* slab, long long record,

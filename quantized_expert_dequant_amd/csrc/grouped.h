@@ -83,7 +83,11 @@ void launch_route_batched(const float* x, int B, const float* W, const float* bi
                           double* partial, int32_t* idx, float* w, const TokenPrep& P, hipStream_t s, Timing t);
 // experts with fewer tokens than this run as GEMV groups (1: none)
 int gemv_tokens(const Layout& L);
-void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const GroupOut& O, hipStream_t s);
+// flags (nullable): per expert (index E: the shared one), nonzero = run it as GEMV groups
+void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const int32_t* flags, const GroupOut& O,
+                  hipStream_t s);
+// flags[e] of records [0, n): 1 if a scale or bias lies outside the matrix-core path's range
+void launch_expert_ranges(const Layout& L, const void* slab, int n, int32_t* flags, hipStream_t s);
 // xq / xst: room for the B tokens' dot2 operands (fp16 pairs + group stats)
 // prepped: the token operands are already written (by the batched top-K kernel)
 void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W, const float* x, const float* w,

@@ -238,7 +238,8 @@ void launch_route_batched(const float* x, int B, const float* W, const float* bi
 // at most GM_GROUP tokens (the shared expert's B entries first, then the routed
 // experts by id), so that every group is one pass of the dequant-GEMM.
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx, int B, int K, int E, int gv_t, GroupOut O)
+__global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx, int B, int K, int E, int gv_t,
+                                                 const int32_t* __restrict__ flags, GroupOut O)
 {
     __shared__ int sidx[MOE_MAX_B * MOE_MAX_K];
     __shared__ int cnt[MOE_MAX_E];
@@ -257,9 +258,13 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
     __syncthreads();
     const int c = tid < E ? cnt[tid] : 0;
     // an expert with fewer than gv_t tokens is one GEMV group, a larger one is
-    // cut into MFMA groups of at most GM_GROUP tokens
-    const int fm = c >= gv_t ? (c + GM_GROUP - 1) / GM_GROUP : 0;
-    const int fg = (c > 0 && c < gv_t) ? 1 : 0;
+    // cut into MFMA groups of at most GM_GROUP tokens; an expert flagged as holding
+    // scales or biases beyond the matrix cores' range is cut into GEMV groups of at
+    // most gv_t - 1 tokens whatever its count (the GEMV applies them in fp32)
+    const int gsz = gv_t > 1 ? gv_t - 1 : 1;
+    const bool fl = flags != nullptr && gv_t > 1 && tid < E && flags[tid] != 0;
+    const int fm = (!fl && c >= gv_t) ? (c + GM_GROUP - 1) / GM_GROUP : 0;
+    const int fg = fl ? (c + gsz - 1) / gsz : ((c > 0 && c < gv_t) ? 1 : 0);
     // exclusive scans of the counts and of both group counts over the block
     int sc = c, sm = fm, sg = fg;
     for (int off = 1; off < 64; off <<= 1) {
@@ -284,8 +289,8 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
     }
     const int excl_c = pc + sc - c, excl_m = pm + sm - fm, excl_g = pg + sg - fg;
     // the shared expert (all B tokens, entries 0 .. B-1) leads its list
-    const bool shared_gemv = B < gv_t;
-    const int vsm = shared_gemv ? 0 : (B + GM_GROUP - 1) / GM_GROUP, vsg = shared_gemv ? 1 : 0;
+    const bool shared_gemv = B < gv_t || (flags != nullptr && gv_t > 1 && flags[E] != 0);
+    const int vsm = shared_gemv ? 0 : (B + GM_GROUP - 1) / GM_GROUP, vsg = shared_gemv ? (B + gsz - 1) / gsz : 0;
     if (tid < E) {
         O.offsets[tid] = excl_c;
         cnt[tid] = excl_c;  // running position of expert tid
@@ -295,10 +300,10 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
                 O.act_off[vsm + excl_m + j] = B + excl_c + j * GM_GROUP;
                 O.act_n[vsm + excl_m + j] = min(GM_GROUP, c - j * GM_GROUP);
             }
-            if (fg) {
-                O.gv_expert[vsg + excl_g] = tid;
-                O.gv_off[vsg + excl_g] = B + excl_c;
-                O.gv_n[vsg + excl_g] = c;
+            for (int j = 0; j < fg; ++j) {
+                O.gv_expert[vsg + excl_g + j] = tid;
+                O.gv_off[vsg + excl_g + j] = B + excl_c + j * gsz;
+                O.gv_n[vsg + excl_g + j] = fl ? min(gsz, c - j * gsz) : c;
             }
         }
     }
@@ -315,10 +320,10 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
             O.act_off[j] = j * GM_GROUP;
             O.act_n[j] = min(GM_GROUP, B - j * GM_GROUP);
         }
-        if (shared_gemv && tid == 0) {
-            O.gv_expert[0] = E;
-            O.gv_off[0] = 0;
-            O.gv_n[0] = B;
+        for (int j = tid; j < vsg; j += 1024) {
+            O.gv_expert[j] = E;
+            O.gv_off[j] = j * gsz;
+            O.gv_n[j] = min(gsz, B - j * gsz);
         }
         for (int b = tid; b < B; b += 1024) O.ent_token[b] = b;
     }
@@ -351,9 +356,42 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
 
 int gemv_tokens(const Layout& L) { return (L.bits == 4 && L.Gh <= 64 && L.Gi <= 64) ? GV_TOKENS : 1; }
 
-void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const GroupOut& O, hipStream_t s)
+void launch_group(const int32_t* idx, int B, int K, int E, int gv_tokens, const int32_t* flags, const GroupOut& O,
+                  hipStream_t s)
 {
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, idx, B, K, E, gv_tokens, O);
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(1024), 0, s, idx, B, K, E, gv_tokens, flags, O);
+}
+
+// flags[e] = 1 if record e holds a group whose scale or bias the matrix-core path
+// cannot take (|s| >= 256, |b| >= 2048, or not finite), else 0; one block per record.
+// The scale/bias areas alternate (s, b) bf16 pairs, so element parity tells them apart.
+__global__ __launch_bounds__(256) void k_expert_ranges(Layout L, const uint8_t* __restrict__ slab,
+                                                       int32_t* __restrict__ flags)
+{
+    const uint8_t* rec = slab + (long long)blockIdx.x * L.record;
+    const long long n_gu = (long long)L.I * L.Gh * 8 / 16, n_dn = (long long)L.H * L.Gi * 4 / 16;
+    const uint4* gu = reinterpret_cast<const uint4*>(rec + L.off_gu_sb);
+    const uint4* dn = reinterpret_cast<const uint4*>(rec + L.off_d_sb);
+    auto bad = [](uint4 v) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        int r = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float sc = fabsf(bf16_lo(w[k])), bi = fabsf(bf16_hi(w[k]));
+            r |= !(sc < 256.f) || !(bi < 2048.f);  // also true for NaN
+        }
+        return r;
+    };
+    int any = 0;
+    for (long long i = threadIdx.x; i < n_gu; i += 256) any |= bad(gu[i]);
+    for (long long i = threadIdx.x; i < n_dn; i += 256) any |= bad(dn[i]);
+    any = __syncthreads_or(any);
+    if (threadIdx.x == 0) flags[blockIdx.x] = any ? 1 : 0;
+}
+
+void launch_expert_ranges(const Layout& L, const void* slab, int n, int32_t* flags, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_expert_ranges, dim3(n), dim3(256), 0, s, L, (const uint8_t*)slab, flags);
 }
 
 // ----------------------------------------------------------------------------
@@ -1089,8 +1127,10 @@ bool grouped_supported(const Layout& L, int B, int K)
            gm_steps(L, MODE_GATEUP) >= GM_KC_GATEUP;
 }
 
-// most work-list groups a call can produce: every expert's entries cut into groups of GM_GROUP
-static int max_groups(int B, int K, int E) { return (B + GM_GROUP - 1) / GM_GROUP + min(E, B * K) + (B * K) / GM_GROUP; }
+// most work-list groups of either list a call can produce: the shared expert's B entries
+// and every expert's entries cut into GEMV groups of at most 2 (experts flagged as out of the
+// matrix cores' range) or into MFMA groups of at most GM_GROUP
+static int max_groups(int B, int K, int E) { return (B + 1) / 2 + min(E, B * K) + (B * K + 1) / 2 + 1; }
 
 size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E)
 {

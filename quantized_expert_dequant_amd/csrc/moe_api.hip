@@ -140,6 +140,26 @@ Work carve(void* ws, int bits, int B, int H, int I, int E, int K)
     return W;
 }
 
+// The backing store as a device address: pinned host memory is translated, device
+// memory is used as it is.
+const void* backing_device_ptr(const void* p)
+{
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (a.type == hipMemoryTypeHost) {
+        void* d = nullptr;
+        if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        return d;
+    }
+    return p;
+}
+
 int hip_status(const char* fn)
 {
     hipError_t e = hipGetLastError();
@@ -267,6 +287,23 @@ int moe_requant_4to2(int H, int I, int group, int n_experts, const uint8_t* gate
     return hip_status(fn);
 }
 
+int moe_expert_ranges(int bits, int H, int I, int group, const void* slab, int n_experts, int32_t* flags_out,
+                      void* stream)
+{
+    const char* fn = "moe_expert_ranges";
+    int rc = check_shape(fn, bits, H, I, group);
+    if (rc) return rc;
+    if (n_experts < 1 || n_experts > (1 << 24)) return fail(MOE_EINVAL, "%s: n_experts=%d", fn, n_experts);
+    CHECK_PTR(slab);
+    CHECK_PTR4(flags_out);
+    const void* src = backing_device_ptr(slab);
+    if (!src) return fail(MOE_EINVAL, "%s: slab is neither device memory nor pinned host memory", fn);
+    const void* dst = backing_device_ptr(flags_out);
+    if (!dst) return fail(MOE_EINVAL, "%s: flags_out is neither device memory nor pinned host memory", fn);
+    launch_expert_ranges(make_layout(bits, H, I), src, n_experts, (int32_t*)dst, (hipStream_t)stream);
+    return hip_status(fn);
+}
+
 int moe_dequant_expert(int bits, int H, int I, int group, const void* record, float* W_out, void* stream)
 {
     const char* fn = "moe_dequant_expert";
@@ -315,7 +352,7 @@ static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, cons
     hipStream_t s = (hipStream_t)stream;
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
     if (W.grouped) {
-        launch_group(idx, B, desc->K, desc->E, gemv_tokens(L), W.gw.g, s);
+        launch_group(idx, B, desc->K, desc->E, gemv_tokens(L), desc->expert_flags, W.gw.g, s);
         launch_ffn_grouped(L, desc->experts, W.gw, x, w, desc->shared_weight, B, desc->K, desc->E, W.xq, W.xst, false,
                            y_out, s, g_timing[KID_GATEUP], g_timing[KID_DOWN]);
         return hip_status(fn);
@@ -350,7 +387,7 @@ static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, i
         const TokenPrep P{x, d->H, W.gw.xh, W.gw.xsum, W.gw.xscale, gemv_tokens(L) > 1 ? W.xq : nullptr, W.xst};
         launch_route_batched(x, B, d->w_router, d->logit_bias, d->H, d->E, d->K, d->renormalize ? 1 : 0,
                              W.gw.partial, idx, w, P, s, g_timing[KID_ROUTER]);
-        launch_group(idx, B, d->K, d->E, gemv_tokens(L), W.gw.g, s);
+        launch_group(idx, B, d->K, d->E, gemv_tokens(L), d->expert_flags, W.gw.g, s);
         launch_ffn_grouped(L, d->experts, W.gw, x, w, d->shared_weight, B, d->K, d->E, W.xq, W.xst, true, y_out, s,
                            g_timing[KID_GATEUP], g_timing[KID_DOWN]);
         return hip_status(fn);
@@ -431,9 +468,9 @@ size_t moe_cache_state_bytes(int E, int slots)
 // Workspace of a cached decode: the layer's workspace carved for max(E, slots)
 // experts (the router works on E ids, the expert FFNs on slot ids), then the slot
 // ids of the selection and the copy plan.
-static size_t cached_extra_bytes(int B, int K, int E)
+static size_t cached_extra_bytes(int B, int K, int E, int slots)
 {
-    return up256((size_t)B * K * 4) + up256(4 * (1 + 2 * (size_t)std::min(E, B * K)));
+    return up256((size_t)B * K * 4) + up256(4 * (1 + 2 * (size_t)std::min(E, B * K))) + up256(4 * ((size_t)slots + 1));
 }
 
 size_t moe_cache_workspace_bytes(const moe_layer_desc* desc, int slots, int B)
@@ -442,27 +479,8 @@ size_t moe_cache_workspace_bytes(const moe_layer_desc* desc, int slots, int B)
         check_routing("moe_cache_workspace_bytes", B, desc->E, desc->K) || slots < 1 || slots > MOE_MAX_CACHE_SLOTS)
         return 0;
     const int Eb = std::max(desc->E, slots);
-    return carve(nullptr, desc->bits, B, desc->H, desc->I, Eb, desc->K).bytes + cached_extra_bytes(B, desc->K, desc->E);
-}
-
-// The backing store as a device address: pinned host memory is translated, device
-// memory is used as it is.
-static const void* backing_device_ptr(const void* p)
-{
-    hipPointerAttribute_t a;
-    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
-        (void)hipGetLastError();
-        return nullptr;
-    }
-    if (a.type == hipMemoryTypeHost) {
-        void* d = nullptr;
-        if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess) {
-            (void)hipGetLastError();
-            return nullptr;
-        }
-        return d;
-    }
-    return p;
+    return carve(nullptr, desc->bits, B, desc->H, desc->I, Eb, desc->K).bytes +
+           cached_extra_bytes(B, desc->K, desc->E, slots);
 }
 
 static int check_cache(const char* fn, const moe_layer_desc* d, const moe_expert_cache* c)
@@ -519,10 +537,12 @@ int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* 
     if (!src) return fail(MOE_EINVAL, "%s: desc->experts is neither device memory nor pinned host memory", fn);
     const int Eb = std::max(E, S);
     const Work W = carve(ws, desc->bits, B, desc->H, desc->I, Eb, K);
-    const size_t need = W.bytes + cached_extra_bytes(B, K, E);
+    const size_t need = W.bytes + cached_extra_bytes(B, K, E, S);
     if (ws_bytes < need) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
     int32_t* idx_slot = (int32_t*)((char*)ws + W.bytes);
     int32_t* plan = (int32_t*)((char*)ws + W.bytes + up256((size_t)B * K * 4));
+    int32_t* slot_flags = desc->expert_flags ? (int32_t*)((char*)plan + up256(4 * (1 + 2 * (size_t)std::min(E, B * K))))
+                                             : nullptr;
     int32_t* idx = idx_out ? idx_out : W.idx;
     float* w = w_out ? w_out : W.w;
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
@@ -539,11 +559,11 @@ int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* 
         launch_topk(W.logits, B, E, K, renorm, idx, w, s);
     }
     // 2. map the selection onto slots and bring in the missing records
-    launch_cache_plan(idx, B * K, E, S, cache->state, idx_slot, plan, L.record, s);
+    launch_cache_plan(idx, B * K, E, S, cache->state, idx_slot, plan, L.record, desc->expert_flags, slot_flags, s);
     launch_cache_copy(plan, std::min(E, B * K), src, cache->slab, L.record, s);
     // 3. the expert FFNs on the cache, by slot id (the shared expert at slot S)
     if (W.grouped) {
-        launch_group(idx_slot, B, K, S, gemv_tokens(L), W.gw.g, s);
+        launch_group(idx_slot, B, K, S, gemv_tokens(L), slot_flags, W.gw.g, s);
         launch_ffn_grouped(L, cache->slab, W.gw, x, w, desc->shared_weight, B, K, S, W.xq, W.xst, true, y_out, s,
                            g_timing[KID_GATEUP], g_timing[KID_DOWN]);
     } else {
@@ -567,7 +587,7 @@ int moe_group_tokens(const int32_t* idx, int B, int K, int E, int32_t* offsets_o
     O.offsets = offsets_out;
     O.tokens = tokens_out;
     O.slots = slots_out;
-    launch_group(idx, B, K, E, 1, O, (hipStream_t)stream);
+    launch_group(idx, B, K, E, 1, nullptr, O, (hipStream_t)stream);
     return hip_status(fn);
 }
 

@@ -11,7 +11,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-from . import make_desc, pack_experts, record_bytes, requant_4to2, workspace_bytes, stack_extra_bytes
+from . import (expert_ranges, make_desc, pack_experts, record_bytes, requant_4to2, workspace_bytes,
+               stack_extra_bytes)
 
 
 def upload_experts(source, n_total, bits, H, I, device="cuda", chunk=32, slab=None):
@@ -87,11 +88,18 @@ class DeviceLayer:
     logit_bias: torch.Tensor = None
     shared_weight: float = 1.0
     renormalize: bool = True
+    range_flags: bool = True    # scan the records for the matrix-core range (moe_expert_ranges)
     desc: object = field(init=False)
+    expert_flags: torch.Tensor = field(init=False, default=None)
 
     def __post_init__(self):
+        if self.range_flags:
+            # on the GPU even when the records are a store in pinned host memory
+            self.expert_flags = torch.empty(self.E + 1, dtype=torch.int32, device=self.w_router.device)
+            expert_ranges(self.bits, self.H, self.I, self.slab, self.E + 1, self.expert_flags)
         self.desc = make_desc(self.H, self.I, self.E, self.K, self.bits, self.slab, self.w_router,
-                              self.logit_bias, self.shared_weight, self.renormalize)
+                              self.logit_bias, self.shared_weight, self.renormalize,
+                              expert_flags=self.expert_flags)
 
     def record(self, e):
         rb = record_bytes(self.bits, self.H, self.I)

@@ -256,3 +256,54 @@ def test_large_scales_and_biases(B):
     assert np.all(np.isfinite(y))
     for b in range(B):
         assert rel_err(y[b], y_ref[b]) <= TOL, "token %d" % b
+
+
+def _bf16_scaled(bits16, k):
+    """bf16 patterns times 2^k (exponent field shifted; zeros and subnormals left alone)."""
+    b = bits16.astype(np.int32)
+    e = (b >> 7) & 0xFF
+    ok = (e > 0) & (e + k < 255)
+    return np.where(ok, (b & ~(0xFF << 7)) | ((e + k) << 7), b).astype(np.uint16)
+
+
+def test_batched_scales_beyond_the_matrix_core_range():
+    """Experts 3 and 5 and the shared expert get scales x 2^14 (many |s| >= 256) or biases
+    x 2^18 (many |b| >= 2048): moe_expert_ranges flags exactly those records, and with the
+    flags in the descriptor a 32-token batch that gives each of them every token (matrix-core
+    sized groups otherwise) matches the oracle on every token, through the fp32-scaled GEMV."""
+    cfg, seed = dict(WORKLOADS[0]), seed_of(0)
+    H, I, E, K = cfg["H"], cfg["I"], cfg["E"], cfg["K"]
+    from quantized_expert_dequant_amd.slab import DeviceLayer, upload_experts
+    ex = synth.experts(seed, 0, 0, E + 1, 4, H, I)
+    ex.scales[3] = _bf16_scaled(ex.scales[3], 14)
+    ex.biases[5] = _bf16_scaled(ex.biases[5], 18)
+    ex.scales[E] = _bf16_scaled(ex.scales[E], 14)
+
+    def src(first, n):
+        return synth.Canonical(4, H, I, 64, ex.gate[first:first + n], ex.up[first:first + n],
+                               ex.down[first:first + n], ex.scales[first:first + n], ex.biases[first:first + n])
+
+    slab = upload_experts(src, E + 1, 4, H, I, device=DEV)
+    wr = torch.from_numpy(synth.router(seed, 0, E, H)).to(DEV)
+    L = DeviceLayer(H, I, E, K, 4, slab, wr)
+    flags = L.expert_flags.cpu().numpy()
+    want = np.zeros(E + 1, np.int32)
+    want[[3, 5, E]] = 1
+    np.testing.assert_array_equal(flags, want)
+    B = 32
+    x = synth.tokens(seed, 88, B, H)
+    idx = np.stack([[3, 5, 6 + b % 10, b % 3] for b in range(B)]).astype(np.int32)
+    w = np.random.default_rng(1).random((B, K)).astype(np.float32)
+    ws, nb = workspace(L.desc, B)
+    y = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    moe.expert_ffn_q4(L.desc, _t(x), B, _t(idx), _t(w), y, ws, nb)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+
+    def ffn(e, xb):
+        return oracle.expert_ffn(4, H, I, ex.gate[e], ex.up[e], ex.down[e], ex.scales[e], ex.biases[e], xb)[1]
+
+    for b in range(B):
+        ref = ffn(E, x[b]) + sum(float(w[b, k]) * ffn(int(idx[b, k]), x[b]) for k in range(K))
+        assert np.all(np.isfinite(yh[b])), "token %d" % b
+        assert rel_err(yh[b], ref) <= TOL, "token %d: %.3e" % (b, rel_err(yh[b], ref))
