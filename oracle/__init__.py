@@ -62,6 +62,9 @@ def lib():
         L.oracle_bf16_round.argtypes = [dbl]
         L.oracle_requant_group.argtypes = [i32, vp, ctypes.c_uint16, ctypes.c_uint16, vp, vp, vp]
         L.oracle_requant_expert.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_gdn_step.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_attn_decode.restype = i32
+        L.oracle_attn_decode.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -257,4 +260,28 @@ def requant_expert(H, I, gate, up, down, scales, biases, group=64):
     lib().oracle_requant_expert(H, I, group, _p(g4), _p(u4), _p(d4), _p(s4), _p(b4), _p(g2), _p(u2), _p(d2),
                                 _p(s2), _p(b2))
     return g2, u2, d2, s2, b2
+
+
+def gdn_step(S, q, k, v, alpha, beta):
+    """One gated-delta-rule step: (S' [n][dv][dk], o [n][dv]) in float64 (S is not modified)."""
+    S = np.array(S, np.float64, copy=True)
+    n, dv, dk = S.shape
+    q, k = _c(q, np.float64).reshape(n, dk), _c(k, np.float64).reshape(n, dk)
+    v = _c(v, np.float64).reshape(n, dv)
+    a, b = _c(alpha, np.float64).reshape(n), _c(beta, np.float64).reshape(n)
+    o = np.empty((n, dv), np.float64)
+    lib().oracle_gdn_step(n, dk, dv, _p(S), _p(q), _p(k), _p(v), _p(a), _p(b), _p(o))
+    return S, o
+
+
+def attn_decode(q, K, V):
+    """One grouped-query attention decode step: q [n_q][d] float, K, V bf16 bits [n_kv][T][d] -> o [n_q][d]."""
+    q = _c(q, np.float64)
+    K, V = _c(K, np.uint16), _c(V, np.uint16)
+    n_q, d = q.shape
+    n_kv, T, _ = K.shape
+    o = np.empty((n_q, d), np.float64)
+    if lib().oracle_attn_decode(n_q, n_kv, d, T, _p(q), _p(K), _p(V), _p(o)) != 0:
+        raise ValueError("oracle_attn_decode: bad shape")
+    return o
 

@@ -485,3 +485,90 @@ void oracle_requant_expert(int H, int I, int group, const uint8_t* gate4, const 
     requant_matrix(H, I, group, down4, scales4 + 2 * ngu, biases4 + 2 * ngu, down2, scales2 + 2 * ngu,
                    biases2 + 2 * ngu);
 }
+
+/* ---- the attention half of a decode step ----------------------------------------- */
+
+/*
+ * The pages name the two kinds of attention layer of the model, 45 GatedDeltaNet
+ * (linear attention) layers and 15 full-attention layers, and say the linear
+ * attention ran on the CPU with BLAS ([LLMAPIS] section 深度分析; [MFFB] section
+ * 有效的优化), without formulas.  The readings used here:
+ *
+ * GatedDeltaNet, one decode step of the gated delta rule per head h (state S_h,
+ * dv x dk, row-major; the rule as published by Yang, Kautz and Hatamizadeh, 2024):
+ *   S_h <- alpha_h * S_h (I - beta_h k_h k_h^T) + beta_h v_h k_h^T,   o_h = S_h q_h
+ * with q_h, k_h in R^dk, v_h in R^dv, a decay alpha_h and a write strength beta_h,
+ * all given (the projections that make them are plain GEMVs and not part of this
+ * step).
+ *
+ * Full attention, one decode step of grouped-query attention: query head h reads
+ * key/value head g = h / (n_q / n_kv) over T cached positions,
+ *   o_h = sum_t softmax_t(q_h . K_g[t] / sqrt(d)) V_g[t],
+ * with K and V as bf16 bit patterns [n_kv][T][d].
+ */
+
+/* One step of the gated delta rule for n_heads heads; S [n][dv][dk] is updated in place. */
+void oracle_gdn_step(int n_heads, int dk, int dv, double* S, const double* q, const double* k,
+                     const double* v, const double* alpha, const double* beta, double* o)
+{
+    double* Sk = (double*)malloc(sizeof(double) * (size_t)dv);
+    if (!Sk) return;
+    for (int h = 0; h < n_heads; ++h) {
+        double* Sh = S + (long)h * dv * dk;
+        const double* kh = k + (long)h * dk;
+        const double* qh = q + (long)h * dk;
+        const double* vh = v + (long)h * dv;
+        /* S (I - beta k k^T) = S - beta (S k) k^T */
+        for (int r = 0; r < dv; ++r) {
+            double acc = 0.0;
+            for (int c = 0; c < dk; ++c) acc += Sh[(long)r * dk + c] * kh[c];
+            Sk[r] = acc;
+        }
+        for (int r = 0; r < dv; ++r)
+            for (int c = 0; c < dk; ++c) {
+                double m = Sh[(long)r * dk + c] - beta[h] * Sk[r] * kh[c];
+                Sh[(long)r * dk + c] = alpha[h] * m + beta[h] * vh[r] * kh[c];
+            }
+        for (int r = 0; r < dv; ++r) {
+            double acc = 0.0;
+            for (int c = 0; c < dk; ++c) acc += Sh[(long)r * dk + c] * qh[c];
+            o[(long)h * dv + r] = acc;
+        }
+    }
+    free(Sk);
+}
+
+/* One decode step of grouped-query attention over T cached positions (n_q % n_kv == 0). */
+int oracle_attn_decode(int n_q, int n_kv, int d, int T, const double* q, const uint16_t* K,
+                       const uint16_t* V, double* o)
+{
+    if (n_kv < 1 || n_q % n_kv != 0 || T < 1) return -1;
+    double* sc = (double*)malloc(sizeof(double) * (size_t)T);
+    if (!sc) return -1;
+    int per = n_q / n_kv;
+    double scale = 1.0 / sqrt((double)d);
+    for (int h = 0; h < n_q; ++h) {
+        int g = h / per;
+        const uint16_t* Kg = K + (long)g * T * d;
+        const uint16_t* Vg = V + (long)g * T * d;
+        double mx = -INFINITY;
+        for (int t = 0; t < T; ++t) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += q[(long)h * d + c] * oracle_bf16_to_double(Kg[(long)t * d + c]);
+            sc[t] = acc * scale;
+            if (sc[t] > mx) mx = sc[t];
+        }
+        double z = 0.0;
+        for (int t = 0; t < T; ++t) {
+            sc[t] = exp(sc[t] - mx);
+            z += sc[t];
+        }
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int t = 0; t < T; ++t) acc += sc[t] * oracle_bf16_to_double(Vg[(long)t * d + c]);
+            o[(long)h * d + c] = acc / z;
+        }
+    }
+    free(sc);
+    return 0;
+}

@@ -50,6 +50,11 @@ void oracle_requant_expert(int H, int I, int group, const uint8_t* gate4, const 
                            const uint16_t* scales4, const uint16_t* biases4, uint8_t* gate2, uint8_t* up2,
                            uint8_t* down2, uint16_t* scales2, uint16_t* biases2);
 
+void oracle_gdn_step(int n_heads, int dk, int dv, double* S, const double* q, const double* k, const double* v,
+                     const double* alpha, const double* beta, double* o);
+int oracle_attn_decode(int n_q, int n_kv, int d, int T, const double* q, const uint16_t* K, const uint16_t* V,
+                       double* o);
+
 /* synth.c */
 size_t synth_codes_bytes(int bits, int rows, int cols);
 void synth_experts(uint64_t seed, int64_t layer, int64_t first, int n, int bits, int H, int I, int group,
@@ -232,6 +237,26 @@ int main(void)
     EXPECT(oracle_bf16_round(1.0 + 1.0 / 256) == 0x3F80 && oracle_bf16_round(1.0 + 3.0 / 256) == 0x3F82,
            "bf16 rounding ties to even");
     EXPECT(oracle_bf16_round(3.4e38) == 0x7F80 && oracle_bf16_round(-0.0) == 0x8000, "bf16 rounding edges");
+    {   /* the attention half: a gated-delta step with beta = 0 only decays the state; one cached
+           position makes attention return that position's value */
+        enum { NH = 3, DK = 8, DV = 6, T = 5, D = 8 };
+        double S[NH * DV * DK], S0[NH * DV * DK], q[NH * DK], k[NH * DK], v[NH * DV], a[NH], b[NH], o[NH * DV];
+        for (int i = 0; i < NH * DV * DK; ++i) S[i] = S0[i] = (double)((i * 37) % 11) - 5.0;
+        for (int i = 0; i < NH * DK; ++i) q[i] = k[i] = (double)((i * 13) % 7) - 3.0;
+        for (int i = 0; i < NH * DV; ++i) v[i] = (double)(i % 5);
+        for (int h = 0; h < NH; ++h) { a[h] = 0.5; b[h] = 0.0; }
+        oracle_gdn_step(NH, DK, DV, S, q, k, v, a, b, o);
+        for (int i = 0; i < NH * DV * DK; ++i) EXPECT(S[i] == 0.5 * S0[i], "gdn decay %d", i);
+        uint16_t K[2 * T * D], V[2 * T * D];
+        double qa[4 * D], oa[4 * D];
+        for (int i = 0; i < 2 * T * D; ++i) { K[i] = 0x3F80; V[i] = (uint16_t)(0x3F80 + (i % 3)); }
+        for (int i = 0; i < 4 * D; ++i) qa[i] = 0.25 * (i % 4);
+        EXPECT(oracle_attn_decode(4, 2, D, 1, qa, K, V, oa) == 0, "attention T=1");
+        for (int h = 0; h < 4; ++h)
+            for (int c = 0; c < D; ++c)
+                EXPECT(oa[h * D + c] == oracle_bf16_to_double(V[(h / 2) * 1 * D + c]), "attention h=%d c=%d", h, c);
+        EXPECT(oracle_attn_decode(4, 3, D, T, qa, K, V, oa) == -1, "attention n_q %% n_kv rejected");
+    }
     run_layer(4, 128, 64, 16, 4, 3, 0);
     run_layer(2, 128, 64, 16, 4, 3, 1);
     run_layer(4, 192, 128, 37, 5, 4, 1);

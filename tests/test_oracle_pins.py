@@ -481,3 +481,99 @@ def test_requant_expert_group_and_row_indexing():
                 assert (ss, bb) == (int(s2[gi]), int(b2[gi])), (name, r, g)
                 np.testing.assert_array_equal(W2[r, 64 * g:64 * g + 64],
                                               bf16_value(ss) * q2.astype(np.float64) + bf16_value(bb))
+
+
+# ------------------- the attention half: GatedDeltaNet and full attention -------------------
+
+def _gdn_inputs(rng, n=3, dk=8, dv=6):
+    S = rng.normal(0, 1, (n, dv, dk))
+    q, k = rng.normal(0, 1, (n, dk)), rng.normal(0, 1, (n, dk))
+    v = rng.normal(0, 1, (n, dv))
+    return S, q, k, v, rng.uniform(0.5, 1.0, n), rng.uniform(0.0, 1.0, n)
+
+
+def test_gdn_no_write_decays_the_state():
+    """beta = 0: the state is only decayed, S' = alpha S, and o = S' q."""
+    S, q, k, v, a, _ = _gdn_inputs(np.random.default_rng(1))
+    S1, o = oracle.gdn_step(S, q, k, v, a, np.zeros(3))
+    np.testing.assert_array_equal(S1, a[:, None, None] * S)
+    for h in range(3):
+        np.testing.assert_allclose(o[h], S1[h] @ q[h], rtol=1e-13, atol=1e-13)
+
+
+def test_gdn_write_into_an_empty_state_is_the_outer_product():
+    _, q, k, v, a, b = _gdn_inputs(np.random.default_rng(2))
+    S1, o = oracle.gdn_step(np.zeros((3, 6, 8)), q, k, v, a, b)
+    for h in range(3):
+        np.testing.assert_array_equal(S1[h], np.outer(b[h] * v[h], k[h]))
+
+
+def test_gdn_delta_rule_fixed_point():
+    """alpha = beta = 1 and a unit key: the new state maps k exactly onto v (S' k = v)."""
+    rng = np.random.default_rng(3)
+    S, q, k, v, _, _ = _gdn_inputs(rng, n=4, dk=16, dv=12)
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    S1, _ = oracle.gdn_step(S, q, k, v, np.ones(4), np.ones(4))
+    for h in range(4):
+        np.testing.assert_allclose(S1[h] @ k[h], v[h], rtol=1e-12, atol=1e-12)
+    # a key orthogonal to k keeps its image, decayed: S' u = alpha S u for u . k = 0
+    u = rng.normal(0, 1, 16)
+    u -= (u @ k[0]) * k[0]
+    S2, _ = oracle.gdn_step(S, q, k, v, np.full(4, 0.7), np.full(4, 0.3))
+    np.testing.assert_allclose(S2[0] @ u, 0.7 * (S[0] @ u), rtol=1e-12, atol=1e-12)
+
+
+def test_gdn_heads_are_independent():
+    S, q, k, v, a, b = _gdn_inputs(np.random.default_rng(4), n=5)
+    p = np.array([3, 0, 4, 1, 2])
+    S1, o1 = oracle.gdn_step(S, q, k, v, a, b)
+    S2, o2 = oracle.gdn_step(S[p], q[p], k[p], v[p], a[p], b[p])
+    np.testing.assert_array_equal(S2, S1[p])
+    np.testing.assert_array_equal(o2, o1[p])
+
+
+def _bf16_bits(x):
+    return np.array([synth.bf16_from_double(float(v)) for v in np.ravel(x)], np.uint16).reshape(np.shape(x))
+
+
+def test_attention_single_position_returns_its_value():
+    rng = np.random.default_rng(5)
+    K, V = _bf16_bits(rng.normal(0, 1, (2, 1, 8))), _bf16_bits(rng.normal(0, 1, (2, 1, 8)))
+    o = oracle.attn_decode(rng.normal(0, 1, (4, 8)), K, V)
+    for h in range(4):
+        np.testing.assert_array_equal(o[h], [bf16_value(b) for b in V[h // 2, 0]])
+
+
+def test_attention_two_positions_closed_form():
+    """d = 4, q = (1, 2, 0, 0), keys (1, 0, 0, 0) and (0, 1, 0, 0): scores 1/2 and 1, so the
+    weights are e^0.5 / (e^0.5 + e^1) and e^1 / (e^0.5 + e^1)."""
+    q = np.array([[1.0, 2.0, 0.0, 0.0]])
+    K = _bf16_bits(np.array([[[1, 0, 0, 0], [0, 1, 0, 0]]], np.float64))
+    V = _bf16_bits(np.array([[[2, 0, 0, 1], [0, 4, 0, 1]]], np.float64))
+    o = oracle.attn_decode(q, K, V)
+    w0, w1 = math.exp(0.5) / (math.exp(0.5) + math.exp(1.0)), math.exp(1.0) / (math.exp(0.5) + math.exp(1.0))
+    np.testing.assert_allclose(o[0], [2 * w0, 4 * w1, 0.0, 1.0], rtol=1e-15, atol=1e-15)
+
+
+def test_attention_uniform_keys_average_the_values_and_gqa_mapping():
+    """Equal keys (or q = 0) give uniform weights: o is the mean of V over the positions;
+    query heads 0..3 read KV head 0 and heads 4..7 KV head 1."""
+    rng = np.random.default_rng(6)
+    T, d = 9, 8
+    K = _bf16_bits(np.broadcast_to(rng.normal(0, 1, (2, 1, d)), (2, T, d)))
+    V = _bf16_bits(rng.normal(0, 1, (2, T, d)))
+    Vd = np.vectorize(bf16_value)(V)
+    o = oracle.attn_decode(rng.normal(0, 1, (8, d)), K, V)
+    for h in range(8):
+        np.testing.assert_allclose(o[h], Vd[h // 4].mean(axis=0), rtol=1e-13, atol=1e-13)
+
+
+def test_attention_positions_are_a_set():
+    """Shuffling the cached positions (keys and values together) leaves o unchanged."""
+    rng = np.random.default_rng(7)
+    T, d = 33, 16
+    q = rng.normal(0, 1, (6, d))
+    K, V = _bf16_bits(rng.normal(0, 1, (3, T, d))), _bf16_bits(rng.normal(0, 1, (3, T, d)))
+    p = rng.permutation(T)
+    np.testing.assert_allclose(oracle.attn_decode(q, K[:, p], V[:, p]), oracle.attn_decode(q, K, V),
+                               rtol=1e-13, atol=1e-13)
