@@ -146,6 +146,35 @@ int moe_requant_4to2(int H, int I, int group, int n_experts, const uint8_t* gate
                      uint8_t* up2, uint8_t* down2, uint16_t* scales2, uint16_t* biases2, void* stream);
 
 /*
+ * The attention half of a decode step.  The pages name the model's attention
+ * layers, 45 GatedDeltaNet (linear attention) and 15 full-attention layers, and say
+ * the linear attention ran on the CPU with BLAS ([LLMAPIS] section 深度分析; [MFFB]
+ * section 有效的优化), without formulas; the readings below are the library's.
+ *
+ * moe_gdn_step: one step of the gated delta rule per head h (as published by Yang,
+ * Kautz and Hatamizadeh, 2024): S_h <- alpha_h S_h (I - beta_h k_h k_h^T) +
+ * beta_h v_h k_h^T, then o_h = S_h q_h.
+ *   state: fp32 [n_heads][dv][dk], updated in place; q, k: fp32 [n_heads][dk];
+ *   v: fp32 [n_heads][dv]; alpha, beta: fp32 [n_heads]; o_out: fp32 [n_heads][dv].
+ *   dk must be 64, 128 or 256 (MOE_EUNSUPPORTED otherwise); 4-byte alignment.
+ */
+int moe_gdn_step(int n_heads, int dk, int dv, float* state, const float* q, const float* k, const float* v,
+                 const float* alpha, const float* beta, float* o_out, void* stream);
+
+/*
+ * moe_attn_decode: one decode step of grouped-query attention over T cached
+ * positions: query head h reads KV head g = h / (n_q / n_kv),
+ * o_h = sum_t softmax_t(q_h . K_g[t] / sqrt(d)) V_g[t].
+ *   q: fp32 [n_q][d]; K, V: bf16 bit patterns [n_kv][T][d] (16-byte aligned);
+ *   o_out: fp32 [n_q][d]; ws: moe_attn_workspace_bytes bytes (per 64-position slice
+ *   partial results).  d must be 64, 128 or 256 and n_q / n_kv at most 16
+ *   (MOE_EUNSUPPORTED otherwise).
+ */
+size_t moe_attn_workspace_bytes(int n_q, int n_kv, int d, int T);
+int moe_attn_decode(int n_q, int n_kv, int d, int T, const float* q, const uint16_t* K, const uint16_t* V,
+                    float* o_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Dequantize one packed record back to dense fp32, reading it exactly as the
  * compute kernels do: W_out = [Wg (I x H) | Wu (I x H) | Wd (H x I)] row-major,
  * each element fmaf(s, q, b).  A check of the packed layout, not a hot path.

@@ -69,6 +69,9 @@ def lib():
             "moe_pack_experts": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]),
             "moe_dequant_expert": (i32, [i32, i32, i32, i32, vp, vp, vp]),
             "moe_expert_ranges": (i32, [i32, i32, i32, i32, vp, i32, vp, vp]),
+            "moe_gdn_step": (i32, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "moe_attn_workspace_bytes": (sz, [i32, i32, i32, i32]),
+            "moe_attn_decode": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "moe_requant_4to2": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
             "moe_route_topk": (i32, [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]),
             "moe_expert_ffn_q4": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
@@ -161,6 +164,20 @@ def requant_4to2(H, I, n, gate4, up4, down4, scales4, biases4, gate2, up2, down2
 
 def expert_ranges(bits, H, I, slab, n, flags_out, stream=None, group=64):
     return _check(lib().moe_expert_ranges(bits, H, I, group, _p(slab), n, _p(flags_out), _stream(stream)))
+
+
+def gdn_step(n_heads, dk, dv, state, q, k, v, alpha, beta, o_out, stream=None):
+    return _check(lib().moe_gdn_step(n_heads, dk, dv, _p(state), _p(q), _p(k), _p(v), _p(alpha), _p(beta), _p(o_out),
+                                     _stream(stream)))
+
+
+def attn_workspace_bytes(n_q, n_kv, d, T):
+    return lib().moe_attn_workspace_bytes(n_q, n_kv, d, T)
+
+
+def attn_decode(n_q, n_kv, d, T, q, K, V, o_out, ws, ws_bytes, stream=None):
+    return _check(lib().moe_attn_decode(n_q, n_kv, d, T, _p(q), _p(K), _p(V), _p(o_out), _p(ws), ws_bytes,
+                                        _stream(stream)))
 
 
 def dequant_expert(bits, H, I, record, W_out, stream=None, group=64):

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["moe_api.hip", "kernels.hip", "grouped.hip", "requant.hip", "cache.hip"]
+SOURCES = ["moe_api.hip", "kernels.hip", "grouped.hip", "requant.hip", "cache.hip", "attention.hip"]
 LIB = os.path.join(HERE, "libmoe.so")
 
 HIPCC_FLAGS = [

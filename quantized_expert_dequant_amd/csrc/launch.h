@@ -26,6 +26,13 @@ void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4
                 int renorm, int32_t* idx, float* w, int B, int K, int E, float shared_w, void* hq, float* y,
                 hipStream_t s, Timing t_gateup = Timing(), Timing t_down = Timing());
 void launch_rmsnorm(const float* y, int B, int H, float eps, float* x, hipStream_t s);
+// the attention half of a decode step (attention.hip)
+void launch_gdn_step(int n_heads, int dk, int dv, float* S, const float* q, const float* k, const float* v,
+                     const float* alpha, const float* beta, float* o, hipStream_t s);
+size_t attn_workspace_bytes(int n_q, int d, int T);
+int attn_max_per();
+void launch_attn_decode(int n_q, int n_kv, int d, int T, const float* q, const uint16_t* K, const uint16_t* V,
+                        float* part, float* o, hipStream_t s);
 // canonical 4-bit experts -> canonical 2-bit experts (requant.hip)
 void launch_requant_4to2(int H, int I, int n, const uint8_t* gate4, const uint8_t* up4, const uint8_t* down4,
                          const uint16_t* s4, const uint16_t* b4, uint8_t* gate2, uint8_t* up2, uint8_t* down2,

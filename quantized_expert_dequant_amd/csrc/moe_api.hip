@@ -304,6 +304,58 @@ int moe_expert_ranges(int bits, int H, int I, int group, const void* slab, int n
     return hip_status(fn);
 }
 
+int moe_gdn_step(int n_heads, int dk, int dv, float* state, const float* q, const float* k, const float* v,
+                 const float* alpha, const float* beta, float* o_out, void* stream)
+{
+    const char* fn = "moe_gdn_step";
+    if (n_heads < 1 || n_heads > 4096) return fail(MOE_EINVAL, "%s: n_heads=%d", fn, n_heads);
+    if (dk != 64 && dk != 128 && dk != 256) return fail(MOE_EUNSUPPORTED, "%s: dk=%d (must be 64, 128 or 256)", fn, dk);
+    if (dv < 1 || dv > 4096) return fail(MOE_EINVAL, "%s: dv=%d", fn, dv);
+    CHECK_PTR4(state);
+    CHECK_PTR4(q);
+    CHECK_PTR4(k);
+    CHECK_PTR4(v);
+    CHECK_PTR4(alpha);
+    CHECK_PTR4(beta);
+    CHECK_PTR4(o_out);
+    launch_gdn_step(n_heads, dk, dv, state, q, k, v, alpha, beta, o_out, (hipStream_t)stream);
+    return hip_status(fn);
+}
+
+static int check_attn(const char* fn, int n_q, int n_kv, int d, int T)
+{
+    if (n_kv < 1 || n_q < n_kv || n_q % n_kv) return fail(MOE_EINVAL, "%s: n_q=%d must be a multiple of n_kv=%d", fn, n_q, n_kv);
+    if (n_q / n_kv > attn_max_per())
+        return fail(MOE_EUNSUPPORTED, "%s: %d query heads per KV head (at most %d)", fn, n_q / n_kv, attn_max_per());
+    if (n_kv > 65535 || n_q > 65536) return fail(MOE_EUNSUPPORTED, "%s: n_q=%d n_kv=%d", fn, n_q, n_kv);
+    if (d != 64 && d != 128 && d != 256) return fail(MOE_EUNSUPPORTED, "%s: d=%d (must be 64, 128 or 256)", fn, d);
+    if (T < 1 || T > (1 << 22)) return fail(MOE_EINVAL, "%s: T=%d", fn, T);
+    return MOE_OK;
+}
+
+size_t moe_attn_workspace_bytes(int n_q, int n_kv, int d, int T)
+{
+    if (check_attn("moe_attn_workspace_bytes", n_q, n_kv, d, T)) return 0;
+    return attn_workspace_bytes(n_q, d, T);
+}
+
+int moe_attn_decode(int n_q, int n_kv, int d, int T, const float* q, const uint16_t* K, const uint16_t* V,
+                    float* o_out, void* ws, size_t ws_bytes, void* stream)
+{
+    const char* fn = "moe_attn_decode";
+    int rc = check_attn(fn, n_q, n_kv, d, T);
+    if (rc) return rc;
+    CHECK_PTR4(q);
+    CHECK_PTR(K);
+    CHECK_PTR(V);
+    CHECK_PTR4(o_out);
+    CHECK_PTR4(ws);
+    const size_t need = attn_workspace_bytes(n_q, d, T);
+    if (ws_bytes < need) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+    launch_attn_decode(n_q, n_kv, d, T, q, K, V, (float*)ws, o_out, (hipStream_t)stream);
+    return hip_status(fn);
+}
+
 int moe_dequant_expert(int bits, int H, int I, int group, const void* record, float* W_out, void* stream)
 {
     const char* fn = "moe_dequant_expert";
