@@ -505,6 +505,78 @@ def requant_throughput(dev, n=64, reps=5):
             "bytes_4bit_per_expert": moe.record_bytes(4, H, I), "bytes_2bit_per_expert": moe.record_bytes(2, H, I)}
 
 
+ATTN_SHAPES = {
+    # GatedDeltaNet: heads, key and value dims; full attention: query heads, KV heads, head dim
+    "gdn": dict(n=64, dk=128, dv=128),
+    "attn": dict(n_q=32, n_kv=2, d=256),
+}
+
+
+def measure_attention(dev, reps=5, calls=48, contexts=(4096, 32768)):
+    """Per-call GPU time of the attention half of a decode step at the synthetic shapes
+    above: moe_gdn_step over `calls` distinct states (so each call reads its state from
+    HBM, not from the previous call's cache lines) and moe_attn_decode over distinct KV
+    caches per context length.  The calls are captured in one HIP graph; GPU events
+    around a replay, median of `reps` replays, divided by the calls.  Bytes are the
+    algorithmic ones: the state read and written, or the cache read once, plus q and o."""
+    import torch
+    import quantized_expert_dequant_amd as moe
+    torch.manual_seed(5)
+    out = {}
+
+    def timed(fn, count):
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3 / count)
+        del g
+        return _median(ts)
+
+    def entry(shape, us, nbytes):
+        gbps = nbytes / (us * 1e-6) / 1e9
+        return {"shape": shape, "us_per_call": round(us, 3), "bytes_per_call": nbytes, "gbps": round(gbps, 1),
+                "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+
+    gs = ATTN_SHAPES["gdn"]
+    n, dk, dv = gs["n"], gs["dk"], gs["dv"]
+    states = torch.randn(calls, n, dv, dk, device=dev).mul_(0.05)
+    q = torch.randn(n, dk, device=dev).div_(dk ** 0.5)
+    k = torch.nn.functional.normalize(torch.randn(n, dk, device=dev), dim=1)
+    v = torch.randn(n, dv, device=dev)
+    alpha = torch.rand(n, device=dev).mul_(0.2).add_(0.8)
+    beta = torch.rand(n, device=dev)
+    o = torch.empty(n, dv, device=dev)
+    us = timed(lambda i: moe.gdn_step(n, dk, dv, states[i], q, k, v, alpha, beta, o), calls)
+    out["gdn_step"] = entry(gs, us, 8 * n * dv * dk + 4 * (2 * n * dk + 2 * n * dv + 2 * n))
+    del states
+    a = ATTN_SHAPES["attn"]
+    n_q, n_kv, d = a["n_q"], a["n_kv"], a["d"]
+    qa = torch.randn(n_q, d, device=dev)
+    oa = torch.empty(n_q, d, device=dev)
+    for T in contexts:
+        per = calls if T <= 4096 else max(4, calls // 8)
+        K = torch.randn(per, n_kv, T, d, device=dev).to(torch.bfloat16).view(torch.int16)
+        V = torch.randn(per, n_kv, T, d, device=dev).to(torch.bfloat16).view(torch.int16)
+        wsb = moe.attn_workspace_bytes(n_q, n_kv, d, T)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        us = timed(lambda i: moe.attn_decode(n_q, n_kv, d, T, qa, K[i], V[i], oa, ws, wsb), per)
+        out["attn_decode_T%d" % T] = entry(dict(a, T=T), us, 2 * 2 * n_kv * T * d + 4 * 2 * n_q * d)
+        del K, V
+    return out
+
+
 def cpu_baseline(c, budget_s=15.0):
     """The float64 oracle as it stands on the host cores, on a bounded sample of tokens of the
     timed layer: tokens decoded on OpenMP threads (oracle_layer_decode_par, each token by the
@@ -662,6 +734,7 @@ def main():
                 e["requant_kernel"] = requant_throughput(dev)
             cfgs[name] = e
         cfgs["tiered"] = measure_tiered(dev)
+        cfgs["attention"] = measure_attention(dev)
         out["configs"] = cfgs
     if not args.cpu_seconds <= 0:
         log("timing the oracle on the host ...")

@@ -165,10 +165,12 @@ int moe_gdn_step(int n_heads, int dk, int dv, float* state, const float* q, cons
  * moe_attn_decode: one decode step of grouped-query attention over T cached
  * positions: query head h reads KV head g = h / (n_q / n_kv),
  * o_h = sum_t softmax_t(q_h . K_g[t] / sqrt(d)) V_g[t].
- *   q: fp32 [n_q][d]; K, V: bf16 bit patterns [n_kv][T][d] (16-byte aligned);
- *   o_out: fp32 [n_q][d]; ws: moe_attn_workspace_bytes bytes (per 64-position slice
- *   partial results).  d must be 64, 128 or 256 and n_q / n_kv at most 16
- *   (MOE_EUNSUPPORTED otherwise).
+ *   q: fp32 [n_q][d]; K, V: bf16 bit patterns [n_kv][T][d]; o_out: fp32 [n_q][d];
+ *   ws: moe_attn_workspace_bytes bytes (per-block partial results over the cached
+ *   positions); q, K, V and ws 16-byte aligned.  d must be 64, 128 or 256 and
+ *   n_q / n_kv at most 16 (MOE_EUNSUPPORTED otherwise).  The products run on the
+ *   matrix cores in bf16 with q and the softmax weights split into two bf16 terms
+ *   each (relative residual about 2^-17), accumulating in fp32.
  */
 size_t moe_attn_workspace_bytes(int n_q, int n_kv, int d, int T);
 int moe_attn_decode(int n_q, int n_kv, int d, int T, const float* q, const uint16_t* K, const uint16_t* V,

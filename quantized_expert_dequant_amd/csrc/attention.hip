@@ -103,126 +103,382 @@ void launch_gdn_step(int n_heads, int dk, int dv, float* S, const float* q, cons
 }
 
 // ----------------------------------------------------------------------------
-// Decode attention, split over the cached positions (64 per slice).  One wave per
-// (KV head g, slice): lane t first scores position t of the slice against every
-// query head of the group (the K row is read once for all of them), the wave
-// takes each head's slice maximum and exp-weights, then lane c accumulates
-// columns c + 64 j of sum_t p[h][t] V[t] for every head from the V rows (read once,
-// coalesced).  Each (head, slice) leaves (max, sum of weights, weighted V); the
-// combine kernel merges the slices in slice order.
+// Decode attention on the matrix cores.  For one KV head g the per query heads
+// of its group (at most 16, padded with zero rows) form the 16-wide side of the
+// MFMAs, over sub-tiles of 16 cached positions:
+//   scores  S^T [16 positions x 16 heads] = K [16 x d] . Q^T [d x 16]
+//           (v_mfma_f32_16x16x32_bf16, d / 32 steps)
+//   values  O   [16 heads x 16 columns]  += P [16 x 16 positions] . V [16 x 16]
+//           (v_mfma_f32_16x16x16_bf16, one per 16 columns)
+// The contraction index of either product only has to be labelled the same way
+// on both operands, so each operand is loaded in its natural layout:
+//   - K: lane (j, r) (j = lane % 16, r = lane / 16) reads row j of the sub-tile;
+//     its chunk c (8 elements) is chunk 4c + r of the row, so the four lanes of a
+//     row read 64 contiguous bytes per load.  q carries the same labels; it is
+//     prepared once per block (scaled by log2(e)/sqrt(d), split into bf16 hi + lo)
+//     and read from LDS.
+//   - P: the score product leaves lane (j, r) with head j at positions 4r..4r+3,
+//     which is exactly the A operand of the value product.
+//   - V: lane (j, r) reads rows 4r..4r+3; for d >= 128 its columns are
+//     128 w + 8 j + (0..7), so the 16 lanes of a row read 256 contiguous bytes per
+//     load (d = 64: columns 4 j + (0..3)).  Pairing rows in registers gives one B
+//     operand per column: value MFMA u yields one column per lane j.
+// q and the weights p are fp32, each split into bf16 hi + lo (relative residual
+// about 2^-17) and multiplied twice; K and V are exact bf16, the products exact,
+// the sums fp32.
+//
+// Work split: a block of AT_WAVES waves covers AT_WAVES * R sub-tiles of one KV
+// head (wave w takes sub-tiles w, w + AT_WAVES, ...); two waves share a SIMD.  A
+// wave issues the next sub-tile's K loads as soon as the score MFMAs have read its
+// K registers, and the V loads once the value MFMAs have read V, so its loads are
+// in flight while it computes.  It keeps, per head, a reference
+// maximum M, the weight sum L and O, all relative to M: weights are 2^(s - M), and
+// M (with L and O) moves only when a score exceeds it by more than 2^AT_SLACK, so
+// the weights stay below 2^AT_SLACK and O is rarely rescaled; the result does not
+// depend on the reference.  The waves merge in LDS and the block writes one
+// partial (M, L, O) per query head; the combine kernel merges the partials.
+// Scores are in the log2 domain throughout.
 // ----------------------------------------------------------------------------
-constexpr int AT_SLICE = 64;
+constexpr int AT_SUB = 16;      // positions per sub-tile
+constexpr int AT_WAVES = 4;     // waves per block
 constexpr int AT_MAX_PER = 16;  // query heads per KV head
+constexpr int AT_TARGET_BLOCKS = 512;
+constexpr int AT_MAX_NBLK = 1024;  // most partials per head
+constexpr float AT_SLACK = 8.f;
 
-__device__ inline float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef float fl2 __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
-template <int NC>
-__global__ __launch_bounds__(64) void k_attn_partial(int n_q, int n_kv, int T, const float* __restrict__ q,
-                                                     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                                                     float* __restrict__ part)
+__device__ inline f4v mfma_k32(u4v a, u4v b, f4v c)
 {
-    constexpr int D = 64 * NC;
-    __shared__ float qs[AT_MAX_PER][D];
-    __shared__ float ps[AT_MAX_PER][AT_SLICE];
-    const int g = blockIdx.y, sl = blockIdx.x, lane = threadIdx.x;
-    const int per = n_q / n_kv, nsl = gridDim.x;
-    const int t0 = sl * AT_SLICE;
-    for (int i = lane; i < per * D; i += 64) qs[i / D][i % D] = q[(long long)(g * per + i / D) * D + i % D];
-    __syncthreads();
-    // scores: lane = position
-    const int t = min(t0 + lane, T - 1);
-    const bool tv = t0 + lane < T;
-    const uint16_t* Kt = K + ((long long)g * T + t) * D;
-    float sc[AT_MAX_PER];
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, a), __builtin_bit_cast(bf8, b), c, 0, 0, 0);
+}
+__device__ inline f4v mfma_k16(u2v a, u2v b, f4v c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4v, a), __builtin_bit_cast(s4v, b), c, 0, 0, 0);
+}
+
+// (x0, x1) -> packed bf16 hi and lo terms: x = hi + lo + O(2^-17 |x|), each term
+// rounded to nearest even by the hardware conversion; returns (hi, lo)
+__device__ inline uint2 split_pair(float x0, float x1)
+{
+    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(fl2{x0, x1}, bf2));
+    const float r0 = x0 - __uint_as_float(hi << 16), r1 = x1 - __uint_as_float(hi & 0xFFFF0000u);
+    return make_uint2(hi, __builtin_bit_cast(uint32_t, __builtin_convertvector(fl2{r0, r1}, bf2)));
+}
+
+// op over the four 16-lane rows of a wave (lanes j, j + 16, j + 32, j + 48)
+template <typename Op>
+__device__ inline float across_rows(float v, Op op)
+{
+    float a, b;
+    swap<false>(v, a, b);
+    v = op(a, b);
+    swap<true>(v, a, b);
+    return op(a, b);
+}
+
+struct AttnPlan {
+    int R;     // sub-tiles per wave
+    int nblk;  // blocks per KV head
+};
+
+__host__ __device__ inline AttnPlan attn_plan(int n_kv, int T)
+{
+    const long long st = (T + AT_SUB - 1) / AT_SUB;
+    long long R = (long long)n_kv * st / ((long long)AT_WAVES * AT_TARGET_BLOCKS);
+    if (R < 1) R = 1;
+    long long nblk = (st + AT_WAVES * R - 1) / (AT_WAVES * R);
+    if (nblk > AT_MAX_NBLK) {
+        R = (st + AT_WAVES * AT_MAX_NBLK - 1) / (AT_WAVES * AT_MAX_NBLK);
+        nblk = (st + AT_WAVES * R - 1) / (AT_WAVES * R);
+    }
+    AttnPlan p;
+    p.R = (int)R;
+    p.nblk = (int)nblk;
+    return p;
+}
+
+// V column of value MFMA u in lane j
+template <int VC>
+__device__ inline int v_col(int u, int j)
+{
+    return VC >= 8 ? (u >> 3) * 128 + 8 * j + (u & 7) : VC * j + u;
+}
+
+template <int D>
+struct AttnTile {
+    static constexpr int KC = D / 32;  // 16-byte K chunks per lane = score MFMAs (x2 for hi, lo)
+    static constexpr int VC = D / 16;  // V columns per lane = value MFMAs (x2)
+    static constexpr int VW = VC / 2;  // dwords per V row and lane
+    u4v k[KC];                         // K row p0 + j, chunks 4c + r
+    uint32_t v[4][VW];                 // V rows p0 + 4r + e, the lane's columns
+};
+
+template <int D>
+__device__ inline void attn_load_k(AttnTile<D>& t, const uint16_t* __restrict__ Kg, int p0, int T, int j, int r)
+{
+    const u4v* kp = reinterpret_cast<const u4v*>(Kg + (long long)min(p0 + j, T - 1) * D) + r;
 #pragma unroll
-    for (int h = 0; h < AT_MAX_PER; ++h) sc[h] = 0.f;
+    for (int c = 0; c < AttnTile<D>::KC; ++c) t.k[c] = kp[4 * c];
+}
+
+template <int D>
+__device__ inline void attn_load_v(AttnTile<D>& t, const uint16_t* __restrict__ Vg, int p0, int T, int j, int r)
+{
+    constexpr int VC = AttnTile<D>::VC, VW = AttnTile<D>::VW;
 #pragma unroll
-    for (int c0 = 0; c0 < D; c0 += 8) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(Kt + c0);
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int e = 0; e < 4; ++e) {
+        const uint16_t* vp = Vg + (long long)min(p0 + 4 * r + e, T - 1) * D;
+        if constexpr (VW == 2) {
+            const uint2 w = *reinterpret_cast<const uint2*>(vp + VC * j);
+            t.v[e][0] = w.x;
+            t.v[e][1] = w.y;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float k0 = bf16_lo(w4[e]), k1 = bf16_hi(w4[e]);
-#pragma unroll
-            for (int h = 0; h < AT_MAX_PER; ++h) {
-                if (h < per) sc[h] = fmaf(k1, qs[h][c0 + 2 * e + 1], fmaf(k0, qs[h][c0 + 2 * e], sc[h]));
+            for (int w4 = 0; w4 < VW / 4; ++w4) {
+                const uint4 w = *reinterpret_cast<const uint4*>(vp + 128 * w4 + 8 * j);
+                t.v[e][4 * w4 + 0] = w.x;
+                t.v[e][4 * w4 + 1] = w.y;
+                t.v[e][4 * w4 + 2] = w.z;
+                t.v[e][4 * w4 + 3] = w.w;
             }
         }
     }
-    const float scale = rsqrtf((float)D);
-    float mh[AT_MAX_PER], lh[AT_MAX_PER];
-#pragma unroll
-    for (int h = 0; h < AT_MAX_PER; ++h) {
-        if (h >= per) continue;
-        const float s = tv ? sc[h] * scale : -INFINITY;
-        const float m = wave_max(s);
-        const float p = tv ? __expf(s - m) : 0.f;
-        lh[h] = wave_sum(p);
-        mh[h] = m;
-        ps[h][lane] = p;
+}
+
+// partials: O [n_q][nblk][D] floats, then (M, L) [n_q][nblk][2]
+template <int D>
+__global__ __launch_bounds__(64 * AT_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attn_partial(int n_q, int n_kv, int T, int R,
+                                                               const float* __restrict__ q,
+                                                               const uint16_t* __restrict__ K,
+                                                               const uint16_t* __restrict__ V,
+                                                               float* __restrict__ part_o,
+                                                               float* __restrict__ part_ml)
+{
+    constexpr int KC = AttnTile<D>::KC, VC = AttnTile<D>::VC;
+    __shared__ u4v q_s[2][KC][64];  // hi, lo operands per (chunk, lane)
+    __shared__ float ml_s[AT_WAVES][2][16];
+    __shared__ float o_s[2][4 * VC * 64];
+
+    const int g = blockIdx.y, blk = blockIdx.x, nblk = gridDim.x;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, j = lane & 15, r = lane >> 4;
+    const int per = n_q / n_kv;
+    const long long st = (T + AT_SUB - 1) / AT_SUB;
+    const uint16_t* Kg = K + (long long)g * T * D;
+    const uint16_t* Vg = V + (long long)g * T * D;
+
+    long long sub = (long long)blk * R * AT_WAVES + wave;  // the wave's first sub-tile
+    AttnTile<D> t;
+    attn_load_k<D>(t, Kg, (int)(min(sub, st - 1) * AT_SUB), T, j, r);
+    attn_load_v<D>(t, Vg, (int)(min(sub, st - 1) * AT_SUB), T, j, r);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // q operands: entry (c, l) holds head l % 16, elements 8 (4c + l / 16) + (0..7)
+    {
+        const float sc = 1.4426950408889634f * rsqrtf((float)D);
+        for (int e = threadIdx.x; e < KC * 64; e += 64 * AT_WAVES) {
+            const int c = e >> 6, l = e & 63, hj = l & 15;
+            const float z = hj < per ? sc : 0.f;
+            const float* qp = q + (long long)(g * per + min(hj, per - 1)) * D + 8 * (4 * c + (l >> 4));
+            const float4 a = *reinterpret_cast<const float4*>(qp), b = *reinterpret_cast<const float4*>(qp + 4);
+            const uint2 s0 = split_pair(a.x * z, a.y * z), s1 = split_pair(a.z * z, a.w * z);
+            const uint2 s2 = split_pair(b.x * z, b.y * z), s3 = split_pair(b.z * z, b.w * z);
+            q_s[0][c][l] = u4v{s0.x, s1.x, s2.x, s3.x};
+            q_s[1][c][l] = u4v{s0.y, s1.y, s2.y, s3.y};
+        }
     }
     __syncthreads();
-    // weighted values: lane = column
-    float acc[AT_MAX_PER][NC];
+
+    float M = -INFINITY, L = 0.f;  // head j
+    f4v O[VC];                     // heads 4r + i, columns v_col(u, j)
 #pragma unroll
-    for (int h = 0; h < AT_MAX_PER; ++h)
+    for (int u = 0; u < VC; ++u) O[u] = f4v{0.f, 0.f, 0.f, 0.f};
+
+    for (int it = 0; it < R && sub < st; ++it) {
+        const int p0 = (int)sub * AT_SUB;
+        const long long nx = sub + AT_WAVES;
+        const bool more = it + 1 < R && nx < st;
+        // scores, two accumulator chains
+        f4v a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < NC; ++j) acc[h][j] = 0.f;
-    const int nt = min(AT_SLICE, T - t0);
-    for (int i = 0; i < nt; ++i) {
-        const uint16_t* Vt = V + ((long long)g * T + t0 + i) * D;
-        float vv[NC];
-#pragma unroll
-        for (int j = 0; j < NC; ++j) vv[j] = bf16f(Vt[lane + 64 * j]);
-#pragma unroll
-        for (int h = 0; h < AT_MAX_PER; ++h) {
-            if (h >= per) continue;
-            const float p = ps[h][i];
-#pragma unroll
-            for (int j = 0; j < NC; ++j) acc[h][j] = fmaf(p, vv[j], acc[h][j]);
+        for (int c = 0; c < KC; c += 2) {
+            a0 = mfma_k32(t.k[c], q_s[0][c][lane], a0);
+            if (c + 1 < KC) a1 = mfma_k32(t.k[c + 1], q_s[0][c + 1][lane], a1);
+            a0 = mfma_k32(t.k[c], q_s[1][c][lane], a0);
+            if (c + 1 < KC) a1 = mfma_k32(t.k[c + 1], q_s[1][c + 1][lane], a1);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) attn_load_k<D>(t, Kg, (int)nx * AT_SUB, T, j, r);
+        __builtin_amdgcn_sched_barrier(0);
+        float s[4];  // position p0 + 4r + i, head j
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = (p0 + 4 * r + i < T) ? a0[i] + a1[i] : -INFINITY;
+        float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+        mx = across_rows(mx, OpMax());
+        if (__builtin_amdgcn_ballot_w64(mx > M + AT_SLACK)) {  // a head's reference moves
+            const float Mn = mx > M + AT_SLACK ? mx : M;
+            const float f = __builtin_amdgcn_exp2f(M - Mn);  // 1 where M stays, 0 from -inf
+            L *= f;
+            M = Mn;
+            if (it > 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float fi = __shfl(f, 4 * r + i);
+#pragma unroll
+                    for (int u = 0; u < VC; ++u) O[u][i] *= fi;
+                }
+            }
+        }
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - M);
+        L += across_rows((p[0] + p[1]) + (p[2] + p[3]), OpAdd());
+        const uint2 p01 = split_pair(p[0], p[1]), p23 = split_pair(p[2], p[3]);
+        const u2v phi = {p01.x, p23.x}, plo = {p01.y, p23.y};
+#pragma unroll
+        for (int u = 0; u < VC; ++u) {
+            const uint32_t x0 = t.v[0][u >> 1], x1 = t.v[1][u >> 1], x2 = t.v[2][u >> 1], x3 = t.v[3][u >> 1];
+            const u2v b = (u & 1) ? u2v{(x0 >> 16) | (x1 & 0xFFFF0000u), (x2 >> 16) | (x3 & 0xFFFF0000u)}
+                                  : u2v{(x0 & 0xFFFFu) | (x1 << 16), (x2 & 0xFFFFu) | (x3 << 16)};
+            O[u] = mfma_k16(phi, b, O[u]);
+            O[u] = mfma_k16(plo, b, O[u]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) attn_load_v<D>(t, Vg, (int)nx * AT_SUB, T, j, r);
+        __builtin_amdgcn_sched_barrier(0);
+        sub = nx;
     }
-    // part[(head, slice)] = (max, sum, acc[D])
+
+    // merge the waves: block reference and sum per head, each wave's O scaled to it
+    if (r == 0) {
+        ml_s[wave][0][j] = M;
+        ml_s[wave][1][j] = L;
+    }
+    __syncthreads();
+    float fself[4];
 #pragma unroll
-    for (int h = 0; h < AT_MAX_PER; ++h) {
-        if (h >= per) continue;
-        float* pp = part + ((long long)(g * per + h) * nsl + sl) * (D + 2);
-        if (lane == 0) {
-            pp[0] = mh[h];
-            pp[1] = lh[h];
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * r + i;
+        float Mb = ml_s[0][0][m];
 #pragma unroll
-        for (int j = 0; j < NC; ++j) pp[2 + lane + 64 * j] = acc[h][j];
+        for (int w = 1; w < AT_WAVES; ++w) Mb = fmaxf(Mb, ml_s[w][0][m]);
+        fself[i] = __builtin_amdgcn_exp2f(ml_s[wave][0][m] - Mb);  // 0 for a wave without positions
+    }
+#pragma unroll
+    for (int u = 0; u < VC; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[u][i] *= fself[i];
+    // tree sum: waves 2, 3 -> 0, 1 -> 0; slot (i, u, lane) is conflict-free
+    auto put = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < VC; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o_s[buf][(i * VC + u) * 64 + lane] = O[u][i];
+    };
+    auto add = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < VC; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[u][i] += o_s[buf][(i * VC + u) * 64 + lane];
+    };
+    if (wave >= 2) put(wave - 2);
+    __syncthreads();
+    if (wave < 2) add(wave);
+    __syncthreads();
+    if (wave == 1) put(0);
+    __syncthreads();
+    if (wave != 0) return;
+    add(0);
+    const long long hb = (long long)g * per;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = 4 * r + i;
+        if (m >= per) continue;
+        float* op = part_o + ((hb + m) * nblk + blk) * D;
+#pragma unroll
+        for (int u = 0; u < VC; u += 4)
+            *reinterpret_cast<float4*>(op + v_col<VC>(u, j)) = make_float4(O[u][i], O[u + 1][i], O[u + 2][i], O[u + 3][i]);
+    }
+    if (r == 0 && j < per) {
+        float Mb = ml_s[0][0][j], Lb = 0.f;
+#pragma unroll
+        for (int w = 1; w < AT_WAVES; ++w) Mb = fmaxf(Mb, ml_s[w][0][j]);
+#pragma unroll
+        for (int w = 0; w < AT_WAVES; ++w) Lb += ml_s[w][1][j] * __builtin_amdgcn_exp2f(ml_s[w][0][j] - Mb);
+        float* mp = part_ml + ((hb + j) * nblk + blk) * 2;
+        mp[0] = Mb;
+        mp[1] = Lb;
     }
 }
 
-template <int NC>
-__global__ __launch_bounds__(64) void k_attn_combine(int nsl, const float* __restrict__ part, float* __restrict__ o)
+// One block per (query head, 64 columns), 16 waves; wave w merges the partials
+// w, w + 16, ... for its lane's column, 8 at a time with the loads issued together,
+// and the waves meet in LDS.
+constexpr int AC_WAVES = 16;
+constexpr int AC_BATCH = 8;
+
+__global__ __launch_bounds__(64 * AC_WAVES) void k_attn_combine(int D, int nblk, const float* __restrict__ part_o,
+                                                               const float* __restrict__ part_ml,
+                                                               float* __restrict__ o)
 {
-    constexpr int D = 64 * NC;
-    const int h = blockIdx.x, lane = threadIdx.x;
-    const float* ph = part + (long long)h * nsl * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < nsl; ++s) M = fmaxf(M, ph[(long long)s * (D + 2)]);
-    float L = 0.f, acc[NC];
+    __shared__ float red[AC_WAVES][3][64];
+    const int h = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const float* ph = part_o + (long long)h * nblk * D + blockIdx.y * 64 + lane;
+    const float* mh = part_ml + (long long)h * nblk * 2;
+    float M = -INFINITY, L = 0.f, A = 0.f;
+    for (int b0 = wave; b0 < nblk; b0 += AC_WAVES * AC_BATCH) {
+        float x[AC_BATCH], m[AC_BATCH], l[AC_BATCH];
 #pragma unroll
-    for (int j = 0; j < NC; ++j) acc[j] = 0.f;
-    for (int s = 0; s < nsl; ++s) {
-        const float* p = ph + (long long)s * (D + 2);
-        const float f = __expf(p[0] - M);
-        L = fmaf(p[1], f, L);
+        for (int k = 0; k < AC_BATCH; ++k) {
+            const int b = b0 + k * AC_WAVES;
+            const bool ok = b < nblk;
+            x[k] = ok ? ph[(long long)b * D] : 0.f;
+            m[k] = ok ? mh[2 * b] : -INFINITY;
+            l[k] = ok ? mh[2 * b + 1] : 0.f;
+        }
+        float mc = m[0];
 #pragma unroll
-        for (int j = 0; j < NC; ++j) acc[j] = fmaf(p[2 + lane + 64 * j], f, acc[j]);
+        for (int k = 1; k < AC_BATCH; ++k) mc = fmaxf(mc, m[k]);
+        const float Mn = fmaxf(M, mc);  // finite: partial b0 exists
+        const float f = __builtin_amdgcn_exp2f(M - Mn);
+        A *= f;
+        L *= f;
+#pragma unroll
+        for (int k = 0; k < AC_BATCH; ++k) {
+            const float w = __builtin_amdgcn_exp2f(m[k] - Mn);
+            A = fmaf(x[k], w, A);
+            L = fmaf(l[k], w, L);
+        }
+        M = Mn;
     }
-    const float inv = 1.f / L;
+    red[wave][0][lane] = M;
+    red[wave][1][lane] = L;
+    red[wave][2][lane] = A;
+    __syncthreads();
+    if (wave != 0) return;
+    float Mb = red[0][0][lane];
 #pragma unroll
-    for (int j = 0; j < NC; ++j) o[(long long)h * D + lane + 64 * j] = acc[j] * inv;
+    for (int w = 1; w < AC_WAVES; ++w) Mb = fmaxf(Mb, red[w][0][lane]);
+    float Lb = 0.f, Ab = 0.f;
+#pragma unroll
+    for (int w = 0; w < AC_WAVES; ++w) {
+        const float f = __builtin_amdgcn_exp2f(red[w][0][lane] - Mb);  // 0 for a wave without partials
+        Lb = fmaf(red[w][1][lane], f, Lb);
+        Ab = fmaf(red[w][2][lane], f, Ab);
+    }
+    o[(long long)h * D + blockIdx.y * 64 + lane] = Ab / Lb;
 }
 
-size_t attn_workspace_bytes(int n_q, int d, int T)
+size_t attn_workspace_bytes(int n_q, int n_kv, int d, int T)
 {
-    const long long nsl = (T + AT_SLICE - 1) / AT_SLICE;
-    return (size_t)n_q * nsl * (d + 2) * 4;
+    const AttnPlan p = attn_plan(n_kv, T);
+    return (size_t)n_q * p.nblk * (d + 2) * 4;
 }
 
 int attn_max_per() { return AT_MAX_PER; }
@@ -230,22 +486,16 @@ int attn_max_per() { return AT_MAX_PER; }
 void launch_attn_decode(int n_q, int n_kv, int d, int T, const float* q, const uint16_t* K, const uint16_t* V,
                         float* part, float* o, hipStream_t s)
 {
-    const int nsl = (T + AT_SLICE - 1) / AT_SLICE;
-    const dim3 grid(nsl, n_kv);
+    const AttnPlan p = attn_plan(n_kv, T);
+    float* part_o = part;
+    float* part_ml = part + (size_t)n_q * p.nblk * d;
+    const dim3 grid(p.nblk, n_kv), blk(64 * AT_WAVES);
     switch (d) {
-    case 64:
-        hipLaunchKernelGGL(k_attn_partial<1>, grid, dim3(64), 0, s, n_q, n_kv, T, q, K, V, part);
-        hipLaunchKernelGGL(k_attn_combine<1>, dim3(n_q), dim3(64), 0, s, nsl, part, o);
-        break;
-    case 128:
-        hipLaunchKernelGGL(k_attn_partial<2>, grid, dim3(64), 0, s, n_q, n_kv, T, q, K, V, part);
-        hipLaunchKernelGGL(k_attn_combine<2>, dim3(n_q), dim3(64), 0, s, nsl, part, o);
-        break;
-    default:
-        hipLaunchKernelGGL(k_attn_partial<4>, grid, dim3(64), 0, s, n_q, n_kv, T, q, K, V, part);
-        hipLaunchKernelGGL(k_attn_combine<4>, dim3(n_q), dim3(64), 0, s, nsl, part, o);
-        break;
+    case 64: hipLaunchKernelGGL(k_attn_partial<64>, grid, blk, 0, s, n_q, n_kv, T, p.R, q, K, V, part_o, part_ml); break;
+    case 128: hipLaunchKernelGGL(k_attn_partial<128>, grid, blk, 0, s, n_q, n_kv, T, p.R, q, K, V, part_o, part_ml); break;
+    default: hipLaunchKernelGGL(k_attn_partial<256>, grid, blk, 0, s, n_q, n_kv, T, p.R, q, K, V, part_o, part_ml); break;
     }
+    hipLaunchKernelGGL(k_attn_combine, dim3(n_q, d / 64), dim3(64 * AC_WAVES), 0, s, d, p.nblk, part_o, part_ml, o);
 }
 
 }  // namespace moe

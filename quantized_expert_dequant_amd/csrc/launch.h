@@ -29,7 +29,7 @@ void launch_rmsnorm(const float* y, int B, int H, float eps, float* x, hipStream
 // the attention half of a decode step (attention.hip)
 void launch_gdn_step(int n_heads, int dk, int dv, float* S, const float* q, const float* k, const float* v,
                      const float* alpha, const float* beta, float* o, hipStream_t s);
-size_t attn_workspace_bytes(int n_q, int d, int T);
+size_t attn_workspace_bytes(int n_q, int n_kv, int d, int T);
 int attn_max_per();
 void launch_attn_decode(int n_q, int n_kv, int d, int T, const float* q, const uint16_t* K, const uint16_t* V,
                         float* part, float* o, hipStream_t s);

@@ -336,7 +336,7 @@ static int check_attn(const char* fn, int n_q, int n_kv, int d, int T)
 size_t moe_attn_workspace_bytes(int n_q, int n_kv, int d, int T)
 {
     if (check_attn("moe_attn_workspace_bytes", n_q, n_kv, d, T)) return 0;
-    return attn_workspace_bytes(n_q, d, T);
+    return attn_workspace_bytes(n_q, n_kv, d, T);
 }
 
 int moe_attn_decode(int n_q, int n_kv, int d, int T, const float* q, const uint16_t* K, const uint16_t* V,
@@ -345,12 +345,12 @@ int moe_attn_decode(int n_q, int n_kv, int d, int T, const float* q, const uint1
     const char* fn = "moe_attn_decode";
     int rc = check_attn(fn, n_q, n_kv, d, T);
     if (rc) return rc;
-    CHECK_PTR4(q);
+    CHECK_PTR(q);
     CHECK_PTR(K);
     CHECK_PTR(V);
     CHECK_PTR4(o_out);
-    CHECK_PTR4(ws);
-    const size_t need = attn_workspace_bytes(n_q, d, T);
+    CHECK_PTR(ws);
+    const size_t need = attn_workspace_bytes(n_q, n_kv, d, T);
     if (ws_bytes < need) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
     launch_attn_decode(n_q, n_kv, d, T, q, K, V, (float*)ws, o_out, (hipStream_t)stream);
     return hip_status(fn);
