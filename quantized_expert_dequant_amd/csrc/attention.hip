@@ -273,20 +273,34 @@ __global__ __launch_bounds__(64 * AT_WAVES) __attribute__((amdgpu_waves_per_eu(2
     const uint16_t* Kg = K + (long long)g * T * D;
     const uint16_t* Vg = V + (long long)g * T * D;
 
+    // q first (its wait then does not wait for the cache loads behind it)
+    constexpr int QE = (KC * 64 + 64 * AT_WAVES - 1) / (64 * AT_WAVES);  // q entries per thread
+    float4 qa[QE], qb[QE];
+#pragma unroll
+    for (int x = 0; x < QE; ++x) {
+        const int e = min((int)threadIdx.x + x * 64 * AT_WAVES, KC * 64 - 1);
+        const int c = e >> 6, l = e & 63;
+        const float* qp = q + (long long)(g * per + min(l & 15, per - 1)) * D + 8 * (4 * c + (l >> 4));
+        qa[x] = *reinterpret_cast<const float4*>(qp);
+        qb[x] = *reinterpret_cast<const float4*>(qp + 4);
+    }
     long long sub = (long long)blk * R * AT_WAVES + wave;  // the wave's first sub-tile
     AttnTile<D> t;
     attn_load_k<D>(t, Kg, (int)(min(sub, st - 1) * AT_SUB), T, j, r);
     attn_load_v<D>(t, Vg, (int)(min(sub, st - 1) * AT_SUB), T, j, r);
     __builtin_amdgcn_sched_barrier(0);
 
-    // q operands: entry (c, l) holds head l % 16, elements 8 (4c + l / 16) + (0..7)
+    // q operands: entry (c, l) holds head l % 16, elements 8 (4c + l / 16) + (0..7),
+    // scaled by log2(e)/sqrt(d) and split
     {
         const float sc = 1.4426950408889634f * rsqrtf((float)D);
-        for (int e = threadIdx.x; e < KC * 64; e += 64 * AT_WAVES) {
-            const int c = e >> 6, l = e & 63, hj = l & 15;
-            const float z = hj < per ? sc : 0.f;
-            const float* qp = q + (long long)(g * per + min(hj, per - 1)) * D + 8 * (4 * c + (l >> 4));
-            const float4 a = *reinterpret_cast<const float4*>(qp), b = *reinterpret_cast<const float4*>(qp + 4);
+#pragma unroll
+        for (int x = 0; x < QE; ++x) {
+            const int e = threadIdx.x + x * 64 * AT_WAVES;
+            if (e >= KC * 64) break;
+            const int c = e >> 6, l = e & 63;
+            const float z = (l & 15) < per ? sc : 0.f;
+            const float4 a = qa[x], b = qb[x];
             const uint2 s0 = split_pair(a.x * z, a.y * z), s1 = split_pair(a.z * z, a.w * z);
             const uint2 s2 = split_pair(b.x * z, b.y * z), s3 = split_pair(b.z * z, b.w * z);
             q_s[0][c][l] = u4v{s0.x, s1.x, s2.x, s3.x};
