@@ -50,6 +50,7 @@ WORKLOADS = {
     "layer2": dict(H=4096, I=1024, E=512, K=4, bits=2, B=1, layers=1, zipf=None, seed=1002),
     "stack": dict(H=4096, I=1024, E=512, K=4, bits=4, B=1, layers=60, zipf=None, seed=1003),
     "batched": dict(H=4096, I=1024, E=512, K=10, bits=4, B=64, layers=1, zipf=1.1, seed=1004),
+    "batched2": dict(H=4096, I=1024, E=512, K=10, bits=2, B=64, layers=1, zipf=1.1, seed=1004),
     # the layer workload's 4-bit experts requantized to 2-bit on the GPU (moe_requant_4to2)
     "requant": dict(H=4096, I=1024, E=512, K=4, bits=2, B=1, layers=1, zipf=None, seed=1001, requant=True),
 }
@@ -716,7 +717,8 @@ def main():
     if not args.no_configs:
         # every other workload at its own shape, fewer steps, same measurement
         extra = {"layer2": dict(steps=100, warmup=10), "requant": dict(steps=100, warmup=10),
-                 "batched": dict(steps=40, warmup=5), "stack": dict(steps=10, warmup=2, distinct=4),
+                 "batched": dict(steps=40, warmup=5), "batched2": dict(steps=40, warmup=5),
+                 "stack": dict(steps=10, warmup=2, distinct=4),
                  "layer": dict(steps=100, warmup=10)}
         cfgs = {}
         for name, kw in extra.items():

@@ -214,10 +214,10 @@ int moe_route_topk(const float* x, int B, const float* w_router, const float* lo
  * y[b] = sum_k w[b][k] * FFN_{idx[b][k]}(x[b]) + shared_weight * FFN_shared(x[b]).
  *   x: fp32 [B][H]; idx: int32 [B][K]; w: fp32 [B][K]; y_out: fp32 [B][H].
  * _q4 requires desc->bits == 4, _q2 requires desc->bits == 2.
- * With 4-bit codes and B > 1 the tokens are grouped by expert (as
- * moe_group_tokens) so each active expert's weights are read once per call and
- * multiplied against all of its tokens on the matrix cores (value range as
- * for moe_layer_decode); 2-bit batches run token by token.
+ * With B > 1 the tokens are grouped by expert (as moe_group_tokens) so each
+ * active expert's weights are read once per call and multiplied against all of
+ * its tokens on the matrix cores (value range as for moe_layer_decode); a 2-bit
+ * batch whose desc->expert_flags is set runs token by token instead.
  */
 int moe_expert_ffn_q4(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx,
                       const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
@@ -230,12 +230,13 @@ int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const i
  * full precision): route, then expert FFNs and combine, as above.
  *   x: fp32 [B][H]; y_out: fp32 [B][H]; idx_out: int32 [B][K] or NULL;
  *   w_out: fp32 [B][K] or NULL.
- * Value range: with 4-bit codes and B >= 2 the experts that several tokens
- * share run on the matrix cores, which take each group's scale s as fp16 and
- * (b + 8 s) through fp16 operands 2^5 b and 2^8 s: there |s| < 256 and
- * |b| < 2048 per group (larger values overflow to inf in y) unless
- * desc->expert_flags (moe_expert_ranges) marks such experts, which then run on
- * the GEMV path (at H, I <= 4096).  The other paths apply scale and bias in fp32.
+ * Value range: with B >= 2 the experts that several tokens share run on the
+ * matrix cores, which take each group's scale s as fp16 and (b + 8 s) through
+ * fp16 operands 2^5 b and 2^8 s: there |s| < 256 and |b| < 2048 per group
+ * (larger values overflow to inf in y) unless desc->expert_flags
+ * (moe_expert_ranges) marks such experts: with 4-bit codes these then run on the
+ * GEMV path (at H, I <= 4096); a 2-bit batch with flags runs token by token.
+ * The other paths apply scale and bias in fp32.
  */
 int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y_out,
                      int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream);
@@ -246,10 +247,11 @@ int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y
  * graph capture, tight serving loops, harnesses that forbid allocation).  Same
  * arguments, results and kernels as moe_layer_decode; its scratch is a
  * library-owned array of MOE_NOALLOC_SCRATCH_BYTES in each GPU's memory, held
- * until the process ends.  Calls whose workspace (moe_workspace_bytes) would
- * exceed it return MOE_EUNSUPPORTED: at H = 4096, I = 1024, E = 512, K = 4
- * single tokens and 2-bit batches up to about 240 tokens fit, 4-bit batches of
- * two or more tokens (the grouped path) do not.  Every call on one GPU shares
+ * until the process ends.  A batch whose grouped-path workspace
+ * (moe_workspace_bytes) would exceed it runs the token-by-token kernels instead
+ * (same results within the same bounds); calls whose token-by-token workspace
+ * exceeds it too return MOE_EUNSUPPORTED: at H = 4096, I = 1024, E = 512, K = 4
+ * batches up to about 240 tokens fit.  Every call on one GPU shares
  * that GPU's array: calls that overlap in time on one GPU (different streams or
  * threads without ordering) race and must not be issued.  The array's contents
  * need no initialization.  MOE_EHIP if the array's device address cannot be

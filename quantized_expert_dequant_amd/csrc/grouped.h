@@ -56,6 +56,7 @@ bool grouped_supported(const Layout& L, int B, int K);
 // blocks of the batched launches on the current device (each as many as stay resident)
 struct GroupedBlocks {
     int gateup, down, gemv_gateup, gemv_down;
+    int gateup2, down2;  // the 2-bit matrix-core launches
 };
 GroupedBlocks grouped_blocks();
 // MFMA tiles of one work-list group (128 output rows) in the gate/up and the down phase

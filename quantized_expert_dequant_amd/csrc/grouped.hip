@@ -455,6 +455,30 @@ __device__ inline h8 dequant_dword_q4(uint32_t w, h2 s2, const Masks& M)
     return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// 2-bit records: a group is one 16-byte chunk whose code k (column 64 g + k) sits
+// at bits 2k, so the 32 columns of the 4-bit chunk (half h, group g) are the
+// chunk's bytes 8h .. 8h + 7, and dword d of that 4-bit chunk (columns 8d .. 8d+7
+// of the half) is the 16-bit field d of those 8 bytes.  Copying the field's high
+// byte up by 8 bits puts codes r and r + 4 of the dword into the two 16-bit halves
+// at bit 2r, so the 2-bit masks yield the pairs in the order the 4-bit unpacking
+// gives (codes 0 and 4, 1 and 5, 2 and 6, 3 and 7); the fp16 values 1024 + 4^r q
+// become q - 2 exactly (the 2-bit codes' centre, where the 4-bit ones use 8), and
+// times s exactly.  The chunk term then carries b + 2 s.
+__device__ inline h8 dequant_field_q2(uint32_t x16, h2 s2, const Masks& M)
+{
+    const h2 k1026 = {(_Float16)1026.f, (_Float16)1026.f};
+    const h2 k4 = {(_Float16)0.25f, (_Float16)0.25f}, k258 = {(_Float16)-258.f, (_Float16)-258.f};
+    const h2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f}, k66 = {(_Float16)-66.f, (_Float16)-66.f};
+    const h2 k64 = {(_Float16)0.015625f, (_Float16)0.015625f}, k18 = {(_Float16)-18.f, (_Float16)-18.f};
+    const uint32_t y = x16 | (x16 << 8);
+    const h2 q0 = __builtin_bit_cast(h2, (y & M.m2[0]) | M.magic) - k1026;
+    const h2 q1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (y & M.m2[1]) | M.magic), k4, k258);
+    const h2 q2 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (y & M.m2[2]) | M.magic), k16, k66);
+    const h2 q3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (y & M.m2[3]) | M.magic), k64, k18);
+    const h2 p0 = q0 * s2, p1 = q1 * s2, p2 = q2 * s2, p3 = q3 * s2;
+    return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
 // The chunk term (b + 8 s) * sum: one MFMA per tile and step whose K slots of a
 // lane's chunk hold (b', b', s', s') against (X_hi, X_lo, X_hi, X_lo), with
 // b' = 2^5 b and s' = 2^5 * 8 s (exact in fp16 for |b| < 2^11 and |s| < 2^8) and
@@ -563,7 +587,7 @@ __device__ inline void store_h(const GroupedArgs& A, int ent, int row, float g, 
     hrow[((long long)dd * A.L.Gi + grp) * 8 + (r & 3) * 2 + (r >> 2)] = h;
 }
 
-template <int MODE>
+template <int MODE, int BITS>
 __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void k_grouped_mfma(GroupedArgs A)
 {
     using S = GmShape<MODE>;
@@ -583,8 +607,10 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
     const int i = lane & 15, kk = lane >> 4;
     const Masks M = load_masks();
 
+    // a lane's codes of one chunk: 16 bytes (4-bit) or the 8 bytes of its half of a 2-bit chunk
+    typedef uint32_t cw_t __attribute__((ext_vector_type(BITS == 4 ? 4 : 2)));
     struct WRegs {
-        u4 c[NM];
+        cw_t c[NM];
         uint32_t sb[NM];
     };
 
@@ -645,11 +671,15 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         };
         auto weight_load = [&](int ks, WRegs& W) {
             const int P = min(4 * ks + kk, 2 * G - 1), g = P >= G ? P - G : P;
-            const uint32_t co = (MODE == MODE_GATEUP) ? row_off + (uint32_t)P * 16u
-                                                      : (uint32_t)(L.off_d_codes + d_chunk_off(L, row, P));
-            W.c[0] = *reinterpret_cast<const u4*>(rec + co);
+            // 4-bit: chunk P; 2-bit: half P / G of chunk g
+            const uint32_t co = (BITS == 4) ? ((MODE == MODE_GATEUP) ? row_off + (uint32_t)P * 16u
+                                                                     : (uint32_t)(L.off_d_codes + d_chunk_off(L, row, P)))
+                                            : ((MODE == MODE_GATEUP) ? row_off + (uint32_t)g * 16u
+                                                                     : (uint32_t)(L.off_d_codes + d_chunk_off(L, row, g))) +
+                                                  (P >= G ? 8u : 0u);
+            W.c[0] = *reinterpret_cast<const cw_t*>(rec + co);
             if (MODE == MODE_GATEUP) {
-                W.c[NM - 1] = *reinterpret_cast<const u4*>(rec + (co + up_off));
+                W.c[NM - 1] = *reinterpret_cast<const cw_t*>(rec + (co + up_off));
                 const uint2 v = *reinterpret_cast<const uint2*>(rec + (sb_off + (uint32_t)g * 8u));
                 W.sb[0] = v.x;
                 W.sb[NM - 1] = v.y;
@@ -693,7 +723,9 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             for (int mm = 0; mm < NM; ++mm) {
                 const uint32_t sb = pad ? 0u : Wc.sb[mm];
                 const float s = bf16_lo(sb);
-                const _Float16 sh = (_Float16)s, bh = (_Float16)(bf16_hi(sb) * GM_CT), s8 = (_Float16)(s * (8.f * GM_CT));
+                // the codes' centre: 8 (4-bit) or 2 (2-bit), so q - C averages about zero
+                constexpr float C = BITS == 4 ? 8.f : 2.f;
+                const _Float16 sh = (_Float16)s, bh = (_Float16)(bf16_hi(sb) * GM_CT), s8 = (_Float16)(s * (C * GM_CT));
                 s2[mm] = h2{sh, sh};
                 cw[mm] = h8{bh, bh, s8, s8, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
             }
@@ -722,7 +754,12 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                 if (d + 1 < 4) bread(d + 1, bv[(d + 1) & 1]);
                 h8 a[NM];
 #pragma unroll
-                for (int mm = 0; mm < NM; ++mm) a[mm] = dequant_dword_q4(Wc.c[mm][d], s2[mm], M);
+                for (int mm = 0; mm < NM; ++mm) {
+                    if constexpr (BITS == 4)
+                        a[mm] = dequant_dword_q4(Wc.c[mm][d], s2[mm], M);
+                    else
+                        a[mm] = dequant_field_q2((d & 1) ? Wc.c[mm][d >> 1] >> 16 : Wc.c[mm][d >> 1] & 0xFFFFu, s2[mm], M);
+                }
 #pragma unroll
                 for (int tt = 0; tt < GM_TT; ++tt) {
                     if (tt < ntt) {
@@ -1123,7 +1160,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
 bool grouped_supported(const Layout& L, int B, int K)
 {
     // every gate/up K chunk of a tile must hold at least one step (H >= 448)
-    return L.bits == 4 && B >= 2 && B <= MOE_MAX_B && K <= MOE_MAX_K && L.H % 64 == 0 && L.I % 64 == 0 &&
+    return (L.bits == 4 || L.bits == 2) && B >= 2 && B <= MOE_MAX_B && K <= MOE_MAX_K && L.H % 64 == 0 && L.I % 64 == 0 &&
            gm_steps(L, MODE_GATEUP) >= GM_KC_GATEUP;
 }
 
@@ -1218,8 +1255,10 @@ GroupedBlocks grouped_blocks()
     std::lock_guard<std::mutex> lock(mu);
     if (slot >= 0 && filled[slot]) return cache[slot];
     GroupedBlocks n;
-    n.gateup = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_GATEUP>, GM_THREADS);
-    n.down = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_DOWN>, GM_THREADS);
+    n.gateup = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_GATEUP, 4>, GM_THREADS);
+    n.down = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_DOWN, 4>, GM_THREADS);
+    n.gateup2 = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_GATEUP, 2>, GM_THREADS);
+    n.down2 = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_DOWN, 2>, GM_THREADS);
     n.gemv_gateup = resident_blocks(dev, (const void*)k_gemv_gateup, 64 * GV_WAVES);
     n.gemv_down = resident_blocks(dev, (const void*)k_gemv_down, 64 * GV_WAVES);
     if (slot >= 0) {
@@ -1234,7 +1273,9 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
                         hipStream_t s, Timing tg, Timing td)
 {
     const GroupedBlocks nb = grouped_blocks();
-    const int nb_gu = nb.gateup, nb_dn = nb.down, nb_gvu = nb.gemv_gateup, nb_gvd = nb.gemv_down;
+    const bool q2 = L.bits == 2;
+    const int nb_gu = q2 ? nb.gateup2 : nb.gateup, nb_dn = q2 ? nb.down2 : nb.down;
+    const int nb_gvu = nb.gemv_gateup, nb_gvd = nb.gemv_down;
     const int gv_t = gemv_tokens(L);
     const bool gv = gv_t > 1;
 
@@ -1270,7 +1311,10 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     // gate/up phase, timed as a whole (MFMA groups, split-tile fixup, GEMV groups):
     // together they read every active expert's gate/up rows once
     if (tg.start) (void)hipEventRecord(tg.start, s);
-    hipLaunchKernelGGL(k_grouped_mfma<MODE_GATEUP>, dim3(nb_gu), dim3(GM_THREADS), 0, s, A);
+    if (q2)
+        hipLaunchKernelGGL((k_grouped_mfma<MODE_GATEUP, 2>), dim3(nb_gu), dim3(GM_THREADS), 0, s, A);
+    else
+        hipLaunchKernelGGL((k_grouped_mfma<MODE_GATEUP, 4>), dim3(nb_gu), dim3(GM_THREADS), 0, s, A);
     if (gv)  // the GEMV kernel runs the split-tile fixups first
         hipLaunchKernelGGL(k_gemv_gateup, dim3(nbu), dim3(64 * GV_WAVES), lds_gu, s, A, (const uint4*)xq,
                            (const float4*)xst, nb_gu);
@@ -1283,7 +1327,10 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
 
     // down phase, timed as a whole
     if (td.start) (void)hipEventRecord(td.start, s);
-    hipLaunchKernelGGL(k_grouped_mfma<MODE_DOWN>, dim3(nb_dn), dim3(GM_THREADS), 0, s, A);
+    if (q2)
+        hipLaunchKernelGGL((k_grouped_mfma<MODE_DOWN, 2>), dim3(nb_dn), dim3(GM_THREADS), 0, s, A);
+    else
+        hipLaunchKernelGGL((k_grouped_mfma<MODE_DOWN, 4>), dim3(nb_dn), dim3(GM_THREADS), 0, s, A);
     if (gv) hipLaunchKernelGGL(k_gemv_down, dim3(nbd), dim3(64 * GV_WAVES), lds_dn, s, A, (const float4*)W.hstats);
     if (td.stop) (void)hipEventRecord(td.stop, s);
     hipLaunchKernelGGL(k_combine, dim3((L.H + 255) / 256, B), dim3(256), 0, s, W.part, W.g.slot_pos, w, K, L.H,

@@ -111,7 +111,8 @@ struct Work {
     size_t bytes;
 };
 
-Work carve(void* ws, int bits, int B, int H, int I, int E, int K)
+// allow_grouped = false: the per-token path's workspace only
+Work carve(void* ws, int bits, int B, int H, int I, int E, int K, bool allow_grouped = true)
 {
     Work W;
     char* p = (char*)ws;
@@ -129,7 +130,7 @@ Work carve(void* ws, int bits, int B, int H, int I, int E, int K)
     W.xst = (float4*)take((size_t)B * Gh * 16);
     W.hq = take(S * Gi * 256);  // h in fp32
     const Layout L = make_layout(bits, H, I);
-    W.grouped = grouped_supported(L, B, K);
+    W.grouped = allow_grouped && grouped_supported(L, B, K);
     W.gw = GroupedWork{};
     if (W.grouped) {
         const size_t n = grouped_workspace_bytes(L, B, K, E);
@@ -388,6 +389,11 @@ int moe_route_topk(const float* x, int B, const float* w_router, const float* lo
     return hip_status(fn);
 }
 
+// The batched (grouped) path of a call: the shapes allow it (the workspace always has
+// room for it then) and, at 2 bits, no range flags are given: the 2-bit batches have
+// no GEMV groups to move flagged experts to, so with flags they take the per-token path.
+static bool use_grouped(const Work& W, int bits, const int32_t* flags) { return W.grouped && (bits == 4 || !flags); }
+
 static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, const float* x, int B,
                       const int32_t* idx, const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream)
 {
@@ -403,7 +409,7 @@ static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, cons
     if (ws_bytes < W.bytes) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, W.bytes);
     hipStream_t s = (hipStream_t)stream;
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
-    if (W.grouped) {
+    if (use_grouped(W, desc->bits, desc->expert_flags)) {
         launch_group(idx, B, desc->K, desc->E, gemv_tokens(L), desc->expert_flags, W.gw.g, s);
         launch_ffn_grouped(L, desc->experts, W.gw, x, w, desc->shared_weight, B, desc->K, desc->E, W.xq, W.xst, false,
                            y_out, s, g_timing[KID_GATEUP], g_timing[KID_DOWN]);
@@ -428,14 +434,15 @@ int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const i
 }
 
 // norm_eps >= 0 (per-token path only): x is the previous layer's output, renormalized
-// by the router kernel on the fly
+// by the router kernel on the fly; grouped: the call takes the batched path (use_grouped)
 static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, int B, float* y_out,
-                      int32_t* idx_out, float* w_out, const Work& W, hipStream_t s, float norm_eps = -1.f)
+                      int32_t* idx_out, float* w_out, const Work& W, bool grouped, hipStream_t s,
+                      float norm_eps = -1.f)
 {
     int32_t* idx = idx_out ? idx_out : W.idx;
     float* w = w_out ? w_out : W.w;
     const Layout L = make_layout(d->bits, d->H, d->I);
-    if (W.grouped) {
+    if (grouped) {
         const TokenPrep P{x, d->H, W.gw.xh, W.gw.xsum, W.gw.xscale, gemv_tokens(L) > 1 ? W.xq : nullptr, W.xst};
         launch_route_batched(x, B, d->w_router, d->logit_bias, d->H, d->E, d->K, d->renormalize ? 1 : 0,
                              W.gw.partial, idx, w, P, s, g_timing[KID_ROUTER]);
@@ -466,7 +473,8 @@ int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y
     CHECK_PTR(ws);
     const Work W = carve(ws, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
     if (ws_bytes < W.bytes) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, W.bytes);
-    return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, (hipStream_t)stream);
+    return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, use_grouped(W, desc->bits, desc->expert_flags),
+                      (hipStream_t)stream);
 }
 
 int moe_grouped_launch_info(const moe_layer_desc* desc, int B, int32_t* info_out)
@@ -476,13 +484,13 @@ int moe_grouped_launch_info(const moe_layer_desc* desc, int B, int32_t* info_out
     if (rc) return rc;
     if (!info_out) return fail(MOE_EINVAL, "%s: info_out is NULL", fn);
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
-    const bool grouped = grouped_supported(L, B, desc->K);
+    const bool grouped = grouped_supported(L, B, desc->K) && (desc->bits == 4 || !desc->expert_flags);
     const GroupedBlocks nb = grouped_blocks();
     info_out[0] = grouped ? 1 : 0;
-    info_out[1] = nb.gateup;
+    info_out[1] = desc->bits == 2 ? nb.gateup2 : nb.gateup;
     info_out[2] = grouped_tiles(L, 0);
     info_out[3] = grouped_gateup_chunks();
-    info_out[4] = nb.down;
+    info_out[4] = desc->bits == 2 ? nb.down2 : nb.down;
     info_out[5] = grouped_tiles(L, 1);
     info_out[6] = gemv_tokens(L);
     info_out[7] = grouped_group_tokens();
@@ -501,14 +509,21 @@ int moe_layer_decode_noalloc(const moe_layer_desc* desc, const float* x, int B, 
     CHECK_PTR(y_out);
     CHECK_OPT_PTR4(idx_out);
     CHECK_OPT_PTR4(w_out);
-    const Work need = carve(nullptr, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
+    // the batched path when its workspace fits the scratch, else the per-token kernels
+    bool allow_grouped = true;
+    Work need = carve(nullptr, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
+    if (need.bytes > (size_t)MOE_NOALLOC_SCRATCH_BYTES) {
+        allow_grouped = false;
+        need = carve(nullptr, desc->bits, B, desc->H, desc->I, desc->E, desc->K, false);
+    }
     if (need.bytes > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
         return fail(MOE_EUNSUPPORTED, "%s: B=%d needs %zu bytes of scratch, more than the %d this entry point holds "
                     "per GPU (use moe_layer_decode with a workspace)", fn, B, need.bytes, MOE_NOALLOC_SCRATCH_BYTES);
     void* ws = scratch_ptr(fn, rc);
     if (!ws) return rc;
-    const Work W = carve(ws, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
-    return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, (hipStream_t)stream);
+    const Work W = carve(ws, desc->bits, B, desc->H, desc->I, desc->E, desc->K, allow_grouped);
+    return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, use_grouped(W, desc->bits, desc->expert_flags),
+                      (hipStream_t)stream);
 }
 
 size_t moe_cache_state_bytes(int E, int slots)
@@ -600,8 +615,9 @@ int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* 
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
     hipStream_t s = (hipStream_t)stream;
     const int renorm = desc->renormalize ? 1 : 0;
+    const bool grouped = use_grouped(W, desc->bits, desc->expert_flags);
     // 1. route on the E expert ids
-    if (W.grouped) {
+    if (grouped) {
         const TokenPrep P{x, desc->H, W.gw.xh, W.gw.xsum, W.gw.xscale, gemv_tokens(L) > 1 ? W.xq : nullptr, W.xst};
         launch_route_batched(x, B, desc->w_router, desc->logit_bias, desc->H, E, K, renorm, W.gw.partial, idx, w, P,
                              s, g_timing[KID_ROUTER]);
@@ -614,7 +630,7 @@ int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* 
     launch_cache_plan(idx, B * K, E, S, cache->state, idx_slot, plan, L.record, desc->expert_flags, slot_flags, s);
     launch_cache_copy(plan, std::min(E, B * K), src, cache->slab, L.record, s);
     // 3. the expert FFNs on the cache, by slot id (the shared expert at slot S)
-    if (W.grouped) {
+    if (grouped) {
         launch_group(idx_slot, B, K, S, gemv_tokens(L), slot_flags, W.gw.g, s);
         launch_ffn_grouped(L, cache->slab, W.gw, x, w, desc->shared_weight, B, K, S, W.xq, W.xst, true, y_out, s,
                            g_timing[KID_GATEUP], g_timing[KID_DOWN]);
@@ -688,15 +704,17 @@ int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* x,
     // writes the y it reads; the grouped path renormalizes ybuf into xbuf.
     const float* xl = x;
     float norm = -1.f;
+    bool grouped = W.grouped;  // one path for the whole stack
+    for (int l = 0; l < n_layers; ++l) grouped = grouped && use_grouped(W, layers[l].bits, layers[l].expert_flags);
     for (int l = 0; l < n_layers; ++l) {
         const bool last = (l == n_layers - 1);
-        float* yl = last ? y_out : ((W.grouped || !(l & 1)) ? ybuf : xbuf);
+        float* yl = last ? y_out : ((grouped || !(l & 1)) ? ybuf : xbuf);
         int32_t* il = idx_out ? idx_out + (size_t)l * B * d0.K : nullptr;
         float* wl = w_out ? w_out + (size_t)l * B * d0.K : nullptr;
-        int rc = layer_impl(fn, &layers[l], xl, B, yl, il, wl, W, s, norm);
+        int rc = layer_impl(fn, &layers[l], xl, B, yl, il, wl, W, grouped, s, norm);
         if (rc) return rc;
         if (!last) {
-            if (W.grouped) {
+            if (grouped) {
                 launch_rmsnorm(ybuf, B, d0.H, eps, xbuf, s);
                 xl = xbuf;
             } else {

@@ -93,13 +93,18 @@ class DeviceLayer:
     expert_flags: torch.Tensor = field(init=False, default=None)
 
     def __post_init__(self):
+        flags = None
         if self.range_flags:
             # on the GPU even when the records are a store in pinned host memory
             self.expert_flags = torch.empty(self.E + 1, dtype=torch.int32, device=self.w_router.device)
             expert_ranges(self.bits, self.H, self.I, self.slab, self.E + 1, self.expert_flags)
+            # the descriptor carries the flags only when an expert is out of range: flags
+            # that are all zero change nothing on the 4-bit paths, and would keep 2-bit
+            # batches off the grouped path (one host read here, when the layer is built)
+            if bool(self.expert_flags.any()):
+                flags = self.expert_flags
         self.desc = make_desc(self.H, self.I, self.E, self.K, self.bits, self.slab, self.w_router,
-                              self.logit_bias, self.shared_weight, self.renormalize,
-                              expert_flags=self.expert_flags)
+                              self.logit_bias, self.shared_weight, self.renormalize, expert_flags=flags)
 
     def record(self, e):
         rb = record_bytes(self.bits, self.H, self.I)

@@ -64,11 +64,13 @@ def _same(got, ref):
         assert rel_err(y[b], y_ref[b]) <= TOL, "token %d" % b
 
 
-@pytest.mark.parametrize("first,second", [((2, 4), (2, 1)), ((1, 1), (0, 1))])
+@pytest.mark.parametrize("first,second", [((2, 4), (2, 1)), ((1, 1), (0, 1)), ((1, 8), (1, 2))])
 def test_noalloc_matches_layer_decode_twice(first, second):
     """Two calls in a row, the second smaller than the first: workload 2 (2-bit) with 4
-    tokens then 1, and workload 1 (the full 4-bit layer) then workload 0 (the tiny layer).
-    The second call must not see the first's leftovers in the shared scratch."""
+    tokens then 1, workload 1 (the full 4-bit layer) then workload 0 (the tiny layer), and
+    workload 1 with 8 tokens then 2 (batches whose grouped workspace exceeds the scratch,
+    so they run token by token here and grouped with a workspace).  The second call must
+    not see the first's leftovers in the shared scratch."""
     layers = {}
     calls = []
     for t, (n, B) in enumerate((first, second)):
@@ -88,12 +90,13 @@ def test_noalloc_matches_layer_decode_twice(first, second):
 
 
 def test_noalloc_rejects_a_workspace_that_does_not_fit():
-    """A 4-bit batch takes the grouped path, whose workspace exceeds the static scratch:
-    the call returns MOE_EUNSUPPORTED, launches nothing and leaves the outputs alone."""
+    """A batch of 256 tokens with K = 10 exceeds the static scratch on both paths (the
+    token-by-token one holds h of 11 experts per token): the call returns
+    MOE_EUNSUPPORTED, launches nothing and leaves the outputs alone."""
     cfg, seed = dict(WORKLOADS[0]), seed_of(0)
     cfg["H"], cfg["I"], cfg["E"], cfg["K"] = 4096, 1024, 512, 10
     L = build_layer(dict(cfg, bits=4), seed)
-    B = 64
+    B = 256
     assert moe.workspace_bytes(L.desc, B) > moe.MOE_NOALLOC_SCRATCH_BYTES
     x = torch.from_numpy(synth.tokens(seed, 502, B, L.H)).to(DEV)
     y, idx, w = _outputs(L, B)
