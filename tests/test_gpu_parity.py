@@ -228,8 +228,8 @@ def test_layer_decode_full_size(layers, n, step):
 
 
 def test_layer_decode_full_size_2bit_several_tokens(layers):
-    """Four tokens through the full 2-bit layer in one call: 2-bit batches run token by
-    token through the fused single-token kernels, each token's routing its own."""
+    """Four tokens through the full 2-bit layer in one call (the grouped path: every active
+    expert read once, its tokens on the matrix cores), each token's routing its own."""
     n = 2
     L = layers(n)
     x = synth.tokens(seed_of(n), 30, 4, L.H)
