@@ -569,6 +569,22 @@ int grouped_gateup_chunks() { return GM_KC_GATEUP; }
 int grouped_group_tokens() { return GM_GROUP; }
 // first unit of block b when T units are cut into nb ranges (T * nb < 2^32)
 __device__ inline int gm_lo(int b, int T, int nb) { return (int)(((uint32_t)b * (uint32_t)T) / (uint32_t)nb); }
+// Logical index of block b of an nb-block launch.  The dispatcher deals blocks to
+// the 8 XCDs in turn (block b to XCD b % 8); this gives each XCD a contiguous run of
+// logical indices, so the consecutive units of one group (its tiles and K chunks,
+// which all read the group's token operands) mostly run under one XCD's L2 instead
+// of pulling the operands into all eight.  A bijection on [0, nb): XCD x holds
+// blocks x, x + 8, ... and takes logical indices from the sum of the counts below x.
+constexpr int GM_XCDS = 8, GM_RUN = 4;
+__device__ inline int gm_logical(int b, int nb)
+{
+    // runs of GM_RUN logical indices per XCD, dealt in turn; a partial last round keeps b
+    const int round = GM_XCDS * GM_RUN, full = nb - nb % round;
+    if (b >= full) return b;
+    const int base = b - b % round, j = b % round;  // j = position within the round: XCD j % 8, slot j / 8
+    return base + (j % GM_XCDS) * GM_RUN + j / GM_XCDS;
+}
+
 // the block whose range holds unit x
 __device__ inline int gm_blk(int x, int T, int nb)
 {
@@ -599,7 +615,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
     const int NR = (MODE == MODE_GATEUP) ? L.I : L.H;
     const int tiles = gm_tiles(L, MODE);
     const int nsteps = gm_steps(L, MODE);
-    const int nb = gridDim.x, blk = blockIdx.x;
+    const int nb = gridDim.x, blk = gm_logical(blockIdx.x, nb);
     const int KC = (MODE == MODE_GATEUP) ? gm_kc(A.grp_u[0] * tiles, nb) : 1;
     const int T = A.grp_u[0] * tiles * KC;
     const int lo = gm_lo(blk, T, nb), hi = gm_lo(blk + 1, T, nb);
