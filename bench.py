@@ -640,6 +640,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="time the named workload only")
     ap.add_argument("--lead-ms", type=float, default=30.0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--attention", action="store_true",
+                    help="only time the attention half (GatedDeltaNet step, decode attention) and print its JSON")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (PMC counter calibration) and exit")
     args = ap.parse_args()
@@ -665,6 +667,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    if args.attention:
+        print(json.dumps({"attention": measure_attention(dev)}), flush=True)
         return
 
     c = dict(WORKLOADS[args.workload])
@@ -701,7 +707,8 @@ def main():
                    **({"distinct_layers": r["distinct_layers"]} if stack else {})},
         "roofline": {"bound": "hbm", "achieved": r["gateup_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(r["gateup_gbps"] / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                     "kernel": ("gate/up phase: k_grouped_mfma<0> + k_gemv_gateup" if B > 1 else "k_gateup_fast"),
+                     "kernel": (("gate/up phase: k_grouped_mfma<0, 4> + k_gemv_gateup" if c["bits"] == 4 else
+                                 "gate/up phase: k_grouped_mfma<0, 2> + k_fixup") if B > 1 else "k_gateup_fast"),
                      "bytes_per_launch": r["gateup_bytes_per_launch"], "avg_us": gu_us,
                      "step_frac": r["step_frac"]},
         "expert_weight_gbps": r["expert_weight_gbps"],

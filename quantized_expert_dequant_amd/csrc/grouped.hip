@@ -492,8 +492,9 @@ __device__ inline h8 dequant_field_q2(uint32_t x16, h2 s2, const Masks& M)
 // Grouped dequant-GEMM.  A block of 8 waves owns a tile of 128 rows of one
 // group's expert (16 rows per wave) and multiplies it by the group's tokens
 // (at most 32: two 16-token MFMA tiles).  K advances 128 columns (4 chunks of
-// 16 bytes) per step: lane (i, kk) of a wave holds chunk 4*step + kk of its
-// row i, turns it into the exact fp16 operand s*(q - 8), and MFMA d (16 x 16 x
+// 32 columns) per step: lane (i, kk) of a wave holds chunk gm_chunk(step, kk) of
+// its row i (4-bit: 16 code bytes; 2-bit: the 8 bytes of a half group), turns it
+// into the exact fp16 operand s*(q - 8) (2-bit: s*(q - 2)), and MFMA d (16 x 16 x
 // 32) takes dword d of the four lanes' chunks against the token operands of the
 // same 32 columns, staged in LDS as [tt][kk][token][d]; one more MFMA per step
 // adds (b + 8 s) times each chunk's token-operand sum, staged beside them.  Both
@@ -603,6 +604,25 @@ __device__ inline void store_h(const GroupedArgs& A, int ent, int row, float g, 
     hrow[((long long)dd * A.L.Gi + grp) * 8 + (r & 3) * 2 + (r >> 2)] = h;
 }
 
+// The chunk (4-bit chunk order P = h G + g: columns 64 g + 32 h .. + 31) that K slot k
+// of step ks multiplies; past the row end, the last chunk with *pad set (zero weights).
+// 4-bit: chunks 4 ks .. 4 ks + 3, 64 contiguous code bytes of a row.  2-bit: both halves
+// of groups 2 ks and 2 ks + 1, 32 contiguous code bytes, so a row's 2-bit codes are read
+// in order and each 128-byte line in consecutive steps.  The contraction does not depend
+// on the order; the token operand of slot k is staged from the same chunk.
+template <int BITS>
+__device__ inline int gm_chunk(int ks, int k, int G, bool* pad)
+{
+    if (BITS == 4) {
+        const int P = 4 * ks + k;
+        *pad = P >= 2 * G;
+        return min(P, 2 * G - 1);
+    }
+    const int g = 2 * ks + (k >> 1);
+    *pad = g >= G;
+    return (k & 1) * G + min(g, G - 1);
+}
+
 template <int MODE, int BITS>
 __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4))) void k_grouped_mfma(GroupedArgs A)
 {
@@ -648,7 +668,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         const char* tok_base = (MODE == MODE_GATEUP) ? (const char*)A.xh : (const char*)A.hb16;
 
         // Stage element t = threadIdx.x = ((tt*16 + j)*4 + k2)*4 + d: dword d of chunk
-        // 4 * step + k2 of the tile's token j (gate/up: x of the entry's token, down: h
+        // gm_chunk(step, k2) of the tile's token j (gate/up: x of the entry's token, down: h
         // of the entry), so 16 consecutive lanes read a step's 256 contiguous bytes of
         // one operand row.  It lands in LDS row (tt*4 + k2)*16 + j, whose last slot takes
         // the chunk sum for the chunk-term MFMA: gate/up loads the one the token-operand
@@ -668,7 +688,9 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             uint32_t cs;  // gate/up: the row's chunk sum
         };
         auto stage_load = [&](int ks, Stage& S) {
-            const int P = min(4 * ks + st_k2, 2 * G - 1);
+            bool stpad;  // a padded slot stages a valid chunk; its weights are zero
+            const int P = gm_chunk<BITS>(ks, st_k2, G, &stpad);
+            (void)stpad;
             S.v = *reinterpret_cast<const u4*>(tok_base + (uint32_t)(st_src + P * 4) * 16u);
             if (MODE == MODE_GATEUP) S.cs = A.xsum[st_sum + P];
         };
@@ -686,7 +708,9 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             if (st_d == 0) bs[buf][st_row + 4] = u4{cs, 0u, 0u, 0u};
         };
         auto weight_load = [&](int ks, WRegs& W) {
-            const int P = min(4 * ks + kk, 2 * G - 1), g = P >= G ? P - G : P;
+            bool wpad;  // the step applies the zero weights of a padded slot
+            const int P = gm_chunk<BITS>(ks, kk, G, &wpad), g = P >= G ? P - G : P;
+            (void)wpad;
             // 4-bit: chunk P; 2-bit: half P / G of chunk g
             const uint32_t co = (BITS == 4) ? ((MODE == MODE_GATEUP) ? row_off + (uint32_t)P * 16u
                                                                      : (uint32_t)(L.off_d_codes + d_chunk_off(L, row, P)))
@@ -732,7 +756,8 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             weight_load(min(ks + RING - 1, k_end - 1), Wp);
             __builtin_amdgcn_sched_barrier(0);
             const u4* buf = bs[(ks - k_begin) & 1];
-            const bool pad = 4 * ks + kk >= 2 * G;  // chunk past the row end: zero weights
+            bool pad;  // chunk past the row end: zero weights
+            (void)gm_chunk<BITS>(ks, kk, G, &pad);
             h2 s2[NM];
             h8 cw[NM];  // the chunk term's weight operand
 #pragma unroll
