@@ -154,3 +154,63 @@ def test_shape_errors():
     with pytest.raises(moe.MoeError) as e:
         moe.gdn_step(4, 96, 64, x, x, x, x, x, x, x)
     assert e.value.code == moe.MOE_EUNSUPPORTED
+
+
+def _capture(fn):
+    """Capture fn() on a side stream after one eager warm-up call there."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_graph_replays_match_eager_calls():
+    """The bench times both entry points as graph replays.  One captured call of each is
+    replayed four times, with fresh inputs copied into its static buffers, its outputs
+    poisoned and an eager call of the same entry point on other buffers in between:
+    every replay equals that eager call bit for bit (fixed summation orders), and the
+    attention output the oracle within its bar."""
+    n, dk, dv = 8, 128, 64
+    n_q, n_kv, d, T = 8, 2, 128, 300
+    S0 = torch.empty((n, dv, dk), device=DEV)
+    gq, gk, gv, ga, gb = (torch.empty(sh, device=DEV) for sh in ((n, dk), (n, dk), (n, dv), (n,), (n,)))
+    go = torch.empty((n, dv), device=DEV)
+    aq = torch.empty((n_q, d), device=DEV)
+    aK = torch.empty((n_kv, T, d), dtype=torch.int16, device=DEV)
+    aV = torch.empty_like(aK)
+    ao = torch.empty((n_q, d), device=DEV)
+    wsb = moe.attn_workspace_bytes(n_q, n_kv, d, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    g_gdn = _capture(lambda: moe.gdn_step(n, dk, dv, S0, gq, gk, gv, ga, gb, go))
+    g_att = _capture(lambda: moe.attn_decode(n_q, n_kv, d, T, aq, aK, aV, ao, ws, wsb))
+    ws2 = torch.empty_like(ws)
+    for rep in range(4):
+        S, q, k, v, a, b = _gdn_inputs(500 + rep, n, dk, dv)
+        for dst, src in zip((S0, gq, gk, gv, ga, gb), (S, q, k, v, a, b)):
+            dst.copy_(torch.from_numpy(src))
+        qa, K, V = _attn_inputs(600 + rep, n_q, n_kv, d, T)
+        aq.copy_(torch.from_numpy(qa))
+        aK.copy_(torch.from_numpy(K.view(np.int16)))
+        aV.copy_(torch.from_numpy(V.view(np.int16)))
+        # the eager calls first, on their own buffers
+        S_e = S0.clone()
+        o_e = torch.empty_like(go)
+        moe.gdn_step(n, dk, dv, S_e, gq, gk, gv, ga, gb, o_e)
+        ao_e = torch.empty_like(ao)
+        moe.attn_decode(n_q, n_kv, d, T, aq, aK, aV, ao_e, ws2, wsb)
+        go.fill_(float("nan"))
+        ao.fill_(float("nan"))
+        g_gdn.replay()
+        g_att.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(S0, S_e) and torch.equal(go, o_e), "gated delta rule, replay %d" % rep
+        assert torch.equal(ao, ao_e), "attention, replay %d" % rep
+        assert _head_err(ao.cpu().numpy(), oracle.attn_decode(qa, K, V)) <= ATTN_TOL
+    del g_gdn, g_att
