@@ -142,7 +142,7 @@ void launch_gdn_step(int n_heads, int dk, int dv, float* S, const float* q, cons
 constexpr int AT_SUB = 16;      // positions per sub-tile
 constexpr int AT_WAVES = 4;     // waves per block
 constexpr int AT_MAX_PER = 16;  // query heads per KV head
-constexpr int AT_TARGET_BLOCKS = 512;
+constexpr int AT_TARGET_BLOCKS = 256;
 constexpr int AT_MAX_NBLK = 1024;  // most partials per head
 constexpr float AT_SLACK = 8.f;
 
