@@ -113,7 +113,8 @@ def _attn_gpu(q, K, V):
 
 @pytest.mark.parametrize("n_q,n_kv,d,T", [
     (32, 2, 256, 4096),   # 16 query heads per KV head, a 4096-position cache
-    (32, 2, 256, 32768),  # two sub-tiles per wave (the running reference carries over)
+    (32, 2, 256, 32768),  # four sub-tiles per wave (the running reference carries over)
+    (8, 2, 128, 16384),   # two sub-tiles per wave
     (16, 8, 128, 4096),   # 8 KV heads, 2 query heads each
     (12, 3, 128, 1000),   # ragged last slice
     (8, 8, 64, 1),        # one position: o = V[0]
