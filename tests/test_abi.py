@@ -109,6 +109,29 @@ def test_other_entry_points_validate():
     assert L.moe_stack_decode(None, 0, 16, 1, 1e-6, 16, None, None, 16, 1 << 30, None) == moe.MOE_EINVAL
 
 
+def test_attention_entry_points_validate():
+    """The attention entry points reject shapes and buffers before touching the GPU."""
+    L = moe.lib()
+    A = 1 << 24  # a 16-byte aligned stand-in address (never dereferenced on these paths)
+    # moe_gdn_step(n_heads, dk, dv, state, q, k, v, alpha, beta, o, stream)
+    assert L.moe_gdn_step(4, 96, 64, A, A, A, A, A, A, A, None) == moe.MOE_EUNSUPPORTED   # dk not 64/128/256
+    assert L.moe_gdn_step(0, 128, 64, A, A, A, A, A, A, A, None) == moe.MOE_EINVAL
+    assert L.moe_gdn_step(4, 128, 0, A, A, A, A, A, A, A, None) == moe.MOE_EINVAL
+    assert L.moe_gdn_step(4, 128, 64, None, A, A, A, A, A, A, None) == moe.MOE_EINVAL
+    assert L.moe_gdn_step(4, 128, 64, A, A, A + 2, A, A, A, A, None) == moe.MOE_EINVAL  # misaligned k
+    # moe_attn_decode(n_q, n_kv, d, T, q, K, V, o, ws, ws_bytes, stream)
+    assert L.moe_attn_workspace_bytes(8, 3, 128, 16) == 0                              # n_q % n_kv
+    assert L.moe_attn_workspace_bytes(8, 2, 128, 4096) > 0
+    need = L.moe_attn_workspace_bytes(32, 2, 256, 4096)
+    assert L.moe_attn_decode(8, 3, 128, 16, A, A, A, A, A, need, None) == moe.MOE_EINVAL
+    assert L.moe_attn_decode(8, 2, 96, 16, A, A, A, A, A, need, None) == moe.MOE_EUNSUPPORTED
+    assert L.moe_attn_decode(34, 2, 128, 16, A, A, A, A, A, need, None) == moe.MOE_EUNSUPPORTED  # 17 per KV head
+    assert L.moe_attn_decode(8, 2, 128, 0, A, A, A, A, A, need, None) == moe.MOE_EINVAL
+    assert L.moe_attn_decode(32, 2, 256, 4096, A, A, A, A, A, need - 1, None) == moe.MOE_EINVAL
+    assert L.moe_attn_decode(32, 2, 256, 4096, A, A + 8, A, A, A, need, None) == moe.MOE_EINVAL  # K not 16-byte aligned
+    assert L.moe_attn_decode(32, 2, 256, 4096, A, A, A, None, A, need, None) == moe.MOE_EINVAL
+
+
 def test_product_path_has_no_oracle_dependency():
     """The package never imports or links the oracle (test infrastructure only)."""
     root = os.path.dirname(moe.__file__)
