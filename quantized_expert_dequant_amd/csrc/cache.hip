@@ -27,6 +27,7 @@
 #include <stdint.h>
 
 #include "cache.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -76,30 +77,53 @@ void launch_cache_reset(void* state, int E, int slots, hipStream_t s)
     hipLaunchKernelGGL(k_cache_reset, dim3(blocks < 1 ? 1 : blocks), dim3(256), 0, s, state, E, slots);
 }
 
-// One block: the call's plan.  idx [n] (n = B*K, ids outside [0, E) are passed
-// through as -1); writes idx_slot [n], the copy list (expert, slot) [n] and its
-// length at plan[0].  Needs E <= MOE_MAX_E and as many free slots as misses (the
-// caller guarantees slots >= min(E, n)).
+// One block: the call's plan.  The selection idx [n] (n = B*K, ids outside [0, E)
+// are passed through as -1) is given, or, with logits (B <= CP_ROUTE_MAX_B tokens),
+// selected here first: wave b takes token b's top-K and softmax weights as the
+// route-only kernel does, writes them to idx and w, and the plan reads them from
+// LDS, which saves that launch.  Writes idx_slot [n], the copy list (expert, slot)
+// [n] and its length at plan[0].  Needs E <= MOE_MAX_E and as many free slots as
+// misses (the caller guarantees slots >= min(E, n)).
 constexpr int CP_THREADS = 1024;
+static_assert(CP_THREADS >= MOE_MAX_E, "one thread per expert in the miss scan");
+static_assert(CP_ROUTE_MAX_B <= CP_THREADS / 64, "one wave per token selected in the plan");
 
-__global__ __launch_bounds__(CP_THREADS) void k_cache_plan(const int32_t* __restrict__ idx, int n, int E, int slots,
+__global__ __launch_bounds__(CP_THREADS) void k_cache_plan(int32_t* __restrict__ idx, int n, int E, int slots,
                                                           void* state, int32_t* __restrict__ idx_slot,
                                                           int32_t* __restrict__ plan, unsigned long long record,
                                                           const int32_t* __restrict__ flags,
-                                                          int32_t* __restrict__ slot_flags)
+                                                          int32_t* __restrict__ slot_flags,
+                                                          const double* __restrict__ logits, int K, int renorm,
+                                                          float* __restrict__ w)
 {
     __shared__ uint32_t sel[MOE_MAX_E / 32];
     __shared__ int miss[MOE_MAX_E];
     __shared__ int n_miss, n_hit;
+    __shared__ int wcount[CP_THREADS / 64];
+    __shared__ int sidx[CP_ROUTE_MAX_B * MOE_MAX_K];
     __shared__ unsigned long long red_key[CP_THREADS / 64];
     const CacheView v = cache_view(state, E, slots);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t clock = *v.clock;
+    const bool route = logits != nullptr;
+    if (route && wave < n / K) {  // token `wave`'s selection (wave-uniform)
+        int id;
+        float wt;
+        double lv[16];
+        topk_load<16>(logits + (long long)wave * E, E, lane, lv);
+        topk_select<32, 16>(lv, E, K, renorm, lane, id, wt);
+        if (lane < K) {
+            idx[wave * K + lane] = id;
+            w[wave * K + lane] = wt;
+            sidx[wave * K + lane] = id;
+        }
+    }
     for (int i = tid; i < MOE_MAX_E / 32; i += CP_THREADS) sel[i] = 0u;
     if (tid == 0) n_hit = 0;
     __syncthreads();
+    auto idx_at = [&](int i) { return route ? sidx[i] : idx[i]; };
     for (int i = tid; i < n; i += CP_THREADS) {
-        const int e = idx[i];
+        const int e = idx_at(i);
         if (e >= 0 && e < E) atomicOr(&sel[e >> 5], 1u << (e & 31));
     }
     __syncthreads();
@@ -115,12 +139,20 @@ __global__ __launch_bounds__(CP_THREADS) void k_cache_plan(const int32_t* __rest
     }
     if (hits) atomicAdd(&n_hit, hits);
     __syncthreads();
-    // the misses in ascending expert id
-    if (tid == 0) {
-        int m = 0;
-        for (int e = 0; e < E; ++e)
-            if (((sel[e >> 5] >> (e & 31)) & 1u) && v.slot_of[e] < 0) miss[m++] = e;
-        n_miss = m;
+    // the misses in ascending expert id: thread e tests expert e, each wave counts its
+    // misses with a ballot, and a miss's place is the misses of the lower waves and lanes
+    const bool is_miss = tid < E && ((sel[tid >> 5] >> (tid & 31)) & 1u) && v.slot_of[tid] < 0;
+    const unsigned long long bal = __ballot(is_miss);
+    if (lane == 0) wcount[wave] = __popcll(bal);
+    __syncthreads();
+    {
+        int base = 0, total = 0;
+        for (int q = 0; q < CP_THREADS / 64; ++q) {
+            base += q < wave ? wcount[q] : 0;
+            total += wcount[q];
+        }
+        if (is_miss) miss[base + __popcll(bal & ((1ull << lane) - 1ull))] = tid;
+        if (tid == 0) n_miss = total;
     }
     __syncthreads();
     const int nm = n_miss;
@@ -161,7 +193,7 @@ __global__ __launch_bounds__(CP_THREADS) void k_cache_plan(const int32_t* __rest
         __syncthreads();
     }
     for (int i = tid; i < n; i += CP_THREADS) {
-        const int e = idx[i];
+        const int e = idx_at(i);
         idx_slot[i] = (e >= 0 && e < E) ? v.slot_of[e] : -1;
     }
     if (flags) {  // the range flags by slot, the shared expert's last
@@ -198,11 +230,12 @@ __global__ __launch_bounds__(256) void k_cache_copy(const int32_t* __restrict__ 
     for (long long o = begin / 16 + threadIdx.x; o < end / 16; o += 256) to[o] = from[o];
 }
 
-void launch_cache_plan(const int32_t* idx, int n, int E, int slots, void* state, int32_t* idx_slot, int32_t* plan,
-                       long long record, const int32_t* flags, int32_t* slot_flags, hipStream_t s)
+void launch_cache_plan(int32_t* idx, int n, int E, int slots, void* state, int32_t* idx_slot, int32_t* plan,
+                       long long record, const int32_t* flags, int32_t* slot_flags, const double* logits, int K,
+                       int renorm, float* w, hipStream_t s)
 {
     hipLaunchKernelGGL(k_cache_plan, dim3(1), dim3(CP_THREADS), 0, s, idx, n, E, slots, state, idx_slot, plan,
-                       (unsigned long long)record, flags, slot_flags);
+                       (unsigned long long)record, flags, slot_flags, logits, K, renorm, w);
 }
 
 void launch_cache_copy(const int32_t* plan, int max_copies, const void* src, void* slab, long long record,

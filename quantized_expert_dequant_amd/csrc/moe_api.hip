@@ -624,10 +624,13 @@ int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* 
     } else {
         launch_router(desc->bits, x, B, desc->w_router, desc->logit_bias, desc->H, E, W.logits, W.xq, W.xst, s,
                       g_timing[KID_ROUTER]);
-        launch_topk(W.logits, B, E, K, renorm, idx, w, s);
+        if (B > CP_ROUTE_MAX_B) launch_topk(W.logits, B, E, K, renorm, idx, w, s);
     }
-    // 2. map the selection onto slots and bring in the missing records
-    launch_cache_plan(idx, B * K, E, S, cache->state, idx_slot, plan, L.record, desc->expert_flags, slot_flags, s);
+    // 2. map the selection onto slots (small per-token batches select there too) and
+    //    bring in the missing records
+    const bool plan_routes = !grouped && B <= CP_ROUTE_MAX_B;
+    launch_cache_plan(idx, B * K, E, S, cache->state, idx_slot, plan, L.record, desc->expert_flags, slot_flags,
+                      plan_routes ? W.logits : nullptr, K, renorm, w, s);
     launch_cache_copy(plan, std::min(E, B * K), src, cache->slab, L.record, s);
     // 3. the expert FFNs on the cache, by slot id (the shared expert at slot S)
     if (grouped) {
