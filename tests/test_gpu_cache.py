@@ -11,11 +11,12 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 import quantized_expert_dequant_amd as moe
-from quantized_expert_dequant_amd.slab import DeviceLayer, host_store, workspace
+from quantized_expert_dequant_amd.slab import DeviceLayer, host_store, upload_experts, workspace
 
-from helpers import TOL, WORKLOADS, build_layer, oracle_layer, rel_err, seed_of
+from helpers import TOL, W_RTOL, WORKLOADS, build_layer, oracle_layer, rel_err, seed_of
 
 pytestmark = pytest.mark.gpu
 
@@ -75,12 +76,16 @@ def _state(state, E, slots):
 
 
 class Cached:
-    def __init__(self, n, slots, store=None):
+    def __init__(self, n, slots, store=None, bits=None, source=None):
         cfg, seed = dict(WORKLOADS[n]), seed_of(n)
+        if bits is not None:
+            cfg["bits"] = bits
         self.cfg, self.seed = cfg, seed
         H, I, E, K, bits = cfg["H"], cfg["I"], cfg["E"], cfg["K"], cfg["bits"]
+        if source is None:
+            source = lambda f, m: synth.experts(seed, 0, f, m, bits, H, I)
         if store is None:
-            store = host_store(lambda f, m: synth.experts(seed, 0, f, m, bits, H, I), E + 1, bits, H, I, device=DEV)
+            store = host_store(source, E + 1, bits, H, I, device=DEV)
         self.store = store
         wr = torch.from_numpy(synth.router(seed, 0, E, H)).to(DEV)
         bias = torch.from_numpy(synth.zipf_bias(E, cfg["zipf"])).to(DEV) if cfg.get("zipf") else None
@@ -143,6 +148,71 @@ def test_cache_policy_and_outputs_tiny(B, slots):
     np.testing.assert_array_equal(idx, idx_ref)
     for b in range(B):
         assert rel_err(y[b], y_ref[b]) <= TOL
+
+
+def _bf16_scaled(bits16, k):
+    """bf16 bit patterns times 2^k (exponent raised; zeros and values that would overflow kept)."""
+    b = bits16.astype(np.int32)
+    e = (b >> 7) & 0xFF
+    ok = (e > 0) & (e + k < 255)
+    return np.where(ok, (b & ~(0xFF << 7)) | ((e + k) << 7), b).astype(np.uint16)
+
+
+@pytest.mark.parametrize("B,slots", [(3, 12), (5, 16), (16, 16), (17, 16)])
+def test_cache_per_token_routing_batches(B, slots):
+    """A 2-bit tiny layer whose expert 4 has its scales x 2^14 keeps the range flags, so a
+    batch runs the token-by-token kernels: up to 16 tokens the plan kernel selects each
+    token's top-K from the router logits itself, past 16 the top-K kernel does it first.
+    20 calls of B tokens: the routing, the weights and the outputs equal those of the
+    resident decode of the same records bit for bit, and the cache state the model's."""
+    cfg, seed = dict(WORKLOADS[0], bits=2), seed_of(0)  # the seed Cached(0, ...) routes with
+    H, I, E, K = cfg["H"], cfg["I"], cfg["E"], cfg["K"]
+    ex = synth.experts(seed, 0, 0, E + 1, 2, H, I)
+    ex.scales[4] = _bf16_scaled(ex.scales[4], 14)
+
+    def src(first, n):
+        return synth.Canonical(2, H, I, 64, ex.gate[first:first + n], ex.up[first:first + n],
+                               ex.down[first:first + n], ex.scales[first:first + n], ex.biases[first:first + n])
+
+    c = Cached(0, slots, bits=2, source=src)
+    assert c.L.desc.expert_flags is not None and int(c.L.expert_flags[4]) == 1
+    assert c.seed == seed
+    wr = torch.from_numpy(synth.router(seed, 0, E, H)).to(DEV)
+    resident = DeviceLayer(H, I, E, K, 2, upload_experts(src, E + 1, 2, H, I, device=DEV), wr)
+    assert moe.grouped_launch_info(resident.desc, B)["grouped"] == 0
+    model = CacheModel(E, slots)
+    routed_to_4 = 0
+    for t in range(20):
+        x = torch.from_numpy(synth.tokens(seed, 700 + t, B, H)).to(DEV)
+        y, idx, w = c.decode(x)
+        yr, idxr, wres = _resident(resident, x)
+        np.testing.assert_array_equal(idx, idxr, err_msg="call %d" % t)
+        np.testing.assert_array_equal(w, wres, err_msg="call %d" % t)
+        np.testing.assert_array_equal(y, yr, err_msg="call %d" % t)
+        assert np.all(np.isfinite(y))
+        routed_to_4 += int((idx == 4).sum())
+        model.call(idx.reshape(-1))
+        counters, clock, slot_of, expert_of = _state(c.state, E, slots)
+        assert list(slot_of) == model.slot_of and list(expert_of) == model.expert_of, "call %d" % t
+        assert clock == model.clock
+        assert (int(counters[0]), int(counters[1]), int(counters[3])) == (model.hits, model.misses, model.calls)
+    assert routed_to_4 > 0, "no token reached the flagged expert"
+    if slots < E:
+        assert model.misses > slots  # evictions happened
+
+    # the last call against the oracle's routing and expert FFNs on the same records
+    xh = x.cpu().numpy()
+    _, idx_ref, w_ref, margin = oracle_layer(cfg, seed, 0, xh)
+    assert margin.min() > 1e-9
+    np.testing.assert_array_equal(idx, idx_ref)
+    np.testing.assert_allclose(w, w_ref, rtol=W_RTOL)
+
+    def ffn(e, xb):
+        return oracle.expert_ffn(2, H, I, ex.gate[e], ex.up[e], ex.down[e], ex.scales[e], ex.biases[e], xb)[1]
+
+    for b in range(B):
+        ref = ffn(E, xh[b]) + sum(float(w_ref[b, k]) * ffn(int(idx_ref[b, k]), xh[b]) for k in range(K))
+        assert rel_err(y[b], ref) <= TOL, "token %d" % b
 
 
 def test_cache_full_layer_from_pinned_host_memory():
