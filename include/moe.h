@@ -216,8 +216,9 @@ int moe_route_topk(const float* x, int B, const float* w_router, const float* lo
  * _q4 requires desc->bits == 4, _q2 requires desc->bits == 2.
  * With B > 1 the tokens are grouped by expert (as moe_group_tokens) so each
  * active expert's weights are read once per call and multiplied against all of
- * its tokens on the matrix cores (value range as for moe_layer_decode); a 2-bit
- * batch whose desc->expert_flags is set runs token by token instead.
+ * its tokens on the matrix cores (value range as for moe_layer_decode); a batch
+ * whose desc->expert_flags is set runs token by token instead unless its codes
+ * are 4-bit with H, I <= 4096.
  */
 int moe_expert_ffn_q4(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx,
                       const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
@@ -234,9 +235,9 @@ int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const i
  * matrix cores, which take each group's scale s as fp16 and (b + 8 s) through
  * fp16 operands 2^5 b and 2^8 s: there |s| < 256 and |b| < 2048 per group
  * (larger values overflow to inf in y) unless desc->expert_flags
- * (moe_expert_ranges) marks such experts: with 4-bit codes these then run on the
- * GEMV path (at H, I <= 4096); a 2-bit batch with flags runs token by token.
- * The other paths apply scale and bias in fp32.
+ * (moe_expert_ranges) marks such experts: with 4-bit codes and H, I <= 4096 these
+ * then run on the GEMV path; any other batch with flags (2-bit codes, or H or I
+ * above 4096) runs token by token.  The other paths apply scale and bias in fp32.
  */
 int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y_out,
                      int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes, void* stream);

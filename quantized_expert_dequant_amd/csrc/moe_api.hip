@@ -390,9 +390,14 @@ int moe_route_topk(const float* x, int B, const float* w_router, const float* lo
 }
 
 // The batched (grouped) path of a call: the shapes allow it (the workspace always has
-// room for it then) and, at 2 bits, no range flags are given: the 2-bit batches have
-// no GEMV groups to move flagged experts to, so with flags they take the per-token path.
-static bool use_grouped(const Work& W, int bits, const int32_t* flags) { return W.grouped && (bits == 4 || !flags); }
+// room for it then) and, when range flags are given, the grouping has GEMV groups to
+// move the flagged experts to.  It has them for 4-bit layers with rows of at most 64
+// groups (gemv_tokens > 1); a 2-bit or wider layer given flags takes the per-token path.
+static bool flags_groupable(const Layout& L, const int32_t* flags) { return !flags || gemv_tokens(L) > 1; }
+static bool use_grouped(const Work& W, const moe_layer_desc& d)
+{
+    return W.grouped && flags_groupable(make_layout(d.bits, d.H, d.I), d.expert_flags);
+}
 
 static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, const float* x, int B,
                       const int32_t* idx, const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream)
@@ -409,7 +414,7 @@ static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, cons
     if (ws_bytes < W.bytes) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, W.bytes);
     hipStream_t s = (hipStream_t)stream;
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
-    if (use_grouped(W, desc->bits, desc->expert_flags)) {
+    if (use_grouped(W, *desc)) {
         launch_group(idx, B, desc->K, desc->E, gemv_tokens(L), desc->expert_flags, W.gw.g, s);
         launch_ffn_grouped(L, desc->experts, W.gw, x, w, desc->shared_weight, B, desc->K, desc->E, W.xq, W.xst, false,
                            y_out, s, g_timing[KID_GATEUP], g_timing[KID_DOWN]);
@@ -473,7 +478,7 @@ int moe_layer_decode(const moe_layer_desc* desc, const float* x, int B, float* y
     CHECK_PTR(ws);
     const Work W = carve(ws, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
     if (ws_bytes < W.bytes) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, W.bytes);
-    return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, use_grouped(W, desc->bits, desc->expert_flags),
+    return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, use_grouped(W, *desc),
                       (hipStream_t)stream);
 }
 
@@ -484,7 +489,7 @@ int moe_grouped_launch_info(const moe_layer_desc* desc, int B, int32_t* info_out
     if (rc) return rc;
     if (!info_out) return fail(MOE_EINVAL, "%s: info_out is NULL", fn);
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
-    const bool grouped = grouped_supported(L, B, desc->K) && (desc->bits == 4 || !desc->expert_flags);
+    const bool grouped = grouped_supported(L, B, desc->K) && flags_groupable(L, desc->expert_flags);
     const GroupedBlocks nb = grouped_blocks();
     info_out[0] = grouped ? 1 : 0;
     info_out[1] = desc->bits == 2 ? nb.gateup2 : nb.gateup;
@@ -522,7 +527,7 @@ int moe_layer_decode_noalloc(const moe_layer_desc* desc, const float* x, int B, 
     void* ws = scratch_ptr(fn, rc);
     if (!ws) return rc;
     const Work W = carve(ws, desc->bits, B, desc->H, desc->I, desc->E, desc->K, allow_grouped);
-    return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, use_grouped(W, desc->bits, desc->expert_flags),
+    return layer_impl(fn, desc, x, B, y_out, idx_out, w_out, W, use_grouped(W, *desc),
                       (hipStream_t)stream);
 }
 
@@ -615,7 +620,7 @@ int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* 
     const Layout L = make_layout(desc->bits, desc->H, desc->I);
     hipStream_t s = (hipStream_t)stream;
     const int renorm = desc->renormalize ? 1 : 0;
-    const bool grouped = use_grouped(W, desc->bits, desc->expert_flags);
+    const bool grouped = use_grouped(W, *desc);
     // 1. route on the E expert ids
     if (grouped) {
         const TokenPrep P{x, desc->H, W.gw.xh, W.gw.xsum, W.gw.xscale, gemv_tokens(L) > 1 ? W.xq : nullptr, W.xst};
@@ -708,7 +713,7 @@ int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* x,
     const float* xl = x;
     float norm = -1.f;
     bool grouped = W.grouped;  // one path for the whole stack
-    for (int l = 0; l < n_layers; ++l) grouped = grouped && use_grouped(W, layers[l].bits, layers[l].expert_flags);
+    for (int l = 0; l < n_layers; ++l) grouped = grouped && use_grouped(W, layers[l]);
     for (int l = 0; l < n_layers; ++l) {
         const bool last = (l == n_layers - 1);
         float* yl = last ? y_out : ((grouped || !(l & 1)) ? ybuf : xbuf);
