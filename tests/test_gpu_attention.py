@@ -58,7 +58,7 @@ def _gdn_gpu(S, q, k, v, alpha, beta):
     return t[0].cpu().numpy(), o.cpu().numpy()
 
 
-@pytest.mark.parametrize("n,dk,dv", [(64, 128, 128), (3, 64, 37), (2, 256, 130), (5, 128, 1)])
+@pytest.mark.parametrize("n,dk,dv", [(64, 128, 128), (3, 64, 37), (2, 256, 130), (5, 128, 1), (2, 256, 4096)])
 def test_gdn_step_matches_oracle(n, dk, dv):
     S, q, k, v, a, b = _gdn_inputs(100 + dk + dv, n, dk, dv)
     S_ref, o_ref = oracle.gdn_step(S, q, k, v, a, b)
@@ -123,6 +123,19 @@ def _attn_gpu(q, K, V):
 ])
 def test_attention_decode_matches_oracle(n_q, n_kv, d, T):
     q, K, V = _attn_inputs(200 + T, n_q, n_kv, d, T)
+    o_ref = oracle.attn_decode(q, K, V)
+    assert _head_err(_attn_gpu(q, K, V), o_ref) <= ATTN_TOL
+
+
+def test_attention_longest_cache():
+    """T = 2^22, the longest cache the entry point accepts (two query heads on one KV head,
+    d = 64): 256 sub-tiles per wave, the running reference carried through all of them, and
+    256 partials per head in the combine."""
+    n_q, n_kv, d, T = 2, 1, 64, 1 << 22
+    rng = np.random.default_rng(4242)
+    q = rng.standard_normal((n_q, d), dtype=np.float32)
+    K = _bf16_bits(rng.standard_normal((n_kv, T, d), dtype=np.float32))
+    V = _bf16_bits(rng.standard_normal((n_kv, T, d), dtype=np.float32))
     o_ref = oracle.attn_decode(q, K, V)
     assert _head_err(_attn_gpu(q, K, V), o_ref) <= ATTN_TOL
 
