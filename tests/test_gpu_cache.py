@@ -76,8 +76,8 @@ def _state(state, E, slots):
 
 
 class Cached:
-    def __init__(self, n, slots, store=None, bits=None, source=None):
-        cfg, seed = dict(WORKLOADS[n]), seed_of(n)
+    def __init__(self, n, slots, store=None, bits=None, source=None, cfg=None):
+        cfg, seed = dict(WORKLOADS[n] if cfg is None else cfg), seed_of(n)
         if bits is not None:
             cfg["bits"] = bits
         self.cfg, self.seed = cfg, seed
@@ -213,6 +213,34 @@ def test_cache_per_token_routing_batches(B, slots):
     for b in range(B):
         ref = ffn(E, xh[b]) + sum(float(w_ref[b, k]) * ffn(int(idx_ref[b, k]), xh[b]) for k in range(K))
         assert rel_err(y[b], ref) <= TOL, "token %d" % b
+
+
+@pytest.mark.parametrize("B,slots", [(1, 40), (2, 70)])
+def test_cache_most_experts_and_largest_k(B, slots):
+    """E = 1024 and K = 32, the library's maxima, through a cache smaller than the expert set:
+    one token per call (the plan kernel selects its 32 experts from 1024 logits itself) and
+    two (the grouped path on slot ids).  20 calls: the state equals the policy model's after
+    every call and the outputs equal the resident decode's bit for bit."""
+    cfg = dict(H=512, I=128, E=1024, K=32, bits=4, B=B, layers=1, zipf=None)
+    c = Cached(0, slots, cfg=cfg)
+    resident = build_layer(c.cfg, c.seed)
+    model = CacheModel(1024, slots)
+    for t in range(20):
+        x = torch.from_numpy(synth.tokens(c.seed, 900 + t, B, c.L.H)).to(DEV)
+        y, idx, w = c.decode(x)
+        yr, idxr, wr = _resident(resident, x)
+        np.testing.assert_array_equal(idx, idxr, err_msg="call %d" % t)
+        np.testing.assert_array_equal(w, wr, err_msg="call %d" % t)
+        np.testing.assert_array_equal(y, yr, err_msg="call %d" % t)
+        model.call(idx.reshape(-1))
+        counters, clock, slot_of, expert_of = _state(c.state, 1024, slots)
+        assert list(slot_of) == model.slot_of and list(expert_of) == model.expert_of, "call %d" % t
+        assert (int(counters[0]), int(counters[1]), int(counters[3])) == (model.hits, model.misses, model.calls)
+    assert model.misses > slots
+    y_ref, idx_ref, _, _ = oracle_layer(c.cfg, c.seed, 0, x.cpu().numpy())
+    np.testing.assert_array_equal(idx, idx_ref)
+    for b in range(B):
+        assert rel_err(y[b], y_ref[b]) <= TOL
 
 
 def test_cache_full_layer_from_pinned_host_memory():
