@@ -675,6 +675,8 @@ def main():
         print("bench.py measures one GPU only: the decode path is built and measured on a single MI355X "
               "(see the sharding notes); --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0 or args.replays < 1 or args.rotate < 1 or args.distinct < 0:
+        ap.error("--steps, --replays and --rotate must be >= 1, --warmup and --distinct >= 0")
 
     import torch
     import quantized_expert_dequant_amd as moe
