@@ -27,7 +27,7 @@ The float64 oracle is timed on the host cores on a small sample of tokens
 (cpu_baseline).  Each workload's first step is checked against the oracle
 before timing; a mismatch reports no throughput.
 
-    python bench.py [--steps K] [--warmup W] [--workload layer|layer2|batched|stack]
+    python bench.py [--steps K] [--warmup W] [--workload layer|layer2|layer_g128|requant|batched|batched2|stack]
 """
 import argparse
 import ctypes
@@ -53,6 +53,8 @@ WORKLOADS = {
     "batched2": dict(H=4096, I=1024, E=512, K=10, bits=2, B=64, layers=1, zipf=1.1, seed=1004),
     # the layer workload's 4-bit experts requantized to 2-bit on the GPU (moe_requant_4to2)
     "requant": dict(H=4096, I=1024, E=512, K=4, bits=2, B=1, layers=1, zipf=None, seed=1001, requant=True),
+    # the layer workload's shape with one scale and bias per 128 weights
+    "layer_g128": dict(H=4096, I=1024, E=512, K=4, bits=4, B=1, layers=1, zipf=None, seed=1005, group=128),
 }
 RMS_EPS = 1e-6
 
@@ -97,11 +99,11 @@ class Hip:
 
 
 def gateup_bytes_per_expert(c):
-    return 2 * c["I"] * c["H"] * c["bits"] // 8 + 2 * c["I"] * (c["H"] // 64) * 4
+    return 2 * c["I"] * c["H"] * c["bits"] // 8 + 2 * c["I"] * (c["H"] // c.get("group", 64)) * 4
 
 
 def down_bytes_per_expert(c):
-    return c["H"] * c["I"] * c["bits"] // 8 + c["H"] * (c["I"] // 64) * 4
+    return c["H"] * c["I"] * c["bits"] // 8 + c["H"] * (c["I"] // c.get("group", 64)) * 4
 
 
 def build_layers(c, n_distinct, n_copies, dev):
@@ -109,25 +111,26 @@ def build_layers(c, n_distinct, n_copies, dev):
     import synth
     from quantized_expert_dequant_amd.slab import DeviceLayer, upload_experts
     H, I, E, K, bits = c["H"], c["I"], c["E"], c["K"], c["bits"]
+    group = c.get("group", 64)
     base = []
     for l in range(n_distinct):
         t0 = time.time()
         if c.get("requant"):
             from quantized_expert_dequant_amd.slab import upload_requantized
-            src = lambda first, n, l=l: synth.experts(c["seed"], l, first, n, 4, H, I)
-            slab = upload_requantized(src, E + 1, H, I, device=dev)
+            src = lambda first, n, l=l: synth.experts(c["seed"], l, first, n, 4, H, I, group)
+            slab = upload_requantized(src, E + 1, H, I, device=dev, group=group)
         else:
-            src = lambda first, n, l=l: synth.experts(c["seed"], l, first, n, bits, H, I)
-            slab = upload_experts(src, E + 1, bits, H, I, device=dev)
+            src = lambda first, n, l=l: synth.experts(c["seed"], l, first, n, bits, H, I, group)
+            slab = upload_experts(src, E + 1, bits, H, I, device=dev, group=group)
         wr = torch.from_numpy(synth.router(c["seed"], l, E, H)).to(dev)
         bias = torch.from_numpy(synth.zipf_bias(E, c["zipf"])).to(dev) if c["zipf"] else None
-        base.append(DeviceLayer(H, I, E, K, bits, slab, wr, bias))
+        base.append(DeviceLayer(H, I, E, K, bits, slab, wr, bias, group=group))
         log("layer %d packed in %.1fs" % (l, time.time() - t0))
     layers = list(base)
     for r in range(n_distinct, n_copies):
         b = base[r % n_distinct]
         layers.append(DeviceLayer(H, I, E, K, bits, b.slab.clone(), b.w_router.clone(),
-                                  None if b.logit_bias is None else b.logit_bias.clone()))
+                                  None if b.logit_bias is None else b.logit_bias.clone(), group=group))
     torch.cuda.synchronize()
     return layers
 
@@ -143,14 +146,17 @@ def oracle_check(c, x_host, y_dev, idx_dev, layer_id=0):
     need = {E}
     for b in range(x_host.shape[0]):
         need |= {int(e) for e in oracle.topk(lg[b], K)[0]}
-    experts = {e: synth.experts(c["seed"], layer_id, e, 1, 4 if c.get("requant") else c["bits"], c["H"], c["I"])
+    group = c.get("group", 64)
+    experts = {e: synth.experts(c["seed"], layer_id, e, 1, 4 if c.get("requant") else c["bits"], c["H"], c["I"],
+                                group)
                for e in sorted(need)}
     if c.get("requant"):
         for e, x4 in experts.items():
             g2, u2, d2, s2, b2 = oracle.requant_expert(c["H"], c["I"], x4.gate[0], x4.up[0], x4.down[0],
-                                                       x4.scales[0], x4.biases[0])
-            experts[e] = synth.Canonical(2, c["H"], c["I"], 64, g2[None], u2[None], d2[None], s2[None], b2[None])
-    y_ref, idx_ref, _, _ = oracle.layer_decode(c["bits"], c["H"], c["I"], E, K, x_host, Wr, experts, prior=prior)
+                                                       x4.scales[0], x4.biases[0], group=group)
+            experts[e] = synth.Canonical(2, c["H"], c["I"], group, g2[None], u2[None], d2[None], s2[None], b2[None])
+    y_ref, idx_ref, _, _ = oracle.layer_decode(c["bits"], c["H"], c["I"], E, K, x_host, Wr, experts, prior=prior,
+                                               group=group)
     # per token max|dy| / max|y_ref|, the denominator floored where fp32 cannot represent the tolerance
     err = max(float(np.max(np.abs(y_dev[b] - y_ref[b])) / max(np.max(np.abs(y_ref[b])), 2.0 ** -126 / 2e-3))
               for b in range(x_host.shape[0]))
@@ -235,8 +241,8 @@ def _median(v):
 
 
 def _workload_name(name, c, n_copies, n_distinct, stack):
-    return "%s: H=%d I=%d E=%d+1 shared K=%d %d-bit group 64 bf16 scale+bias, B=%d%s%s" % (
-        name, c["H"], c["I"], c["E"], c["K"], c["bits"], c["B"],
+    return "%s: H=%d I=%d E=%d+1 shared K=%d %d-bit group %d bf16 scale+bias, B=%d%s%s" % (
+        name, c["H"], c["I"], c["E"], c["K"], c["bits"], c.get("group", 64), c["B"],
         ", %d layers with RMS renorm" % c["layers"] if stack else "",
         ", experts requantized from the layer workload's 4-bit ones on the GPU" if c.get("requant") else "")
 
@@ -751,6 +757,7 @@ def main():
     if not args.no_configs:
         # every other workload at its own shape, fewer steps, same measurement
         extra = {"layer2": dict(steps=100, warmup=10), "requant": dict(steps=100, warmup=10),
+                 "layer_g128": dict(steps=100, warmup=10),
                  "batched": dict(steps=40, warmup=5), "batched2": dict(steps=40, warmup=5),
                  "stack": dict(steps=10, warmup=2, distinct=4),
                  "layer": dict(steps=100, warmup=10)}

@@ -53,7 +53,7 @@ extern "C" {
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)        /* null / misaligned pointer, bad shape, workspace too small */
-#define MOE_EUNSUPPORTED (-2)  /* bits not 2 or 4, group not 64, K > 32, E > 1024, B > 256, H > 65536, I > 8192 */
+#define MOE_EUNSUPPORTED (-2)  /* bits not 2 or 4, group not 64/128/256, K > 32, E > 1024, B > 256, H > 65536, I > 8192 */
 #define MOE_EHIP (-3)          /* the HIP runtime refused a launch */
 
 #define MOE_MAX_K 32
@@ -62,8 +62,10 @@ extern "C" {
 
 /*
  * One MoE layer.  All pointers are device memory owned by the caller.
- *   H: hidden size, I: expert intermediate size (both multiples of 64).
- *   E: routed experts, K: experts kept per token, bits: 4 or 2, group: 64.
+ *   H: hidden size, I: expert intermediate size (both multiples of the group).
+ *   E: routed experts, K: experts kept per token, bits: 4 or 2, group: weights per
+ *   scale/bias group along each row, 64, 128 or 256 (the pages give per-group
+ *   scales and biases, [LLMAPIS] section 深度分析, without a size).
  *   experts: packed slab of E + 1 records written by moe_pack_experts, the
  *            shared expert at index E; record stride moe_expert_record_bytes().
  *   w_router: fp32 [E][H] row-major.  logit_bias: fp32 [E] added to the
@@ -88,10 +90,10 @@ typedef struct moe_layer_desc {
 
 /*
  * Bytes of one packed expert record: gate and up [I][H] plus down [H][I]
- * codes at `bits` per weight, plus a bf16 scale and bias per group of 64.
- * Equal to the canonical size of one expert, e.g. 7,077,888 B (6.75 MiB) at
- * H = 4096, I = 1024, 4-bit ([LLMAPIS] section 深度分析 gives about 6.75MB
- * per expert).  Returns 0 for unsupported arguments.
+ * codes at `bits` per weight, plus a bf16 scale and bias per group of `group`
+ * weights.  Equal to the canonical size of one expert, e.g. 7,077,888 B
+ * (6.75 MiB) at H = 4096, I = 1024, 4-bit, group 64 ([LLMAPIS] section 深度分析
+ * gives about 6.75MB per expert).  Returns 0 for unsupported arguments.
  */
 size_t moe_expert_record_bytes(int bits, int H, int I, int group);
 
@@ -132,14 +134,14 @@ int moe_pack_experts(int bits, int H, int I, int group, int n_experts, const uin
  * Offline requantization of n_experts canonical 4-bit experts to canonical 2-bit
  * experts of the same shape ([CLAUDAY] and [LLMAPIS] section 数据和技术细节: the
  * experts were requantized from 4-bit to 2-bit, 209 GB -> 120 GB; the pages give no
- * procedure).  Per group of 64 weights w_c = s4 q4_c + b4: b2 = bf16(min w),
+ * procedure).  Per group of `group` weights w_c = s4 q4_c + b4: b2 = bf16(min w),
  * s2 = bf16((max w - min w) / 3), q2_c = clamp(rint((w_c - b2) / s2), 0, 3) (0 when
  * s2 = 0 or the quotient is not a number), every operation in IEEE double and bf16() the nearest bf16, ties to even.
  * Inputs: the canonical 4-bit tensors as for moe_pack_experts (device, stacked
  * over the n experts); outputs: gate2, up2 uint8 [n][I][H/4], down2 [n][H][I/4],
  * scales2, biases2 uint16 [n][ng] in the same order as the inputs' scales.  The
  * result is packed with moe_pack_experts(bits = 2).  MOE_EINVAL / MOE_EUNSUPPORTED
- * as for moe_pack_experts (group must be 64).
+ * as for moe_pack_experts.
  */
 int moe_requant_4to2(int H, int I, int group, int n_experts, const uint8_t* gate4, const uint8_t* up4,
                      const uint8_t* down4, const uint16_t* scales4, const uint16_t* biases4, uint8_t* gate2,

@@ -41,13 +41,17 @@ namespace moe {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
+// Gh, Gi: 64-column units of a gate/up row and of a down row (the kernels' unit of
+// work: one lane's two 16-byte chunks at 4 bits).  A quantization group spans 64 << gs
+// columns (gs = 0, 1, 2: groups of 64, 128, 256), so unit g takes the scale and bias
+// of group g >> gs; Sh, Si: groups per gate/up and per down row.
 struct Layout {
-    int bits, H, I, Gh, Gi;
+    int bits, H, I, Gh, Gi, gs, Sh, Si;
     long long hb, ib;  // code bytes per gate/up row and per down row
     long long off_gu_sb, off_d_codes, off_d_sb, record;
 };
 
-__host__ __device__ inline Layout make_layout(int bits, int H, int I)
+__host__ __device__ inline Layout make_layout(int bits, int H, int I, int group)
 {
     Layout L;
     L.bits = bits;
@@ -55,12 +59,15 @@ __host__ __device__ inline Layout make_layout(int bits, int H, int I)
     L.I = I;
     L.Gh = H / 64;
     L.Gi = I / 64;
+    L.gs = group >= 256 ? 2 : (group >= 128 ? 1 : 0);
+    L.Sh = L.Gh >> L.gs;
+    L.Si = L.Gi >> L.gs;
     L.hb = (long long)H * bits / 8;
     L.ib = (long long)I * bits / 8;
     L.off_gu_sb = 2LL * I * L.hb;
-    L.off_d_codes = L.off_gu_sb + 8LL * I * L.Gh;
+    L.off_d_codes = L.off_gu_sb + 8LL * I * L.Sh;
     L.off_d_sb = L.off_d_codes + (long long)H * L.ib;
-    L.record = L.off_d_sb + 4LL * H * L.Gi;
+    L.record = L.off_d_sb + 4LL * H * L.Si;
     return L;
 }
 

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void k_expert_ranges(Layout L, const uint8_t* 
                                                        int32_t* __restrict__ flags)
 {
     const uint8_t* rec = slab + (long long)blockIdx.x * L.record;
-    const long long n_gu = (long long)L.I * L.Gh * 8 / 16, n_dn = (long long)L.H * L.Gi * 4 / 16;
+    const long long n_gu = (long long)L.I * L.Sh * 8 / 16, n_dn = (long long)L.H * L.Si * 4 / 16;
     const uint4* gu = reinterpret_cast<const uint4*>(rec + L.off_gu_sb);
     const uint4* dn = reinterpret_cast<const uint4*>(rec + L.off_d_sb);
     auto bad = [](uint4 v) {
@@ -662,8 +662,8 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         const uint8_t* rec = A.slab + (long long)e * L.record;
         const int row = min(tile * GM_ROWS + wave * 16 + i, NR - 1);
         const uint32_t row_off = (uint32_t)(row * 2 * L.hb);  // gate/up; down chunks go through d_chunk_off
-        const uint32_t sb_off = (MODE == MODE_GATEUP) ? (uint32_t)(L.off_gu_sb + (long long)row * G * 8)
-                                                      : (uint32_t)(L.off_d_sb + (long long)row * G * 4);
+        const uint32_t sb_off = (MODE == MODE_GATEUP) ? (uint32_t)(L.off_gu_sb + (long long)row * L.Sh * 8)
+                                                      : (uint32_t)(L.off_d_sb + (long long)row * L.Si * 4);
         const uint32_t up_off = (uint32_t)L.hb;
         const char* tok_base = (MODE == MODE_GATEUP) ? (const char*)A.xh : (const char*)A.hb16;
 
@@ -720,11 +720,11 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             W.c[0] = *reinterpret_cast<const cw_t*>(rec + co);
             if (MODE == MODE_GATEUP) {
                 W.c[NM - 1] = *reinterpret_cast<const cw_t*>(rec + (co + up_off));
-                const uint2 v = *reinterpret_cast<const uint2*>(rec + (sb_off + (uint32_t)g * 8u));
+                const uint2 v = *reinterpret_cast<const uint2*>(rec + (sb_off + (uint32_t)(g >> L.gs) * 8u));
                 W.sb[0] = v.x;
                 W.sb[NM - 1] = v.y;
             } else {
-                W.sb[0] = *reinterpret_cast<const uint32_t*>(rec + (sb_off + (uint32_t)g * 4u));
+                W.sb[0] = *reinterpret_cast<const uint32_t*>(rec + (sb_off + (uint32_t)(g >> L.gs) * 4u));
             }
         };
 
@@ -1081,7 +1081,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_gateup(GroupedArgs A, co
         w.c[1] = *reinterpret_cast<const uint4*>(base + (G + g) * 16);
         w.c[2] = *reinterpret_cast<const uint4*>(base + L.hb + g * 16);
         w.c[3] = *reinterpret_cast<const uint4*>(base + L.hb + (G + g) * 16);
-        w.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)r * G + g) * 8);
+        w.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)r * L.Sh + (g >> L.gs)) * 8);
     };
     int v_prev = -1;
     auto work = [&](const GvGateUp& w, int it, GvGateUp& next) {
@@ -1145,7 +1145,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_down(GroupedArgs A, cons
         const uint8_t* base = rec + L.off_d_codes;
         w.c[0] = *reinterpret_cast<const uint4*>(base + d_chunk_off(L, r, g));
         w.c[1] = *reinterpret_cast<const uint4*>(base + d_chunk_off(L, r, G + g));
-        w.sb = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)r * G + g) * 4);
+        w.sb = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)r * L.Si + (g >> L.gs)) * 4);
     };
     int v_prev = -1;
     auto work = [&](const GvDown& w, int it, GvDown& next) {

@@ -39,12 +39,12 @@ __global__ __launch_bounds__(256) void k_pack(Layout L, const uint8_t* __restric
 {
     const int j = blockIdx.y;  // expert within the batch
     const long long cb = (long long)L.I * L.hb;  // canonical code bytes of one gate/up matrix
-    const long long ng = 2LL * L.I * L.Gh + (long long)L.H * L.Gi;
-    const int cpg = L.bits / 2;  // 16-byte chunks per group
+    const long long ng = 2LL * L.I * L.Sh + (long long)L.H * L.Si;  // groups (scales) of one expert
+    const int cpg = L.bits / 2;  // 16-byte chunks per 64-column unit
     const long long n_gu_chunks = 2LL * L.I * (L.hb / 16);
-    const long long n_gu_sb = (long long)L.I * L.Gh;
+    const long long n_gu_sb = (long long)L.I * L.Sh;
     const long long n_d_chunks = (long long)L.H * (L.ib / 16);
-    const long long n_d_sb = (long long)L.H * L.Gi;
+    const long long n_d_sb = (long long)L.H * L.Si;
     const long long total = n_gu_chunks + n_gu_sb + n_d_chunks + n_d_sb;
     uint8_t* rec = slab + (long long)(first + j) * L.record;
     const uint16_t* sc = scales + j * ng;
@@ -62,8 +62,8 @@ __global__ __launch_bounds__(256) void k_pack(Layout L, const uint8_t* __restric
             *reinterpret_cast<uint4*>(rec + r * 2 * L.hb + m * L.hb + (long long)pos * 16) =
                 *reinterpret_cast<const uint4*>(src);
         } else if (t < n_gu_chunks + n_gu_sb) {
-            const long long i = t - n_gu_chunks;  // r * Gh + g
-            const long long nu = (long long)L.I * L.Gh;
+            const long long i = t - n_gu_chunks;  // r * Sh + group
+            const long long nu = (long long)L.I * L.Sh;
             ushort4 v = make_ushort4(sc[i], bi[i], sc[nu + i], bi[nu + i]);
             *reinterpret_cast<ushort4*>(rec + L.off_gu_sb + i * 8) = v;
         } else if (t < n_gu_chunks + n_gu_sb + n_d_chunks) {
@@ -76,8 +76,8 @@ __global__ __launch_bounds__(256) void k_pack(Layout L, const uint8_t* __restric
             *reinterpret_cast<uint4*>(rec + L.off_d_codes + d_chunk_off(L, (int)r, pos)) =
                 *reinterpret_cast<const uint4*>(src);
         } else {
-            const long long i = t - n_gu_chunks - n_gu_sb - n_d_chunks;  // r * Gi + g
-            const long long o = 2LL * L.I * L.Gh;
+            const long long i = t - n_gu_chunks - n_gu_sb - n_d_chunks;  // r * Si + group
+            const long long o = 2LL * L.I * L.Sh;
             ushort2 v = make_ushort2(sc[o + i], bi[o + i]);
             *reinterpret_cast<ushort2*>(rec + L.off_d_sb + i * 4) = v;
         }
@@ -87,8 +87,8 @@ __global__ __launch_bounds__(256) void k_pack(Layout L, const uint8_t* __restric
 void launch_pack(const Layout& L, int n, const uint8_t* gate, const uint8_t* up, const uint8_t* down,
                  const uint16_t* scales, const uint16_t* biases, void* slab, int first, hipStream_t s)
 {
-    const long long total = 2LL * L.I * (L.hb / 16) + (long long)L.I * L.Gh + (long long)L.H * (L.ib / 16) +
-                            (long long)L.H * L.Gi;
+    const long long total = 2LL * L.I * (L.hb / 16) + (long long)L.I * L.Sh + (long long)L.H * (L.ib / 16) +
+                            (long long)L.H * L.Si;
     long long blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks, n), dim3(256), 0, s, L, gate, up, down, scales, biases,
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void k_dequant(Layout L, const uint8_t* __rest
             int k;
             const int P = packed_pos(L.bits, L.Gh, c, k);
             q = chunk_code(row + (long long)P * 16, L.bits, k);
-            const uint16_t* sb = reinterpret_cast<const uint16_t*>(rec + L.off_gu_sb + ((long long)r * L.Gh + (c >> 6)) * 8);
+            const uint16_t* sb = reinterpret_cast<const uint16_t*>(rec + L.off_gu_sb + ((long long)r * L.Sh + (c >> (6 + L.gs))) * 8);
             s = __uint_as_float((uint32_t)sb[2 * m] << 16);
             b = __uint_as_float((uint32_t)sb[2 * m + 1] << 16);
         } else {
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void k_dequant(Layout L, const uint8_t* __rest
             int k;
             const int P = packed_pos(L.bits, L.Gi, c, k);
             q = chunk_code(rec + L.off_d_codes + d_chunk_off(L, r, P), L.bits, k);
-            const uint16_t* sb = reinterpret_cast<const uint16_t*>(rec + L.off_d_sb + ((long long)r * L.Gi + (c >> 6)) * 4);
+            const uint16_t* sb = reinterpret_cast<const uint16_t*>(rec + L.off_d_sb + ((long long)r * L.Si + (c >> (6 + L.gs))) * 4);
             s = __uint_as_float((uint32_t)sb[0] << 16);
             b = __uint_as_float((uint32_t)sb[1] << 16);
         }
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
                     R[p].g1 = ld16(base + (G + g) * 16);
                     R[p].u1 = ld16(base + L.hb + (G + g) * 16);
                 }
-                R[p].sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)r * G + g) * 8);
+                R[p].sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)r * L.Sh + (g >> L.gs)) * 8);
             }
         }
     };
@@ -638,7 +638,8 @@ __global__ __launch_bounds__(256) void k_down(FfnArgs A)
                         const uint8_t* base = rec[s] + L.off_d_codes;
                         c0[s][p] = ld16(base + d_chunk_off(L, r, g));
                         if (BITS == 4) c1[s][p] = ld16(base + d_chunk_off(L, r, G + g));
-                        sbv[s][p] = *reinterpret_cast<const uint32_t*>(rec[s] + L.off_d_sb + ((long long)r * G + g) * 4);
+                        sbv[s][p] = *reinterpret_cast<const uint32_t*>(rec[s] + L.off_d_sb +
+                                                                       ((long long)r * L.Si + (g >> L.gs)) * 4);
                     }
                 }
         };
@@ -757,7 +758,7 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
             R.g1 = ld16(base + (G + g) * 16);
             R.u1 = ld16(base + L.hb + (G + g) * 16);
         }
-        R.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)rc * G + g) * 8);
+        R.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)rc * L.Sh + (g >> L.gs)) * 8);
     };
     // 2. the shared expert needs no routing: its loads go out now
     if (slot == 0) issue(A.E);
@@ -868,7 +869,7 @@ __global__ __launch_bounds__(64 * DNF_WAVES) void k_down_fast(FfnArgs A)
         const uint8_t* rec = A.slab + (long long)e * L.record;
         c0[k] = ld16(rec + o0);
         if (BITS == 4) c1[k] = ld16(rec + o1);
-        sbv[k] = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)rc * G + g) * 4);
+        sbv[k] = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)rc * L.Si + (g >> L.gs)) * 4);
     };
     issue(K, A.E);
     float wt[KS];

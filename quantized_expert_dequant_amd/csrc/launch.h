@@ -34,8 +34,8 @@ int attn_max_per();
 void launch_attn_decode(int n_q, int n_kv, int d, int T, const float* q, const uint16_t* K, const uint16_t* V,
                         float* part, float* o, hipStream_t s);
 // canonical 4-bit experts -> canonical 2-bit experts (requant.hip)
-void launch_requant_4to2(int H, int I, int n, const uint8_t* gate4, const uint8_t* up4, const uint8_t* down4,
-                         const uint16_t* s4, const uint16_t* b4, uint8_t* gate2, uint8_t* up2, uint8_t* down2,
-                         uint16_t* s2, uint16_t* b2, hipStream_t s);
+void launch_requant_4to2(int H, int I, int group, int n, const uint8_t* gate4, const uint8_t* up4,
+                         const uint8_t* down4, const uint16_t* s4, const uint16_t* b4, uint8_t* gate2, uint8_t* up2,
+                         uint8_t* down2, uint16_t* s2, uint16_t* b2, hipStream_t s);
 
 }  // namespace moe

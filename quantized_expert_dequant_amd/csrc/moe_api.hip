@@ -63,9 +63,10 @@ bool misaligned4(const void* p) { return ((uintptr_t)p & 3u) != 0; }
 int check_shape(const char* fn, int bits, int H, int I, int group)
 {
     if (bits != 2 && bits != 4) return fail(MOE_EUNSUPPORTED, "%s: bits=%d (must be 2 or 4)", fn, bits);
-    if (group != 64) return fail(MOE_EUNSUPPORTED, "%s: group=%d (must be 64)", fn, group);
-    if (H <= 0 || I <= 0 || H % 64 || I % 64)
-        return fail(MOE_EINVAL, "%s: H=%d and I=%d must be positive multiples of 64", fn, H, I);
+    if (group != 64 && group != 128 && group != 256)
+        return fail(MOE_EUNSUPPORTED, "%s: group=%d (must be 64, 128 or 256)", fn, group);
+    if (H <= 0 || I <= 0 || H % group || I % group)
+        return fail(MOE_EINVAL, "%s: H=%d and I=%d must be positive multiples of the group (%d)", fn, H, I, group);
     if (H > 65536 || I > 8192) return fail(MOE_EUNSUPPORTED, "%s: H=%d > 65536 or I=%d > 8192", fn, H, I);
     return MOE_OK;
 }
@@ -129,7 +130,7 @@ Work carve(void* ws, int bits, int B, int H, int I, int E, int K, bool allow_gro
     W.xq = (uint4*)take((size_t)B * Gh * 128);
     W.xst = (float4*)take((size_t)B * Gh * 16);
     W.hq = take(S * Gi * 256);  // h in fp32
-    const Layout L = make_layout(bits, H, I);
+    const Layout L = make_layout(bits, H, I, 64);  // the workspace does not depend on the weight group
     W.grouped = allow_grouped && grouped_supported(L, B, K);
     W.gw = GroupedWork{};
     if (W.grouped) {
@@ -221,7 +222,7 @@ int moe_set_timing_events(int kernel, void* start_event, void* stop_event)
 size_t moe_expert_record_bytes(int bits, int H, int I, int group)
 {
     if (check_shape("moe_expert_record_bytes", bits, H, I, group)) return 0;
-    return (size_t)make_layout(bits, H, I).record;
+    return (size_t)make_layout(bits, H, I, group).record;
 }
 
 size_t moe_workspace_bytes(const moe_layer_desc* desc, int B)
@@ -259,7 +260,7 @@ int moe_pack_experts(int bits, int H, int I, int group, int n_experts, const uin
     CHECK_PTR(scales_bf16);
     CHECK_PTR(biases_bf16);
     CHECK_PTR(slab_out);
-    const Layout L = make_layout(bits, H, I);
+    const Layout L = make_layout(bits, H, I, group);
     launch_pack(L, n_experts, gate_codes, up_codes, down_codes, scales_bf16, biases_bf16, slab_out, first_expert,
                 (hipStream_t)stream);
     return hip_status(fn);
@@ -283,7 +284,7 @@ int moe_requant_4to2(int H, int I, int group, int n_experts, const uint8_t* gate
     CHECK_PTR(down2);
     CHECK_PTR4(scales2);
     CHECK_PTR4(biases2);
-    launch_requant_4to2(H, I, n_experts, gate4, up4, down4, scales4, biases4, gate2, up2, down2, scales2, biases2,
+    launch_requant_4to2(H, I, group, n_experts, gate4, up4, down4, scales4, biases4, gate2, up2, down2, scales2, biases2,
                         (hipStream_t)stream);
     return hip_status(fn);
 }
@@ -301,7 +302,7 @@ int moe_expert_ranges(int bits, int H, int I, int group, const void* slab, int n
     if (!src) return fail(MOE_EINVAL, "%s: slab is neither device memory nor pinned host memory", fn);
     const void* dst = backing_device_ptr(flags_out);
     if (!dst) return fail(MOE_EINVAL, "%s: flags_out is neither device memory nor pinned host memory", fn);
-    launch_expert_ranges(make_layout(bits, H, I), src, n_experts, (int32_t*)dst, (hipStream_t)stream);
+    launch_expert_ranges(make_layout(bits, H, I, group), src, n_experts, (int32_t*)dst, (hipStream_t)stream);
     return hip_status(fn);
 }
 
@@ -364,7 +365,7 @@ int moe_dequant_expert(int bits, int H, int I, int group, const void* record, fl
     if (rc) return rc;
     CHECK_PTR(record);
     CHECK_PTR(W_out);
-    launch_dequant(make_layout(bits, H, I), record, W_out, (hipStream_t)stream);
+    launch_dequant(make_layout(bits, H, I, group), record, W_out, (hipStream_t)stream);
     return hip_status(fn);
 }
 
@@ -396,7 +397,7 @@ int moe_route_topk(const float* x, int B, const float* w_router, const float* lo
 static bool flags_groupable(const Layout& L, const int32_t* flags) { return !flags || gemv_tokens(L) > 1; }
 static bool use_grouped(const Work& W, const moe_layer_desc& d)
 {
-    return W.grouped && flags_groupable(make_layout(d.bits, d.H, d.I), d.expert_flags);
+    return W.grouped && flags_groupable(make_layout(d.bits, d.H, d.I, d.group), d.expert_flags);
 }
 
 static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, const float* x, int B,
@@ -413,7 +414,7 @@ static int expert_ffn(const char* fn, int bits, const moe_layer_desc* desc, cons
     const Work W = carve(ws, desc->bits, B, desc->H, desc->I, desc->E, desc->K);
     if (ws_bytes < W.bytes) return fail(MOE_EINVAL, "%s: workspace %zu < %zu bytes", fn, ws_bytes, W.bytes);
     hipStream_t s = (hipStream_t)stream;
-    const Layout L = make_layout(desc->bits, desc->H, desc->I);
+    const Layout L = make_layout(desc->bits, desc->H, desc->I, desc->group);
     if (use_grouped(W, *desc)) {
         launch_group(idx, B, desc->K, desc->E, gemv_tokens(L), desc->expert_flags, W.gw.g, s);
         launch_ffn_grouped(L, desc->experts, W.gw, x, w, desc->shared_weight, B, desc->K, desc->E, W.xq, W.xst, false,
@@ -446,7 +447,7 @@ static int layer_impl(const char* fn, const moe_layer_desc* d, const float* x, i
 {
     int32_t* idx = idx_out ? idx_out : W.idx;
     float* w = w_out ? w_out : W.w;
-    const Layout L = make_layout(d->bits, d->H, d->I);
+    const Layout L = make_layout(d->bits, d->H, d->I, d->group);
     if (grouped) {
         const TokenPrep P{x, d->H, W.gw.xh, W.gw.xsum, W.gw.xscale, gemv_tokens(L) > 1 ? W.xq : nullptr, W.xst};
         launch_route_batched(x, B, d->w_router, d->logit_bias, d->H, d->E, d->K, d->renormalize ? 1 : 0,
@@ -488,7 +489,7 @@ int moe_grouped_launch_info(const moe_layer_desc* desc, int B, int32_t* info_out
     int rc = check_desc(fn, desc, B);
     if (rc) return rc;
     if (!info_out) return fail(MOE_EINVAL, "%s: info_out is NULL", fn);
-    const Layout L = make_layout(desc->bits, desc->H, desc->I);
+    const Layout L = make_layout(desc->bits, desc->H, desc->I, desc->group);
     const bool grouped = grouped_supported(L, B, desc->K) && flags_groupable(L, desc->expert_flags);
     const GroupedBlocks nb = grouped_blocks();
     info_out[0] = grouped ? 1 : 0;
@@ -575,7 +576,7 @@ int moe_cache_init(const moe_layer_desc* desc, const moe_expert_cache* cache, vo
     if (rc) return rc;
     const void* src = backing_device_ptr(desc->experts);
     if (!src) return fail(MOE_EINVAL, "%s: desc->experts is neither device memory nor pinned host memory", fn);
-    const Layout L = make_layout(desc->bits, desc->H, desc->I);
+    const Layout L = make_layout(desc->bits, desc->H, desc->I, desc->group);
     hipStream_t s = (hipStream_t)stream;
     launch_cache_reset(cache->state, desc->E, cache->slots, s);
     // the shared expert (record E of the store) has a slot of its own, after the routed ones
@@ -617,7 +618,7 @@ int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* 
                                              : nullptr;
     int32_t* idx = idx_out ? idx_out : W.idx;
     float* w = w_out ? w_out : W.w;
-    const Layout L = make_layout(desc->bits, desc->H, desc->I);
+    const Layout L = make_layout(desc->bits, desc->H, desc->I, desc->group);
     hipStream_t s = (hipStream_t)stream;
     const int renorm = desc->renormalize ? 1 : 0;
     const bool grouped = use_grouped(W, *desc);

@@ -9,8 +9,8 @@
 // The pages report that the experts were requantized from 4-bit to 2-bit, the
 // expert files shrinking from 209 GB to 120 GB ([CLAUDAY]; [LLMAPIS] section
 // 数据和技术细节), and give no procedure.  This library's reading is a per-group
-// min/max affine refit of the dequantized 4-bit weights: for the 64 weights of a
-// group, w_c = s4 q4_c + b4 (exact in double), b2 = bf16(min w), s2 =
+// min/max affine refit of the dequantized 4-bit weights: for the weights of a
+// group (64, 128 or 256), w_c = s4 q4_c + b4 (exact in double), b2 = bf16(min w), s2 =
 // bf16((max w - min w) / 3), q2_c = clamp(rint((w_c - b2) / s2), 0, 3) (0 when
 // s2 = 0 or when the quotient is not a number), every operation in IEEE double and bf16() one rounding of the double
 // to the nearest bf16, ties to even.  The integer codes follow from these
@@ -58,70 +58,79 @@ __device__ inline uint16_t bf16_nearest_even(double v)
 
 __device__ inline double bf16_to_f64(uint16_t b) { return (double)__uint_as_float((uint32_t)b << 16); }
 
-// One thread per group of 64: 32 bytes of 4-bit codes in, 16 bytes of 2-bit codes out.
-// Group t of expert j: gate groups [0, I*Gh), up groups [I*Gh, 2*I*Gh), down groups after.
-__global__ __launch_bounds__(256) void k_requant(int H, int I, const uint8_t* __restrict__ gate4,
+// One thread per group of 64 << gs weights: 32 << gs bytes of 4-bit codes in, 16 << gs
+// bytes of 2-bit codes out, in units of 64 weights (two passes: the extremes, then the
+// codes).  Group t of expert j: gate groups [0, I*Sh), up groups [I*Sh, 2*I*Sh), down
+// groups after (Sh, Si: groups per gate/up and per down row).
+__global__ __launch_bounds__(256) void k_requant(int H, int I, int gs, const uint8_t* __restrict__ gate4,
                                                  const uint8_t* __restrict__ up4, const uint8_t* __restrict__ down4,
                                                  const uint16_t* __restrict__ s4, const uint16_t* __restrict__ b4,
                                                  uint8_t* __restrict__ gate2, uint8_t* __restrict__ up2,
                                                  uint8_t* __restrict__ down2, uint16_t* __restrict__ s2,
                                                  uint16_t* __restrict__ b2)
 {
-    const int j = blockIdx.y;
-    const long long Gh = H / 64, Gi = I / 64;
-    const long long ngu = (long long)I * Gh, ng = 2 * ngu + (long long)H * Gi;
+    const int j = blockIdx.y, nu = 1 << gs;  // 64-weight units per group
+    const long long Sh = (H / 64) >> gs, Si = (I / 64) >> gs;
+    const long long ngu = (long long)I * Sh, ng = 2 * ngu + (long long)H * Si;
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= ng) return;
-    // the group's 4-bit codes (32 bytes) and 2-bit destination (16 bytes), canonical order
+    // the group's 4-bit codes and 2-bit destination, canonical order
     const uint8_t* src;
     uint8_t* dst;
     if (t < 2 * ngu) {
         const bool up = t >= ngu;
-        const long long gi = up ? t - ngu : t;  // r * Gh + g
-        const long long off4 = (long long)j * I * (H / 2) + gi * 32, off2 = (long long)j * I * (H / 4) + gi * 16;
+        const long long gi = up ? t - ngu : t;  // r * Sh + group
+        const long long off4 = (long long)j * I * (H / 2) + gi * 32 * nu, off2 = (long long)j * I * (H / 4) + gi * 16 * nu;
         src = (up ? up4 : gate4) + off4;
         dst = (up ? up2 : gate2) + off2;
     } else {
-        const long long gi = t - 2 * ngu;  // r * Gi + g
-        src = down4 + (long long)j * H * (I / 2) + gi * 32;
-        dst = down2 + (long long)j * H * (I / 4) + gi * 16;
+        const long long gi = t - 2 * ngu;  // r * Si + group
+        src = down4 + (long long)j * H * (I / 2) + gi * 32 * nu;
+        dst = down2 + (long long)j * H * (I / 4) + gi * 16 * nu;
     }
     const long long si = (long long)j * ng + t;
     const double s = bf16_to_f64(s4[si]), b = bf16_to_f64(b4[si]);
-    const uint4 c0 = *reinterpret_cast<const uint4*>(src), c1 = *reinterpret_cast<const uint4*>(src + 16);
-    const uint32_t words[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     double lo = 0.0, hi = 0.0;
+    for (int u = 0; u < nu; ++u) {
+        const uint4 c0 = *reinterpret_cast<const uint4*>(src + 32 * u), c1 = *reinterpret_cast<const uint4*>(src + 32 * u + 16);
+        const uint32_t words[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-    for (int k = 0; k < 64; ++k) {
-        const double w = s * (double)((words[k >> 3] >> (4 * (k & 7))) & 15u) + b;
-        lo = k == 0 ? w : fmin(lo, w);
-        hi = k == 0 ? w : fmax(hi, w);
+        for (int k = 0; k < 64; ++k) {
+            const double w = s * (double)((words[k >> 3] >> (4 * (k & 7))) & 15u) + b;
+            lo = (u == 0 && k == 0) ? w : fmin(lo, w);
+            hi = (u == 0 && k == 0) ? w : fmax(hi, w);
+        }
     }
     const uint16_t nb = bf16_nearest_even(lo), ns = bf16_nearest_even((hi - lo) / 3.0);
     const double bd = bf16_to_f64(nb), sd = bf16_to_f64(ns);
-    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    for (int u = 0; u < nu; ++u) {
+        const uint4 c0 = *reinterpret_cast<const uint4*>(src + 32 * u), c1 = *reinterpret_cast<const uint4*>(src + 32 * u + 16);
+        const uint32_t words[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        uint32_t out[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int k = 0; k < 64; ++k) {
-        const double w = s * (double)((words[k >> 3] >> (4 * (k & 7))) & 15u) + b;
-        uint32_t q = 0u;
-        if (sd != 0.0) {
-            const double r = rint((w - bd) / sd);
-            q = r >= 3.0 ? 3u : (r > 0.0 ? (uint32_t)r : 0u);  // a quotient that is not a number gives 0
+        for (int k = 0; k < 64; ++k) {
+            const double w = s * (double)((words[k >> 3] >> (4 * (k & 7))) & 15u) + b;
+            uint32_t q = 0u;
+            if (sd != 0.0) {
+                const double r = rint((w - bd) / sd);
+                q = r >= 3.0 ? 3u : (r > 0.0 ? (uint32_t)r : 0u);  // a quotient that is not a number gives 0
+            }
+            out[k >> 4] |= q << (2 * (k & 15));
         }
-        out[k >> 4] |= q << (2 * (k & 15));
+        *reinterpret_cast<uint4*>(dst + 16 * u) = make_uint4(out[0], out[1], out[2], out[3]);
     }
-    *reinterpret_cast<uint4*>(dst) = make_uint4(out[0], out[1], out[2], out[3]);
     s2[si] = ns;
     b2[si] = nb;
 }
 
-void launch_requant_4to2(int H, int I, int n, const uint8_t* gate4, const uint8_t* up4, const uint8_t* down4,
-                         const uint16_t* s4, const uint16_t* b4, uint8_t* gate2, uint8_t* up2, uint8_t* down2,
-                         uint16_t* s2, uint16_t* b2, hipStream_t s)
+void launch_requant_4to2(int H, int I, int group, int n, const uint8_t* gate4, const uint8_t* up4,
+                         const uint8_t* down4, const uint16_t* s4, const uint16_t* b4, uint8_t* gate2, uint8_t* up2,
+                         uint8_t* down2, uint16_t* s2, uint16_t* b2, hipStream_t s)
 {
-    const long long ng = 2LL * I * (H / 64) + (long long)H * (I / 64);
-    hipLaunchKernelGGL(k_requant, dim3((unsigned)((ng + 255) / 256), n), dim3(256), 0, s, H, I, gate4, up4, down4, s4,
-                       b4, gate2, up2, down2, s2, b2);
+    const int gs = group >= 256 ? 2 : (group >= 128 ? 1 : 0);
+    const long long ng = 2LL * I * ((H / 64) >> gs) + (long long)H * ((I / 64) >> gs);
+    hipLaunchKernelGGL(k_requant, dim3((unsigned)((ng + 255) / 256), n), dim3(256), 0, s, H, I, gs, gate4, up4,
+                       down4, s4, b4, gate2, up2, down2, s2, b2);
 }
 
 }  // namespace moe

@@ -33,13 +33,14 @@ def build_layer(cfg, seed, layer=0, device="cuda"):
     import torch
     from quantized_expert_dequant_amd.slab import DeviceLayer, upload_experts
     H, I, E, K, bits = cfg["H"], cfg["I"], cfg["E"], cfg["K"], cfg["bits"]
-    src = lambda first, n: synth.experts(seed, layer, first, n, bits, H, I)
-    slab = upload_experts(src, E + 1, bits, H, I, device=device)
+    group = cfg.get("group", 64)
+    src = lambda first, n: synth.experts(seed, layer, first, n, bits, H, I, group)
+    slab = upload_experts(src, E + 1, bits, H, I, device=device, group=group)
     wr = torch.from_numpy(synth.router(seed, layer, E, H)).to(device)
     bias = None
     if cfg.get("zipf"):
         bias = torch.from_numpy(synth.zipf_bias(E, cfg["zipf"])).to(device)
-    return DeviceLayer(H, I, E, K, bits, slab, wr, bias)
+    return DeviceLayer(H, I, E, K, bits, slab, wr, bias, group=group)
 
 
 FP32_FLOOR = 2.0 ** -126   # smallest normal fp32: y is delivered in fp32
@@ -72,9 +73,10 @@ def oracle_layer(cfg, seed, layer, x, shared_weight=1.0, parallel=False):
     x = np.atleast_2d(np.asarray(x, np.float32))
     Wr, prior, lg, sel = oracle_route(cfg, seed, layer, x)
     need = sorted({int(e) for s in sel for e in s[0]} | {cfg["E"]})
-    experts = {e: synth.experts(seed, layer, e, 1, cfg["bits"], cfg["H"], cfg["I"]) for e in need}
+    group = cfg.get("group", 64)
+    experts = {e: synth.experts(seed, layer, e, 1, cfg["bits"], cfg["H"], cfg["I"], group) for e in need}
     return oracle.layer_decode(cfg["bits"], cfg["H"], cfg["I"], cfg["E"], cfg["K"], x, Wr, experts, prior=prior,
-                               shared_weight=shared_weight, parallel=parallel)
+                               shared_weight=shared_weight, group=group, parallel=parallel)
 
 
 def mfma_tiles(idx, E, info):

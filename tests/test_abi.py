@@ -42,6 +42,22 @@ def test_record_bytes_closed_form_and_page_figures(golden_dir):
     assert moe.record_bytes(4, 4096, 1000) == 0
 
 
+@pytest.mark.parametrize("group", [128, 256])
+def test_record_bytes_larger_groups(group):
+    """Groups of 128 and 256 weights: the codes as before, one (scale, bias) pair of bf16 per
+    group (gate and up rows: H / group pairs each; down rows: I / group)."""
+    for bits in (4, 2):
+        codes = 3 * 4096 * 1024 * bits // 8
+        assert moe.record_bytes(bits, 4096, 1024, group) == codes + 3 * 4096 * 1024 // group * 4
+    assert moe.record_bytes(4, 4096, 1024, 128) == 6_291_456 + 393_216
+    assert moe.record_bytes(4, 4096 + 64, 1024, 128) == 0   # H not a multiple of the group
+    assert moe.record_bytes(4, 4096, 1024 + 128, 256) == 0  # I not a multiple of the group
+    for bad in (32, 96, 192, 512):
+        assert moe.record_bytes(4, 4096, 1024, bad) == 0
+    rc = moe.lib().moe_expert_ranges(4, 4096, 1024, 32, 1 << 20, 1, 1 << 21, None)
+    assert rc == moe.MOE_EUNSUPPORTED and "group" in moe.last_error()
+
+
 def _desc(**kw):
     d = dict(H=512, I=128, E=16, K=4, bits=4, experts=1 << 20, w_router=1 << 21)
     d.update(kw)
