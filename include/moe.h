@@ -16,8 +16,8 @@
  * 4-bit or 2-bit codes with a per-group scale and bias ([LLMAPIS] sections
  * 为什么值得关注 and 深度分析); the router stays at full precision
  * ([CLAUDAY]).  Readings this library fixes where the pages are silent:
- * w = s*q + b with unsigned q, bf16 s and b per 64 consecutive weights along
- * each row's input dimension; SwiGLU experts h = silu(Wg x) * (Wu x),
+ * w = s*q + b with unsigned q, bf16 s and b per group of 64 (or 128, 256)
+ * consecutive weights along each row's input dimension; SwiGLU experts h = silu(Wg x) * (Wu x),
  * y_e = Wd h; softmax over all E, keep the top K (ties to the lower id,
  * output in rank order), renormalize; y = sum_k w_k y_{idx_k} +
  * shared_weight * y_shared.

@@ -1,14 +1,15 @@
 // common.h - packed expert layout and device helpers shared by the gfx950 kernels.
 //
-// Packed record of one expert (bits = 4 or 2, G_h = H/64, G_i = I/64 groups per row),
+// Packed record of one expert (bits = 4 or 2, G_h = H/64, G_i = I/64 units of 64
+// columns per row; S_h = H/group, S_i = I/group scale/bias groups per row),
 // byte-for-byte the same size as the canonical expert:
 //   [gu_codes]  I row pairs, each [gate row codes (H*bits/8 B) | up row codes (H*bits/8 B)]
-//   [gu_sb]     I x G_h entries of 8 B: bf16 (gate scale, gate bias, up scale, up bias)
+//   [gu_sb]     I x S_h entries of 8 B: bf16 (gate scale, gate bias, up scale, up bias)
 //   [d_codes]   H rows of I*bits/8 B, in panels of 16 rows (d_chunk_off below)
-//   [d_sb]      H x G_i entries of 4 B: bf16 (scale, bias)
-// Inside a row the codes of group g are split into 16-byte chunks; chunk j of
-// group g sits at chunk position j*G + g (4-bit: 2 chunks per group, 2-bit: 1),
-// so that 64 lanes working on 64 consecutive groups issue fully contiguous
+//   [d_sb]      H x S_i entries of 4 B: bf16 (scale, bias)
+// Inside a row the codes of unit g are split into 16-byte chunks; chunk j of
+// unit g sits at chunk position j*G + g (4-bit: 2 chunks per unit, 2-bit: 1),
+// so that 64 lanes working on 64 consecutive units issue fully contiguous
 // 16-byte loads.  A gate/up row's chunks are contiguous.  The down rows are
 // stored in panels of 16 rows: each row's chunks are cut into units of 4 chunks
 // (64 bytes), and unit u of the panel's 16 rows is stored as 16 consecutive runs,
@@ -21,7 +22,7 @@
 // fp16 pattern of 1024 turns two codes into the fp16 pair (1024 + t*q_a, 1024 + t*q_b)
 // with t a power of two, ready for v_dot2 against an fp16 pair of activations.
 //
-// Activation operand ("prep") of a vector v split in groups of 64:
+// Activation operand ("prep") of a vector v split in units ("groups") of 64 columns:
 //   q  [8][G] uint4: 32 fp16 pairs per group; pair p of group g is element p%4
 //                    of uint4 (p/4)*G + g.  Pair p holds v_h at columns
 //                    4-bit: (8*(p/4) + p%4, +4);  2-bit: (16*(p/8) + p%8, +8),

@@ -11,7 +11,7 @@
 //   k_router  logits (fp32 products accumulated in fp64); also preps the token:
 //             fp16 pairs + per-group stats, the operand of the folded dequant
 //             (scale*x and bias*x per group, the FMA rearrangement described in
-//             [LLMAPIS] section 深度分析, applied per group of 64)
+//             [LLMAPIS] section 深度分析, applied per 64-column unit)
 //   k_gateup  softmax / top-K per wave, then the fused gate/up dequant-GEMV +
 //             SiLU*mul over the K routed + shared experts
 //   k_down    down dequant-GEMV + router-weighted combine in one pass (no atomics)
