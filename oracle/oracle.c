@@ -55,7 +55,9 @@
 
 /* Element c of a canonically packed row: 4-bit: element 2j is the low nibble
  * of byte j and 2j+1 the high nibble; 2-bit: element 4j+t sits at bits
- * 2t..2t+1 of byte j. */
+ * 2t..2t+1 of byte j; 3-bit: the row is one little-endian bit string and
+ * element c holds its bits 3c..3c+2, lowest bit first (a code may straddle two
+ * bytes). */
 int oracle_code_at(const uint8_t* row, int bits, long c)
 {
     if (bits == 4) {
@@ -65,6 +67,14 @@ int oracle_code_at(const uint8_t* row, int bits, long c)
     if (bits == 2) {
         uint8_t byte = row[c / 4];
         return (byte >> (2 * (c % 4))) & 0x03;
+    }
+    if (bits == 3) {
+        int q = 0;
+        for (int t = 0; t < 3; ++t) {  /* bit 3c + t of the string */
+            long bit = 3 * c + t;
+            q |= ((row[bit / 8] >> (bit % 8)) & 1) << t;
+        }
+        return q;
     }
     return -1;
 }

@@ -232,7 +232,11 @@ int main(void)
     const uint8_t b21 = 0x21, be4 = 0xE4;
     EXPECT(oracle_code_at(&b21, 4, 0) == 1 && oracle_code_at(&b21, 4, 1) == 2, "nibbles of 0x21");
     for (int t = 0; t < 4; ++t) EXPECT(oracle_code_at(&be4, 2, t) == t, "crumb %d of 0xE4", t);
-    EXPECT(oracle_code_at(&b21, 3, 0) == -1, "bits=3 rejected");
+    {   /* 3-bit: one bit string, codes straddling bytes (codes 0..7 in three bytes) */
+        const uint8_t r3[3] = {0x88, 0xC6, 0xFA};
+        for (int c = 0; c < 8; ++c) EXPECT(oracle_code_at(r3, 3, c) == c, "3-bit code %d", c);
+    }
+    EXPECT(oracle_code_at(&b21, 5, 0) == -1, "bits=5 rejected");
     EXPECT(oracle_bf16_to_double(0x3F00) == 0.5 && oracle_bf16_to_double(0xBF80) == -1.0, "bf16 widening");
     EXPECT(oracle_bf16_round(1.0 + 1.0 / 256) == 0x3F80 && oracle_bf16_round(1.0 + 3.0 / 256) == 0x3F82,
            "bf16 rounding ties to even");

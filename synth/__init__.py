@@ -9,7 +9,9 @@ consume the same bytes without sharing any of the method's code.
 Canonical expert format (one expert; groups of ``group`` run along each row):
   gate_codes [I][H*bits/8], up_codes [I][H*bits/8], down_codes [H][I*bits/8]
   (4-bit: element 2j is the low nibble of byte j; 2-bit: element 4j+t sits at
-  bits 2t..2t+1 of byte j), scales/biases: bf16 bit patterns, concatenated
+  bits 2t..2t+1 of byte j; 3-bit: a row is one little-endian bit string with
+  element c at bits 3c..3c+2; the codes are uniform random bits for any width),
+  scales/biases: bf16 bit patterns, concatenated
   gate [I][H/group] | up [I][H/group] | down [H][I/group].
 """
 import ctypes

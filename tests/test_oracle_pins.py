@@ -22,9 +22,18 @@ H_T, I_T, E_T = 128, 64, 16   # tiny shapes that still span two groups per gate/
 # ---------- independent canonical encoder / decoder (test-side only) ----------
 
 def encode_codes(q, bits):
-    """Pack an integer matrix [rows][cols] into canonical bytes (low bits = lower element)."""
+    """Pack an integer matrix [rows][cols] into canonical bytes (low bits = lower element;
+    3-bit: each row as one little-endian bit string, element c at bits 3c..3c+2)."""
     q = np.asarray(q, dtype=np.uint8)
     rows, cols = q.shape
+    if bits == 3:
+        out = np.zeros((rows, cols * 3 // 8), np.uint8)
+        for r in range(rows):
+            acc = 0
+            for c in range(cols):
+                acc |= int(q[r, c]) << (3 * c)
+            out[r] = np.frombuffer(acc.to_bytes(cols * 3 // 8, "little"), np.uint8)
+        return out
     per = 8 // bits
     out = np.zeros((rows, cols // per), np.uint8)
     for t in range(per):
@@ -75,6 +84,15 @@ def test_byte_unpack_handbuilt(golden_dir):
         assert got == case["codes"], case
 
 
+def test_byte_unpack_3bit_handbuilt(golden_dir):
+    """3-bit codes straddle bytes: hand-derived rows of three bytes decode to their eight codes."""
+    g = json.load(open(os.path.join(golden_dir, "dequant_handbuilt.json")))
+    for case in g["byte_unpack_3bit"]["cases"]:
+        row = np.array([int(x, 16) for x in case["bytes"]], np.uint8)
+        assert [oracle.code_at(row, 3, c) for c in range(8)] == case["codes"], case
+        np.testing.assert_array_equal(encode_codes(np.array([case["codes"]]), 3)[0], row)
+
+
 def test_dequant_handbuilt(golden_dir):
     g = json.load(open(os.path.join(golden_dir, "dequant_handbuilt.json")))
     for case in g["cases"]:
@@ -95,7 +113,7 @@ def test_bf16_widening_exact():
     assert oracle.bf16_to_double(0x7F7F) == (2 - 2 ** -7) * 2.0 ** 127
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_dequant_group_and_row_indexing(bits):
     """Independent encoding of known (q, s, b): catches row/col/group mix-ups."""
     rng = np.random.default_rng(7 + bits)
@@ -203,7 +221,7 @@ def test_ffn_constant_weights_closed_form():
     np.testing.assert_allclose(y, I * h_ref, rtol=1e-14)
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_ffn_matches_independent_dense(bits):
     """Known (q, s, b) -> dense numpy SwiGLU vs the oracle reading the encoded bytes."""
     rng = np.random.default_rng(21 + bits)
