@@ -27,7 +27,7 @@ The float64 oracle is timed on the host cores on a small sample of tokens
 (cpu_baseline).  Each workload's first step is checked against the oracle
 before timing; a mismatch reports no throughput.
 
-    python bench.py [--steps K] [--warmup W] [--workload layer|layer2|layer_g128|requant|batched|batched2|stack]
+    python bench.py [--steps K] [--warmup W] [--workload layer|layer2|layer3|layer_g128|requant|batched|batched2|stack]
 """
 import argparse
 import ctypes
@@ -55,6 +55,8 @@ WORKLOADS = {
     "requant": dict(H=4096, I=1024, E=512, K=4, bits=2, B=1, layers=1, zipf=None, seed=1001, requant=True),
     # the layer workload's shape with one scale and bias per 128 weights
     "layer_g128": dict(H=4096, I=1024, E=512, K=4, bits=4, B=1, layers=1, zipf=None, seed=1005, group=128),
+    # the layer workload's shape with 3-bit codes
+    "layer3": dict(H=4096, I=1024, E=512, K=4, bits=3, B=1, layers=1, zipf=None, seed=1006),
 }
 RMS_EPS = 1e-6
 
@@ -757,7 +759,7 @@ def main():
     if not args.no_configs:
         # every other workload at its own shape, fewer steps, same measurement
         extra = {"layer2": dict(steps=100, warmup=10), "requant": dict(steps=100, warmup=10),
-                 "layer_g128": dict(steps=100, warmup=10),
+                 "layer_g128": dict(steps=100, warmup=10), "layer3": dict(steps=100, warmup=10),
                  "batched": dict(steps=40, warmup=5), "batched2": dict(steps=40, warmup=5),
                  "stack": dict(steps=10, warmup=2, distinct=4),
                  "layer": dict(steps=100, warmup=10)}

@@ -13,7 +13,7 @@
  * token (E = 512, K = 4, plus one always-on shared expert), the active experts'
  * quantized weights are read and dequantized, each expert's FFN is computed,
  * and the results are combined with the routing weights.  Expert weights are
- * 4-bit or 2-bit codes with a per-group scale and bias ([LLMAPIS] sections
+ * 4-bit or 2-bit codes (3-bit also built) with a per-group scale and bias ([LLMAPIS] sections
  * 为什么值得关注 and 深度分析); the router stays at full precision
  * ([CLAUDAY]).  Readings this library fixes where the pages are silent:
  * w = s*q + b with unsigned q, bf16 s and b per group of 64 (or 128, 256)
@@ -53,7 +53,7 @@ extern "C" {
 
 #define MOE_OK 0
 #define MOE_EINVAL (-1)        /* null / misaligned pointer, bad shape, workspace too small */
-#define MOE_EUNSUPPORTED (-2)  /* bits not 2 or 4, group not 64/128/256, K > 32, E > 1024, B > 256, H > 65536, I > 8192 */
+#define MOE_EUNSUPPORTED (-2)  /* bits not 2, 3 or 4, group not 64/128/256, K > 32, E > 1024, B > 256, H > 65536, I > 8192 */
 #define MOE_EHIP (-3)          /* the HIP runtime refused a launch */
 
 #define MOE_MAX_K 32
@@ -63,7 +63,8 @@ extern "C" {
 /*
  * One MoE layer.  All pointers are device memory owned by the caller.
  *   H: hidden size, I: expert intermediate size (both multiples of the group).
- *   E: routed experts, K: experts kept per token, bits: 4 or 2, group: weights per
+ *   E: routed experts, K: experts kept per token, bits: 4, 3 or 2 (3-bit: I a
+ *   multiple of 128; a 3-bit batch runs token by token), group: weights per
  *   scale/bias group along each row, 64, 128 or 256 (the pages give per-group
  *   scales and biases, [LLMAPIS] section 深度分析, without a size).
  *   experts: packed slab of E + 1 records written by moe_pack_experts, the
@@ -118,9 +119,10 @@ size_t moe_route_workspace_bytes(int B, int E, int K);
  * Canonical inputs (device, stacked over the n experts):
  *   gate_codes, up_codes: uint8 [n][I][H*bits/8]; down_codes: uint8 [n][H][I*bits/8]
  *     (4-bit: element 2j is the low nibble of byte j; 2-bit: element 4j+t sits
- *     at bits 2t..2t+1 of byte j);
+ *     at bits 2t..2t+1 of byte j; 3-bit: each row is one little-endian bit
+ *     string with element c at bits 3c..3c+2);
  *   scales_bf16, biases_bf16: uint16 bf16 bit patterns [n][ng], per expert
- *     concatenated gate [I][H/64] | up [I][H/64] | down [H][I/64].
+ *     concatenated gate [I][H/group] | up [I][H/group] | down [H][I/group].
  * The record layout is private to the library ([LLMAPIS] section 深度分析:
  * each expert is fetched as one unit; here one contiguous record).
  * slab_out must hold at least (first_expert + n_experts) records.
@@ -225,6 +227,9 @@ int moe_route_topk(const float* x, int B, const float* w_router, const float* lo
 int moe_expert_ffn_q4(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx,
                       const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
 int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx,
+                      const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
+/* 3-bit experts (desc->bits == 3; a batch runs token by token). */
+int moe_expert_ffn_q3(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx,
                       const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
 
 /*

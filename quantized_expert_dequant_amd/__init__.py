@@ -76,6 +76,7 @@ def lib():
             "moe_route_topk": (i32, [vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp, sz, vp]),
             "moe_expert_ffn_q4": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_expert_ffn_q2": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
+            "moe_expert_ffn_q3": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_layer_decode": (i32, [dp, vp, i32, vp, vp, vp, vp, sz, vp]),
             "moe_layer_decode_noalloc": (i32, [dp, vp, i32, vp, vp, vp, vp]),
             "moe_group_tokens": (i32, [vp, i32, i32, i32, vp, vp, vp, vp]),
@@ -190,7 +191,7 @@ def route_topk(x, B, w_router, logit_bias, H, E, K, idx_out, w_out, ws, ws_bytes
 
 
 def expert_ffn(desc, x, B, idx, w, y_out, ws, ws_bytes, stream=None):
-    fn = lib().moe_expert_ffn_q4 if desc.bits == 4 else lib().moe_expert_ffn_q2
+    fn = {4: lib().moe_expert_ffn_q4, 3: lib().moe_expert_ffn_q3}.get(desc.bits, lib().moe_expert_ffn_q2)
     return _check(fn(ctypes.byref(desc), _p(x), B, _p(idx), _p(w), _p(y_out), _p(ws), ws_bytes, _stream(stream)))
 
 
@@ -201,6 +202,11 @@ def expert_ffn_q4(desc, x, B, idx, w, y_out, ws, ws_bytes, stream=None):
 
 def expert_ffn_q2(desc, x, B, idx, w, y_out, ws, ws_bytes, stream=None):
     return _check(lib().moe_expert_ffn_q2(ctypes.byref(desc), _p(x), B, _p(idx), _p(w), _p(y_out), _p(ws),
+                                          ws_bytes, _stream(stream)))
+
+
+def expert_ffn_q3(desc, x, B, idx, w, y_out, ws, ws_bytes, stream=None):
+    return _check(lib().moe_expert_ffn_q3(ctypes.byref(desc), _p(x), B, _p(idx), _p(w), _p(y_out), _p(ws),
                                           ws_bytes, _stream(stream)))
 
 

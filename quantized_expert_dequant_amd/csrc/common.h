@@ -25,12 +25,12 @@
 // Activation operand ("prep") of a vector v split in units ("groups") of 64 columns:
 //   q  [8][G] uint4: 32 fp16 pairs per group; pair p of group g is element p%4
 //                    of uint4 (p/4)*G + g.  Pair p holds v_h at columns
-//                    4-bit: (8*(p/4) + p%4, +4);  2-bit: (16*(p/8) + p%8, +8),
+//                    4-bit: (8*(p/4) + p%4, +4);  2- and 3-bit: (16*(p/8) + p%8, +8),
 //                    where v_h = fp16(v * 2^-e_g) with a power-of-two per-group scale.
 //   st [G]    float4: (C_g, S_g, 2^e_g, 0) with S_g = sum of v over the group and
 //                    C_g = 1024 * sum_p (v_h pair sum) / t(p) + mid * sum_c (v_h - v 2^-e_g):
 //                    the offset the fp16 code patterns add to the dot products, plus
-//                    the code midpoint (7.5 or 1.5) times the group's rounding error.
+//                    the code midpoint (7.5, 3.5 or 1.5) times the group's rounding error.
 // Per group and row:  sum_c (s*q_c + b) v_c ~= s * 2^e_g * (sum_t acc_t / t - C_g) + b * S_g,
 // where sum_t acc_t / t - C_g = sum_c (q_c - mid) v_h,c + mid * sum_c v_c 2^-e_g: the
 // fp16 rounding of v only meets the zero-mean part of the codes.
@@ -96,7 +96,7 @@ __device__ inline float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0
 // Opaque register constants: keeps the masks in SGPRs and the fp16 pattern in a
 // VGPR so each code pair costs a single v_and_or_b32 (gfx9 VOP3 takes no literals).
 struct Masks {
-    uint32_t magic, m4a, m4b, m2[5];
+    uint32_t magic, m4a, m4b, m2[5], m3[4];
 };
 
 __device__ inline Masks load_masks()
@@ -110,6 +110,10 @@ __device__ inline Masks load_masks()
     asm volatile("s_mov_b32 %0, 0x300030" : "=s"(m.m2[2]));
     asm volatile("s_mov_b32 %0, 0xc000c0" : "=s"(m.m2[3]));
     asm volatile("s_mov_b32 %0, 0x3000300" : "=s"(m.m2[4]));
+    asm volatile("s_mov_b32 %0, 0x40004" : "=s"(m.m3[0]));
+    asm volatile("s_mov_b32 %0, 0x100010" : "=s"(m.m3[1]));
+    asm volatile("s_mov_b32 %0, 0x400040" : "=s"(m.m3[2]));
+    asm volatile("s_mov_b32 %0, 0x1000100" : "=s"(m.m3[3]));
     return m;
 }
 
@@ -160,10 +164,42 @@ __device__ inline float group_dot_q2(const Masks& M, uint4 c0, const uint4* xp)
     return r + a1;
 }
 
+// 3-bit: one unit = a 16-byte chunk of the codes' low 2 bits (the 2-bit chunk
+// order) and two dwords of their high bits, arranged when packed so that the
+// dword hi[d / 2], rotated right by 8 for odd d, holds the high bits of dword d's
+// code pairs (c, c + 8) at bits (2k + 2, 2k + 18) for pair field k = c % 4 of the
+// dword itself and at bits (2k + 3, 2k + 19) for the fields of the dword shifted
+// right by 8.  OR-ing them in beside the low field gives the pair
+// (1024 + t q_a, 1024 + t q_b) with t = 4^k <= 64, in the fp16 mantissa.
+__device__ inline float group_dot_q3(const Masks& M, uint4 c0, uint2 hi, const uint4* xp)
+{
+    const uint32_t w[4] = {c0.x, c0.y, c0.z, c0.w};
+    float a1 = 0.f, a4 = 0.f, a16 = 0.f, a64 = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t v = w[d], v8 = v >> 8;
+        const uint32_t W = d < 2 ? hi.x : hi.y;
+        const uint32_t S = (d & 1) ? __builtin_amdgcn_alignbit(W, W, 8) : W, S1 = S >> 1;
+        const uint4 x0 = xp[2 * d], x1 = xp[2 * d + 1];
+        a1 = dot2((v & M.m2[0]) | M.magic | (S & M.m3[0]), x0.x, a1);
+        a4 = dot2((v & M.m2[1]) | M.magic | (S & M.m3[1]), x0.y, a4);
+        a16 = dot2((v & M.m2[2]) | M.magic | (S & M.m3[2]), x0.z, a16);
+        a64 = dot2((v & M.m2[3]) | M.magic | (S & M.m3[3]), x0.w, a64);
+        a1 = dot2((v8 & M.m2[0]) | M.magic | (S1 & M.m3[0]), x1.x, a1);
+        a4 = dot2((v8 & M.m2[1]) | M.magic | (S1 & M.m3[1]), x1.y, a4);
+        a16 = dot2((v8 & M.m2[2]) | M.magic | (S1 & M.m3[2]), x1.z, a16);
+        a64 = dot2((v8 & M.m2[3]) | M.magic | (S1 & M.m3[3]), x1.w, a64);
+    }
+    float r = fmaf(a64, 1.f / 64.f, a16 * (1.f / 16.f));
+    r = fmaf(a4, 0.25f, r);
+    return r + a1;
+}
+
 // divisor t of pair p (see the prep layout above)
 __device__ inline float pair_class_inv(int bits, int p)
 {
     if (bits == 4) return (p & 1) ? 0.0625f : 1.f;
+    if (bits == 3) return 1.f / (float)(1 << (2 * (p & 3)));
     switch (p & 7) {
     case 0: case 5: return 1.f;
     case 1: case 6: return 0.25f;
@@ -323,7 +359,7 @@ __device__ inline void prep_group(const float* __restrict__ v, int G, int vec, i
     // midpoint times the group's fp16 rounding error, so that the kernels compute
     // sum (q - mid) v_h + mid * sum v: the rounding errors of v then meet only
     // zero-mean code offsets and do not add up coherently across rows.
-    constexpr float mid = BITS == 4 ? 7.5f : 1.5f;
+    constexpr float mid = BITS == 4 ? 7.5f : (BITS == 3 ? 3.5f : 1.5f);
     const float off = wave_sum((float)vh * pair_class_inv(BITS, p));
     const float rnd = wave_sum((float)vh - vs);  // exact per lane
     const float C = fmaf(off, 1024.f, mid * rnd);

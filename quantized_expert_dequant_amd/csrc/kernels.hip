@@ -26,6 +26,23 @@
 namespace moe {
 
 __device__ inline uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// the 8 bytes of a 3-bit unit's high bits, in .x and .y
+__device__ inline uint4 ld8(const uint8_t* p)
+{
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return make_uint4(v.x, v.y, 0u, 0u);
+}
+
+// sum_t acc_t / t of one row unit (64 columns) against the token operand xp:
+// 4-bit c0, c1 = the unit's two chunks; 3-bit c0 = its low-bit chunk, c1.xy its
+// high bits; 2-bit c0 = its chunk
+template <int BITS>
+__device__ inline float group_dot(const Masks& M, uint4 c0, uint4 c1, const uint4* xp)
+{
+    if constexpr (BITS == 4) return group_dot_q4(M, c0, c1, xp);
+    else if constexpr (BITS == 3) return group_dot_q3(M, c0, make_uint2(c1.x, c1.y), xp);
+    else return group_dot_q2(M, c0, xp);
+}
 
 // ----------------------------------------------------------------------------
 // pack: canonical -> packed record
@@ -84,9 +101,98 @@ __global__ __launch_bounds__(256) void k_pack(Layout L, const uint8_t* __restric
     }
 }
 
+// 3-bit: the 24 canonical bytes of one 64-column unit (a little-endian bit string,
+// code c at bits 3c..3c+2) -> the unit's low-bit chunk (2-bit chunk order: code c at
+// bits 2(c % 16) of dword c / 16) and its two high-bit dwords (the order group_dot_q3
+// reads: dword d's code pairs (c, c + 8), c % 16 = i < 8, at bits (2i + 2, 2i + 18)
+// for i < 4 and (2i - 5, 2i + 11) for i >= 4; odd d rotated left by 8 beside d - 1).
+__device__ inline void pack_unit3(const uint8_t* __restrict__ src, uint4& lo, uint2& hi)
+{
+    uint32_t lw[4] = {0u, 0u, 0u, 0u}, S[4] = {0u, 0u, 0u, 0u};
+    for (int c = 0; c < 64; ++c) {
+        const int bit = 3 * c, by = bit >> 3;
+        const uint32_t win = (uint32_t)src[by] | (by + 1 < 24 ? (uint32_t)src[by + 1] << 8 : 0u);
+        const uint32_t q = (win >> (bit & 7)) & 7u;
+        const int d = c >> 4, r = c & 15, i = r & 7, half = r >> 3;
+        lw[d] |= (q & 3u) << (2 * r);
+        const int pos = (i < 4 ? 2 * i + 2 : 2 * (i - 4) + 3) + 16 * half;
+        S[d] |= (q >> 2) << pos;
+    }
+    lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    hi = make_uint2(S[0] | ((S[1] << 8) | (S[1] >> 24)), S[2] | ((S[3] << 8) | (S[3] >> 24)));
+}
+
+// byte offsets in a record of unit g's low-bit chunk and high-bit dwords: gate/up row r
+// of matrix m (0 gate, 1 up) is [G_h low chunks | G_h x 8 bytes of high bits]; a down
+// row is G_i low chunks then the high bits as chunks G_i + g / 2, through the panel order
+__host__ __device__ inline long long q3_gu_lo(const Layout& L, int r, int m, int g)
+{
+    return (long long)r * 2 * L.hb + m * L.hb + 16LL * g;
+}
+__host__ __device__ inline long long q3_gu_hi(const Layout& L, int r, int m, int g)
+{
+    return (long long)r * 2 * L.hb + m * L.hb + 16LL * L.Gh + 8LL * g;
+}
+__host__ __device__ inline long long q3_d_lo(const Layout& L, int r, int g) { return L.off_d_codes + d_chunk_off(L, r, g); }
+__host__ __device__ inline long long q3_d_hi(const Layout& L, int r, int g)
+{
+    return L.off_d_codes + d_chunk_off(L, r, L.Gi + (g >> 1)) + 8 * (g & 1);
+}
+
+__global__ __launch_bounds__(256) void k_pack3(Layout L, const uint8_t* __restrict__ gate,
+                                               const uint8_t* __restrict__ up, const uint8_t* __restrict__ down,
+                                               const uint16_t* __restrict__ scales,
+                                               const uint16_t* __restrict__ biases, uint8_t* __restrict__ slab,
+                                               int first)
+{
+    const int j = blockIdx.y;
+    const long long cb = (long long)L.I * L.hb;
+    const long long ng = 2LL * L.I * L.Sh + (long long)L.H * L.Si;
+    const long long n_gu_units = 2LL * L.I * L.Gh, n_gu_sb = (long long)L.I * L.Sh;
+    const long long n_d_units = (long long)L.H * L.Gi, n_d_sb = (long long)L.H * L.Si;
+    const long long total = n_gu_units + n_gu_sb + n_d_units + n_d_sb;
+    uint8_t* rec = slab + (long long)(first + j) * L.record;
+    const uint16_t* sc = scales + j * ng;
+    const uint16_t* bi = biases + j * ng;
+    for (long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (long long)gridDim.x * blockDim.x) {
+        uint4 lo;
+        uint2 hi;
+        if (t < n_gu_units) {
+            const int r = (int)(t / (2 * L.Gh)), rem = (int)(t - (long long)r * 2 * L.Gh);
+            const int m = rem / L.Gh, g = rem - m * L.Gh;
+            pack_unit3((m == 0 ? gate : up) + j * cb + (long long)r * L.hb + 24LL * g, lo, hi);
+            *reinterpret_cast<uint4*>(rec + q3_gu_lo(L, r, m, g)) = lo;
+            *reinterpret_cast<uint2*>(rec + q3_gu_hi(L, r, m, g)) = hi;
+        } else if (t < n_gu_units + n_gu_sb) {
+            const long long i = t - n_gu_units;  // r * Sh + group
+            const long long nu = (long long)L.I * L.Sh;
+            *reinterpret_cast<ushort4*>(rec + L.off_gu_sb + i * 8) = make_ushort4(sc[i], bi[i], sc[nu + i], bi[nu + i]);
+        } else if (t < n_gu_units + n_gu_sb + n_d_units) {
+            const long long u = t - n_gu_units - n_gu_sb;
+            const int r = (int)(u / L.Gi), g = (int)(u - (long long)r * L.Gi);
+            pack_unit3(down + j * ((long long)L.H * L.ib) + (long long)r * L.ib + 24LL * g, lo, hi);
+            *reinterpret_cast<uint4*>(rec + q3_d_lo(L, r, g)) = lo;
+            *reinterpret_cast<uint2*>(rec + q3_d_hi(L, r, g)) = hi;
+        } else {
+            const long long i = t - n_gu_units - n_gu_sb - n_d_units;  // r * Si + group
+            const long long o = 2LL * L.I * L.Sh;
+            *reinterpret_cast<ushort2*>(rec + L.off_d_sb + i * 4) = make_ushort2(sc[o + i], bi[o + i]);
+        }
+    }
+}
+
 void launch_pack(const Layout& L, int n, const uint8_t* gate, const uint8_t* up, const uint8_t* down,
                  const uint16_t* scales, const uint16_t* biases, void* slab, int first, hipStream_t s)
 {
+    if (L.bits == 3) {
+        const long long total = 2LL * L.I * L.Gh + (long long)L.I * L.Sh + (long long)L.H * L.Gi + (long long)L.H * L.Si;
+        long long blocks = (total + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        hipLaunchKernelGGL(k_pack3, dim3((unsigned)blocks, n), dim3(256), 0, s, L, gate, up, down, scales, biases,
+                           (uint8_t*)slab, first);
+        return;
+    }
     const long long total = 2LL * L.I * (L.hb / 16) + (long long)L.I * L.Sh + (long long)L.H * (L.ib / 16) +
                             (long long)L.H * L.Si;
     long long blocks = (total + 255) / 256;
@@ -113,6 +219,17 @@ __device__ inline int chunk_code(const uint8_t* chunk, int bits, int k)
     return (chunk[k >> 2] >> ((k & 3) * 2)) & 3;
 }
 
+// 3-bit code cc (0..63) of a unit from its low-bit chunk and high-bit dwords
+__device__ inline int q3_code(const uint8_t* lo, const uint8_t* hi, int cc)
+{
+    const int d = cc >> 4, r = cc & 15, i = r & 7, half = r >> 3;
+    const uint32_t lw = reinterpret_cast<const uint32_t*>(lo)[d];
+    uint32_t S = reinterpret_cast<const uint32_t*>(hi)[d >> 1];
+    if (d & 1) S = (S >> 8) | (S << 24);
+    const int pos = (i < 4 ? 2 * i + 2 : 2 * (i - 4) + 3) + 16 * half;
+    return (int)(((lw >> (2 * r)) & 3u) | (((S >> pos) & 1u) << 2));
+}
+
 __global__ __launch_bounds__(256) void k_dequant(Layout L, const uint8_t* __restrict__ rec,
                                                  float* __restrict__ W)
 {
@@ -126,19 +243,27 @@ __global__ __launch_bounds__(256) void k_dequant(Layout L, const uint8_t* __rest
             const int m = (int)(t / n_gu);
             const long long i = t - m * n_gu;
             const int r = (int)(i / L.H), c = (int)(i - (long long)r * L.H);
-            const uint8_t* row = rec + (long long)r * 2 * L.hb + m * L.hb;
-            int k;
-            const int P = packed_pos(L.bits, L.Gh, c, k);
-            q = chunk_code(row + (long long)P * 16, L.bits, k);
+            if (L.bits == 3) {
+                q = q3_code(rec + q3_gu_lo(L, r, m, c >> 6), rec + q3_gu_hi(L, r, m, c >> 6), c & 63);
+            } else {
+                const uint8_t* row = rec + (long long)r * 2 * L.hb + m * L.hb;
+                int k;
+                const int P = packed_pos(L.bits, L.Gh, c, k);
+                q = chunk_code(row + (long long)P * 16, L.bits, k);
+            }
             const uint16_t* sb = reinterpret_cast<const uint16_t*>(rec + L.off_gu_sb + ((long long)r * L.Sh + (c >> (6 + L.gs))) * 8);
             s = __uint_as_float((uint32_t)sb[2 * m] << 16);
             b = __uint_as_float((uint32_t)sb[2 * m + 1] << 16);
         } else {
             const long long i = t - 2 * n_gu;
             const int r = (int)(i / L.I), c = (int)(i - (long long)r * L.I);
-            int k;
-            const int P = packed_pos(L.bits, L.Gi, c, k);
-            q = chunk_code(rec + L.off_d_codes + d_chunk_off(L, r, P), L.bits, k);
+            if (L.bits == 3) {
+                q = q3_code(rec + q3_d_lo(L, r, c >> 6), rec + q3_d_hi(L, r, c >> 6), c & 63);
+            } else {
+                int k;
+                const int P = packed_pos(L.bits, L.Gi, c, k);
+                q = chunk_code(rec + L.off_d_codes + d_chunk_off(L, r, P), L.bits, k);
+            }
             const uint16_t* sb = reinterpret_cast<const uint16_t*>(rec + L.off_d_sb + ((long long)r * L.Si + (c >> (6 + L.gs))) * 4);
             s = __uint_as_float((uint32_t)sb[0] << 16);
             b = __uint_as_float((uint32_t)sb[1] << 16);
@@ -197,6 +322,8 @@ void launch_prep(int bits, const float* v, int n_vec, int len, uint4* q, float4*
     if (blocks > 1024) blocks = 1024;
     if (bits == 4)
         hipLaunchKernelGGL(k_prep<4>, dim3(blocks), dim3(256), 0, s, v, n_vec, G, q, st);
+    else if (bits == 3)
+        hipLaunchKernelGGL(k_prep<3>, dim3(blocks), dim3(256), 0, s, v, n_vec, G, q, st);
     else
         hipLaunchKernelGGL(k_prep<2>, dim3(blocks), dim3(256), 0, s, v, n_vec, G, q, st);
 }
@@ -317,6 +444,9 @@ void launch_router(int bits, const float* x, int B, const float* W, const float*
     if (bits == 2)
         hipExtLaunchKernelGGL(k_router<2>, dim3(blocks), dim3(64 * rw), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
                               H, E, logits, xq, xst, norm_eps, rblocks);
+    else if (bits == 3)
+        hipExtLaunchKernelGGL(k_router<3>, dim3(blocks), dim3(64 * rw), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
+                              H, E, logits, xq, xst, norm_eps, rblocks);
     else
         hipExtLaunchKernelGGL(k_router<4>, dim3(blocks), dim3(64 * rw), 0, s, t.start, t.stop, 0, x, B, prepB, W, bias,
                               H, E, logits, xq, xst, norm_eps, rblocks);
@@ -415,6 +545,9 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
                 if (BITS == 4) {
                     R[p].g1 = ld16(base + (G + g) * 16);
                     R[p].u1 = ld16(base + L.hb + (G + g) * 16);
+                } else if (BITS == 3) {
+                    R[p].g1 = ld8(base + 16 * G + 8 * g);
+                    R[p].u1 = ld8(base + L.hb + 16 * G + 8 * g);
                 }
                 R[p].sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)r * L.Sh + (g >> L.gs)) * 8);
             }
@@ -471,14 +604,8 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
                 for (int p = 0; p < GU_RPW; ++p) {
                     const int r = row0 + p * RPP;
                     if (i < nr && eid[i] >= 0 && gv && r < L.I) {
-                        float dg, du;
-                        if (BITS == 4) {
-                            dg = group_dot_q4(M, R[i][p].g0, R[i][p].g1, xp);
-                            du = group_dot_q4(M, R[i][p].u0, R[i][p].u1, xp);
-                        } else {
-                            dg = group_dot_q2(M, R[i][p].g0, xp);
-                            du = group_dot_q2(M, R[i][p].u0, xp);
-                        }
+                        const float dg = group_dot<BITS>(M, R[i][p].g0, R[i][p].g1, xp);
+                        const float du = group_dot<BITS>(M, R[i][p].u0, R[i][p].u1, xp);
                         const uint2 sb = R[i][p].sb;
                         gacc[i][p] = fmaf(bf16_lo(sb.x) * st.z, dg - st.x, fmaf(bf16_hi(sb.x), st.y, gacc[i][p]));
                         uacc[i][p] = fmaf(bf16_lo(sb.y) * st.z, du - st.x, fmaf(bf16_hi(sb.y), st.y, uacc[i][p]));
@@ -638,6 +765,7 @@ __global__ __launch_bounds__(256) void k_down(FfnArgs A)
                         const uint8_t* base = rec[s] + L.off_d_codes;
                         c0[s][p] = ld16(base + d_chunk_off(L, r, g));
                         if (BITS == 4) c1[s][p] = ld16(base + d_chunk_off(L, r, G + g));
+                        if (BITS == 3) c1[s][p] = ld8(base + d_chunk_off(L, r, G + (g >> 1)) + 8 * (g & 1));
                         sbv[s][p] = *reinterpret_cast<const uint32_t*>(rec[s] + L.off_d_sb +
                                                                        ((long long)r * L.Si + (g >> L.gs)) * 4);
                     }
@@ -660,8 +788,7 @@ __global__ __launch_bounds__(256) void k_down(FfnArgs A)
                             acc[p] += wt[s];  // NaN for an invalid expert id
                             continue;
                         }
-                        const float d = (BITS == 4) ? group_dot_q4(M, c0[s][p], c1[s][p], xp)
-                                                    : group_dot_q2(M, c0[s][p], xp);
+                        const float d = group_dot<BITS>(M, c0[s][p], c1[s][p], xp);
                         const float part = fmaf(bf16_lo(sbv[s][p]) * st.z, d - st.x, bf16_hi(sbv[s][p]) * st.y);
                         acc[p] = fmaf(wt[s], part, acc[p]);
                     }
@@ -757,6 +884,9 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
         if (BITS == 4) {
             R.g1 = ld16(base + (G + g) * 16);
             R.u1 = ld16(base + L.hb + (G + g) * 16);
+        } else if (BITS == 3) {
+            R.g1 = ld8(base + 16 * G + 8 * g);
+            R.u1 = ld8(base + L.hb + 16 * G + 8 * g);
         }
         R.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)rc * L.Sh + (g >> L.gs)) * 8);
     };
@@ -800,14 +930,8 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
     for (int j = 0; j < 8; ++j) xp[j] = xs[j * G + g];
     const float4 st = __builtin_bit_cast(float4, xs[8 * G + g]);
     // 5. dequant-GEMV of the row's gate and up, SwiGLU, h into the pair-layout order
-    float dg, du;
-    if (BITS == 4) {
-        dg = group_dot_q4(M, R.g0, R.g1, xp);
-        du = group_dot_q4(M, R.u0, R.u1, xp);
-    } else {
-        dg = group_dot_q2(M, R.g0, xp);
-        du = group_dot_q2(M, R.u0, xp);
-    }
+    const float dg = group_dot<BITS>(M, R.g0, R.g1, xp);
+    const float du = group_dot<BITS>(M, R.u0, R.u1, xp);
     float ga = fmaf(bf16_lo(R.sb.x) * st.z, dg - st.x, bf16_hi(R.sb.x) * st.y);
     float ua = fmaf(bf16_lo(R.sb.y) * st.z, du - st.x, bf16_hi(R.sb.y) * st.y);
     ga = lane_group_sum(gv ? ga : 0.f, LPR);
@@ -864,11 +988,14 @@ __global__ __launch_bounds__(64 * DNF_WAVES) void k_down_fast(FfnArgs A)
     // 3. the shared expert's rows need no routing: they go out before the routing returns
     uint4 c0[KS], c1[KS];
     uint32_t sbv[KS];
-    const long long o0 = L.off_d_codes + d_chunk_off(L, rc, g), o1 = L.off_d_codes + d_chunk_off(L, rc, G + g);
+    const long long o0 = L.off_d_codes + d_chunk_off(L, rc, g);
+    const long long o1 = BITS == 3 ? L.off_d_codes + d_chunk_off(L, rc, G + (g >> 1)) + 8 * (g & 1)
+                                   : L.off_d_codes + d_chunk_off(L, rc, G + g);
     auto issue = [&](int k, int e) {
         const uint8_t* rec = A.slab + (long long)e * L.record;
         c0[k] = ld16(rec + o0);
         if (BITS == 4) c1[k] = ld16(rec + o1);
+        if (BITS == 3) c1[k] = ld8(rec + o1);
         sbv[k] = *reinterpret_cast<const uint32_t*>(rec + L.off_d_sb + ((long long)rc * L.Si + (g >> L.gs)) * 4);
     };
     issue(K, A.E);
@@ -898,7 +1025,7 @@ __global__ __launch_bounds__(64 * DNF_WAVES) void k_down_fast(FfnArgs A)
 #pragma unroll
         for (int j = 0; j < 8; ++j) xp[j] = lds[(k * 8 + j) * G + g];
         const float4 sv = __builtin_bit_cast(float4, lst[k * G + g]);
-        const float d = (BITS == 4) ? group_dot_q4(M, c0[k], c1[k], xp) : group_dot_q2(M, c0[k], xp);
+        const float d = group_dot<BITS>(M, c0[k], c1[k], xp);
         const float part = fmaf(bf16_lo(sbv[k]) * sv.z, d - sv.x, bf16_hi(sbv[k]) * sv.y);
         acc = fmaf(wt[k], part, acc);
     }
@@ -970,6 +1097,8 @@ void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4
         const size_t flds = (size_t)KS * 9 * L.Gi * 16;
         if (L.bits == 4)
             launch_fast<4>(KS, logits != nullptr, fg, fd, flds, A, s, t_gateup, t_down);
+        else if (L.bits == 3)
+            launch_fast<3>(KS, logits != nullptr, fg, fd, flds, A, s, t_gateup, t_down);
         else
             launch_fast<2>(KS, logits != nullptr, fg, fd, flds, A, s, t_gateup, t_down);
         return;
@@ -978,6 +1107,9 @@ void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4
     if (L.bits == 4) {
         hipExtLaunchKernelGGL(k_gateup<4>, ggrid, dim3(256), 0, s, t_gateup.start, t_gateup.stop, 0, A);
         hipExtLaunchKernelGGL(k_down<4>, dgrid, dim3(256), lds, s, t_down.start, t_down.stop, 0, A);
+    } else if (L.bits == 3) {
+        hipExtLaunchKernelGGL(k_gateup<3>, ggrid, dim3(256), 0, s, t_gateup.start, t_gateup.stop, 0, A);
+        hipExtLaunchKernelGGL(k_down<3>, dgrid, dim3(256), lds, s, t_down.start, t_down.stop, 0, A);
     } else {
         hipExtLaunchKernelGGL(k_gateup<2>, ggrid, dim3(256), 0, s, t_gateup.start, t_gateup.stop, 0, A);
         hipExtLaunchKernelGGL(k_down<2>, dgrid, dim3(256), lds, s, t_down.start, t_down.stop, 0, A);

@@ -62,12 +62,14 @@ bool misaligned4(const void* p) { return ((uintptr_t)p & 3u) != 0; }
 
 int check_shape(const char* fn, int bits, int H, int I, int group)
 {
-    if (bits != 2 && bits != 4) return fail(MOE_EUNSUPPORTED, "%s: bits=%d (must be 2 or 4)", fn, bits);
+    if (bits != 2 && bits != 3 && bits != 4) return fail(MOE_EUNSUPPORTED, "%s: bits=%d (must be 2, 3 or 4)", fn, bits);
     if (group != 64 && group != 128 && group != 256)
         return fail(MOE_EUNSUPPORTED, "%s: group=%d (must be 64, 128 or 256)", fn, group);
     if (H <= 0 || I <= 0 || H % group || I % group)
         return fail(MOE_EINVAL, "%s: H=%d and I=%d must be positive multiples of the group (%d)", fn, H, I, group);
     if (H > 65536 || I > 8192) return fail(MOE_EUNSUPPORTED, "%s: H=%d > 65536 or I=%d > 8192", fn, H, I);
+    // 3-bit down rows hold their high bits as half chunks, two units to a 16-byte chunk
+    if (bits == 3 && I % 128) return fail(MOE_EINVAL, "%s: 3-bit codes need I=%d to be a multiple of 128", fn, I);
     return MOE_OK;
 }
 
@@ -437,6 +439,12 @@ int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const i
                       float* y_out, void* ws, size_t ws_bytes, void* stream)
 {
     return expert_ffn("moe_expert_ffn_q2", 2, desc, x, B, idx, w, y_out, ws, ws_bytes, stream);
+}
+
+int moe_expert_ffn_q3(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx, const float* w,
+                      float* y_out, void* ws, size_t ws_bytes, void* stream)
+{
+    return expert_ffn("moe_expert_ffn_q3", 3, desc, x, B, idx, w, y_out, ws, ws_bytes, stream);
 }
 
 // norm_eps >= 0 (per-token path only): x is the previous layer's output, renormalized

@@ -38,8 +38,18 @@ def test_record_bytes_closed_form_and_page_figures(golden_dir):
     # the 4-bit figure on the pages (209GB) is ~4% below the closed form; it is not reproduced exactly
     assert 0.9 < pages["total_experts_4bit_gb"]["value"] / (total4 / 1e9) < 1.0
     assert moe.record_bytes(4, 512, 128) == 110_592
-    assert moe.record_bytes(3, 4096, 1024) == 0
+    assert moe.record_bytes(5, 4096, 1024) == 0
     assert moe.record_bytes(4, 4096, 1000) == 0
+
+
+def test_record_bytes_3bit():
+    """3-bit records: 3/8 byte per weight plus the scales and biases (the canonical size);
+    I must be a multiple of 128 (a down row's high bits fill whole 16-byte chunks)."""
+    assert moe.record_bytes(3, 4096, 1024) == 3 * 4096 * 1024 * 3 // 8 + 786_432 == 5_505_024
+    assert moe.record_bytes(3, 512, 128) == 3 * 512 * 128 * 3 // 8 + 3 * 512 * 128 // 64 * 4
+    assert moe.record_bytes(3, 4096, 1024 + 64) == 0
+    rc = moe.lib().moe_expert_ranges(3, 4096, 1024 + 64, 64, 1 << 20, 1, 1 << 21, None)
+    assert rc == moe.MOE_EINVAL and "128" in moe.last_error()
 
 
 @pytest.mark.parametrize("group", [128, 256])
@@ -76,7 +86,7 @@ def test_workspace_sizes():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(bits=3), moe.MOE_EUNSUPPORTED),
+    (dict(bits=5), moe.MOE_EUNSUPPORTED),
     (dict(H=500), moe.MOE_EINVAL),
     (dict(I=100), moe.MOE_EINVAL),
     (dict(K=17), moe.MOE_EINVAL),           # K > E
@@ -106,10 +116,12 @@ def test_layer_decode_rejects_small_workspace_and_nulls():
 
 def test_expert_ffn_bits_must_match_entry_point():
     L = moe.lib()
-    d4, d2 = _desc(bits=4), _desc(bits=2)
+    d4, d3, d2 = _desc(bits=4), _desc(bits=3), _desc(bits=2)
     args = (1 << 22, 1, 1 << 23, 1 << 24, 1 << 25, 1 << 26, 1 << 30, None)
     assert L.moe_expert_ffn_q2(ctypes.byref(d4), *args) == moe.MOE_EINVAL
     assert L.moe_expert_ffn_q4(ctypes.byref(d2), *args) == moe.MOE_EINVAL
+    assert L.moe_expert_ffn_q3(ctypes.byref(d4), *args) == moe.MOE_EINVAL
+    assert L.moe_expert_ffn_q4(ctypes.byref(d3), *args) == moe.MOE_EINVAL
 
 
 def test_other_entry_points_validate():
