@@ -27,7 +27,7 @@ The float64 oracle is timed on the host cores on a small sample of tokens
 (cpu_baseline).  Each workload's first step is checked against the oracle
 before timing; a mismatch reports no throughput.
 
-    python bench.py [--steps K] [--warmup W] [--workload layer|layer2|layer3|layer_g128|requant|batched|batched2|stack]
+    python bench.py [--steps K] [--warmup W] [--workload layer|layer2|layer3|layer_g128|requant|batched|batched2|batched3|stack]
 """
 import argparse
 import ctypes
@@ -57,6 +57,7 @@ WORKLOADS = {
     "layer_g128": dict(H=4096, I=1024, E=512, K=4, bits=4, B=1, layers=1, zipf=None, seed=1005, group=128),
     # the layer workload's shape with 3-bit codes
     "layer3": dict(H=4096, I=1024, E=512, K=4, bits=3, B=1, layers=1, zipf=None, seed=1006),
+    "batched3": dict(H=4096, I=1024, E=512, K=10, bits=3, B=64, layers=1, zipf=1.1, seed=1004),
 }
 RMS_EPS = 1e-6
 
@@ -743,7 +744,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": r["gateup_gbps"], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(r["gateup_gbps"] / PEAK_HBM_GBPS, 4), "traffic": traffic,
                      "kernel": (("gate/up phase: k_grouped_mfma<0, 4> + k_gemv_gateup" if c["bits"] == 4 else
-                                 "gate/up phase: k_grouped_mfma<0, 2> + k_fixup") if B > 1 else "k_gateup_fast"),
+                                 "gate/up phase: k_grouped_mfma<0, %d> + k_fixup" % c["bits"]) if B > 1
+                                else "k_gateup_fast"),
                      "bytes_per_launch": r["gateup_bytes_per_launch"], "avg_us": gu_us,
                      "step_frac": r["step_frac"]},
         "expert_weight_gbps": r["expert_weight_gbps"],
@@ -761,6 +763,7 @@ def main():
         extra = {"layer2": dict(steps=100, warmup=10), "requant": dict(steps=100, warmup=10),
                  "layer_g128": dict(steps=100, warmup=10), "layer3": dict(steps=100, warmup=10),
                  "batched": dict(steps=40, warmup=5), "batched2": dict(steps=40, warmup=5),
+                 "batched3": dict(steps=40, warmup=5),
                  "stack": dict(steps=10, warmup=2, distinct=4),
                  "layer": dict(steps=100, warmup=10)}
         cfgs = {}

@@ -64,7 +64,7 @@ extern "C" {
  * One MoE layer.  All pointers are device memory owned by the caller.
  *   H: hidden size, I: expert intermediate size (both multiples of the group).
  *   E: routed experts, K: experts kept per token, bits: 4, 3 or 2 (3-bit: I a
- *   multiple of 128; a 3-bit batch runs token by token), group: weights per
+ *   multiple of 128), group: weights per
  *   scale/bias group along each row, 64, 128 or 256 (the pages give per-group
  *   scales and biases, [LLMAPIS] section 深度分析, without a size).
  *   experts: packed slab of E + 1 records written by moe_pack_experts, the
@@ -228,7 +228,7 @@ int moe_expert_ffn_q4(const moe_layer_desc* desc, const float* x, int B, const i
                       const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
 int moe_expert_ffn_q2(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx,
                       const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
-/* 3-bit experts (desc->bits == 3; a batch runs token by token). */
+/* 3-bit experts (desc->bits == 3; batches grouped on the matrix cores as at 2 bits). */
 int moe_expert_ffn_q3(const moe_layer_desc* desc, const float* x, int B, const int32_t* idx,
                       const float* w, float* y_out, void* ws, size_t ws_bytes, void* stream);
 

@@ -57,6 +57,7 @@ bool grouped_supported(const Layout& L, int B, int K);
 struct GroupedBlocks {
     int gateup, down, gemv_gateup, gemv_down;
     int gateup2, down2;  // the 2-bit matrix-core launches
+    int gateup3, down3;  // the 3-bit matrix-core launches
 };
 GroupedBlocks grouped_blocks();
 // MFMA tiles of one work-list group (128 output rows) in the gate/up and the down phase

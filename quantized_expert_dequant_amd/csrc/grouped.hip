@@ -479,6 +479,35 @@ __device__ inline h8 dequant_field_q2(uint32_t x16, h2 s2, const Masks& M)
     return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// 3-bit records: the low two bits of a unit's codes form a 2-bit chunk, so field x16
+// is taken as at 2 bits; the unit's high-bit dword hi[h] covers the 32 columns of
+// 4-bit chunk half h.  For dword d of that half, high_bits_q3 moves the high bits of
+// codes r and r + 4 (r < 4) next to their low fields, to bits 2r + 2 and 2r + 18 (the
+// single-token order keeps them at bits 2i + 2 / 2i + 3 of the 16-bit half of the
+// 16-column dword, i = the code's place in it), and dequant_field_q3 ORs them in:
+// 1024 + 4^r q, then q - 4 exactly (the 3-bit codes' centre), times s exactly.  The
+// chunk term carries b + 4 s.
+__device__ inline uint32_t high_bits_q3(uint32_t W, int d)
+{
+    const uint32_t S = ((d >> 1) & 1) ? __builtin_amdgcn_alignbit(W, W, 8) : W;
+    return (d & 1) ? (((S >> 16) & 0x154u) | ((S >> 1) & 0x1540000u)) : ((S & 0x154u) | ((S << 15) & 0x1540000u));
+}
+
+__device__ inline h8 dequant_field_q3(uint32_t x16, uint32_t hb, h2 s2, const Masks& M)
+{
+    const h2 k1028 = {(_Float16)1028.f, (_Float16)1028.f};
+    const h2 k4 = {(_Float16)0.25f, (_Float16)0.25f}, k260 = {(_Float16)-260.f, (_Float16)-260.f};
+    const h2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f}, k68 = {(_Float16)-68.f, (_Float16)-68.f};
+    const h2 k64 = {(_Float16)0.015625f, (_Float16)0.015625f}, k20 = {(_Float16)-20.f, (_Float16)-20.f};
+    const uint32_t y = x16 | (x16 << 8);
+    const h2 q0 = __builtin_bit_cast(h2, (y & M.m2[0]) | M.magic | (hb & M.m3[0])) - k1028;
+    const h2 q1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (y & M.m2[1]) | M.magic | (hb & M.m3[1])), k4, k260);
+    const h2 q2 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (y & M.m2[2]) | M.magic | (hb & M.m3[2])), k16, k68);
+    const h2 q3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, (y & M.m2[3]) | M.magic | (hb & M.m3[3])), k64, k20);
+    const h2 p0 = q0 * s2, p1 = q1 * s2, p2 = q2 * s2, p3 = q3 * s2;
+    return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
 // The chunk term (b + 8 s) * sum: one MFMA per tile and step whose K slots of a
 // lane's chunk hold (b', b', s', s') against (X_hi, X_lo, X_hi, X_lo), with
 // b' = 2^5 b and s' = 2^5 * 8 s (exact in fp16 for |b| < 2^11 and |s| < 2^8) and
@@ -613,7 +642,7 @@ __device__ inline void store_h(const GroupedArgs& A, int ent, int row, float g, 
 template <int BITS>
 __device__ inline int gm_chunk(int ks, int k, int G, bool* pad)
 {
-    if (BITS == 4) {
+    if (BITS == 4) {  // (3-bit rows: the low-bit chunks, in the 2-bit order)
         const int P = 4 * ks + k;
         *pad = P >= 2 * G;
         return min(P, 2 * G - 1);
@@ -648,6 +677,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
     struct WRegs {
         cw_t c[NM];
         uint32_t sb[NM];
+        uint32_t hi[NM];  // 3-bit: the high-bit dword of the lane's 32 columns
     };
 
     for (int x = lo; x < hi;) {
@@ -718,6 +748,15 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                                                                      : (uint32_t)(L.off_d_codes + d_chunk_off(L, row, g))) +
                                                   (P >= G ? 8u : 0u);
             W.c[0] = *reinterpret_cast<const cw_t*>(rec + co);
+            if constexpr (BITS == 3) {
+                // the high-bit dword of half P / G of unit g
+                const uint32_t ho = ((MODE == MODE_GATEUP)
+                                         ? row_off + (uint32_t)(16 * G + 8 * g)
+                                         : (uint32_t)(L.off_d_codes + d_chunk_off(L, row, G + (g >> 1)) + 8 * (g & 1))) +
+                                    (P >= G ? 4u : 0u);
+                W.hi[0] = *reinterpret_cast<const uint32_t*>(rec + ho);
+                if (MODE == MODE_GATEUP) W.hi[NM - 1] = *reinterpret_cast<const uint32_t*>(rec + (ho + up_off));
+            }
             if (MODE == MODE_GATEUP) {
                 W.c[NM - 1] = *reinterpret_cast<const cw_t*>(rec + (co + up_off));
                 const uint2 v = *reinterpret_cast<const uint2*>(rec + (sb_off + (uint32_t)(g >> L.gs) * 8u));
@@ -764,8 +803,8 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
             for (int mm = 0; mm < NM; ++mm) {
                 const uint32_t sb = pad ? 0u : Wc.sb[mm];
                 const float s = bf16_lo(sb);
-                // the codes' centre: 8 (4-bit) or 2 (2-bit), so q - C averages about zero
-                constexpr float C = BITS == 4 ? 8.f : 2.f;
+                // the codes' centre: 8 (4-bit), 4 (3-bit) or 2 (2-bit), so q - C averages about zero
+                constexpr float C = BITS == 4 ? 8.f : (BITS == 3 ? 4.f : 2.f);
                 const _Float16 sh = (_Float16)s, bh = (_Float16)(bf16_hi(sb) * GM_CT), s8 = (_Float16)(s * (C * GM_CT));
                 s2[mm] = h2{sh, sh};
                 cw[mm] = h8{bh, bh, s8, s8, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
@@ -798,6 +837,9 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                 for (int mm = 0; mm < NM; ++mm) {
                     if constexpr (BITS == 4)
                         a[mm] = dequant_dword_q4(Wc.c[mm][d], s2[mm], M);
+                    else if constexpr (BITS == 3)
+                        a[mm] = dequant_field_q3((d & 1) ? Wc.c[mm][d >> 1] >> 16 : Wc.c[mm][d >> 1] & 0xFFFFu,
+                                                 high_bits_q3(Wc.hi[mm], d), s2[mm], M);
                     else
                         a[mm] = dequant_field_q2((d & 1) ? Wc.c[mm][d >> 1] >> 16 : Wc.c[mm][d >> 1] & 0xFFFFu, s2[mm], M);
                 }
@@ -1201,7 +1243,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part,
 bool grouped_supported(const Layout& L, int B, int K)
 {
     // every gate/up K chunk of a tile must hold at least one step (H >= 448)
-    return (L.bits == 4 || L.bits == 2) && B >= 2 && B <= MOE_MAX_B && K <= MOE_MAX_K && L.H % 64 == 0 && L.I % 64 == 0 &&
+    return (L.bits >= 2 && L.bits <= 4) && B >= 2 && B <= MOE_MAX_B && K <= MOE_MAX_K && L.H % 64 == 0 && L.I % 64 == 0 &&
            gm_steps(L, MODE_GATEUP) >= GM_KC_GATEUP;
 }
 
@@ -1300,6 +1342,8 @@ GroupedBlocks grouped_blocks()
     n.down = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_DOWN, 4>, GM_THREADS);
     n.gateup2 = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_GATEUP, 2>, GM_THREADS);
     n.down2 = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_DOWN, 2>, GM_THREADS);
+    n.gateup3 = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_GATEUP, 3>, GM_THREADS);
+    n.down3 = resident_blocks(dev, (const void*)k_grouped_mfma<MODE_DOWN, 3>, GM_THREADS);
     n.gemv_gateup = resident_blocks(dev, (const void*)k_gemv_gateup, 64 * GV_WAVES);
     n.gemv_down = resident_blocks(dev, (const void*)k_gemv_down, 64 * GV_WAVES);
     if (slot >= 0) {
@@ -1314,8 +1358,8 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
                         hipStream_t s, Timing tg, Timing td)
 {
     const GroupedBlocks nb = grouped_blocks();
-    const bool q2 = L.bits == 2;
-    const int nb_gu = q2 ? nb.gateup2 : nb.gateup, nb_dn = q2 ? nb.down2 : nb.down;
+    const int nb_gu = L.bits == 2 ? nb.gateup2 : (L.bits == 3 ? nb.gateup3 : nb.gateup);
+    const int nb_dn = L.bits == 2 ? nb.down2 : (L.bits == 3 ? nb.down3 : nb.down);
     const int nb_gvu = nb.gemv_gateup, nb_gvd = nb.gemv_down;
     const int gv_t = gemv_tokens(L);
     const bool gv = gv_t > 1;
@@ -1352,8 +1396,10 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     // gate/up phase, timed as a whole (MFMA groups, split-tile fixup, GEMV groups):
     // together they read every active expert's gate/up rows once
     if (tg.start) (void)hipEventRecord(tg.start, s);
-    if (q2)
+    if (L.bits == 2)
         hipLaunchKernelGGL((k_grouped_mfma<MODE_GATEUP, 2>), dim3(nb_gu), dim3(GM_THREADS), 0, s, A);
+    else if (L.bits == 3)
+        hipLaunchKernelGGL((k_grouped_mfma<MODE_GATEUP, 3>), dim3(nb_gu), dim3(GM_THREADS), 0, s, A);
     else
         hipLaunchKernelGGL((k_grouped_mfma<MODE_GATEUP, 4>), dim3(nb_gu), dim3(GM_THREADS), 0, s, A);
     if (gv)  // the GEMV kernel runs the split-tile fixups first
@@ -1368,8 +1414,10 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
 
     // down phase, timed as a whole
     if (td.start) (void)hipEventRecord(td.start, s);
-    if (q2)
+    if (L.bits == 2)
         hipLaunchKernelGGL((k_grouped_mfma<MODE_DOWN, 2>), dim3(nb_dn), dim3(GM_THREADS), 0, s, A);
+    else if (L.bits == 3)
+        hipLaunchKernelGGL((k_grouped_mfma<MODE_DOWN, 3>), dim3(nb_dn), dim3(GM_THREADS), 0, s, A);
     else
         hipLaunchKernelGGL((k_grouped_mfma<MODE_DOWN, 4>), dim3(nb_dn), dim3(GM_THREADS), 0, s, A);
     if (gv) hipLaunchKernelGGL(k_gemv_down, dim3(nbd), dim3(64 * GV_WAVES), lds_dn, s, A, (const float4*)W.hstats);

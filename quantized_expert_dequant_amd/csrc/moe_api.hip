@@ -501,10 +501,10 @@ int moe_grouped_launch_info(const moe_layer_desc* desc, int B, int32_t* info_out
     const bool grouped = grouped_supported(L, B, desc->K) && flags_groupable(L, desc->expert_flags);
     const GroupedBlocks nb = grouped_blocks();
     info_out[0] = grouped ? 1 : 0;
-    info_out[1] = desc->bits == 2 ? nb.gateup2 : nb.gateup;
+    info_out[1] = desc->bits == 2 ? nb.gateup2 : (desc->bits == 3 ? nb.gateup3 : nb.gateup);
     info_out[2] = grouped_tiles(L, 0);
     info_out[3] = grouped_gateup_chunks();
-    info_out[4] = desc->bits == 2 ? nb.down2 : nb.down;
+    info_out[4] = desc->bits == 2 ? nb.down2 : (desc->bits == 3 ? nb.down3 : nb.down);
     info_out[5] = grouped_tiles(L, 1);
     info_out[6] = gemv_tokens(L);
     info_out[7] = grouped_group_tokens();

@@ -6,7 +6,9 @@ mask and one OR per code pair build the fp16 pattern 1024 + t*q the dot2 kernels
 multiply.  Bars as for the other widths: the packed layout's dequantized weights
 bit-exact against the oracle's exact dequantization rounded once to fp32; expert
 indices bit-exact, routing weights within 1e-6 relative, each token's output within
-2e-3 of its largest magnitude.  A 3-bit batch runs the token-by-token kernels.
+2e-3 of its largest magnitude.  A 3-bit batch is grouped by expert like the other widths:
+the matrix-core kernels load each lane's 8 bytes of low bits and 4 bytes of high bits
+for the 32 columns of a 4-bit chunk and build the exact fp16 operands s * (q - 4).
 """
 import numpy as np
 import pytest
@@ -17,7 +19,7 @@ import synth
 import quantized_expert_dequant_amd as moe
 from quantized_expert_dequant_amd.slab import upload_experts, workspace
 
-from helpers import TOL, W_RTOL, build_layer, oracle_layer, rel_err
+from helpers import TOL, W_RTOL, build_layer, mfma_tiles, oracle_layer, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +65,8 @@ def _decode(layer, x):
 
 def _check(cfg, seed, B, step=0):
     L = build_layer(cfg, seed)
-    assert moe.grouped_launch_info(L.desc, B)["grouped"] == 0
+    info = moe.grouped_launch_info(L.desc, B)
+    assert info["grouped"] == (1 if B > 1 else 0)
     x = synth.tokens(seed, step, B, cfg["H"])
     y, idx, w = _decode(L, x)
     y_ref, idx_ref, w_ref, margin = oracle_layer(cfg, seed, 0, x, parallel=B > 1)
@@ -74,12 +77,15 @@ def _check(cfg, seed, B, step=0):
     print("3-bit H=%d I=%d K=%d B=%d: max rel err %.2e" % (cfg["H"], cfg["I"], cfg["K"], B, max(errs)))
     for b in range(B):
         assert errs[b] <= TOL, "token %d: %.3e" % (b, errs[b])
+    return L, idx, info
 
 
-@pytest.mark.parametrize("K,B", [(4, 1), (1, 1), (2, 1), (6, 1), (8, 1), (5, 1), (4, 3), (4, 40)])
+@pytest.mark.parametrize("K,B", [(4, 1), (1, 1), (2, 1), (6, 1), (8, 1), (5, 1), (4, 2), (4, 3), (4, 16), (4, 37),
+                                 (4, 256)])
 def test_layer_decode_tiny(K, B):
     """The tiny layer in 3-bit: the straight-line kernels at every K they are built for
-    (1, 2, 4, 6, 8), the general ones at K = 5, and batches of 3 and 40 tokens."""
+    (1, 2, 4, 6, 8), the general ones at K = 5, and grouped batches of 2 to 256 tokens
+    (several 16-token tiles, a ragged tail, two 32-token groups per expert)."""
     cfg = dict(H=512, I=128, E=16, K=K, bits=3, B=B, layers=1, zipf=None)
     _check(cfg, 1800 + K + B, B)
 
@@ -89,6 +95,22 @@ def test_layer_decode_full_size(step):
     """The workload-1 shape (H = 4096, I = 1024, E = 512, K = 4) in 3-bit, one token."""
     cfg = dict(H=4096, I=1024, E=512, K=4, bits=3, B=1, layers=1, zipf=None)
     _check(cfg, 1850, 1, step)
+
+
+@pytest.mark.parametrize("step", range(2))
+def test_batched_full_size(step):
+    """B = 64, K = 10 with the Zipf(1.1) prior at full size in 3-bit: every token."""
+    cfg = dict(H=4096, I=1024, E=512, K=10, bits=3, B=64, layers=1, zipf=1.1)
+    _check(cfg, 1880, 64, step)
+
+
+def test_batched_largest_batch():
+    """B = 256 at full size in 3-bit: the gate/up tiles outnumber the blocks, so they are cut
+    into K chunks and finished from partial sums; every token against the oracle."""
+    cfg = dict(H=4096, I=1024, E=512, K=10, bits=3, B=256, layers=1, zipf=1.1)
+    L, idx, info = _check(cfg, 1890, 256, 0)
+    assert info["gateup_k_chunks"] > 1
+    assert mfma_tiles(idx, cfg["E"], info) > info["gateup_blocks"], "the K-chunk split is not taken"
 
 
 def test_layer_decode_wide_rows_and_groups():
