@@ -1,6 +1,6 @@
 // common.h - packed expert layout and device helpers shared by the gfx950 kernels.
 //
-// Packed record of one expert (bits = 4 or 2, G_h = H/64, G_i = I/64 units of 64
+// Packed record of one expert (bits = 4, 3 or 2; 3-bit rows below; G_h = H/64, G_i = I/64 units of 64
 // columns per row; S_h = H/group, S_i = I/group scale/bias groups per row),
 // byte-for-byte the same size as the canonical expert:
 //   [gu_codes]  I row pairs, each [gate row codes (H*bits/8 B) | up row codes (H*bits/8 B)]
@@ -21,6 +21,10 @@
 // two 16-bit halves of a dword: masking one field of each half and OR-ing in the
 // fp16 pattern of 1024 turns two codes into the fp16 pair (1024 + t*q_a, 1024 + t*q_b)
 // with t a power of two, ready for v_dot2 against an fp16 pair of activations.
+// 3-bit rows: a gate/up row is [G_h chunks of the codes' low two bits, in the 2-bit
+// order | G_h x 8 bytes of their high bits]; a down row holds the low-bit chunks at
+// positions 0..G_i-1 and the high bits as chunks G_i + g/2 (two units to a chunk), so
+// I must be a multiple of 128 (group_dot_q3 gives the high bits' order).
 //
 // Activation operand ("prep") of a vector v split in units ("groups") of 64 columns:
 //   q  [8][G] uint4: 32 fp16 pairs per group; pair p of group g is element p%4
