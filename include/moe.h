@@ -346,8 +346,9 @@ int moe_rmsnorm(const float* y, int B, int H, float eps, float* x_out, void* str
  * n_layers layers in sequence ([LLMAPIS] section 数据和技术细节: a stack of 60
  * MoE layers): x_0 = x; y_l = layer_l(x_l); x_{l+1} = rmsnorm(y_l, eps).
  * y_out receives y of the last layer.  idx_out / w_out: [n_layers][B][K] or
- * NULL.  Every layer must have the same H, I, K, bits (ws sized by
- * moe_workspace_bytes of any of them, plus moe_stack_extra_bytes).
+ * NULL.  Every layer must have the same H, I, E and K; code widths and group
+ * sizes may differ from layer to layer (ws sized by moe_workspace_bytes of any
+ * of them, plus moe_stack_extra_bytes).
  */
 size_t moe_stack_extra_bytes(int B, int H);
 int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* x, int B, float eps,

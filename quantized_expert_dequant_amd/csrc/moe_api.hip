@@ -698,7 +698,9 @@ int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* x,
         if (rc) return rc;
         const moe_layer_desc& a = layers[l];
         const moe_layer_desc& z = layers[0];
-        if (a.H != z.H || a.I != z.I || a.K != z.K || a.bits != z.bits || a.E != z.E)
+        // the workspace depends on H, I, E, K and B only, so the code width and the group
+        // size may differ between layers
+        if (a.H != z.H || a.I != z.I || a.K != z.K || a.E != z.E)
             return fail(MOE_EINVAL, "%s: layer %d differs in shape from layer 0", fn, l);
         CHECK_PTR(a.w_router);
         CHECK_OPT_PTR4(a.logit_bias);

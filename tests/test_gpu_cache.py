@@ -150,6 +150,31 @@ def test_cache_policy_and_outputs_tiny(B, slots):
         assert rel_err(y[b], y_ref[b]) <= TOL
 
 
+@pytest.mark.parametrize("B,slots", [(1, 5), (3, 12)])
+def test_cache_3bit_layer(B, slots):
+    """The tiny layer with 3-bit codes through a small cache: 20 calls, the state equal to the
+    policy model's after every call and the outputs to the resident decode's bit for bit."""
+    c = Cached(0, slots, bits=3)
+    E = c.cfg["E"]
+    resident = build_layer(c.cfg, c.seed)
+    model = CacheModel(E, slots)
+    for t in range(20):
+        x = torch.from_numpy(synth.tokens(c.seed, 950 + t, B, c.L.H)).to(DEV)
+        y, idx, w = c.decode(x)
+        yr, idxr, wr = _resident(resident, x)
+        np.testing.assert_array_equal(idx, idxr)
+        np.testing.assert_array_equal(w, wr)
+        np.testing.assert_array_equal(y, yr)
+        model.call(idx.reshape(-1))
+        _, _, slot_of, _ = _state(c.state, E, slots)
+        assert list(slot_of) == model.slot_of, "call %d" % t
+    assert model.misses > slots
+    y_ref, idx_ref, _, _ = oracle_layer(c.cfg, c.seed, 0, x.cpu().numpy())
+    np.testing.assert_array_equal(idx, idx_ref)
+    for b in range(B):
+        assert rel_err(y[b], y_ref[b]) <= TOL
+
+
 def _bf16_scaled(bits16, k):
     """bf16 bit patterns times 2^k (exponent raised; zeros and values that would overflow kept)."""
     b = bits16.astype(np.int32)

@@ -95,3 +95,47 @@ def test_stack_teacher_forced(n, n_layers, B):
             for b in range(B):
                 np.testing.assert_allclose(xs[l + 1][b], oracle.rms_renorm(ys[l][b].astype(np.float64), RMS_EPS),
                                            rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_stack_mixed_code_widths(B):
+    """A stack whose layers have 4-, 3- and 2-bit experts and groups of 64 and 128 (the tiny
+    shape; one token through the straight-line kernels, three through the grouped ones): the
+    stack call equals the layer-by-layer run bit for bit, and every layer matches the oracle
+    teacher-forced."""
+    base = dict(WORKLOADS[0])
+    cfgs = [dict(base, bits=4), dict(base, bits=3), dict(base, bits=2, group=128), dict(base, bits=3, group=128)]
+    seed = 1900 + B
+    H, K = base["H"], base["K"]
+    layers = [build_layer(c, seed, layer=l) for l, c in enumerate(cfgs)]
+    x0 = synth.tokens(seed, 0, B, H)
+    ws, n = workspace(layers[0].desc, B)
+    xs, ys, idxs = [x0], [], []
+    x = _t(x0)
+    for l, L in enumerate(layers):
+        y = torch.empty((B, H), dtype=torch.float32, device=DEV)
+        idx = torch.empty((B, K), dtype=torch.int32, device=DEV)
+        w = torch.empty((B, K), dtype=torch.float32, device=DEV)
+        moe.layer_decode(L.desc, x, B, y, idx, w, ws, n)
+        ys.append(y.cpu().numpy())
+        idxs.append(idx.cpu().numpy())
+        if l + 1 < len(layers):
+            xn = torch.empty((B, H), dtype=torch.float32, device=DEV)
+            moe.rmsnorm(y, B, H, RMS_EPS, xn)
+            x = xn
+            xs.append(xn.cpu().numpy())
+    ws2, n2 = workspace(layers[0].desc, B, stack=True)
+    y_s = torch.empty((B, H), dtype=torch.float32, device=DEV)
+    idx_s = torch.empty((len(layers), B, K), dtype=torch.int32, device=DEV)
+    w_s = torch.empty((len(layers), B, K), dtype=torch.float32, device=DEV)
+    moe.stack_decode([L.desc for L in layers], _t(x0), B, RMS_EPS, y_s, idx_s, w_s, ws2, n2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y_s.cpu().numpy(), ys[-1])
+    np.testing.assert_array_equal(idx_s.cpu().numpy(), np.stack(idxs))
+    for l, c in enumerate(cfgs):
+        y_ref, idx_ref, _, margin = oracle_layer(c, seed, l, xs[l])
+        assert margin.min() > 1e-9, "layer %d" % l
+        np.testing.assert_array_equal(idxs[l], idx_ref, err_msg="layer %d" % l)
+        for b in range(B):
+            assert rel_err(ys[l][b], y_ref[b]) <= TOL, "layer %d (%d-bit) token %d" % (l, c["bits"], b)
+
