@@ -40,8 +40,9 @@ struct GroupOut {
 struct GroupedWork {
     double* partial;  // router partial logits [splits][B][E]
     GroupOut g;
-    uint4* xh;        // MFMA token operands: x * 2^-e as fp16 in chunk order [B][2 G_h][4] uint4
-    uint32_t* xsum;   // their chunk sums: 2^-5 * sum, fp16 (hi, lo) [B][2 G_h]
+    uint4* xh;        // MFMA token operands: x * 2^-e minus its chunk mean, as fp16 in chunk order [B][2 G_h][4] uint4
+    uint2* xsum;      // per chunk: 2^-5 * sum as fp16 (hi, lo), and the fp16 pair (2m, 2m) of the
+                      // chunk mean m the operands are deviations from [B][2 G_h]
     float* xscale;    // [B]
     float* hb;        // h in fp32, pair-layout order [B + B*K][8][G_i][8]
     uint4* hb16;      // h * 2^-e(entry) as fp16 pairs in chunk order [B + B*K][2 G_i][4]:
@@ -76,7 +77,7 @@ struct TokenPrep {
     const float* x;
     int H;
     uint4* xh;
-    uint32_t* xsum;
+    uint2* xsum;
     float* xscale;
     uint4* xq;
     float4* xst;

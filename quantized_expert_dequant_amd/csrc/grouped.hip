@@ -52,12 +52,16 @@ __device__ inline f4 mfma16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32
 
 // ----------------------------------------------------------------------------
 // The MFMA token operand: v = x scaled by the power of two that puts the token's
-// largest |x| in [2^14, 2^15), rounded to fp16, in chunk order: element c lands
-// in chunk P = (c / 32 % 2) * G + c / 64 (the code chunks' order in a row), dword
-// dd = c % 32 / 8, at xh[(t * 2G + P) * 4 + dd] element (r % 4) * 2 + r / 4 for
-// r = c % 8 (the pair order the packed codes unpack to), so a step's 4 chunks are
-// 256 contiguous bytes; and, for the MFMA kernel's chunk term, each chunk's sum
-// of the unrounded v, as fp16 hi + lo of 2^-5 times it, at xsum[t * 2G + P].
+// largest |x| in [2^13, 2^14); per chunk of 32 columns its mean rounded to fp16,
+// m, and each element's deviation v - m rounded to fp16, in chunk order: element c
+// lands in chunk P = (c / 32 % 2) * G + c / 64 (the code chunks' order in a row),
+// dword dd = c % 32 / 8, at xh[(t * 2G + P) * 4 + dd] element (r % 4) * 2 + r / 4
+// for r = c % 8 (the pair order the packed codes unpack to), so a step's 4 chunks
+// are 256 contiguous bytes.  For the MFMA kernel's chunk term, xsum[t * 2G + P]
+// holds the chunk's sum of the unrounded v, as fp16 hi + lo of 2^-5 times it, and
+// the fp16 pair (2m, 2m).  The rounding error of an element is then relative to its
+// deviation from the chunk mean, so a token whose elements are (nearly) equal does
+// not carry one rounding error, of one sign, into every column of a row.
 // ----------------------------------------------------------------------------
 // 2^5: the chunk term's fp16 operands are 2^5 b, 2^5 * 8 s and 2^-5 * chunk sum
 constexpr float GM_CT = 32.f;
@@ -66,7 +70,7 @@ __device__ inline int token_exponent(float amax)
 {
     int e = 0;
     if (amax > 0.f && amax <= 3.4e38f) {
-        e = ilogbf(amax) - 14;
+        e = ilogbf(amax) - 13;
         e = e < -110 ? -110 : (e > 113 ? 113 : e);
     }
     return e;
@@ -79,13 +83,17 @@ __device__ inline uint32_t hi_lo_pair(float v)
 // Element c of token row xt; the 32 columns of a chunk must be 32 consecutive
 // lanes of one wave, all calling together (c % 32 == lane % 32).
 __device__ inline void token_operand(const float* __restrict__ xt, int c, float inv, int G, uint16_t* __restrict__ out,
-                                     uint32_t* __restrict__ sums)
+                                     uint2* __restrict__ sums)
 {
     const float v = xt[c] * inv;
     const int P = ((c >> 5) & 1) * G + (c >> 6), dd = (c >> 3) & 3, r = c & 7;
-    out[((long long)P * 4 + dd) * 8 + (r & 3) * 2 + (r >> 2)] = __builtin_bit_cast(uint16_t, (_Float16)v);
-    const float sum = group_reduce(v, OpAdd(), 32);
-    if ((c & 31) == 0) sums[P] = hi_lo_pair(sum * (1.f / GM_CT));
+    const float sum = group_reduce(v, OpAdd(), 32);  // every lane of the chunk gets the same sum
+    const _Float16 m = (_Float16)(sum * (1.f / 32.f));
+    out[((long long)P * 4 + dd) * 8 + (r & 3) * 2 + (r >> 2)] = __builtin_bit_cast(uint16_t, (_Float16)(v - (float)m));
+    if ((c & 31) == 0) {
+        const _Float16 m2 = m + m;  // exact
+        sums[P] = make_uint2(hi_lo_pair(sum * (1.f / GM_CT)), __builtin_bit_cast(uint32_t, h2{m2, m2}));
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -405,7 +413,7 @@ void launch_expert_ranges(const Layout& L, const void* slab, int n, int32_t* fla
 constexpr int PT_DOT2_BLOCKS = 4;
 
 __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x, int H, uint4* __restrict__ xh,
-                                                     uint32_t* __restrict__ xsum, float* __restrict__ xscale,
+                                                     uint2* __restrict__ xsum, float* __restrict__ xscale,
                                                      uint4* __restrict__ xq, float4* __restrict__ xst)
 {
     __shared__ float red[4];
@@ -508,6 +516,32 @@ __device__ inline h8 dequant_field_q3(uint32_t x16, uint32_t hb, h2 s2, const Ma
     return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// Sum over a lane's 32 codes of q - C (C = 8, 4, 2: the width's centre): 4-bit, the
+// nibbles of 4 dwords; 2-bit, the crumbs of 2 dwords; 3-bit, those crumbs (the low
+// bits) plus 4 per set high bit.  Byte sums by v_sad_u8 against zero.
+template <int BITS, typename CW>
+__device__ inline int code_sum_centered(const CW& c, uint32_t hi)
+{
+    uint32_t acc = 0u;
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            acc = __builtin_amdgcn_sad_u8(c[d] & 0x0F0F0F0Fu, 0u, acc);
+            acc = __builtin_amdgcn_sad_u8((c[d] >> 4) & 0x0F0F0F0Fu, 0u, acc);
+        }
+        return (int)acc - 8 * 32;
+    } else {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const uint32_t t = (c[d] & 0x33333333u) + ((c[d] >> 2) & 0x33333333u);  // nibbles: pair sums
+            acc = __builtin_amdgcn_sad_u8(t & 0x0F0F0F0Fu, 0u, acc);
+            acc = __builtin_amdgcn_sad_u8((t >> 4) & 0x0F0F0F0Fu, 0u, acc);
+        }
+        if constexpr (BITS == 3) return (int)acc + 4 * __builtin_popcount(hi) - 4 * 32;
+        return (int)acc - 2 * 32;
+    }
+}
+
 // The chunk term (b + 8 s) * sum: one MFMA per tile and step whose K slots of a
 // lane's chunk hold (b', b', s', s') against (X_hi, X_lo, X_hi, X_lo), with
 // b' = 2^5 b and s' = 2^5 * 8 s (exact in fp16 for |b| < 2^11 and |s| < 2^8) and
@@ -572,7 +606,7 @@ struct GroupedArgs {
     const int32_t* n_ent;   // offsets[E]: routed entries placed (entries B .. B + n_ent - 1)
     const int32_t* ent_token;
     const uint4* xh;        // gate/up operand: x * 2^-e(token) as fp16 in chunk order [token][2 G_h][4]
-    const uint32_t* xsum;   // its chunk sums: 2^-5 * sum of x * 2^-e over each chunk, fp16 (hi, lo)
+    const uint2* xsum;      // per chunk: 2^-5 * sum of x * 2^-e as fp16 (hi, lo), and the pair (2m, 2m)
     const float* xscale;
     float* hb;       // gate/up output: h in fp32, pair-layout order [entry][8][G_i][8]
     const uint4* hb16;     // down operand: h * 2^-e(entry) as fp16 pairs in chunk order [entry][2 G_i][4]
@@ -715,7 +749,7 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         }
         struct Stage {
             u4 v;
-            uint32_t cs;  // gate/up: the row's chunk sum
+            uint2 cs;  // gate/up: the row's chunk sum and mean pair
         };
         auto stage_load = [&](int ks, Stage& S) {
             bool stpad;  // a padded slot stages a valid chunk; its weights are zero
@@ -726,16 +760,16 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
         };
         auto stage_store = [&](int buf, const Stage& S) {
             bs[buf][st_row + st_d] = S.v;
-            uint32_t cs;
+            uint2 cs;
             if (MODE == MODE_GATEUP) {
                 cs = S.cs;
             } else {
                 float sum = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sum = dot2(S.v[e], 0x3C003C00u, sum);  // fp16 (1, 1)
-                cs = hi_lo_pair(group_reduce(sum, OpAdd(), 4) * (1.f / GM_CT));
+                cs = make_uint2(hi_lo_pair(group_reduce(sum, OpAdd(), 4) * (1.f / GM_CT)), 0u);  // h: no mean term
             }
-            if (st_d == 0) bs[buf][st_row + 4] = u4{cs, 0u, 0u, 0u};
+            if (st_d == 0) bs[buf][st_row + 4] = u4{cs.x, cs.y, 0u, 0u};
         };
         auto weight_load = [&](int ks, WRegs& W) {
             bool wpad;  // the step applies the zero weights of a padded slot
@@ -807,15 +841,24 @@ __global__ __launch_bounds__(GM_THREADS) __attribute__((amdgpu_waves_per_eu(4)))
                 constexpr float C = BITS == 4 ? 8.f : (BITS == 3 ? 4.f : 2.f);
                 const _Float16 sh = (_Float16)s, bh = (_Float16)(bf16_hi(sb) * GM_CT), s8 = (_Float16)(s * (C * GM_CT));
                 s2[mm] = h2{sh, sh};
-                cw[mm] = h8{bh, bh, s8, s8, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+                _Float16 qh = (_Float16)0.f, ql = (_Float16)0.f;
+                if constexpr (MODE == MODE_GATEUP) {
+                    // the token operand is the chunk mean m plus deviations: the mean's share,
+                    // m * s * Q with Q = sum of (q - C) over the lane's 32 codes, rides in the
+                    // chunk term as (Q s / 2) in fp16 hi + lo against (2m, 2m), all exact
+                    const float qs = (float)code_sum_centered<BITS>(Wc.c[mm], BITS == 3 ? Wc.hi[mm] : 0u) * s * 0.5f;
+                    qh = (_Float16)qs;
+                    ql = (_Float16)(qs - (float)qh);
+                }
+                cw[mm] = h8{bh, bh, s8, s8, qh, ql, (_Float16)0.f, (_Float16)0.f};
             }
             // (b + 8 s) of each lane's chunk times the token operand's chunk sum
 #pragma unroll
             for (int tt = 0; tt < GM_TT; ++tt) {
                 if (tt < ntt) {
                     const int r = (tt * 4 + kk) * 16 + i;
-                    const uint32_t xsum = buf[r * 5 + 4].x;
-                    const h8 bx = __builtin_bit_cast(h8, u4{xsum, xsum, 0u, 0u});
+                    const u4 cv = buf[r * 5 + 4];  // (chunk sum hi, lo; the mean pair)
+                    const h8 bx = __builtin_bit_cast(h8, u4{cv.x, cv.x, cv.y, 0u});
 #pragma unroll
                     for (int mm = 0; mm < NM; ++mm) acc[mm][tt] = mfma16(cw[mm], bx, acc[mm][tt]);
                 }
@@ -1266,7 +1309,7 @@ size_t grouped_workspace_bytes(const Layout& L, int B, int K, int E)
     add(sizeof(int32_t) * ents);                       // ent_token
     add(sizeof(int32_t) * B * K);                      // slot_pos
     add(16ull * B * 2 * L.Gh * 4);                     // xh
-    add(4ull * B * 2 * L.Gh);                          // xsum
+    add(8ull * B * 2 * L.Gh);                          // xsum
     add(sizeof(float) * B);                            // xscale
     add(4ull * ents * L.I);                            // hb (fp32)
     add(2ull * ents * L.I);                            // hb16
@@ -1301,7 +1344,7 @@ GroupedWork carve_grouped(void* base, const Layout& L, int B, int K, int E)
     W.g.ent_token = (int32_t*)take(sizeof(int32_t) * ents);
     W.g.slot_pos = (int32_t*)take(sizeof(int32_t) * B * K);
     W.xh = (uint4*)take(16ull * B * 2 * L.Gh * 4);
-    W.xsum = (uint32_t*)take(4ull * B * 2 * L.Gh);
+    W.xsum = (uint2*)take(8ull * B * 2 * L.Gh);
     W.xscale = (float*)take(sizeof(float) * B);
     W.hb = (float*)take(4ull * ents * L.I);
     W.hb16 = (uint4*)take(2ull * ents * L.I);

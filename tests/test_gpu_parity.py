@@ -364,16 +364,19 @@ def test_rmsnorm_matches_oracle():
 
 
 @pytest.mark.parametrize("c", [2.0, 4.0, 8.0])
-@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("B", [1, 2, 3, 5])
 def test_saturated_silu_tiny_outputs(layers, c, B):
     """x = -c everywhere drives every gate row deep into SiLU's negative tail: the exact outputs are
     1e-10 (c=2), 1e-23 (c=4) and 1e-49 (c=8, below fp32: delivered as zero).  The per-token bar
-    (relative, floored at fp32's smallest normal) must hold on both the single-token (B=1) and the
-    grouped (B=2) path."""
+    (relative, floored at fp32's smallest normal) must hold on the single-token path (B=1), the
+    grouped path's GEMV groups (B=2: every expert has 2 tokens) and its matrix-core groups (B=3, 5).
+    Token b is x = -c (1 + b/10): values fp16 does not hold, all equal, so every column of a row
+    would carry one rounding error of one sign, which the saturated gate turns into a relative error
+    of the output."""
     L = layers(0)
     x = np.full((B, L.H), -c, np.float32)
-    if B > 1:
-        x[1] *= 1.1
+    for b in range(1, B):
+        x[b] *= 1.0 + 0.1 * b
     y, idx, w = _decode(L, x)
     y_ref, idx_ref, w_ref, margin = oracle_layer(WORKLOADS[0], seed_of(0), 0, x)
     np.testing.assert_array_equal(idx, idx_ref)
