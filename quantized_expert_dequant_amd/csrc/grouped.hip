@@ -41,9 +41,12 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));  // native vector: copi
 
 constexpr int GM_GROUP = 32;         // most tokens of one MFMA work-list group
 #ifndef MOE_GV_TOKENS
-#define MOE_GV_TOKENS 3
+#define MOE_GV_TOKENS 2
 #endif
 constexpr int GV_TOKENS = MOE_GV_TOKENS;  // an expert with fewer tokens than this runs as a dot2 GEMV group
+constexpr int GV_GROUP = 2;  // most tokens of one GEMV group of an expert flagged as out of the matrix cores' range
+// most tokens of any GEMV group when experts below gv_t tokens run as GEMV groups
+__host__ __device__ constexpr int gv_max_tokens(int gv_t) { return gv_t - 1 > GV_GROUP ? gv_t - 1 : GV_GROUP; }
 constexpr int GM_MAX_BLOCKS = 1024;  // most blocks of a stream-split launch
 constexpr int GM_MAX_DEVICES = 64;   // devices whose launch shapes are cached
 
@@ -268,8 +271,8 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t* __restrict__ idx,
     // an expert with fewer than gv_t tokens is one GEMV group, a larger one is
     // cut into MFMA groups of at most GM_GROUP tokens; an expert flagged as holding
     // scales or biases beyond the matrix cores' range is cut into GEMV groups of at
-    // most gv_t - 1 tokens whatever its count (the GEMV applies them in fp32)
-    const int gsz = gv_t > 1 ? gv_t - 1 : 1;
+    // most GV_GROUP tokens whatever its count (the GEMV applies them in fp32)
+    const int gsz = gv_t > 1 ? GV_GROUP : 1;
     const bool fl = flags != nullptr && gv_t > 1 && tid < E && flags[tid] != 0;
     const int fm = (!fl && c >= gv_t) ? (c + GM_GROUP - 1) / GM_GROUP : 0;
     const int fg = fl ? (c + gsz - 1) / gsz : ((c > 0 && c < gv_t) ? 1 : 0);
@@ -1430,8 +1433,9 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     A.hscale = W.hscale;
     A.part = W.part;
     A.split = W.split;
-    // the GEMV groups' operands in LDS: up to gv_t - 1 vectors of 9 * G uint4
-    const size_t lds_gu = 16ull * 9 * L.Gh * (gv_t - 1), lds_dn = 16ull * 9 * L.Gi * (gv_t - 1);
+    // the GEMV groups' operands in LDS: up to gv_max_tokens vectors of 9 * G uint4
+    const int gv_n = gv ? gv_max_tokens(gv_t) : 0;
+    const size_t lds_gu = 16ull * 9 * L.Gh * gv_n, lds_dn = 16ull * 9 * L.Gi * gv_n;
     // a block's item range spans at most ceil(V / nb) + 1 groups: keep that below GV_META
     const int v_max = max_groups(B, K, E), nb_meta = (v_max + GV_META - 3) / (GV_META - 2);
     const int nbu = max(nb_gvu, nb_meta), nbd = max(nb_gvd, nb_meta);
