@@ -85,8 +85,9 @@ class _Bufs:
 
 
 # (entry point, workload, tokens): workload 1 is the full single-token layer (fused
-# selection); workload 0 at B = 16 has experts with >= 3 tokens (matrix-core groups),
-# at B = 2 only GEMV groups; the stack renormalizes inside the next router at B = 1
+# selection); workload 0 at B = 16 has experts with >= 2 tokens (matrix-core groups),
+# at B = 2 mostly GEMV groups (experts with one token) and the shared expert's group on
+# the matrix cores; the stack renormalizes inside the next router at B = 1
 # and with the separate renorm kernel on the grouped path; the given-routing entry point
 # at B = 16 writes its own token operands (k_prep_tokens) before the grouped FFNs.
 CASES = [("layer", 1, 1), ("layer", 0, 16), ("layer", 0, 2), ("stack", 0, 1), ("stack", 0, 3), ("ffn", 0, 16)]

@@ -368,8 +368,8 @@ def test_rmsnorm_matches_oracle():
 def test_saturated_silu_tiny_outputs(layers, c, B):
     """x = -c everywhere drives every gate row deep into SiLU's negative tail: the exact outputs are
     1e-10 (c=2), 1e-23 (c=4) and 1e-49 (c=8, below fp32: delivered as zero).  The per-token bar
-    (relative, floored at fp32's smallest normal) must hold on the single-token path (B=1), the
-    grouped path's GEMV groups (B=2: every expert has 2 tokens) and its matrix-core groups (B=3, 5).
+    (relative, floored at fp32's smallest normal) must hold on the single-token path (B=1) and the
+    grouped path's matrix-core groups (B=2, 3, 5: all tokens choose the same experts).
     Token b is x = -c (1 + b/10): values fp16 does not hold, all equal, so every column of a row
     would carry one rounding error of one sign, which the saturated gate turns into a relative error
     of the output."""
