@@ -26,18 +26,27 @@
 // positions 0..G_i-1 and the high bits as chunks G_i + g/2 (two units to a chunk), so
 // I must be a multiple of 128 (group_dot_q3 gives the high bits' order).
 //
-// Activation operand ("prep") of a vector v split in units ("groups") of 64 columns:
-//   q  [8][G] uint4: 32 fp16 pairs per group; pair p of group g is element p%4
-//                    of uint4 (p/4)*G + g.  Pair p holds v_h at columns
-//                    4-bit: (8*(p/4) + p%4, +4);  2- and 3-bit: (16*(p/8) + p%8, +8),
-//                    where v_h = fp16(v * 2^-e_g) with a power-of-two per-group scale.
-//   st [G]    float4: (C_g, S_g, 2^e_g, 0) with S_g = sum of v over the group and
-//                    C_g = 1024 * sum_p (v_h pair sum) / t(p) + mid * sum_c (v_h - v 2^-e_g):
-//                    the offset the fp16 code patterns add to the dot products, plus
-//                    the code midpoint (7.5, 3.5 or 1.5) times the group's rounding error.
-// Per group and row:  sum_c (s*q_c + b) v_c ~= s * 2^e_g * (sum_t acc_t / t - C_g) + b * S_g,
-// where sum_t acc_t / t - C_g = sum_c (q_c - mid) v_h,c + mid * sum_c v_c 2^-e_g: the
-// fp16 rounding of v only meets the zero-mean part of the codes.
+// Activation operand ("prep") of a vector v split in units ("groups") of 64 columns,
+// 8 uint4 per group (uint4 d*G + g covers columns 8d..8d+7 of group g) then G stats:
+//   2- and 3-bit: 32 fp16 pairs per group; pair p of group g is element p%4 of
+//     uint4 (p/4)*G + g and holds v_h at columns (16*(p/8) + p%8, +8), where
+//     v_h = fp16(v * 2^-e_g) with a power-of-two per-group scale;
+//     st [G] float4: (C_g, S_g, 2^e_g, 0) with S_g = sum of v over the group and
+//     C_g = 1024 * sum_p (v_h pair sum) / t(p) + mid * sum_c (v_h - v 2^-e_g):
+//     the offset the fp16 code patterns add to the dot products, plus the code
+//     midpoint (3.5 or 1.5) times the group's rounding error.
+//   Per group and row:  sum_c (s*q_c + b) v_c ~= s * 2^e_g * (sum_t acc_t / t - C_g) + b * S_g,
+//   where sum_t acc_t / t - C_g = sum_c (q_c - mid) v_h,c + mid * sum_c v_c 2^-e_g: the
+//   fp16 rounding of v only meets the zero-mean part of the codes.
+//   4-bit: the integers X_c = rint(v_c * 2^-e_g), |X_c| <= 2^14 (the largest |v| of
+//     the group scaled into [2^13, 2^14)), as four signed base-16 digits each,
+//     X = sum_j 16^j d_j with d_j in [-8, 7]; uint4 d of group g holds the digit
+//     planes j = 0..3 of its 8 columns, column 8d+i in nibble i of dword j (the
+//     nibble the column's code has in the code dword);
+//     st [G] float4: (C_g, S_g, 2^e_g, 0) with C_g = -(sum_c X_c / 2 + 7.5 S_g 2^-e_g).
+//   Per group and row:  sum_c (s*q_c + b) v_c ~= s * 2^e_g * (A - C_g) + b * S_g with
+//   A = sum_c (q_c - 8) X_c, exact in integers (v_dot8 of the codes, top bits
+//   flipped, against each plane): the rounding of v only meets q - 7.5.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -127,8 +136,29 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c)
 }
 
 // 4-bit: one group = two 16-byte chunks c0 (columns 0..31) and c1 (32..63);
-// xp = the group's 8 uint4 of activation pairs.  Returns sum_t acc_t / t.
-__device__ inline float group_dot_q4(const Masks& M, uint4 c0, uint4 c1, const uint4* xp)
+// xp = the group's 8 uint4 of digit planes.  Returns A = sum_c (q_c - 8) X_c:
+// flipping each code's top bit gives the signed nibble q - 8, and one v_dot8
+// per plane sums eight products of nibbles exactly; |A| < 2^25.
+__device__ inline float group_dot_q4(const Masks&, uint4 c0, uint4 c1, const uint4* xp)
+{
+    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+        const int v = (int)(w[d] ^ 0x88888888u);
+        const uint4 x = xp[d];
+        a0 = __builtin_amdgcn_sdot8(v, (int)x.x, a0, false);
+        a1 = __builtin_amdgcn_sdot8(v, (int)x.y, a1, false);
+        a2 = __builtin_amdgcn_sdot8(v, (int)x.z, a2, false);
+        a3 = __builtin_amdgcn_sdot8(v, (int)x.w, a3, false);
+    }
+    return (float)(a0 + 16 * a1 + 256 * a2 + 4096 * a3);
+}
+
+// 4-bit against fp16 pairs, pair p holding columns (8*(p/4) + p%4, +4) (element
+// p%4 of uint4 p/4, scaled as the 2-bit operand): the batched down's dot2 groups,
+// whose h operand is also the matrix cores' fp16 operand.  Returns sum_t acc_t / t.
+__device__ inline float group_dot_q4_f16(const Masks& M, uint4 c0, uint4 c1, const uint4* xp)
 {
     const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
     float a1 = 0.f, a16 = 0.f;
@@ -259,6 +289,8 @@ __device__ inline uint32_t dpp32(uint32_t v)
 template <int CTRL>
 __device__ inline float xchg(float v) { return __uint_as_float(dpp32<CTRL>(__float_as_uint(v))); }
 template <int CTRL>
+__device__ inline uint32_t xchg(uint32_t v) { return dpp32<CTRL>(v); }
+template <int CTRL>
 __device__ inline double xchg(double v)
 {
     uint2 u = __builtin_bit_cast(uint2, v);
@@ -280,6 +312,8 @@ __device__ inline void swap_u32(uint32_t v, uint32_t& a, uint32_t& b)
         b = p[1];
     }
 }
+template <bool ROW32>
+__device__ inline void swap(uint32_t v, uint32_t& a, uint32_t& b) { swap_u32<ROW32>(v, a, b); }
 template <bool ROW32>
 __device__ inline void swap(float v, float& a, float& b)
 {
@@ -332,14 +366,74 @@ __device__ inline T wave_sum(T v) { return group_reduce(v, OpAdd(), 64); }
 __device__ inline float wave_max(float v) { return group_reduce(v, OpMax(), 64); }
 __device__ inline float lane_group_sum(float v, int width) { return group_reduce(v, OpAdd(), width); }
 
+// ---- 4-bit digit planes.  q4_exponent: e with amax * 2^-e in [2^13, 2^14) (below
+// 2^-97 clamped at -110, which only costs precision); 0 for zero.  q4_bits: for
+// |v * inv| <= 2^14 the fma rounds v * inv + 34952 + 1.5 * 2^23 once, to nearest
+// even, into a float whose low 16 bits are U = X + 0x8888 with X = rint(v * inv):
+// U lies in [0, 65535] and its nibbles are the digits d_j + 8 (so U ^ 0x8888 holds
+// the d_j as signed nibbles); the bits above are 0x4B40 for every such v.
+__device__ inline int q4_exponent(float amax)
+{
+    if (!(amax > 0.f) || !(amax <= 3.4e38f)) return 0;
+    const int e = ilogbf(amax) - 13;  // <= 114, so 2^e and 2^-e are normal floats
+    return e < -110 ? -110 : e;
+}
+constexpr uint32_t Q4_HIGH = 0x4B400000u;  // the bits above U
+__device__ inline uint32_t q4_bits(float v, float inv) { return __float_as_uint(fmaf(v, inv, 12617864.0f)); }
+
+// the four digit planes of 8 columns from their q4_bits W[i] (column i in natural
+// order): the U halves paired and their bytes of even and odd columns gathered
+// with v_perm, then one bitfield insert per plane puts column i at nibble i, and
+// flipping every nibble's top bit turns d_j + 8 into the signed d_j
+__device__ inline uint4 digit_planes(const uint32_t (&W)[8])
+{
+    const uint32_t p02 = __builtin_amdgcn_perm(W[2], W[0], 0x05040100u);
+    const uint32_t p46 = __builtin_amdgcn_perm(W[6], W[4], 0x05040100u);
+    const uint32_t p13 = __builtin_amdgcn_perm(W[3], W[1], 0x05040100u);
+    const uint32_t p57 = __builtin_amdgcn_perm(W[7], W[5], 0x05040100u);
+    const uint32_t E = __builtin_amdgcn_perm(p46, p02, 0x06040200u);   // low bytes, columns 0 2 4 6
+    const uint32_t Eh = __builtin_amdgcn_perm(p46, p02, 0x07050301u);  // high bytes
+    const uint32_t O = __builtin_amdgcn_perm(p57, p13, 0x06040200u);   // columns 1 3 5 7
+    const uint32_t Oh = __builtin_amdgcn_perm(p57, p13, 0x07050301u);
+    constexpr uint32_t m = 0x0F0F0F0Fu, flip = 0x88888888u;
+    return make_uint4(((E & m) | ((O << 4) & ~m)) ^ flip, (((E >> 4) & m) | (O & ~m)) ^ flip,
+                      ((Eh & m) | ((Oh << 4) & ~m)) ^ flip, (((Eh >> 4) & m) | (Oh & ~m)) ^ flip);
+}
+
+struct OpOr {
+    __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; }
+};
+
 // ---- token prep (the operand layout at the top of this file): one wave per
 // (vector, group) writes the group's fp16 pairs and its stats (C, S, 2^e).
 template <int BITS>
 __device__ inline void prep_group(const float* __restrict__ v, int G, int vec, int g, int lane, uint4* __restrict__ q,
                                   float4* __restrict__ st, float scale = 1.f)
 {
+    // val is rounded before every use, so a renormalizing scale (the stacked layers)
+    // gives the operand a separate renormalization pass would: no product of v and
+    // scale may be fused into the sums below
+#pragma clang fp contract(off)
     const float val = v[(long long)vec * G * 64 + g * 64 + lane] * scale;
     const float amax = wave_max(fabsf(val));
+    const float S = wave_sum(val);
+    if constexpr (BITS == 4) {
+        // lane = column: its digit word, OR-ed into the planes of its 8-column uint4
+        const int e = q4_exponent(amax);
+        const float inv = exp2i_f(-e);
+        const uint32_t U = q4_bits(val, inv) & 0xFFFFu, V = U ^ 0x8888u;
+        const int sh = 4 * (lane & 7);
+        uint32_t pl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pl[j] = group_reduce(((V >> (4 * j)) & 0xFu) << sh, OpOr(), 8);
+        if ((lane & 7) == 0)
+            q[(long long)vec * 8 * G + (lane >> 3) * G + g] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+        const float sx = wave_sum((float)((int)U - 0x8888));  // sum of X, exact (|sum| <= 2^20)
+        // a group with a non-finite value gets a NaN scale, so its dot products are NaN
+        const float sc = (amax <= 3.4e38f) ? exp2i_f(e) : __builtin_nanf("");
+        if (lane == 0) st[(long long)vec * G + g] = make_float4(-fmaf(0.5f, sx, 7.5f * (S * inv)), S, sc, 0.f);
+        return;
+    }
     int e = 0;
     if (amax > 0.f && amax <= 3.4e38f) {
         e = ilogbf(amax) - 14;  // amax * 2^-e in [2^14, 2^15)
@@ -347,27 +441,18 @@ __device__ inline void prep_group(const float* __restrict__ v, int G, int vec, i
     }
     const float vs = val * exp2i_f(-e);  // exact power-of-two scaling
     const _Float16 vh = (_Float16)vs;
-    int p, hi;
-    if (BITS == 4) {
-        const int d = lane >> 3, r = lane & 7;
-        p = 4 * d + (r & 3);
-        hi = r >> 2;
-    } else {
-        const int d = lane >> 4, r = lane & 15;
-        p = 8 * d + (r & 7);
-        hi = r >> 3;
-    }
+    const int d = lane >> 4, r = lane & 15;
+    const int p = 8 * d + (r & 7), hi = r >> 3;
     uint16_t* qb = reinterpret_cast<uint16_t*>(q + (long long)vec * 8 * G);
     qb[((long long)(p >> 2) * G + g) * 8 + (p & 3) * 2 + hi] = __builtin_bit_cast(uint16_t, vh);
     // C = offset the fp16 code patterns add (1024 * sum_t S_t / t) plus the code
     // midpoint times the group's fp16 rounding error, so that the kernels compute
     // sum (q - mid) v_h + mid * sum v: the rounding errors of v then meet only
     // zero-mean code offsets and do not add up coherently across rows.
-    constexpr float mid = BITS == 4 ? 7.5f : (BITS == 3 ? 3.5f : 1.5f);
+    constexpr float mid = BITS == 3 ? 3.5f : 1.5f;
     const float off = wave_sum((float)vh * pair_class_inv(BITS, p));
     const float rnd = wave_sum((float)vh - vs);  // exact per lane
     const float C = fmaf(off, 1024.f, mid * rnd);
-    const float S = wave_sum(val);
     if (lane == 0) st[(long long)vec * G + g] = make_float4(C, S, exp2i_f(e), 0.f);
 }
 

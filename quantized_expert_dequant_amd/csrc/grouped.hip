@@ -1253,7 +1253,7 @@ __global__ __launch_bounds__(64 * GV_WAVES) void k_gemv_down(GroupedArgs A, cons
 #pragma unroll
             for (int j = 0; j < 8; ++j) hp[j] = hv[((j >> 2) * G + g) * 4 + (j & 3)];
             const float4 sv = __builtin_bit_cast(float4, hv[8 * G + g]);
-            float acc = fmaf(bf16_lo(w.sb) * sv.z, group_dot_q4(M, w.c[0], w.c[1], hp) - sv.x, bf16_hi(w.sb) * sv.y);
+            float acc = fmaf(bf16_lo(w.sb) * sv.z, group_dot_q4_f16(M, w.c[0], w.c[1], hp) - sv.x, bf16_hi(w.sb) * sv.y);
             acc = lane_group_sum(gv ? acc : 0.f, LPR);
             if (gl == 0 && r < L.H) A.part[(long long)(ent0 + m) * L.H + r] = acc;
         }

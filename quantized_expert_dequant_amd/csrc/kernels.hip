@@ -646,7 +646,8 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
 // h staging of the down kernels.  An item is one quarter of a (slot s, group g)
 // pair: the pair-layout uint4 j = 2*part and 2*part + 1 of that group, 16 fp32
 // values of h.  The group's four items scale it by a power of two taken from
-// the group's largest |h|, store it as fp16 pairs and derive the group's stats
+// the group's largest |h|, store it in the operand format of the code width
+// (4-bit: digit planes; 2- and 3-bit: fp16 pairs) and derive the group's stats
 // (C, S, scale) in one pass: a group whose h is tiny keeps its relative precision.
 // pairs: uint4 (s, j, g) at pair_base + s * pair_slot + j * G + g
 // stats: uint4 (s, g) at stat_base + s * stat_slot + g
@@ -679,6 +680,34 @@ __device__ inline void h_item_stage(const HItem& H, int G, int it, int n_items, 
     const int sl = sg / G, g = sg - sl * G;
     float m = fmaxf(absmax8(H.v[0], H.v[1]), absmax8(H.v[2], H.v[3]));
     m = group_reduce(m, OpMax(), 4);
+    if constexpr (BITS == 4) {
+        const int e = q4_exponent(m);
+        const float inv = exp2i_f(-e);
+        float sx = 0.f, sum = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            // the 8 values of pair-layout uint4 j hold columns 0 4 1 5 2 6 3 7 of its 8
+            const float4 a = H.v[2 * jj], b = H.v[2 * jj + 1];
+            const float c[8] = {a.x, a.z, b.x, b.z, a.y, a.w, b.y, b.w};
+            uint32_t W[8], su = 0u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                W[i] = q4_bits(c[i], inv);
+                su += W[i];
+            }
+            sx += (float)(int)(su - 8u * (Q4_HIGH + 0x8888u));  // sum of the 8 X, mod 2^32 exact
+            sum += ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+            if (ok) lds[sl * pair_slot + (2 * part + jj) * G + g] = digit_planes(W);
+        }
+        sx = group_reduce(sx, OpAdd(), 4);
+        sum = group_reduce(sum, OpAdd(), 4);
+        if (ok && part == 0) {
+            const float sc = (m <= 3.4e38f) ? exp2i_f(e) : __builtin_nanf("");
+            lds[stat_base + sl * stat_slot + g] =
+                __builtin_bit_cast(uint4, make_float4(-fmaf(0.5f, sx, 7.5f * (sum * inv)), sum, sc, 0.f));
+        }
+        return;
+    }
     const int e = h_exponent(m);
     const float inv = exp2i_f(-e);
     float off = 0.f, sum = 0.f;
