@@ -27,26 +27,27 @@
 // I must be a multiple of 128 (group_dot_q3 gives the high bits' order).
 //
 // Activation operand ("prep") of a vector v split in units ("groups") of 64 columns,
-// 8 uint4 per group (uint4 d*G + g covers columns 8d..8d+7 of group g) then G stats:
-//   2- and 3-bit: 32 fp16 pairs per group; pair p of group g is element p%4 of
-//     uint4 (p/4)*G + g and holds v_h at columns (16*(p/8) + p%8, +8), where
-//     v_h = fp16(v * 2^-e_g) with a power-of-two per-group scale;
-//     st [G] float4: (C_g, S_g, 2^e_g, 0) with S_g = sum of v over the group and
-//     C_g = 1024 * sum_p (v_h pair sum) / t(p) + mid * sum_c (v_h - v 2^-e_g):
-//     the offset the fp16 code patterns add to the dot products, plus the code
-//     midpoint (3.5 or 1.5) times the group's rounding error.
-//   Per group and row:  sum_c (s*q_c + b) v_c ~= s * 2^e_g * (sum_t acc_t / t - C_g) + b * S_g,
-//   where sum_t acc_t / t - C_g = sum_c (q_c - mid) v_h,c + mid * sum_c v_c 2^-e_g: the
-//   fp16 rounding of v only meets the zero-mean part of the codes.
-//   4-bit: the integers X_c = rint(v_c * 2^-e_g), |X_c| <= 2^14 (the largest |v| of
-//     the group scaled into [2^13, 2^14)), as four signed base-16 digits each,
-//     X = sum_j 16^j d_j with d_j in [-8, 7]; uint4 d of group g holds the digit
-//     planes j = 0..3 of its 8 columns, column 8d+i in nibble i of dword j (the
-//     nibble the column's code has in the code dword);
-//     st [G] float4: (C_g, S_g, 2^e_g, 0) with C_g = -(sum_c X_c / 2 + 7.5 S_g 2^-e_g).
+// 8 uint4 per group then G float4 stats (C_g, S_g, 2^e_g, 0), S_g = sum of v over the group:
+//   4- and 2-bit: the integers X_c = rint(v_c * 2^-e_g), |X_c| <= 2^14 (the largest |v|
+//     of the group scaled into [2^13, 2^14)), as four signed base-16 digits each,
+//     X = sum_j 16^j d_j with d_j in [-8, 7], stored as digit planes: dword j of a
+//     uint4 holds digit j of 8 columns, one per nibble, each in the nibble its code
+//     takes in the matching code word.  4-bit: uint4 d*G + g covers columns 8d + i
+//     (nibble i), the code dword of those columns; 2-bit: uint4 (2d + t)*G + g covers
+//     columns 16d + 2i + t (nibble i), t = 0 the even, t = 1 the odd columns of code
+//     dword d, whose codes spread to nibbles as (w >> 2t) & 0x33333333.
+//     C_g = -((8 - mid) sum_c X_c + mid S_g 2^-e_g), mid = 7.5 (4-bit) or 1.5 (2-bit).
 //   Per group and row:  sum_c (s*q_c + b) v_c ~= s * 2^e_g * (A - C_g) + b * S_g with
-//   A = sum_c (q_c - 8) X_c, exact in integers (v_dot8 of the codes, top bits
-//   flipped, against each plane): the rounding of v only meets q - 7.5.
+//   A = sum_c (q_c - 8) X_c, exact in integers (v_dot8 of the codes as signed nibbles
+//   q - 8 against each plane): the rounding of v only meets the zero-mean q - mid.
+//   3-bit: 32 fp16 pairs per group; pair p of group g is element p%4 of uint4
+//     (p/4)*G + g and holds v_h at columns (16*(p/8) + p%8, +8), where
+//     v_h = fp16(v * 2^-e_g) with a power-of-two per-group scale;
+//     C_g = 1024 * sum_p (v_h pair sum) / t(p) + 3.5 * sum_c (v_h - v 2^-e_g): the
+//     offset the fp16 code patterns add to the dot products, plus the code midpoint
+//     times the group's rounding error.
+//   Per group and row:  sum_c (s*q_c + b) v_c ~= s * 2^e_g * (sum_t acc_t / t - C_g) + b * S_g,
+//   where sum_t acc_t / t - C_g = sum_c (q_c - 3.5) v_h,c + 3.5 * sum_c v_c 2^-e_g.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -174,28 +175,28 @@ __device__ inline float group_dot_q4_f16(const Masks& M, uint4 c0, uint4 c1, con
     return fmaf(a16, 0.0625f, a1);
 }
 
-// 2-bit: one group = one 16-byte chunk (4 dwords of 16 codes).
-__device__ inline float group_dot_q2(const Masks& M, uint4 c0, const uint4* xp)
+// 2-bit: one group = one 16-byte chunk (4 dwords of 16 codes); xp = its 8 uint4
+// of digit planes (even and odd columns of each dword).  Returns A = sum (q - 8) X:
+// a code OR 8 in a nibble is the signed nibble q - 8.
+__device__ inline float group_dot_q2(const Masks&, uint4 c0, const uint4* xp)
 {
     const uint32_t w[4] = {c0.x, c0.y, c0.z, c0.w};
-    float a1 = 0.f, a4 = 0.f, a16 = 0.f, a64 = 0.f, a256 = 0.f;
+    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const uint32_t v = w[d], v10 = v >> 10;
-        const uint4 x0 = xp[2 * d], x1 = xp[2 * d + 1];
-        a1 = dot2((v & M.m2[0]) | M.magic, x0.x, a1);
-        a4 = dot2((v & M.m2[1]) | M.magic, x0.y, a4);
-        a16 = dot2((v & M.m2[2]) | M.magic, x0.z, a16);
-        a64 = dot2((v & M.m2[3]) | M.magic, x0.w, a64);
-        a256 = dot2((v & M.m2[4]) | M.magic, x1.x, a256);
-        a1 = dot2((v10 & M.m2[0]) | M.magic, x1.y, a1);
-        a4 = dot2((v10 & M.m2[1]) | M.magic, x1.z, a4);
-        a16 = dot2((v10 & M.m2[2]) | M.magic, x1.w, a16);
+        const int lo = (int)((w[d] & 0x33333333u) | 0x88888888u);
+        const int hi = (int)(((w[d] >> 2) & 0x33333333u) | 0x88888888u);
+        const uint4 xe = xp[2 * d], xo = xp[2 * d + 1];
+        a0 = __builtin_amdgcn_sdot8(lo, (int)xe.x, a0, false);
+        a1 = __builtin_amdgcn_sdot8(lo, (int)xe.y, a1, false);
+        a2 = __builtin_amdgcn_sdot8(lo, (int)xe.z, a2, false);
+        a3 = __builtin_amdgcn_sdot8(lo, (int)xe.w, a3, false);
+        a0 = __builtin_amdgcn_sdot8(hi, (int)xo.x, a0, false);
+        a1 = __builtin_amdgcn_sdot8(hi, (int)xo.y, a1, false);
+        a2 = __builtin_amdgcn_sdot8(hi, (int)xo.z, a2, false);
+        a3 = __builtin_amdgcn_sdot8(hi, (int)xo.w, a3, false);
     }
-    float r = fmaf(a256, 1.f / 256.f, a64 * (1.f / 64.f));
-    r = fmaf(a16, 1.f / 16.f, r);
-    r = fmaf(a4, 0.25f, r);
-    return r + a1;
+    return (float)(a0 + 16 * a1 + 256 * a2 + 4096 * a3);
 }
 
 // 3-bit: one unit = a 16-byte chunk of the codes' low 2 bits (the 2-bit chunk
@@ -366,8 +367,12 @@ __device__ inline T wave_sum(T v) { return group_reduce(v, OpAdd(), 64); }
 __device__ inline float wave_max(float v) { return group_reduce(v, OpMax(), 64); }
 __device__ inline float lane_group_sum(float v, int width) { return group_reduce(v, OpAdd(), width); }
 
-// ---- 4-bit digit planes.  q4_exponent: e with amax * 2^-e in [2^13, 2^14) (below
-// 2^-97 clamped at -110, which only costs precision); 0 for zero.  q4_bits: for
+// ---- integer digit planes (4- and 2-bit).  q4_exponent: e with amax * 2^-e in
+// [2^13, 2^14); 0 for zero.  e stays in [-126, 114], so 2^e and 2^-e are normal
+// floats: a group whose largest |v| is below 2^-113 (h after a saturated SiLU
+// reaches 1e-34) gets fewer than 14 bits, and for e near -126 the product of a
+// scale with 2^e may be a denormal, which still carries 13 or more bits for
+// |s| >= 2^-10.  q4_bits: for
 // |v * inv| <= 2^14 the fma rounds v * inv + 34952 + 1.5 * 2^23 once, to nearest
 // even, into a float whose low 16 bits are U = X + 0x8888 with X = rint(v * inv):
 // U lies in [0, 65535] and its nibbles are the digits d_j + 8 (so U ^ 0x8888 holds
@@ -375,8 +380,8 @@ __device__ inline float lane_group_sum(float v, int width) { return group_reduce
 __device__ inline int q4_exponent(float amax)
 {
     if (!(amax > 0.f) || !(amax <= 3.4e38f)) return 0;
-    const int e = ilogbf(amax) - 13;  // <= 114, so 2^e and 2^-e are normal floats
-    return e < -110 ? -110 : e;
+    const int e = ilogbf(amax) - 13;  // <= 114
+    return e < -126 ? -126 : e;
 }
 constexpr uint32_t Q4_HIGH = 0x4B400000u;  // the bits above U
 __device__ inline uint32_t q4_bits(float v, float inv) { return __float_as_uint(fmaf(v, inv, 12617864.0f)); }
@@ -400,6 +405,14 @@ __device__ inline uint4 digit_planes(const uint32_t (&W)[8])
                       ((Eh & m) | ((Oh << 4) & ~m)) ^ flip, (((Eh >> 4) & m) | (Oh & ~m)) ^ flip);
 }
 
+// C_g of the integer operand (the layout above) from sum X, S and 2^-e
+template <int BITS>
+__device__ inline float q_int_C(float sx, float S, float inv)
+{
+    constexpr float mid = BITS == 4 ? 7.5f : 1.5f;
+    return -fmaf(8.f - mid, sx, mid * (S * inv));
+}
+
 struct OpOr {
     __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; }
 };
@@ -417,21 +430,36 @@ __device__ inline void prep_group(const float* __restrict__ v, int G, int vec, i
     const float val = v[(long long)vec * G * 64 + g * 64 + lane] * scale;
     const float amax = wave_max(fabsf(val));
     const float S = wave_sum(val);
-    if constexpr (BITS == 4) {
-        // lane = column: its digit word, OR-ed into the planes of its 8-column uint4
+    if constexpr (BITS == 4 || BITS == 2) {
+        // lane = column: its digit word, OR-ed into the planes of its uint4
         const int e = q4_exponent(amax);
         const float inv = exp2i_f(-e);
         const uint32_t U = q4_bits(val, inv) & 0xFFFFu, V = U ^ 0x8888u;
-        const int sh = 4 * (lane & 7);
-        uint32_t pl[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pl[j] = group_reduce(((V >> (4 * j)) & 0xFu) << sh, OpOr(), 8);
-        if ((lane & 7) == 0)
-            q[(long long)vec * 8 * G + (lane >> 3) * G + g] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
         const float sx = wave_sum((float)((int)U - 0x8888));  // sum of X, exact (|sum| <= 2^20)
         // a group with a non-finite value gets a NaN scale, so its dot products are NaN
         const float sc = (amax <= 3.4e38f) ? exp2i_f(e) : __builtin_nanf("");
-        if (lane == 0) st[(long long)vec * G + g] = make_float4(-fmaf(0.5f, sx, 7.5f * (S * inv)), S, sc, 0.f);
+        if (lane == 0) st[(long long)vec * G + g] = make_float4(q_int_C<BITS>(sx, S, inv), S, sc, 0.f);
+        uint4* qv = q + (long long)vec * 8 * G + g;
+        if constexpr (BITS == 4) {
+            const int sh = 4 * (lane & 7);
+            uint32_t pl[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pl[j] = group_reduce(((V >> (4 * j)) & 0xFu) << sh, OpOr(), 8);
+            if ((lane & 7) == 0) qv[(lane >> 3) * G] = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+        } else {
+            const int sh = 4 * ((lane & 15) >> 1), t = lane & 1;
+            uint32_t pl[2][4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t nib = ((V >> (4 * j)) & 0xFu) << sh;
+                pl[0][j] = group_reduce(t ? 0u : nib, OpOr(), 16);
+                pl[1][j] = group_reduce(t ? nib : 0u, OpOr(), 16);
+            }
+            if ((lane & 15) == 0) {
+                qv[(2 * (lane >> 4)) * G] = make_uint4(pl[0][0], pl[0][1], pl[0][2], pl[0][3]);
+                qv[(2 * (lane >> 4) + 1) * G] = make_uint4(pl[1][0], pl[1][1], pl[1][2], pl[1][3]);
+            }
+        }
         return;
     }
     int e = 0;
@@ -449,7 +477,7 @@ __device__ inline void prep_group(const float* __restrict__ v, int G, int vec, i
     // midpoint times the group's fp16 rounding error, so that the kernels compute
     // sum (q - mid) v_h + mid * sum v: the rounding errors of v then meet only
     // zero-mean code offsets and do not add up coherently across rows.
-    constexpr float mid = BITS == 3 ? 3.5f : 1.5f;
+    constexpr float mid = 3.5f;
     const float off = wave_sum((float)vh * pair_class_inv(BITS, p));
     const float rnd = wave_sum((float)vh - vs);  // exact per lane
     const float C = fmaf(off, 1024.f, mid * rnd);

@@ -680,31 +680,46 @@ __device__ inline void h_item_stage(const HItem& H, int G, int it, int n_items, 
     const int sl = sg / G, g = sg - sl * G;
     float m = fmaxf(absmax8(H.v[0], H.v[1]), absmax8(H.v[2], H.v[3]));
     m = group_reduce(m, OpMax(), 4);
-    if constexpr (BITS == 4) {
+    if constexpr (BITS == 4 || BITS == 2) {
         const int e = q4_exponent(m);
         const float inv = exp2i_f(-e);
-        float sx = 0.f, sum = 0.f;
+        // the item's 16 values in natural column order per output uint4: 4-bit, the
+        // pair-layout uint4 j hold columns 0 4 1 5 2 6 3 7 of their 8; 2-bit, the two
+        // hold columns 0 8 1 9 2 10 3 11 and 4 12 5 13 6 14 7 15 of the item's 16, and
+        // the outputs are the even and the odd columns
+        const float4 v0 = H.v[0], v1 = H.v[1], v2 = H.v[2], v3 = H.v[3];
+        float c[2][8];
+        if constexpr (BITS == 4) {
+            const float a[2][8] = {{v0.x, v0.z, v1.x, v1.z, v0.y, v0.w, v1.y, v1.w},
+                                   {v2.x, v2.z, v3.x, v3.z, v2.y, v2.w, v3.y, v3.w}};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i >> 3][i & 7] = a[i >> 3][i & 7];
+        } else {
+            const float a[2][8] = {{v0.x, v1.x, v2.x, v3.x, v0.y, v1.y, v2.y, v3.y},
+                                   {v0.z, v1.z, v2.z, v3.z, v0.w, v1.w, v2.w, v3.w}};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) c[i >> 3][i & 7] = a[i >> 3][i & 7];
+        }
+        float sx = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-            // the 8 values of pair-layout uint4 j hold columns 0 4 1 5 2 6 3 7 of its 8
-            const float4 a = H.v[2 * jj], b = H.v[2 * jj + 1];
-            const float c[8] = {a.x, a.z, b.x, b.z, a.y, a.w, b.y, b.w};
             uint32_t W[8], su = 0u;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                W[i] = q4_bits(c[i], inv);
+                W[i] = q4_bits(c[jj][i], inv);
                 su += W[i];
             }
             sx += (float)(int)(su - 8u * (Q4_HIGH + 0x8888u));  // sum of the 8 X, mod 2^32 exact
-            sum += ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
             if (ok) lds[sl * pair_slot + (2 * part + jj) * G + g] = digit_planes(W);
         }
+        float sum = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w)) +
+                    (((v2.x + v2.y) + (v2.z + v2.w)) + ((v3.x + v3.y) + (v3.z + v3.w)));
         sx = group_reduce(sx, OpAdd(), 4);
         sum = group_reduce(sum, OpAdd(), 4);
         if (ok && part == 0) {
             const float sc = (m <= 3.4e38f) ? exp2i_f(e) : __builtin_nanf("");
             lds[stat_base + sl * stat_slot + g] =
-                __builtin_bit_cast(uint4, make_float4(-fmaf(0.5f, sx, 7.5f * (sum * inv)), sum, sc, 0.f));
+                __builtin_bit_cast(uint4, make_float4(q_int_C<BITS>(sx, sum, inv), sum, sc, 0.f));
         }
         return;
     }
