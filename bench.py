@@ -243,6 +243,13 @@ def _median(v):
     return v[len(v) // 2]
 
 
+def expert_dtype(c):
+    """The type the expert arithmetic multiplies in: one token's 4- and 2-bit codes as signed 4-bit
+    integers against 4-bit digits of the token (v_dot8, int32 sums); 3-bit codes and the batched
+    matrix cores as exact fp16 (fp32 sums)."""
+    return "i4" if c["B"] == 1 and c["bits"] in (2, 4) else "f16"
+
+
 def _workload_name(name, c, n_copies, n_distinct, stack):
     return "%s: H=%d I=%d E=%d+1 shared K=%d %d-bit group %d bf16 scale+bias, B=%d%s%s" % (
         name, c["H"], c["I"], c["E"], c["K"], c["bits"], c.get("group", 64), c["B"],
@@ -735,7 +742,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",  # fp16 x fp16 products (codes turned exactly into fp16), fp32 accumulation
+        "dtype": expert_dtype(c),
         "data": "synthetic",
         "config": {"workload": r["config"], "global_batch": B, "rotation_copies": r["rotation_copies"],
                    "timing": r["timing"] + (" (median of %d replays, GPU events)" % args.replays
