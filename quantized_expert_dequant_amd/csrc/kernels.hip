@@ -503,6 +503,14 @@ struct FfnArgs {
     float* hq;             // h in fp32, pair-layout order: [B*(K+1)][8][Gi][8]
     float* y;
     int sc;                // down: slots per LDS round
+    // tiered residency, filled inside the gate/up launch (k_gateup_fill): the cache
+    // plan (count, then (expert, slot) pairs of this call's misses), the store of
+    // records in host memory, and the extra blocks that copy the records' scale/bias
+    // and down part
+    const int32_t* fill_plan;
+    const uint8_t* fill_src;
+    int fill_cap;     // most entries the plan holds (<= 64)
+    int fill_blocks;
 };
 
 template <int BITS>
@@ -868,18 +876,17 @@ __global__ __launch_bounds__(256) void k_down(FfnArgs A)
 constexpr int FAST_NL = 8;  // fast path: E <= 512 logits per token, 8 per lane
 
 constexpr int GUF_WAVES = 8;  // fast gate/up: waves per block
+constexpr long long FILL_CHUNK = 64 * 1024;  // bytes of a missed record per extra fill block
 constexpr int GUF_XQ = (64 * 9 + 64 * GUF_WAVES - 1) / (64 * GUF_WAVES);  // operand uint4 per thread (G <= 64)
 
 // One (row pass, expert slot) per wave, blocks in slot-major order: the shared
 // expert's blocks (slot 0) come first and need no routing; a routed block's wave
 // 0 selects its expert while the block stages the token's operand.
 // Many small waves per SIMD overlap one another's loads and dequant arithmetic.
-template <int BITS, int KS, bool ROUTE>
-__global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
+template <int BITS, int KS, bool ROUTE, bool FILL>
+__device__ __forceinline__ void gateup_fast(const FfnArgs& A, uint4* __restrict__ xs, int& s_id, int& s_src)
 {
     constexpr int K = KS - 1;
-    __shared__ uint4 xs[64 * 9];  // the token's operand: 8 uint4 of pairs + stats per group (G <= 64)
-    __shared__ int s_id;          // a routed block's expert
     const Layout& L = A.L;
     const int b = blockIdx.y;
     const int G = L.Gh, LPR = lanes_per_row(G), RPP = 64 / LPR;
@@ -892,6 +899,24 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
     // block groups: the shared expert's first, then the routed experts from the
     // last rank to the first, so that the blocks dispatched last need the fewest
     // selection rounds (a block selects only up to its own rank)
+    if (FILL && (int)blockIdx.x >= KS * bps) {
+        // extra blocks: copy chunk c of the scale/bias and down part of each missed
+        // record (the routed blocks write its gate/up codes), token 0's grid row only
+        if (blockIdx.y != 0) return;
+        const int c = blockIdx.x - KS * bps;
+        const long long part = L.record - L.off_gu_sb;
+        const int nch = (int)((part + FILL_CHUNK - 1) / FILL_CHUNK);
+        const int i = c / nch, ch = c - i * nch;
+        if (i >= A.fill_plan[0]) return;
+        const int e = A.fill_plan[1 + 2 * i], sl = A.fill_plan[2 + 2 * i];
+        if (sl < 0) return;
+        const long long lo = L.off_gu_sb + (long long)ch * FILL_CHUNK;
+        const long long hi = lo + FILL_CHUNK < L.record ? lo + FILL_CHUNK : L.record;
+        const uint4* from = reinterpret_cast<const uint4*>(A.fill_src + (long long)e * L.record);
+        uint4* to = reinterpret_cast<uint4*>(const_cast<uint8_t*>(A.slab) + (long long)sl * L.record);
+        for (long long o = lo / 16 + threadIdx.x; o < hi / 16; o += 64 * GUF_WAVES) to[o] = from[o];
+        return;
+    }
     const int sg = blockIdx.x / bps;
     const int slot = (sg > 0) ? KS - sg : 0;  // 0: shared expert, k + 1: routed expert of rank k
     const int r = ((blockIdx.x - sg * bps) * GUF_WAVES + wave) * RPP + sub;
@@ -903,11 +928,18 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
     //    a routed block's wave 0 the routing inputs, every thread a share of the operand
     double lv[FAST_NL];
     int my_id = 0;
+    int f_n = 0, f_e = 0, f_s = -1;  // FILL: the plan's count and lane l's miss (expert, slot)
     if (slot > 0 && wave == 0) {
         if (ROUTE)
             topk_load<FAST_NL>(A.logits + (long long)b * A.E, A.E, lane, lv);
         else
             my_id = A.idx[(long long)b * K + min(lane, K - 1)];
+        if (FILL) {  // at most 64 misses (the launcher's condition), read with the routing
+            const int l = min(lane, A.fill_cap - 1);
+            f_n = A.fill_plan[0];
+            f_e = A.fill_plan[1 + 2 * l];
+            f_s = A.fill_plan[2 + 2 * l];
+        }
     }
     const int nx = G * 9;  // uint4 of pairs ([8][G]) then stats ([G])
     uint4 xv[GUF_XQ];
@@ -920,8 +952,7 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
     __builtin_amdgcn_sched_barrier(0);
 
     SlotRegs<BITS> R;
-    auto issue = [&](int e) {
-        const uint8_t* rec = A.slab + (long long)e * L.record;
+    auto issue = [&](const uint8_t* rec) {
         const uint8_t* base = rec + (long long)rc * 2 * L.hb;
         R.g0 = ld16(base + g * 16);
         R.u0 = ld16(base + L.hb + g * 16);
@@ -935,7 +966,7 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
         R.sb = *reinterpret_cast<const uint2*>(rec + L.off_gu_sb + ((long long)rc * L.Sh + (g >> L.gs)) * 8);
     };
     // 2. the shared expert needs no routing: its loads go out now
-    if (slot == 0) issue(A.E);
+    if (slot == 0) issue(A.slab + (long long)A.E * L.record);
     __builtin_amdgcn_sched_barrier(0);
     // 3. stage the token's operand; wave 0 of a routed block selects its expert meanwhile
 #pragma unroll
@@ -958,15 +989,21 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
             }
             id = __builtin_amdgcn_readlane(my_id, slot - 1);
         }
+        if (FILL) {  // a slot filled by this call: its record comes from the store, by expert
+            const unsigned long long m = __ballot(lane < f_n && f_s == id);
+            if (lane == 0) s_src = m ? __builtin_amdgcn_readlane(f_e, __builtin_ctzll(m)) : -1;
+        }
         if (lane == 0) s_id = id;
     }
     __syncthreads();
     // 4. a routed block's loads (an invalid id reads expert 0 and yields NaN)
     bool bad = false;
+    int src = -1;
     if (slot > 0) {
         const int e = s_id;
         bad = (e < 0 || e >= A.E);
-        issue(bad ? 0 : e);
+        if (FILL && !bad) src = s_src;
+        issue((FILL && src >= 0) ? A.fill_src + (long long)src * L.record : A.slab + (long long)(bad ? 0 : e) * L.record);
     }
     __builtin_amdgcn_sched_barrier(0);
     uint4 xp[8];
@@ -994,6 +1031,40 @@ __global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
         }
         A.hq[((long long)b * KS + k) * L.Gi * 64 + ((long long)(pp >> 2) * L.Gi + grp) * 8 + (pp & 3) * 2 + hi] = h;
     }
+    if (FILL && src >= 0) {  // the codes this wave read from the store go into the slot
+        uint8_t* base = const_cast<uint8_t*>(A.slab) + (long long)s_id * L.record + (long long)rc * 2 * L.hb;
+        *reinterpret_cast<uint4*>(base + g * 16) = R.g0;
+        *reinterpret_cast<uint4*>(base + L.hb + g * 16) = R.u0;
+        if (BITS == 4) {
+            *reinterpret_cast<uint4*>(base + (G + g) * 16) = R.g1;
+            *reinterpret_cast<uint4*>(base + L.hb + (G + g) * 16) = R.u1;
+        } else if (BITS == 3) {
+            *reinterpret_cast<uint2*>(base + 16 * G + 8 * g) = make_uint2(R.g1.x, R.g1.y);
+            *reinterpret_cast<uint2*>(base + L.hb + 16 * G + 8 * g) = make_uint2(R.u1.x, R.u1.y);
+        }
+    }
+}
+
+template <int BITS, int KS, bool ROUTE>
+__global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fast(FfnArgs A)
+{
+    __shared__ uint4 xs[64 * 9];  // the token's operand: 8 uint4 of pairs + stats per group (G <= 64)
+    __shared__ int s_id;          // a routed block's expert
+    int unused = -1;
+    gateup_fast<BITS, KS, ROUTE, false>(A, xs, s_id, unused);
+}
+
+// The cached decode's gate/up: routing given as slot ids, and the records this
+// call's plan brings in are filled inside the launch.  A routed block whose slot
+// was just assigned reads its rows from the store in host memory and writes the
+// codes into the slot; extra blocks after the gate/up blocks copy the rest of
+// each missed record, so the down launch finds the records whole.
+template <int BITS, int KS>
+__global__ __launch_bounds__(64 * GUF_WAVES) void k_gateup_fill(FfnArgs A)
+{
+    __shared__ uint4 xs[64 * 9];
+    __shared__ int s_id, s_src;
+    gateup_fast<BITS, KS, false, true>(A, xs, s_id, s_src);
 }
 
 constexpr int DNF_WAVES = 4;  // fast down: waves per block
@@ -1087,7 +1158,10 @@ int down_slots_per_round(const Layout& L)
 template <int BITS, int KS>
 void launch_fast_ks(bool route, dim3 fg, dim3 fd, size_t flds, const FfnArgs& A, hipStream_t s, Timing tg, Timing td)
 {
-    if (route)
+    if (A.fill_plan)
+        hipExtLaunchKernelGGL((k_gateup_fill<BITS, KS>), dim3(fg.x + A.fill_blocks, fg.y), dim3(64 * GUF_WAVES), 0, s,
+                              tg.start, tg.stop, 0, A);
+    else if (route)
         hipExtLaunchKernelGGL((k_gateup_fast<BITS, KS, true>), fg, dim3(64 * GUF_WAVES), 0, s, tg.start, tg.stop, 0, A);
     else
         hipExtLaunchKernelGGL((k_gateup_fast<BITS, KS, false>), fg, dim3(64 * GUF_WAVES), 0, s, tg.start, tg.stop, 0,
@@ -1108,11 +1182,27 @@ void launch_fast(int KS, bool route, dim3 fg, dim3 fd, size_t flds, const FfnArg
     }
 }
 
+// The single-token kernels apply (the fast path) and a cache plan of at most cap
+// entries fits the gate/up launch's fill (one entry per lane of a wave).
+static bool fast_path(const Layout& L, int K, int E)
+{
+    const int KS = K + 1;
+    return L.Gh <= 64 && L.Gi <= 64 && KS * 8 * L.Gi <= 1024 && E <= 64 * FAST_NL &&
+           (KS == 2 || KS == 3 || KS == 5 || KS == 7 || KS == 9);
+}
+
+bool ffn_fills_cache(const Layout& L, int K, int E, int cap) { return fast_path(L, K, E) && cap >= 1 && cap <= 64; }
+
 void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4* xst, const double* logits,
                 int renorm, int32_t* idx, float* w, int B, int K, int E, float shared_w, void* hq, float* y,
-                hipStream_t s, Timing t_gateup, Timing t_down)
+                hipStream_t s, Timing t_gateup, Timing t_down, const int32_t* fill_plan, const void* fill_src,
+                int fill_cap)
 {
     FfnArgs A;
+    A.fill_plan = fill_plan;
+    A.fill_src = (const uint8_t*)fill_src;
+    A.fill_cap = fill_cap;
+    A.fill_blocks = fill_plan ? fill_cap * (int)((L.record - L.off_gu_sb + FILL_CHUNK - 1) / FILL_CHUNK) : 0;
     A.slab = (const uint8_t*)slab;
     A.L = L;
     A.xq = xq;
@@ -1131,9 +1221,7 @@ void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4
     const int drows = 4 * DN_RPW * (64 / lanes_per_row(L.Gi));
     const dim3 ggrid((L.I + grows - 1) / grows, B), dgrid((L.H + drows - 1) / drows, B);
     const int KS = K + 1;
-    const bool fast = L.Gh <= 64 && L.Gi <= 64 && KS * 8 * L.Gi <= 1024 && E <= 64 * FAST_NL &&
-                      (KS == 2 || KS == 3 || KS == 5 || KS == 7 || KS == 9);
-    if (fast) {
+    if (fast_path(L, K, E)) {
         const int grows = GUF_WAVES * (64 / lanes_per_row(L.Gh));
         const dim3 fg(KS * ((L.I + grows - 1) / grows), B);
         const int frows = DNF_WAVES * (64 / lanes_per_row(L.Gi));

@@ -24,7 +24,11 @@ void launch_router(int bits, const float* x, int B, const float* W, const float*
 void launch_topk(const double* logits, int B, int E, int K, int renorm, int32_t* idx, float* w, hipStream_t s);
 void launch_ffn(const Layout& L, const void* slab, const uint4* xq, const float4* xst, const double* logits,
                 int renorm, int32_t* idx, float* w, int B, int K, int E, float shared_w, void* hq, float* y,
-                hipStream_t s, Timing t_gateup = Timing(), Timing t_down = Timing());
+                hipStream_t s, Timing t_gateup = Timing(), Timing t_down = Timing(),
+                const int32_t* fill_plan = nullptr, const void* fill_src = nullptr, int fill_cap = 0);
+// fill_plan (a cache plan of at most fill_cap entries) fills the missed records inside the
+// gate/up launch, from the store at fill_src; only where ffn_fills_cache says so
+bool ffn_fills_cache(const Layout& L, int K, int E, int cap);
 void launch_rmsnorm(const float* y, int B, int H, float eps, float* x, hipStream_t s);
 // the attention half of a decode step (attention.hip)
 void launch_gdn_step(int n_heads, int dk, int dv, float* S, const float* q, const float* k, const float* v,

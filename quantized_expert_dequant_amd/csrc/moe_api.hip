@@ -645,7 +645,11 @@ int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* 
     const bool plan_routes = !grouped && B <= CP_ROUTE_MAX_B;
     launch_cache_plan(idx, B * K, E, S, cache->state, idx_slot, plan, L.record, desc->expert_flags, slot_flags,
                       plan_routes ? W.logits : nullptr, K, renorm, w, s);
-    launch_cache_copy(plan, std::min(E, B * K), src, cache->slab, L.record, s);
+    // the single-token kernels fill the missed records inside their gate/up launch;
+    // otherwise a copy launch brings them in first
+    const int cap = std::min(E, B * K);
+    const bool fill = !grouped && ffn_fills_cache(L, K, S, cap);
+    if (!fill) launch_cache_copy(plan, cap, src, cache->slab, L.record, s);
     // 3. the expert FFNs on the cache, by slot id (the shared expert at slot S)
     if (grouped) {
         launch_group(idx_slot, B, K, S, gemv_tokens(L), slot_flags, W.gw.g, s);
@@ -653,7 +657,7 @@ int moe_layer_decode_cached(const moe_layer_desc* desc, const moe_expert_cache* 
                            g_timing[KID_GATEUP], g_timing[KID_DOWN]);
     } else {
         launch_ffn(L, cache->slab, W.xq, W.xst, nullptr, 0, idx_slot, w, B, K, S, desc->shared_weight, W.hq, y_out,
-                   s, g_timing[KID_GATEUP], g_timing[KID_DOWN]);
+                   s, g_timing[KID_GATEUP], g_timing[KID_DOWN], fill ? plan : nullptr, src, cap);
     }
     return hip_status(fn);
 }
