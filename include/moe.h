@@ -278,8 +278,11 @@ int moe_layer_decode_noalloc(const moe_layer_desc* desc, const float* x, int B, 
  * HBM cache.  Each cached decode routes on the GPU, maps the selected experts onto
  * slots (a hit refreshes its slot; each miss evicts the least recently used slot
  * that the call does not use, ties to the lowest slot, misses taken in ascending
- * expert id), copies the missing records from the store with a GPU kernel that reads
- * the host memory directly, and runs the expert FFNs on the cache.  Nothing waits
+ * expert id), brings the missing records in from the store with GPU code that reads
+ * the host memory directly (for one token, or per-token batches of at most 64
+ * (token, expert) pairs, inside the gate/up launch, whose blocks of a missed expert
+ * read its rows from the store; otherwise a copy launch first), and runs the expert
+ * FFNs on the cache.  Nothing waits
  * on the host, so a call can be captured in a HIP graph.
  *   slab:  device, (slots + 1) records of moe_expert_record_bytes; the last holds
  *          the shared expert.
