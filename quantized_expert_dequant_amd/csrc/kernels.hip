@@ -9,7 +9,8 @@
 // Per-token path ([LLMAPIS] section 深度分析: route, read, dequantize, compute,
 // combine):
 //   k_router  logits (fp32 products accumulated in fp64); also preps the token:
-//             fp16 pairs + per-group stats, the operand of the folded dequant
+//             integer digit planes (4- and 2-bit) or fp16 pairs (3-bit) + per-group
+//             stats, the operand of the folded dequant
 //             (scale*x and bias*x per group, the FMA rearrangement described in
 //             [LLMAPIS] section 深度分析, applied per 64-column unit)
 //   k_gateup  softmax / top-K per wave, then the fused gate/up dequant-GEMV +
@@ -281,7 +282,8 @@ void launch_dequant(const Layout& L, const void* rec, float* W, hipStream_t s)
 }
 
 // ----------------------------------------------------------------------------
-// prep of the token activations: fp32 [B][H] -> fp16 pairs + per-group stats.
+// prep of the token activations: fp32 [B][H] -> the operand of the code width
+// (integer digit planes or fp16 pairs, common.h) + per-group stats.
 // One wave per (token, group); shared by the standalone prep kernel and the
 // router kernel, which preps the token while it computes the logits.
 // ----------------------------------------------------------------------------
@@ -333,7 +335,7 @@ void launch_prep(int bits, const float* v, int n_vec, int len, uint4* q, float4*
 // ----------------------------------------------------------------------------
 
 // logits[b][e] = W_r[e] . x[b] (+ bias[e]); one wave per expert.  The token's
-// dequant operand (fp16 pairs + stats) is prepared by the same launch.
+// dequant operand (digit planes or fp16 pairs, + stats) is prepared by the same launch.
 __device__ inline double dot4d(float4 w, float4 x, double acc)
 {
     acc = fma((double)w.x, (double)x.x, acc);
@@ -655,7 +657,7 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs A)
 // pair: the pair-layout uint4 j = 2*part and 2*part + 1 of that group, 16 fp32
 // values of h.  The group's four items scale it by a power of two taken from
 // the group's largest |h|, store it in the operand format of the code width
-// (4-bit: digit planes; 2- and 3-bit: fp16 pairs) and derive the group's stats
+// (4- and 2-bit: digit planes; 3-bit: fp16 pairs) and derive the group's stats
 // (C, S, scale) in one pass: a group whose h is tiny keeps its relative precision.
 // pairs: uint4 (s, j, g) at pair_base + s * pair_slot + j * G + g
 // stats: uint4 (s, g) at stat_base + s * stat_slot + g
@@ -761,7 +763,7 @@ __device__ inline void h_item_stage(const HItem& H, int G, int it, int n_items, 
 // block owns output rows of one token for every active expert.  It fetches
 // the token's h (fp32, cache-resident) first, then issues its weight loads,
 // scales each expert's h by a power of two from its largest |h|, stages it in
-// LDS as fp16 pairs and derives each group's stats there while the weights
+// LDS in the operand format of the code width and derives each group's stats there while the weights
 // stream in, and writes y = sum_k w_k Wd_k h_k + shared_weight * Wd_s h_s.
 // ----------------------------------------------------------------------------
 constexpr int DN_HREG = 4;  // pair-layout uint4 of h staged per thread per round
@@ -1126,7 +1128,7 @@ __global__ __launch_bounds__(64 * DNF_WAVES) void k_down_fast(FfnArgs A)
         issue(k, bad ? 0 : e);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // 3. scale h per group, stage it as fp16 pairs and derive each group's stats
+    // 3. scale h per group, stage it in the operand format and derive each group's stats
     //    while the weights stream in
     uint4* lst = lds + n;
     h_item_stage<BITS>(hi0, G, threadIdx.x, n_items, lds, 8 * G, n, G);
