@@ -18,12 +18,12 @@
 //   k_topk_slices    sums the H-slice partials in a fixed order, then softmax / top-K;
 //                    blocks beside the selecting ones write the token operands
 //   k_group          stable counting sort of the assignments + the MFMA work list
-//   k_prep_tokens    token activations -> fp16 MFMA operands + chunk sums (+ dot2 operands)
+//   k_prep_tokens    token activations -> fp16 MFMA operands + chunk sums (+ GEMV operands)
 //   k_grouped_mfma   gate/up (+ SwiGLU) or down dequant-GEMM over (group, 128 rows, K chunk)
 //   k_fixup          SwiGLU of gate/up tiles whose K chunks two blocks shared
-//   k_gemv_gateup    gate/up (+ SwiGLU) of the small groups as dot2 GEMVs
+//   k_gemv_gateup    gate/up (+ SwiGLU) of the small groups as integer (v_dot8) GEMVs
 //   k_hconvert       h of every entry -> fp16 with the entry's power-of-two scale + group stats
-//   k_gemv_down      down of the small groups as dot2 GEMVs
+//   k_gemv_down      down of the small groups as fp16 (v_dot2) GEMVs
 //   k_combine        per-token routing-weighted sum of the down outputs
 #include <hip/hip_ext.h>
 
@@ -43,7 +43,7 @@ constexpr int GM_GROUP = 32;         // most tokens of one MFMA work-list group
 #ifndef MOE_GV_TOKENS
 #define MOE_GV_TOKENS 2
 #endif
-constexpr int GV_TOKENS = MOE_GV_TOKENS;  // an expert with fewer tokens than this runs as a dot2 GEMV group
+constexpr int GV_TOKENS = MOE_GV_TOKENS;  // an expert with fewer tokens than this runs as a GEMV group
 constexpr int GV_GROUP = 2;  // most tokens of one GEMV group of an expert flagged as out of the matrix cores' range
 // most tokens of any GEMV group when experts below gv_t tokens run as GEMV groups
 __host__ __device__ constexpr int gv_max_tokens(int gv_t) { return gv_t - 1 > GV_GROUP ? gv_t - 1 : GV_GROUP; }
@@ -157,10 +157,10 @@ __global__ __launch_bounds__(256) void k_router_tiled(const float* __restrict__ 
 // added in slice order, then the bias (a fixed order, so they do not depend on
 // the launch); they go to LDS and wave 0 selects the top-K.  Beside them, when
 // the FFNs need token operands: block (t, 1) writes token t's MFMA operand and
-// chunk sums (as k_prep_tokens), blocks (t, y >= 2) its dot2 operand for the GEMV
+// chunk sums (as k_prep_tokens), blocks (t, y >= 2) its GEMV operand for the GEMV
 // groups, one wave per group.  The selecting blocks alone would hold 64 CUs.
 constexpr int TS_CHUNK = 16;       // slice loads in flight per thread
-constexpr int TS_DOT2_BLOCKS = 4;  // blocks per token writing the dot2 operand
+constexpr int TS_GEMV_BLOCKS = 4;  // blocks per token writing the GEMV operand
 
 __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ partial, int nslice,
                                                      const float* __restrict__ bias, int B, int E, int K, int renorm,
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(512) void k_topk_slices(const double* __restrict__ 
         for (int c = tid; c < P.H; c += 512) token_operand(xt, c, inv, G, out, P.xsum + (long long)b * 2 * G);
         return;
     }
-    if (blockIdx.y >= 2) {  // the dot2 operand of the GEMV groups
+    if (blockIdx.y >= 2) {  // the operand of the GEMV groups
         const int G = P.H / 64, step = 8 * (gridDim.y - 2);
         for (int g = (blockIdx.y - 2) * 8 + wave; g < G; g += step) prep_group<4>(P.x, G, b, g, lane, P.xq, P.xst);
         return;
@@ -231,7 +231,7 @@ void launch_route_batched(const float* x, int B, const float* W, const float* bi
     TokenPrep Q = P;
     Q.x = x;
     Q.H = H;
-    const int ny = 1 + (P.xh ? 1 + (P.xq ? TS_DOT2_BLOCKS : 0) : 0);  // selection, MFMA operand, dot2 operand
+    const int ny = 1 + (P.xh ? 1 + (P.xq ? TS_GEMV_BLOCKS : 0) : 0);  // selection, MFMA operand, GEMV operand
     hipLaunchKernelGGL(k_topk_slices, dim3(B, ny), dim3(512), 0, s, partial, router_splits(H), bias, B, E, K, renorm,
                        idx, w, Q);
 }
@@ -410,10 +410,10 @@ void launch_expert_ranges(const Layout& L, const void* slab, int n, int32_t* fla
 // order, and the chunk sums) when the caller brings the routing.
 // ----------------------------------------------------------------------------
 
-// Blocks (t, y >= 1) write token t's dot2 operand instead (fp16 pairs with a
-// per-group scale + group stats, as the single-token kernels take it) for the
-// GEMV groups, one wave per group.
-constexpr int PT_DOT2_BLOCKS = 4;
+// Blocks (t, y >= 1) write token t's GEMV operand instead (the single-token
+// kernels' 4-bit operand: digit planes of a per-group fixed point + group stats)
+// for the GEMV groups, one wave per group.
+constexpr int PT_GEMV_BLOCKS = 4;
 
 __global__ __launch_bounds__(256) void k_prep_tokens(const float* __restrict__ x, int H, uint4* __restrict__ xh,
                                                      uint2* __restrict__ xsum, float* __restrict__ xscale,
@@ -1085,11 +1085,13 @@ __global__ __launch_bounds__(256) void k_hconvert(const float* __restrict__ hb, 
 }
 
 // ----------------------------------------------------------------------------
-// Small groups (fewer than GV_TOKENS tokens): dot2 GEMVs, each weight row read
-// once, its fp16 code patterns built once and multiplied by every token of the
-// group; the matrix cores would pad such a group to 16 tokens.  Same operand
-// formats and group fold as the single-token kernels (xq / xst for x, the
-// scaled fp16 pairs + stats for h).  Work items (group, block of rows) are cut
+// Small groups (fewer than GV_TOKENS tokens): GEMVs, each weight row read once
+// and multiplied by every token of the group; the matrix cores would pad such a
+// group to 16 tokens.  Gate/up takes the single-token kernels' integer operand
+// (xq / xst: digit planes, v_dot8 against the codes as signed nibbles); down
+// takes the fp16 h the matrix cores also read, with the codes as exact fp16
+// patterns (v_dot2) and the stats k_hconvert writes.  The group fold is the
+// single-token kernels'.  Work items (group, block of rows) are cut
 // into equal contiguous ranges, one per block.
 // ----------------------------------------------------------------------------
 constexpr int GV_WAVES = 4;
@@ -1411,7 +1413,7 @@ void launch_ffn_grouped(const Layout& L, const void* slab, const GroupedWork& W,
     const bool gv = gv_t > 1;
 
     if (!prepped)
-        hipLaunchKernelGGL(k_prep_tokens, dim3(B, gv ? 1 + PT_DOT2_BLOCKS : 1), dim3(256), 0, s, x, L.H, W.xh,
+        hipLaunchKernelGGL(k_prep_tokens, dim3(B, gv ? 1 + PT_GEMV_BLOCKS : 1), dim3(256), 0, s, x, L.H, W.xh,
                            W.xsum, W.xscale, xq, xst);
     GroupedArgs A;
     A.slab = (const uint8_t*)slab;
