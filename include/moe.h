@@ -386,7 +386,7 @@ int moe_set_timing_events(int kernel, void* start_event, void* stop_event);
  *   [3] K chunks per gate/up tile when tiles outnumber the blocks of [1] (the
  *       partial sums of a tile shared by two blocks are added in K order)
  *   [4] blocks of the down matrix-core launch   [5] tiles per group, down
- *   [6] experts with fewer tokens than this run as dot2 GEMV groups
+ *   [6] experts with fewer tokens than this run as GEMV groups (not on the matrix cores)
  *   [7] most tokens of one matrix-core work-list group
  */
 int moe_grouped_launch_info(const moe_layer_desc* desc, int B, int32_t* info_out);
